@@ -1,0 +1,296 @@
+"""Float64 numpy oracle of the SSA forward pass (test infrastructure only).
+
+Page references: "Direct3D-S2 page" is the hyper.ai summary of arXiv
+2505.17412; "LSRM page" is the article on LSRM (Meta Reality Labs / NVIDIA).
+
+Readings taken where the pages are silent (each listed in the design notes):
+
+* Blocks and windows are aligned to the grid origin and do not overlap; a block
+  is the set of tokens of one sequence inside one m_cmp^3 cell, a window the
+  set inside one m_win^3 cell (Direct3D-S2 page, "Method": blocks follow 3D
+  coordinates; windows are non-overlapping).
+* Compression is the plain mean over the block's occupied tokens; the learned
+  sparse convolution before it is not part of this path.  The mean is rounded
+  once to the input dtype (the compressed keys/values are tokens of that
+  dtype).
+* Block numbering: ascending hierarchical key (sequence, window in C order,
+  sub-block in C order inside the window).  Ties in the top-k go to the lower
+  block number.
+* Selection score of block j for query t and KV group g: the softmax
+  probability of j in the compressed branch, summed over the query heads of g.
+  k_eff = min(k, blocks in the sequence).  No block is forced, no causality.
+* Softmax scale 1/sqrt(D) in every branch.  Gates are used as given, in the
+  order (compressed, selected, window).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# dtype rounding (the only rounding the method applies: the pooled blocks, and
+# the final output, are values of the input dtype)
+# ----------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range; below the
+    normal range its spacing is the fixed subnormal step 2^-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)                      # x = mant * 2^expo, 0.5 <= |mant| < 1
+    expo = np.maximum(expo, -125)                 # spacing of bf16 below 2^-126 is 2^-133
+    step_exp = expo - 8                           # 8 significant bits
+    return np.ldexp(np.rint(np.ldexp(x, -step_exp)), step_exp)
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# Integer stage: block keys, stable sort, segments
+# ----------------------------------------------------------------------------
+
+def _log2_exact(v: int) -> int:
+    if v <= 0 or v & (v - 1):
+        raise ValueError(f"{v} is not a power of two")
+    return v.bit_length() - 1
+
+
+def block_keys(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int):
+    """Hierarchical block key of every token (input order), plus validity.
+
+    key = ((seq * Rw^3 + lin(w)) * r^3 + lin(s)) with w = floor(c / m_win),
+    s = floor(c / m_cmp) mod r, Rw = R / m_win, r = m_win / m_cmp and
+    lin(x, y, z) = (x * n + y) * n + z.  Sorting by this key groups tokens by
+    sequence, then window, then block (Direct3D-S2 page, "Method": blocking by
+    3D coordinate; non-overlapping windows).
+    """
+    coords = np.asarray(coords, dtype=np.int64).reshape(-1, 3)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = coords.shape[0]
+    if m_win % m_cmp:
+        raise ValueError("m_win must be a multiple of m_cmp")
+    Rw = grid_res // m_win
+    r = m_win // m_cmp
+    seq = np.zeros(n, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        seq[cu[b]:cu[b + 1]] = b
+    valid = np.all((coords >= 0) & (coords < grid_res), axis=1)
+    w = coords // m_win
+    s = (coords // m_cmp) % r
+    lin_w = (w[:, 0] * Rw + w[:, 1]) * Rw + w[:, 2]
+    lin_s = (s[:, 0] * r + s[:, 1]) * r + s[:, 2]
+    key = (seq * Rw ** 3 + lin_w) * r ** 3 + lin_s
+    return key, valid
+
+
+@dataclasses.dataclass
+class Blocks:
+    perm: np.ndarray         # sorted position -> input token index
+    key_sorted: np.ndarray   # block key at each sorted position
+    blk_off: np.ndarray      # [nb + 1] first sorted position of each block
+    win_off: np.ndarray      # [nw + 1] first sorted position of each window
+    win_blk_off: np.ndarray  # [nw + 1] first block id of each window
+    seq_blk_off: np.ndarray  # [B + 1] first block id of each sequence
+    seq_win_off: np.ndarray  # [B + 1] first window id of each sequence
+    n_invalid: int
+    r3: int                  # sub-blocks per window (r^3)
+
+    @property
+    def nb(self) -> int:
+        return len(self.blk_off) - 1
+
+    @property
+    def nw(self) -> int:
+        return len(self.win_off) - 1
+
+
+def build_blocks(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int) -> Blocks:
+    """Stable sort of tokens by block key and the CSR segments over it."""
+    key, valid = block_keys(coords, cu_seqlens, grid_res, m_cmp, m_win)
+    n = len(key)
+    r3 = (m_win // m_cmp) ** 3
+    perm = np.argsort(key, kind="stable")
+    ks = key[perm]
+    wk = ks // r3
+    new_blk = np.ones(n, dtype=bool)
+    new_win = np.ones(n, dtype=bool)
+    if n:
+        new_blk[1:] = ks[1:] != ks[:-1]
+        new_win[1:] = wk[1:] != wk[:-1]
+    blk_start = np.nonzero(new_blk)[0]
+    win_start = np.nonzero(new_win)[0]
+    blk_off = np.append(blk_start, n)
+    win_off = np.append(win_start, n)
+    blk_id_of_pos = np.cumsum(new_blk) - 1
+    win_blk_off = np.append(blk_id_of_pos[win_start], len(blk_start))
+    # sequence of each block / window (the key's top part)
+    Rw3 = (grid_res // m_win) ** 3
+    seq_of_blk = ks[blk_start] // (Rw3 * r3)
+    seq_of_win = ks[win_start] // (Rw3 * r3)
+    B = len(cu_seqlens) - 1
+    seq_blk_off = np.searchsorted(seq_of_blk, np.arange(B + 1), side="left")
+    seq_win_off = np.searchsorted(seq_of_win, np.arange(B + 1), side="left")
+    return Blocks(perm=perm, key_sorted=ks, blk_off=blk_off, win_off=win_off,
+                  win_blk_off=win_blk_off, seq_blk_off=seq_blk_off,
+                  seq_win_off=seq_win_off, n_invalid=int((~valid).sum()), r3=r3)
+
+
+def token_window_and_seq(blocks: Blocks):
+    """For every sorted position: its window id and sequence id."""
+    n = len(blocks.perm)
+    win_of_pos = np.zeros(n, dtype=np.int64)
+    for w in range(blocks.nw):
+        win_of_pos[blocks.win_off[w]:blocks.win_off[w + 1]] = w
+    seq_of_win = np.zeros(blocks.nw, dtype=np.int64)
+    for b in range(len(blocks.seq_win_off) - 1):
+        seq_of_win[blocks.seq_win_off[b]:blocks.seq_win_off[b + 1]] = b
+    return win_of_pos, seq_of_win[win_of_pos] if n else win_of_pos
+
+
+# ----------------------------------------------------------------------------
+# Compression: mean pooling of keys/values per block
+# ----------------------------------------------------------------------------
+
+def pool_blocks(x, blocks: Blocks, dtype: str) -> np.ndarray:
+    """Mean of x over each block's tokens, rounded once to ``dtype``.
+
+    x: [N, H, D] in input order.  Returns [nb, H, D] float64 holding values of
+    ``dtype`` (Direct3D-S2 page, "Method": mean pooling gives block-level
+    compressed keys and values; LSRM page, "Stage 2": AvgPool inside a block).
+    """
+    x = np.asarray(x)
+    out = np.zeros((blocks.nb,) + x.shape[1:], dtype=np.float64)
+    for j in range(blocks.nb):
+        toks = blocks.perm[blocks.blk_off[j]:blocks.blk_off[j + 1]]
+        out[j] = np.asarray(x[toks], dtype=np.float64).sum(axis=0) / len(toks)
+    return round_to(out, dtype)
+
+
+# ----------------------------------------------------------------------------
+# Attention pieces
+# ----------------------------------------------------------------------------
+
+def softmax_attention(q, k, v, scale: float):
+    """Softmax attention of one query q [D] over keys k [n, D], values v [n, D].
+
+    Returns (o [D], p [n]).  The maximum is subtracted before exponentiation.
+    """
+    s = scale * (k @ q)
+    s = s - s.max()
+    e = np.exp(s)
+    p = e / e.sum()
+    return p @ v, p
+
+
+def topk_blocks(score, k: int):
+    """Indices of the k largest scores, largest first; ties to the lower index."""
+    score = np.asarray(score, dtype=np.float64)
+    k_eff = min(k, len(score))
+    order = np.lexsort((np.arange(len(score)), -score))  # primary: -score, secondary: index
+    return order[:k_eff]
+
+
+# ----------------------------------------------------------------------------
+# Full forward
+# ----------------------------------------------------------------------------
+
+def _token_rows(blocks: Blocks, t_sorted: int):
+    """(sequence, window) of the token at sorted position ``t_sorted``."""
+    w = int(np.searchsorted(blocks.win_off, t_sorted, side="right") - 1)
+    b = int(np.searchsorted(blocks.seq_win_off, w, side="right") - 1)
+    return b, w
+
+
+def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=False):
+    """SSA output for selected (input token index, query head) pairs.
+
+    ``wl`` carries q/k/v/gates (float arrays), head counts, topk and dtype.
+    Returns a dict with ``out`` [len(rows), D] (rounded to the dtype), the
+    per-branch outputs (float64), and ``topk`` [len(rows), k] (-1 padded) for
+    the KV group of each row.
+    """
+    H, Hkv, D, K = wl.h_q, wl.h_kv, wl.head_dim, wl.topk
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(D)
+    if kbar is None:
+        kbar = pool_blocks(wl.k, blocks, wl.dtype)
+    if vbar is None:
+        vbar = pool_blocks(wl.v, blocks, wl.dtype)
+    pos_of_tok = np.empty(len(blocks.perm), dtype=np.int64)
+    pos_of_tok[blocks.perm] = np.arange(len(blocks.perm))
+
+    def f64(a):
+        return np.asarray(a, dtype=np.float64)
+
+    out = np.zeros((len(rows), D))
+    o_c = np.zeros((len(rows), D))
+    o_s = np.zeros((len(rows), D))
+    o_w = np.zeros((len(rows), D))
+    sel = -np.ones((len(rows), K), dtype=np.int64)
+    for n_row, (t, h) in enumerate(rows):
+        i = int(pos_of_tok[t])
+        b, w = _token_rows(blocks, i)
+        g = h // G
+        j0, j1 = int(blocks.seq_blk_off[b]), int(blocks.seq_blk_off[b + 1])
+        # (a) compressed attention over the sequence's blocks, for every head of
+        # the group (the selection score sums their probabilities)
+        score = np.zeros(j1 - j0)
+        for hh in range(g * G, (g + 1) * G):
+            o_hh, p_hh = softmax_attention(f64(wl.q[t, hh]), kbar[j0:j1, g], vbar[j0:j1, g], scale)
+            score += p_hh
+            if hh == h:
+                o_cmp = o_hh
+        # (b) top-k blocks; attention over all their tokens
+        chosen = topk_blocks(score, K)
+        sel[n_row, :len(chosen)] = chosen + j0
+        pos = np.concatenate([np.arange(blocks.blk_off[j0 + c], blocks.blk_off[j0 + c + 1])
+                              for c in chosen])
+        toks = blocks.perm[pos]
+        o_sel, _ = softmax_attention(f64(wl.q[t, h]), f64(wl.k[toks, g]), f64(wl.v[toks, g]), scale)
+        # (c) attention inside the token's window
+        toks = blocks.perm[blocks.win_off[w]:blocks.win_off[w + 1]]
+        o_win, _ = softmax_attention(f64(wl.q[t, h]), f64(wl.k[toks, g]), f64(wl.v[toks, g]), scale)
+        gt = f64(wl.gates[t, h])
+        o_c[n_row], o_s[n_row], o_w[n_row] = o_cmp, o_sel, o_win
+        out[n_row] = gt[0] * o_cmp + gt[1] * o_sel + gt[2] * o_win
+    res = dict(out=round_to(out, wl.dtype), out_exact=out, topk=sel)
+    if with_branches:
+        res.update(o_cmp=o_c, o_sel=o_s, o_win=o_w)
+    return res
+
+
+def forward(wl, blocks: Blocks | None = None, with_branches=False):
+    """Full SSA forward for every token and head (small inputs only).
+
+    Returns dict: out [N, H, D] (dtype-rounded, float64), topk [N, Hkv, k]
+    (block ids, -1 padded; identical for all heads of a group), kbar, vbar,
+    and optionally the per-branch outputs.
+    """
+    if blocks is None:
+        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    kbar = pool_blocks(wl.k, blocks, wl.dtype)
+    vbar = pool_blocks(wl.v, blocks, wl.dtype)
+    N, H, Hkv = wl.n_tokens, wl.h_q, wl.h_kv
+    G = H // Hkv
+    rows = [(t, h) for t in range(N) for h in range(H)]
+    res = forward_rows(wl, blocks, rows, kbar=kbar, vbar=vbar, with_branches=with_branches)
+    D = wl.head_dim
+    full = dict(out=res["out"].reshape(N, H, D), out_exact=res["out_exact"].reshape(N, H, D),
+                kbar=kbar, vbar=vbar, blocks=blocks)
+    full["topk"] = res["topk"].reshape(N, H, -1)[:, ::G, :]
+    if with_branches:
+        for name in ("o_cmp", "o_sel", "o_win"):
+            full[name] = res[name].reshape(N, H, D)
+    return full
