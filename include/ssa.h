@@ -1,0 +1,166 @@
+/*
+ * ssa.h - C ABI of the MI355X (gfx950) Spatial Sparse Attention library.
+ *
+ * Spatial Sparse Attention (SSA) is the attention of Direct3D-S2's sparse
+ * diffusion transformer over the variable-length tokens of a sparse voxel grid
+ * (hyper.ai summary of arXiv 2505.17412, "Method", second paragraph):
+ *   - tokens are grouped by their 3D coordinate into m_cmp^3 blocks (not by
+ *     their 1D index) and into non-overlapping m_win^3 windows;
+ *   - compression: keys and values are mean-pooled per block, and every query
+ *     attends to all compressed blocks of its sequence;
+ *   - selection: the query-to-block attention scores pick the top-k blocks and
+ *     the query attends to every token inside them;
+ *   - window: the query attends to every token of its own window;
+ *   - the three results are summed with per-token, per-head gates.
+ * Grouped-query attention (several query heads sharing one key/value head,
+ * LSRM article, "Stage 1": 32 query heads over 2 key/value heads) shares the
+ * selection across the heads of a group: the block score is the softmax
+ * probability summed over the group's query heads.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, caller-allocated and
+ *     caller-owned; the library allocates nothing and keeps no state between
+ *     calls.  Tensors are dense row-major, 16-byte aligned.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t, NULL = default
+ *     stream).  SSA_OK means "validated and enqueued"; only ssa_build_blocks
+ *     with sync_counts != 0 blocks the host.
+ *   - Arguments are validated before anything is enqueued; on an error no
+ *     output is touched and ssa_last_error() describes the problem.
+ *   - Calls are re-entrant; ssa_last_error() is thread-local.
+ */
+#ifndef SSA_H
+#define SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSA_OK = 0,
+  SSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad geometry, out-of-range coords (when synced) */
+  SSA_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (head_dim, top-k, key width) */
+  SSA_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than the *_workspace() query */
+  SSA_ERR_DEVICE = 4            /* a HIP runtime call or kernel launch failed */
+} ssa_status;
+
+typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+
+/* Grid and block geometry.  grid_res (R), m_cmp and m_win are powers of two
+ * with m_cmp <= m_win <= R <= 1024.  Blocks are the m_cmp^3 cells and windows
+ * the m_win^3 cells of the grid, both aligned to the origin. */
+typedef struct {
+  int32_t grid_res;
+  int32_t m_cmp;
+  int32_t m_win;
+} ssa_geometry;
+
+/* Device-side counters written by ssa_build_blocks (int32 each). */
+enum {
+  SSA_COUNT_NB = 0,          /* number of blocks                       */
+  SSA_COUNT_NW = 1,          /* number of windows                      */
+  SSA_COUNT_INVALID = 2,     /* tokens with a coordinate outside [0,R) */
+  SSA_COUNT_MAX_BLK = 3,     /* most tokens in one block               */
+  SSA_COUNT_MAX_WIN = 4,     /* most tokens in one window              */
+  SSA_COUNT_KEY_BITS = 5,    /* bits of the block key                  */
+  SSA_COUNTS = 8             /* length of the counts array             */
+};
+
+/* Result of the block build: the tokens' stable sort by block key and the CSR
+ * segments over the sorted order.  The block key of a token of sequence b at
+ * coordinate c is ((b * Rw^3 + lin(c / m_win)) * r^3 + lin((c / m_cmp) mod r))
+ * with Rw = R / m_win, r = m_win / m_cmp, lin(x,y,z) = (x*n + y)*n + z; block
+ * ids and window ids count up in that key order.  All arrays are DEVICE
+ * int32 buffers owned by the caller, with the capacities given. */
+typedef struct {
+  int32_t *perm;        /* [N]     sorted position -> input token index (stable: ties keep input order) */
+  int32_t *blk_off;     /* [N + 1] first sorted position of block j; blk_off[nb] = N                    */
+  int32_t *win_off;     /* [N + 1] first sorted position of window w; win_off[nw] = N                   */
+  int32_t *win_blk_off; /* [N + 1] first block id of window w; win_blk_off[nw] = nb                     */
+  int32_t *seq_blk_off; /* [B + 1] first block id of sequence b; seq_blk_off[B] = nb                    */
+  int32_t *seq_win_off; /* [B + 1] first window id of sequence b; seq_win_off[B] = nw                   */
+  int32_t *counts;      /* [SSA_COUNTS] device counters (see enum above)                                */
+  int64_t n_tokens;     /* N, filled by ssa_build_blocks                                               */
+  int32_t batch;        /* B, filled by ssa_build_blocks                                               */
+  int32_t nb, nw;       /* host copies of the counts when synced, else -1                              */
+  int32_t max_blk_tokens, max_win_tokens; /* host copies when synced, else -1                          */
+  ssa_geometry geo;     /* filled by ssa_build_blocks                                                  */
+} ssa_blocks;
+
+/* Attention layout.  h_q query heads over h_kv key/value heads (h_q % h_kv
+ * == 0; query head h uses key/value head h / (h_q / h_kv)).  head_dim D in
+ * {32, 64}.  1 <= topk <= 32.  scale <= 0 selects 1/sqrt(D).  q, k, v, gates
+ * and out all have `dtype`; accumulation is float32. */
+typedef struct {
+  int32_t h_q;
+  int32_t h_kv;
+  int32_t head_dim;
+  int32_t topk;
+  float scale;
+  ssa_dtype dtype;
+} ssa_attn;
+
+/* Workspace bytes ssa_build_blocks needs for N tokens in B sequences. */
+size_t ssa_build_blocks_workspace(int64_t n_tokens, int32_t batch, const ssa_geometry *geo);
+
+/* Group tokens into blocks and windows (Direct3D-S2 page, "Method": blocking
+ * by 3D coordinate; non-overlapping windows).
+ *   coords     [N, 3] int32 device, (x, y, z) per token in input order.
+ *   cu_seqlens [B + 1] int32 device, cu_seqlens[0] = 0, non-decreasing,
+ *              cu_seqlens[B] = N; sequence b owns tokens [cu[b], cu[b+1]).
+ *              Empty sequences are allowed.  Duplicate coordinates are
+ *              distinct tokens.
+ *   out        caller struct whose device pointers are set (capacities
+ *              above); the library fills n_tokens, batch, geo and, when
+ *              sync_counts != 0, nb / nw / max_*.
+ *   sync_counts  != 0: copy the counts to the host and wait; then a token
+ *              outside [0, R) gives SSA_ERR_INVALID_ARGUMENT.  == 0: fully
+ *              asynchronous; out-of-range tokens are clamped for memory
+ *              safety and counted in counts[SSA_COUNT_INVALID].
+ *   workspace  device scratch of at least ssa_build_blocks_workspace() bytes.
+ * Errors: INVALID_ARGUMENT (null pointers, N < 0, B < 1, bad geometry),
+ * UNSUPPORTED (block key wider than 32 bits), WORKSPACE, DEVICE. */
+ssa_status ssa_build_blocks(const int32_t *coords, const int32_t *cu_seqlens, int64_t n_tokens,
+                            int32_t batch, const ssa_geometry *geo, ssa_blocks *out,
+                            int sync_counts, void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* Workspace bytes ssa_forward needs for these blocks and this layout.  Uses
+ * blocks->nb when known (synced), else the worst case nb = N. */
+size_t ssa_forward_workspace(const ssa_blocks *blocks, const ssa_attn *attn);
+
+/* SSA forward pass (Direct3D-S2 page, "Method", second paragraph).
+ *   q      [N, h_q, D]  query per token (input order)
+ *   k, v   [N, h_kv, D] key / value per token
+ *   gates  [N, h_q, 3]  per-token, per-head gates in the order
+ *                       (compressed, selected, window); used as given
+ *   out    [N, h_q, D]  G0 * o_cmp + G1 * o_sel + G2 * o_win, rounded once
+ *   k_cmp, v_cmp  optional [nb, h_kv, D] mean-pooled keys / values (NULL = skip)
+ *   topk_idx      optional [N, h_kv, topk] int32 selected block ids per token
+ *                 and key/value group, highest score first, ties to the lower
+ *                 block id, -1 padded when the sequence has fewer blocks
+ *                 (NULL = skip)
+ *   workspace     device scratch of at least ssa_forward_workspace() bytes.
+ * Attention never crosses sequences; the selection is non-causal and forces
+ * no block.  Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim, topk, dtype
+ * combination), WORKSPACE, DEVICE. */
+ssa_status ssa_forward(const ssa_blocks *blocks, const ssa_attn *attn, const void *q,
+                       const void *k, const void *v, const void *gates, void *out,
+                       void *k_cmp, void *v_cmp, int32_t *topk_idx, void *workspace,
+                       size_t ws_bytes, void *hip_stream);
+
+/* Static text for a status code. */
+const char *ssa_status_string(ssa_status status);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char *ssa_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t ssa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H */

@@ -213,13 +213,16 @@ def _token_rows(blocks: Blocks, t_sorted: int):
     return b, w
 
 
-def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=False):
+def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=False,
+                 with_scores=False):
     """SSA output for selected (input token index, query head) pairs.
 
     ``wl`` carries q/k/v/gates (float arrays), head counts, topk and dtype.
     Returns a dict with ``out`` [len(rows), D] (rounded to the dtype), the
     per-branch outputs (float64), and ``topk`` [len(rows), k] (-1 padded) for
-    the KV group of each row.
+    the KV group of each row.  ``with_scores`` adds, per row, the selection
+    score of every block of the row's sequence (float64, sequence-local order)
+    and the sequence's first block id.
     """
     H, Hkv, D, K = wl.h_q, wl.h_kv, wl.head_dim, wl.topk
     G = H // Hkv
@@ -239,6 +242,7 @@ def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=F
     o_s = np.zeros((len(rows), D))
     o_w = np.zeros((len(rows), D))
     sel = -np.ones((len(rows), K), dtype=np.int64)
+    scores, firsts = [], []
     for n_row, (t, h) in enumerate(rows):
         i = int(pos_of_tok[t])
         b, w = _token_rows(blocks, i)
@@ -254,6 +258,9 @@ def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=F
                 o_cmp = o_hh
         # (b) top-k blocks; attention over all their tokens
         chosen = topk_blocks(score, K)
+        if with_scores:
+            scores.append(score)
+            firsts.append(j0)
         sel[n_row, :len(chosen)] = chosen + j0
         pos = np.concatenate([np.arange(blocks.blk_off[j0 + c], blocks.blk_off[j0 + c + 1])
                               for c in chosen])
@@ -268,6 +275,8 @@ def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=F
     res = dict(out=round_to(out, wl.dtype), out_exact=out, topk=sel)
     if with_branches:
         res.update(o_cmp=o_c, o_sel=o_s, o_win=o_w)
+    if with_scores:
+        res.update(scores=scores, first_block=firsts)
     return res
 
 

@@ -1,0 +1,234 @@
+// Host side of libssa: argument validation, workspace layout and launches.
+// Every check runs before anything is enqueued; the library allocates no
+// memory and keeps no state beyond the thread-local error message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ssa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssa_status fail(ssa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ssa_status ok() {
+  g_last_error.clear();
+  return SSA_OK;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << (l + 1)) <= v) ++l;
+  return l;
+}
+
+int ceil_log2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+ssa_status check_geometry(const ssa_geometry* geo) {
+  if (!geo) return fail(SSA_ERR_INVALID_ARGUMENT, "geometry is null");
+  if (!is_pow2(geo->grid_res) || !is_pow2(geo->m_cmp) || !is_pow2(geo->m_win))
+    return fail(SSA_ERR_INVALID_ARGUMENT, "grid_res (%d), m_cmp (%d) and m_win (%d) must be powers of two",
+                geo->grid_res, geo->m_cmp, geo->m_win);
+  if (geo->grid_res > 1024)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "grid_res %d exceeds 1024", geo->grid_res);
+  if (geo->m_cmp > geo->m_win || geo->m_win > geo->grid_res)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "need m_cmp <= m_win <= grid_res (got %d, %d, %d)",
+                geo->m_cmp, geo->m_win, geo->grid_res);
+  return SSA_OK;
+}
+
+ssa::KeyLayout key_layout(const ssa_geometry* geo, int32_t batch) {
+  ssa::KeyLayout kl;
+  kl.l_win = ilog2(geo->m_win);
+  kl.l_cmp = ilog2(geo->m_cmp);
+  kl.l_rw = ilog2(geo->grid_res) - kl.l_win;
+  kl.l_r = kl.l_win - kl.l_cmp;
+  kl.seq_bits = ceil_log2(batch);
+  kl.key_bits = kl.seq_bits + 3 * (kl.l_rw + kl.l_r);
+  kl.grid_res = geo->grid_res;
+  return kl;
+}
+
+ssa_status check_attn(const ssa_attn* a) {
+  if (!a) return fail(SSA_ERR_INVALID_ARGUMENT, "attn is null");
+  if (a->h_q < 1 || a->h_kv < 1 || a->h_q % a->h_kv)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "need h_q, h_kv >= 1 and h_q %% h_kv == 0 (got %d, %d)",
+                a->h_q, a->h_kv);
+  if (a->dtype != SSA_F32 && a->dtype != SSA_BF16)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(a->dtype));
+  if (a->head_dim < 1) return fail(SSA_ERR_INVALID_ARGUMENT, "head_dim %d < 1", a->head_dim);
+  if (a->topk < 1) return fail(SSA_ERR_INVALID_ARGUMENT, "topk %d < 1", a->topk);
+  if (a->head_dim != 32 && a->head_dim != 64)
+    return fail(SSA_ERR_UNSUPPORTED, "head_dim %d not supported (32 or 64)", a->head_dim);
+  if (a->topk > 32) return fail(SSA_ERR_UNSUPPORTED, "topk %d > 32 not supported", a->topk);
+  if (a->h_q / a->h_kv > 32)
+    return fail(SSA_ERR_UNSUPPORTED, "group size %d > 32 not supported", a->h_q / a->h_kv);
+  if (!isfinite(a->scale)) return fail(SSA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  return SSA_OK;
+}
+
+int elt_bytes(ssa_dtype d) { return d == SSA_BF16 ? 2 : 4; }
+
+int64_t nb_capacity(const ssa_blocks* b) { return b->nb >= 0 ? b->nb : b->n_tokens; }
+
+size_t forward_ws_bytes(const ssa_blocks* b, const ssa_attn* a) {
+  const int64_t cap = nb_capacity(b) > 0 ? nb_capacity(b) : 1;
+  size_t s = 0;
+  s += 2 * align256(static_cast<size_t>(elt_bytes(a->dtype)) * a->h_kv * cap * a->head_dim);  // kbar, vbar
+  s += align256(sizeof(int32_t) * static_cast<size_t>(b->n_tokens) * a->h_kv * a->topk);     // topk fallback
+  return s + 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssa_status_string(ssa_status s) {
+  switch (s) {
+    case SSA_OK: return "ok";
+    case SSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SSA_ERR_UNSUPPORTED: return "unsupported";
+    case SSA_ERR_WORKSPACE: return "workspace too small";
+    case SSA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* ssa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ssa_version(void) { return 100; }
+
+size_t ssa_build_blocks_workspace(int64_t n_tokens, int32_t batch, const ssa_geometry* /*geo*/) {
+  if (n_tokens < 0) return 0;
+  return ssa::build_workspace_bytes(n_tokens, batch);
+}
+
+ssa_status ssa_build_blocks(const int32_t* coords, const int32_t* cu_seqlens, int64_t n_tokens,
+                            int32_t batch, const ssa_geometry* geo, ssa_blocks* out,
+                            int sync_counts, void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (n_tokens < 0 || n_tokens > 0x7FFFFFFE)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "n_tokens %lld out of range", static_cast<long long>(n_tokens));
+  if (batch < 1) return fail(SSA_ERR_INVALID_ARGUMENT, "batch %d < 1", batch);
+  ssa_status st = check_geometry(geo);
+  if (st != SSA_OK) return st;
+  if (!out) return fail(SSA_ERR_INVALID_ARGUMENT, "out is null");
+  if (!cu_seqlens) return fail(SSA_ERR_INVALID_ARGUMENT, "cu_seqlens is null");
+  if (n_tokens > 0 && !coords) return fail(SSA_ERR_INVALID_ARGUMENT, "coords is null");
+  if (!out->perm || !out->blk_off || !out->win_off || !out->win_blk_off || !out->seq_blk_off ||
+      !out->seq_win_off || !out->counts)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "an output buffer of ssa_blocks is null");
+  const ssa::KeyLayout kl = key_layout(geo, batch);
+  if (kl.key_bits > 32)
+    return fail(SSA_ERR_UNSUPPORTED, "block key needs %d bits (> 32): batch %d, grid %d, m_cmp %d",
+                kl.key_bits, batch, geo->grid_res, geo->m_cmp);
+  const size_t need = ssa::build_workspace_bytes(n_tokens, batch);
+  if (!workspace || ws_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, need);
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  ssa::BuildWorkspace ws;
+  ssa::carve_build_workspace(workspace, n_tokens, &ws);
+  hipError_t e = ssa::launch_build(coords, cu_seqlens, static_cast<int32_t>(n_tokens), batch, kl, *out, ws, stream);
+  if (e != hipSuccess) return fail(SSA_ERR_DEVICE, "block build launch failed: %s", hipGetErrorString(e));
+  out->n_tokens = n_tokens;
+  out->batch = batch;
+  out->geo = *geo;
+  out->nb = out->nw = out->max_blk_tokens = out->max_win_tokens = -1;
+  if (sync_counts) {
+    int32_t h[SSA_COUNTS];
+    e = hipMemcpyAsync(h, out->counts, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(SSA_ERR_DEVICE, "reading block counts failed: %s", hipGetErrorString(e));
+    out->nb = h[SSA_COUNT_NB];
+    out->nw = h[SSA_COUNT_NW];
+    out->max_blk_tokens = h[SSA_COUNT_MAX_BLK];
+    out->max_win_tokens = h[SSA_COUNT_MAX_WIN];
+    if (h[SSA_COUNT_INVALID] > 0)
+      return fail(SSA_ERR_INVALID_ARGUMENT, "%d token(s) have a coordinate outside [0, %d)",
+                  h[SSA_COUNT_INVALID], geo->grid_res);
+  }
+  return ok();
+}
+
+size_t ssa_forward_workspace(const ssa_blocks* blocks, const ssa_attn* attn) {
+  if (!blocks || !attn || blocks->n_tokens < 0 || attn->h_kv < 1 || attn->head_dim < 1 || attn->topk < 1)
+    return 0;
+  return forward_ws_bytes(blocks, attn);
+}
+
+ssa_status ssa_forward(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                       const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
+                       int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
+  ssa_status st = check_attn(attn);
+  if (st != SSA_OK) return st;
+  if (blocks->n_tokens < 0 || blocks->n_tokens > 0x7FFFFFFE || blocks->batch < 1)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "blocks were not built (n_tokens %lld, batch %d)",
+                static_cast<long long>(blocks->n_tokens), blocks->batch);
+  if (!blocks->perm || !blocks->blk_off || !blocks->win_off || !blocks->seq_blk_off ||
+      !blocks->seq_win_off || !blocks->counts)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "a device buffer of blocks is null");
+  if (blocks->n_tokens > 0 && (!q || !k || !v || !gates || !out))
+    return fail(SSA_ERR_INVALID_ARGUMENT, "q, k, v, gates and out must be non-null");
+  const size_t need = forward_ws_bytes(blocks, attn);
+  if (!workspace || ws_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, need);
+  if (blocks->n_tokens == 0) return ok();
+
+  const int64_t cap = nb_capacity(blocks) > 0 ? nb_capacity(blocks) : 1;
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+  ssa::FwdParams p{};
+  p.perm = blocks->perm;
+  p.blk_off = blocks->blk_off;
+  p.win_off = blocks->win_off;
+  p.seq_blk_off = blocks->seq_blk_off;
+  p.seq_win_off = blocks->seq_win_off;
+  p.counts = blocks->counts;
+  p.n = static_cast<int32_t>(blocks->n_tokens);
+  p.batch = blocks->batch;
+  p.nb_cap = static_cast<int32_t>(cap);
+  p.h_q = attn->h_q;
+  p.h_kv = attn->h_kv;
+  p.d = attn->head_dim;
+  p.topk = attn->topk;
+  p.scale = attn->scale > 0.f ? attn->scale : 1.0f / sqrtf(static_cast<float>(attn->head_dim));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gates = gates;
+  p.out = out;
+  const size_t pooled = align256(static_cast<size_t>(elt_bytes(attn->dtype)) * attn->h_kv * cap * attn->head_dim);
+  p.kbar = w;
+  p.vbar = w + pooled;
+  p.k_cmp = k_cmp;
+  p.v_cmp = v_cmp;
+  p.topk_idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + 2 * pooled);
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = ssa::launch_pool(p, attn->dtype, stream);
+  if (e == hipSuccess) e = ssa::launch_generic(p, attn->dtype, stream);
+  if (e != hipSuccess) return fail(SSA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

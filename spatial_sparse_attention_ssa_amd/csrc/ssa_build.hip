@@ -1,0 +1,421 @@
+// Block build: block keys, stable LSD radix sort, CSR segments.
+//
+// Tokens are grouped by 3D coordinate into m_cmp^3 blocks and m_win^3
+// windows (Direct3D-S2 page, "Method": blocking follows the 3D coordinate,
+// windows do not overlap).  One 32-bit hierarchical key per token orders
+// tokens by (sequence, window cell, block cell); a stable sort on it yields
+// both partitions at once, with ties kept in input order.
+//
+// Sort design (gfx950, wave64): least-significant-digit radix sort, 8-bit
+// digits, three kernels per pass in the reduce-then-scan scheme of Merrill &
+// Grimshaw ("High Performance and Scalable Radix Sorting", 2011): per-tile
+// digit counts, one exclusive scan over (digit, tile), and a scatter in which
+// each wave ranks 64 keys at a time with eight ballots (lanes whose digit
+// bits all agree are peers; a key's rank is the number of peers in lower
+// lanes plus the wave's running count for that digit).
+#include "ssa_internal.h"
+
+namespace ssa {
+namespace {
+
+constexpr int kItems = kSortTile / 256;  // keys per thread per tile (16)
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ void init_counts_kernel(int32_t* counts, int32_t key_bits) {
+  const int i = threadIdx.x;
+  if (i < SSA_COUNTS) counts[i] = (i == SSA_COUNT_KEY_BITS) ? key_bits : 0;
+}
+
+// Offsets for an empty token set: every offset array holds zeros.
+__global__ void empty_offsets_kernel(int32_t batch, int32_t* blk_off, int32_t* win_off,
+                                     int32_t* win_blk_off, int32_t* seq_blk_off,
+                                     int32_t* seq_win_off) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) {
+    blk_off[0] = 0;
+    win_off[0] = 0;
+    win_blk_off[0] = 0;
+  }
+  if (i <= batch) {
+    seq_blk_off[i] = 0;
+    seq_win_off[i] = 0;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+keys_kernel(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, int32_t n,
+            int32_t batch, KeyLayout kl, uint32_t* __restrict__ keys, int32_t* __restrict__ vals,
+            int32_t* __restrict__ counts) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  // sequence b: the largest b < batch with cu[b] <= t (empty sequences skipped)
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  int c[3] = {coords[3 * t], coords[3 * t + 1], coords[3 * t + 2]};
+  bool bad = false;
+  for (int a = 0; a < 3; ++a) {
+    if (c[a] < 0 || c[a] >= kl.grid_res) {
+      bad = true;
+      c[a] = c[a] < 0 ? 0 : kl.grid_res - 1;  // clamp: keeps later stages in bounds
+    }
+  }
+  if (bad) atomicAdd(&counts[SSA_COUNT_INVALID], 1);
+  const uint32_t rmask = (1u << kl.l_r) - 1u;
+  uint64_t key = static_cast<uint64_t>(lo);
+  for (int a = 0; a < 3; ++a) key = (key << kl.l_rw) | static_cast<uint32_t>(c[a] >> kl.l_win);
+  for (int a = 0; a < 3; ++a) key = (key << kl.l_r) | (static_cast<uint32_t>(c[a] >> kl.l_cmp) & rmask);
+  keys[t] = static_cast<uint32_t>(key);
+  vals[t] = t;
+}
+
+__global__ void __launch_bounds__(256)
+radix_upsweep(const uint32_t* __restrict__ keys, int32_t n, int shift,
+              uint32_t* __restrict__ tile_hist, int ntiles) {
+  __shared__ uint32_t hist[256];
+  hist[threadIdx.x] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kSortTile;
+  for (int i = threadIdx.x; i < kSortTile; i += 256) {
+    const int p = base + i;
+    if (p < n) atomicAdd(&hist[(keys[p] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  tile_hist[threadIdx.x * ntiles + blockIdx.x] = hist[threadIdx.x];
+}
+
+// In-place exclusive scan of `m` uint32 values by one 1024-thread workgroup.
+__global__ void __launch_bounds__(1024) scan_exclusive_u32(uint32_t* __restrict__ data, int m) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (m + 1023) / 1024;
+  const int beg = min(tid * per, m), end = min(beg + per, m);
+  uint32_t s = 0;
+  for (int i = beg; i < end; ++i) s += data[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t run = tid ? part[tid - 1] : 0u;
+  for (int i = beg; i < end; ++i) {
+    const uint32_t v = data[i];
+    data[i] = run;
+    run += v;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+                uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t n,
+                int shift, const uint32_t* __restrict__ tile_off, int ntiles) {
+  __shared__ uint32_t whist[4][256];
+  __shared__ uint32_t wbase[4][256];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * 256; i += 256) (&whist[0][0])[i] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kSortTile + wave * (kSortTile / 4);
+  const uint64_t lt = lanemask_lt();
+  uint32_t kk[kItems], rk[kItems], dg[kItems];
+  int32_t vv[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int p = base + r * kWave + lane;
+    const bool valid = p < n;
+    const uint32_t key = valid ? keys_in[p] : 0u;
+    const int32_t val = valid ? vals_in[p] : 0;
+    const uint32_t d = (key >> shift) & 255u;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kRadixBits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint32_t before = whist[wave][d];
+    const uint32_t cnt = static_cast<uint32_t>(__popcll(peers));
+    const bool leader = valid && ((peers & lt) == 0);
+    // every lane of the wave has read its count before any leader writes
+    __builtin_amdgcn_wave_barrier();
+    if (leader) whist[wave][d] = before + cnt;
+    __builtin_amdgcn_wave_barrier();
+    kk[r] = key;
+    vv[r] = val;
+    rk[r] = before + static_cast<uint32_t>(__popcll(peers & lt));
+    dg[r] = d;
+  }
+  __syncthreads();
+  {
+    const int d = threadIdx.x;
+    uint32_t run = tile_off[d * ntiles + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wbase[w][d] = run;
+      run += whist[w][d];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int p = base + r * kWave + lane;
+    if (p < n) {
+      const uint32_t dst = wbase[wave][dg[r]] + rk[r];
+      keys_out[dst] = kk[r];
+      vals_out[dst] = vv[r];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+seg_count(const uint32_t* __restrict__ keys, int32_t n, int win_shift, int32_t* __restrict__ tile_cnt) {
+  __shared__ int32_t red[2][256];
+  const int base = blockIdx.x * kSortTile;
+  int cb = 0, cw = 0;
+  for (int i = threadIdx.x; i < kSortTile; i += 256) {
+    const int p = base + i;
+    if (p < n) {
+      const uint32_t k = keys[p];
+      if (p == 0) {
+        cb += 1;
+        cw += 1;
+      } else {
+        const uint32_t kp = keys[p - 1];
+        cb += (k != kp);
+        cw += ((k >> win_shift) != (kp >> win_shift));
+      }
+    }
+  }
+  red[0][threadIdx.x] = cb;
+  red[1][threadIdx.x] = cw;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + off];
+      red[1][threadIdx.x] += red[1][threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    tile_cnt[2 * blockIdx.x] = red[0][0];
+    tile_cnt[2 * blockIdx.x + 1] = red[1][0];
+  }
+}
+
+// Exclusive scan of the per-tile (block, window) start counts; totals go to
+// counts[NB] / counts[NW].
+__global__ void __launch_bounds__(1024)
+seg_scan(const int32_t* __restrict__ tile_cnt, int ntiles, int32_t* __restrict__ tile_base,
+         int32_t* __restrict__ counts) {
+  __shared__ int32_t part[2][1024];
+  const int tid = threadIdx.x;
+  const int per = (ntiles + 1023) / 1024;
+  const int beg = min(tid * per, ntiles), end = min(beg + per, ntiles);
+  int sb = 0, sw = 0;
+  for (int i = beg; i < end; ++i) {
+    sb += tile_cnt[2 * i];
+    sw += tile_cnt[2 * i + 1];
+  }
+  part[0][tid] = sb;
+  part[1][tid] = sw;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int vb = tid >= off ? part[0][tid - off] : 0;
+    const int vw = tid >= off ? part[1][tid - off] : 0;
+    __syncthreads();
+    part[0][tid] += vb;
+    part[1][tid] += vw;
+    __syncthreads();
+  }
+  int rb = tid ? part[0][tid - 1] : 0, rw = tid ? part[1][tid - 1] : 0;
+  for (int i = beg; i < end; ++i) {
+    const int vb = tile_cnt[2 * i], vw = tile_cnt[2 * i + 1];
+    tile_base[2 * i] = rb;
+    tile_base[2 * i + 1] = rw;
+    rb += vb;
+    rw += vw;
+  }
+  if (tid == 1023) {
+    counts[SSA_COUNT_NB] = part[0][1023];
+    counts[SSA_COUNT_NW] = part[1][1023];
+  }
+}
+
+__device__ __forceinline__ int seq_of(uint32_t key, int seq_shift) {
+  return seq_shift < 0 ? 0 : static_cast<int>(key >> seq_shift);
+}
+
+__global__ void __launch_bounds__(256)
+seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_shift,
+          int seq_shift, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ counts,
+          int32_t* __restrict__ blk_off, int32_t* __restrict__ win_off,
+          int32_t* __restrict__ win_blk_off, int32_t* __restrict__ seq_blk_off,
+          int32_t* __restrict__ seq_win_off) {
+  __shared__ int32_t wcnt[2][4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int base = blockIdx.x * kSortTile + wave * (kSortTile / 4);
+  const uint64_t lt = lanemask_lt();
+  int rb = 0, rw = 0;
+  int rank_b[kItems], rank_w[kItems];
+  uint32_t flags = 0;
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int p = base + r * kWave + lane;
+    const bool valid = p < n;
+    bool isb = false, isw = false;
+    if (valid) {
+      if (p == 0) {
+        isb = isw = true;
+      } else {
+        const uint32_t k = keys[p], kp = keys[p - 1];
+        isb = k != kp;
+        isw = (k >> win_shift) != (kp >> win_shift);
+      }
+    }
+    const uint64_t mb = __ballot(isb), mw = __ballot(isw);
+    rank_b[r] = rb + static_cast<int>(__popcll(mb & lt));
+    rank_w[r] = rw + static_cast<int>(__popcll(mw & lt));
+    rb += static_cast<int>(__popcll(mb));
+    rw += static_cast<int>(__popcll(mw));
+    flags |= (isb ? 1u : 0u) << (2 * r);
+    flags |= (isw ? 1u : 0u) << (2 * r + 1);
+  }
+  if (lane == 0) {
+    wcnt[0][wave] = rb;
+    wcnt[1][wave] = rw;
+  }
+  __syncthreads();
+  int pb = tile_base[2 * blockIdx.x], pw = tile_base[2 * blockIdx.x + 1];
+  for (int w = 0; w < wave; ++w) {
+    pb += wcnt[0][w];
+    pw += wcnt[1][w];
+  }
+  const int nb_tot = counts[SSA_COUNT_NB];
+  const int nw_tot = counts[SSA_COUNT_NW];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int p = base + r * kWave + lane;
+    if (p >= n) continue;
+    const bool isb = (flags >> (2 * r)) & 1u, isw = (flags >> (2 * r + 1)) & 1u;
+    const int bid = pb + rank_b[r];
+    if (isb) blk_off[bid] = p;
+    if (isw) {
+      const int wid = pw + rank_w[r];
+      win_off[wid] = p;
+      win_blk_off[wid] = bid;
+      const uint32_t k = keys[p];
+      const int s = seq_of(k, seq_shift);
+      const int sp = p ? seq_of(keys[p - 1], seq_shift) : -1;
+      for (int b = sp + 1; b <= s; ++b) {
+        seq_blk_off[b] = bid;
+        seq_win_off[b] = wid;
+      }
+    }
+    if (p == n - 1) {
+      const int s = seq_of(keys[p], seq_shift);
+      for (int b = s + 1; b <= batch; ++b) {
+        seq_blk_off[b] = nb_tot;
+        seq_win_off[b] = nw_tot;
+      }
+      blk_off[nb_tot] = n;
+      win_off[nw_tot] = n;
+      win_blk_off[nw_tot] = nb_tot;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+seg_stats(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ win_off,
+          int32_t* __restrict__ counts) {
+  const int nb = counts[SSA_COUNT_NB], nw = counts[SSA_COUNT_NW];
+  const int m = nb > nw ? nb : nw;
+  int mb = 0, mw = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < m; i += gridDim.x * blockDim.x) {
+    if (i < nb) mb = max(mb, blk_off[i + 1] - blk_off[i]);
+    if (i < nw) mw = max(mw, win_off[i + 1] - win_off[i]);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    mb = max(mb, __shfl_xor(mb, off));
+    mw = max(mw, __shfl_xor(mw, off));
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    atomicMax(&counts[SSA_COUNT_MAX_BLK], mb);
+    atomicMax(&counts[SSA_COUNT_MAX_WIN], mw);
+  }
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t build_workspace_bytes(int64_t n, int32_t /*batch*/) {
+  const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
+  size_t b = 0;
+  b += 2 * align256(sizeof(uint32_t) * n);     // keys_a, keys_b
+  b += align256(sizeof(int32_t) * n);          // vals_b
+  b += align256(sizeof(uint32_t) * 256 * ntiles);
+  b += 2 * align256(sizeof(int32_t) * 2 * ntiles);
+  return b + 256;
+}
+
+void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out) {
+  const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
+  char* p = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+  out->keys_a = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * n);
+  out->keys_b = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * n);
+  out->vals_b = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * n);
+  out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * 256 * ntiles);
+  out->tile_cnt = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * 2 * ntiles);
+  out->tile_base = reinterpret_cast<int32_t*>(p);
+}
+
+hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,
+                        const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
+                        hipStream_t stream) {
+  init_counts_kernel<<<1, 64, 0, stream>>>(out.counts, kl.key_bits);
+  if (n == 0) {
+    empty_offsets_kernel<<<(batch + 1 + 255) / 256, 256, 0, stream>>>(
+        batch, out.blk_off, out.win_off, out.win_blk_off, out.seq_blk_off, out.seq_win_off);
+    return hipGetLastError();
+  }
+  const int ntiles = (n + kSortTile - 1) / kSortTile;
+  const int passes = (kl.key_bits + kRadixBits - 1) / kRadixBits;
+  // ping-pong so that the last pass lands in (keys_a, perm)
+  uint32_t* kin = (passes % 2 == 0) ? ws.keys_a : ws.keys_b;
+  int32_t* vin = (passes % 2 == 0) ? out.perm : ws.vals_b;
+  uint32_t* kout = (passes % 2 == 0) ? ws.keys_b : ws.keys_a;
+  int32_t* vout = (passes % 2 == 0) ? ws.vals_b : out.perm;
+  keys_kernel<<<(n + 255) / 256, 256, 0, stream>>>(coords, cu_seqlens, n, batch, kl, kin, vin,
+                                                    out.counts);
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = pass * kRadixBits;
+    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, ws.tile_hist, ntiles);
+    scan_exclusive_u32<<<1, 1024, 0, stream>>>(ws.tile_hist, 256 * ntiles);
+    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, ws.tile_hist, ntiles);
+    uint32_t* tk = kin; kin = kout; kout = tk;
+    int32_t* tv = vin; vin = vout; vout = tv;
+  }
+  // sorted keys now in ws.keys_a, permutation in out.perm
+  const int win_shift = 3 * kl.l_r;
+  const int seq_shift = kl.seq_bits ? 3 * (kl.l_rw + kl.l_r) : -1;
+  seg_count<<<ntiles, 256, 0, stream>>>(ws.keys_a, n, win_shift, ws.tile_cnt);
+  seg_scan<<<1, 1024, 0, stream>>>(ws.tile_cnt, ntiles, ws.tile_base, out.counts);
+  seg_write<<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
+                                        out.counts, out.blk_off, out.win_off, out.win_blk_off,
+                                        out.seq_blk_off, out.seq_win_off);
+  const int sgrid = min((n + 255) / 256, 1024);
+  seg_stats<<<sgrid, 256, 0, stream>>>(out.blk_off, out.win_off, out.counts);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

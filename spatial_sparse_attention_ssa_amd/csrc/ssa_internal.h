@@ -1,0 +1,114 @@
+// Internal declarations shared by the HIP translation units of libssa.
+// gfx950 (CDNA4) only: wave64, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssa.h"
+
+namespace ssa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- numerics
+
+// Orders LDS traffic of one wave around a point where lanes exchange data
+// through LDS (a wave issues its LDS operations in order; this keeps the
+// compiler from moving memory operations across it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float32 -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two storage types: float, or bfloat16 carried as
+// its 16-bit pattern.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elt<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+// ---------------------------------------------------------------- block build
+
+// Bit layout of the block key (all fields are powers of two).
+struct KeyLayout {
+  int l_rw;      // log2(R / m_win): bits per axis of the window cell
+  int l_r;       // log2(m_win / m_cmp): bits per axis of the block cell inside a window
+  int l_win;     // log2(m_win)
+  int l_cmp;     // log2(m_cmp)
+  int seq_bits;  // ceil(log2(B))
+  int key_bits;  // seq_bits + 3 * (l_rw + l_r)
+  int grid_res;
+};
+
+struct BuildWorkspace {
+  uint32_t* keys_a;      // [N]
+  uint32_t* keys_b;      // [N]
+  int32_t* vals_b;       // [N]
+  uint32_t* tile_hist;   // [256 * ntiles]
+  int32_t* tile_cnt;     // [2 * ntiles]
+  int32_t* tile_base;    // [2 * ntiles]
+};
+
+constexpr int kSortTile = 4096;   // keys per workgroup tile (256 threads x 16)
+constexpr int kRadixBits = 8;
+
+size_t build_workspace_bytes(int64_t n, int32_t batch);
+void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out);
+
+hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,
+                        const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
+                        hipStream_t stream);
+
+// ---------------------------------------------------------------- forward
+
+struct FwdParams {
+  // blocks
+  const int32_t* perm;
+  const int32_t* blk_off;
+  const int32_t* win_off;
+  const int32_t* seq_blk_off;
+  const int32_t* seq_win_off;
+  const int32_t* counts;
+  int32_t n;         // tokens
+  int32_t batch;
+  int32_t nb_cap;    // row capacity of the internal pooled arrays
+  // layout
+  int32_t h_q, h_kv, d, topk;
+  float scale;
+  // tensors (input order)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gates;
+  void* out;
+  // pooled keys / values, internal layout [h_kv][nb_cap][D] in the input dtype
+  void* kbar;
+  void* vbar;
+  // optional public outputs
+  void* k_cmp;       // [nb][h_kv][D] or null
+  void* v_cmp;
+  int32_t* topk_idx; // [N][h_kv][topk]  (always valid: library workspace when the caller passes null)
+};
+
+hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_generic(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+
+}  // namespace ssa

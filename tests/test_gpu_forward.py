@@ -1,0 +1,146 @@
+"""GPU SSA forward vs the float64 oracle on the same seeded inputs.
+
+Small workloads (several query tiles, ragged tails, empty sequences) are
+compared element by element over every token and head.  The named workloads
+are run in full on the GPU and compared on sampled (token, head) rows that the
+oracle evaluates one by one; each branch is isolated with one-hot gates
+(Direct3D-S2 page, "Method", second paragraph; LSRM article, "Stage 1" for the
+grouped heads).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import _parity as P
+from workloads import make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_compare(wl, branches=True):
+    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    gb = P.gpu_build(wl)
+    P.check_build(gb, ob)
+    res = P.gpu_forward(wl, gb, return_topk=True, return_pooled=True)
+    N, H, Hkv = wl.n_tokens, wl.h_q, wl.h_kv
+    rows = [(t, h) for t in range(N) for h in range(H)]
+    ref = oracle.forward_rows(wl, ob, rows, with_branches=branches, with_scores=True)
+    got = P.host(res["out"]).reshape(N * H, -1)
+    mx, mean = P.check_outputs(got, ref["out"])
+    G = H // Hkv
+    gsel = res["topk"].cpu().numpy()[[t for t, _ in rows], [h // G for _, h in rows]]
+    agree, gap = P.check_topk(gsel, ref["topk"], ref["scores"], ref["first_block"])
+    kb = oracle.pool_blocks(wl.k, ob, wl.dtype)
+    vb = oracle.pool_blocks(wl.v, ob, wl.dtype)
+    _check_pooled(P.host(res["k_cmp"]), kb, wl.dtype)
+    _check_pooled(P.host(res["v_cmp"]), vb, wl.dtype)
+    if branches:
+        for i, name in enumerate(("o_cmp", "o_sel", "o_win")):
+            o = P.host(P.gpu_forward(wl, gb, gates=P.one_hot_gates(wl, i))).reshape(N * H, -1)
+            P.check_branch(o, ref[name], name)
+    print(f"N={N} H={H}/{Hkv}: max|err| {mx:.2e} mean|err| {mean:.2e} topk agree {agree:.5f} gap {gap:.1e}")
+
+
+def _check_pooled(got, ref, dtype):
+    if dtype == "f32":
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+        return
+    # bfloat16: at most one unit in the last place, almost always identical
+    ulp = np.abs(ref) * 2.0 ** -7 + 2.0 ** -133
+    diff = np.abs(got - ref)
+    assert (diff <= ulp).all(), f"pooled value off by more than 1 ulp: {diff.max():.3e}"
+    assert (diff == 0).mean() >= 0.9999, f"only {(diff == 0).mean():.6f} bit-identical"
+
+
+@pytest.mark.parametrize("case", [
+    dict(seqs=[1500, 0, 900], h_q=4, h_kv=4, head_dim=64, topk=16, dtype="bf16"),
+    dict(seqs=[2100], h_q=8, h_kv=2, head_dim=32, topk=8, dtype="bf16"),
+    dict(seqs=[700, 1300], h_q=2, h_kv=2, head_dim=32, topk=4, dtype="f32"),
+    dict(seqs=[333, 64, 1], h_q=2, h_kv=1, head_dim=64, topk=32, dtype="bf16"),
+])
+def test_small_full(case):
+    wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],
+                     h_kv=case["h_kv"], head_dim=case["head_dim"], dtype=case["dtype"], seed=21)
+    _full_compare(wl)
+
+
+def test_tiny_fp32_workload_full():
+    _full_compare(make_workload(1))
+
+
+def _sampled_compare(cfg, n_rows, branches=True):
+    wl = make_workload(cfg)
+    print(f"workload {cfg}: N={wl.n_tokens}", flush=True)
+    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    gb = P.gpu_build(wl)
+    P.check_build(gb, ob)
+    res = P.gpu_forward(wl, gb, return_topk=True)
+    rows = P.sample_rows(wl, n_rows, seed=cfg)
+    kbar = oracle.pool_blocks(wl.k, ob, wl.dtype)
+    vbar = oracle.pool_blocks(wl.v, ob, wl.dtype)
+    ref = oracle.forward_rows(wl, ob, rows, kbar=kbar, vbar=vbar, with_branches=branches,
+                              with_scores=True)
+    tt = torch.tensor([t for t, _ in rows], device=P.DEV)
+    hh = torch.tensor([h for _, h in rows], device=P.DEV)
+    got = P.host(res["out"][tt, hh])
+    mx, mean = P.check_outputs(got, ref["out"])
+    G = wl.h_q // wl.h_kv
+    gsel = res["topk"][tt, hh // G].cpu().numpy()
+    agree, gap = P.check_topk(gsel, ref["topk"], ref["scores"], ref["first_block"], min_agree=0.99)
+    if branches:
+        for i, name in enumerate(("o_cmp", "o_sel", "o_win")):
+            o = P.gpu_forward(wl, gb, gates=P.one_hot_gates(wl, i))
+            P.check_branch(P.host(o[tt, hh]), ref[name], name)
+    print(f"workload {cfg}: max|err| {mx:.2e} mean|err| {mean:.2e} topk agree {agree:.4f} gap {gap:.1e}")
+    return wl, gb, res
+
+
+def test_workload2_sampled():
+    _sampled_compare(2, 1500)
+
+
+def test_headline_workload3_sampled():
+    _sampled_compare(3, 400)
+
+
+def test_gqa_workload4_sampled():
+    _sampled_compare(4, 96)
+
+
+def test_varlen_workload5_sampled():
+    _sampled_compare(5, 256, branches=False)
+
+
+def test_zero_queries_pick_first_blocks():
+    wl = make_custom([1200, 500], grid_res=64, n_prims=3, topk=16, h_q=4, h_kv=2, head_dim=64,
+                     dtype="bf16", seed=31)
+    wl.q[:] = 0
+    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    gb = P.gpu_build(wl)
+    res = P.gpu_forward(wl, gb, return_topk=True)
+    sel = res["topk"].cpu().numpy()
+    for b in range(wl.batch):
+        j0, j1 = ob.seq_blk_off[b], ob.seq_blk_off[b + 1]
+        toks = ob.perm[ob.blk_off[j0]:ob.blk_off[j1]]
+        expect = np.arange(j0, min(j0 + 16, j1))
+        assert (sel[toks][:, :, :len(expect)] == expect).all()
+
+
+def test_dense_reduction():
+    # one window over the grid, voxel blocks, top-k covering every block:
+    # every branch is dense attention and out = (G0 + G1 + G2) * dense
+    rng = np.random.default_rng(3)
+    lin = rng.choice(16 ** 3, size=30, replace=False)
+    coords = np.stack(np.unravel_index(lin, (16,) * 3), -1)
+    wl = make_custom(None, coords=coords, grid_res=16, m_cmp=1, m_win=16, topk=32, h_q=2, h_kv=2,
+                     head_dim=32, dtype="f32", seed=3)
+    _full_compare(wl)
+
+
+def test_run_to_run_bit_identical():
+    wl = make_workload(2)
+    gb = P.gpu_build(wl)
+    a = P.gpu_forward(wl, gb, return_topk=True)
+    b = P.gpu_forward(wl, gb, return_topk=True)
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["topk"], b["topk"])
