@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""SSA forward throughput on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: the block
+build (keys, stable radix sort, segments) followed by the forward pass
+(pooling, compressed attention with top-k, selected-block attention, window
+attention, gated sum).  Inputs are resident in HBM before timing starts.
+
+Workload: 131072 surface-band voxel tokens of a seeded union of 12 primitives
+on a 1024^3 grid; 16 query / 16 key-value heads, head dim 64, bfloat16;
+m_cmp = 4, m_win = 8, top-k = 16 (the 128k-token setting of the Direct3D-S2
+summary page, "Experiments").
+
+Prints one JSON line (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+WORKLOAD_ID = 3
+
+
+def algorithmic_flops(wl, blocks, topk, torch):
+    """Sum over (token, head) of 4 * D * (blocks in its sequence + tokens in its
+    selected blocks + tokens in its window), with the actual sizes."""
+    dev = blocks.perm.device
+    h = blocks.trimmed()
+    blk_off = h["blk_off"].to(dev).long()
+    win_off = h["win_off"].to(dev).long()
+    seq_blk_off = h["seq_blk_off"].to(dev).long()
+    n = wl.n_tokens
+    cu = torch.as_tensor(wl.cu_seqlens, device=dev).long()
+    seq_of_tok = torch.bucketize(torch.arange(n, device=dev), cu[1:], right=True)
+    nb_seq = (seq_blk_off[1:] - seq_blk_off[:-1])[seq_of_tok].double()          # [N]
+    win_size = (win_off[1:] - win_off[:-1])
+    win_sizes_sorted = torch.repeat_interleave(win_size, win_size)
+    n_win = torch.empty(n, dtype=torch.long, device=dev)
+    n_win[blocks.perm.long()] = win_sizes_sorted
+    blk_size = blk_off[1:] - blk_off[:-1]
+    sel = topk.long()                                                           # [N, Hkv, k]
+    n_sel = torch.where(sel >= 0, blk_size[sel.clamp(min=0)], torch.zeros_like(sel)).sum(-1)  # [N, Hkv]
+    G = wl.h_q // wl.h_kv
+    D = wl.head_dim
+    f_cmp = 4.0 * D * wl.h_q * nb_seq.sum().item()
+    f_sel = 4.0 * D * G * n_sel.double().sum().item()
+    f_win = 4.0 * D * wl.h_q * n_win.double().sum().item()
+    return dict(cmp=f_cmp, sel=f_sel, win=f_win, total=f_cmp + f_sel + f_win,
+                mean_sel_tokens=n_sel.double().mean().item(), mean_win_tokens=n_win.double().mean().item(),
+                nb=int(h["counts"][0]), nw=int(h["counts"][1]))
+
+
+def cpu_baseline(wl, target_s: float):
+    """Time the oracle on a bounded sample of the same workload (test
+    infrastructure, single thread): the full block build and pooling once,
+    then sampled (token, head) rows, extrapolated to all rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+        kbar = oracle.pool_blocks(wl.k, ob, wl.dtype)
+        vbar = oracle.pool_blocks(wl.v, ob, wl.dtype)
+        t_fixed = time.perf_counter() - t0
+        rng = np.random.default_rng(7)
+        rows_done, t_rows = 0, 0.0
+        budget = max(target_s - t_fixed, 2.0)
+        while t_rows < budget:
+            rows = list(zip(rng.integers(0, wl.n_tokens, 16).tolist(), rng.integers(0, wl.h_q, 16).tolist()))
+            t1 = time.perf_counter()
+            oracle.forward_rows(wl, ob, rows, kbar=kbar, vbar=vbar)
+            t_rows += time.perf_counter() - t1
+            rows_done += len(rows)
+    per_row = t_rows / rows_done
+    t_step = t_fixed + per_row * wl.n_tokens * wl.h_q
+    return {
+        "value": wl.n_tokens / t_step,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle, one thread: full block build + pooling ({t_fixed:.1f} s), "
+                   f"then {rows_done} random (token, head) rows ({t_rows:.1f} s); per-step time "
+                   f"extrapolated to all {wl.n_tokens * wl.h_q} rows = {t_step:.0f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import spatial_sparse_attention_ssa_amd as ssa
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    wl = make_workload(WORKLOAD_ID)
+    bf = torch.bfloat16
+    up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    coords, cu = up(wl.coords, torch.int32), up(wl.cu_seqlens, torch.int32)
+    q, k, v, gates = up(wl.q, bf), up(wl.k, bf), up(wl.v, bf), up(wl.gates, bf)
+
+    # reference run for the work counts (untimed)
+    blocks0 = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=True)
+    res0 = ssa.forward(blocks0, q, k, v, gates, wl.topk, return_topk=True)
+    torch.cuda.synchronize()
+    work = algorithmic_flops(wl, blocks0, res0["topk"], torch)
+
+    # buffers for the timed loop: async build (nb unknown on the host)
+    blocks_async = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
+    ws_fwd = torch.empty(ssa.forward_workspace_bytes(blocks_async, q, k, wl.topk), dtype=torch.uint8,
+                         device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
+        ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (event), wall {wall_ms / args.steps:.3f} ms/step",
+          file=sys.stderr, flush=True)
+
+    # per-kernel times: HIP events recorded by the library around each kernel
+    # it launches on this stream (same kernels, same workspace)
+    stage_sum = {}
+    reps = max(3, min(args.steps, 10))
+    for _ in range(reps):
+        st = {}
+        b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
+        ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd, stage_times=st)
+        for name, ms in st.items():
+            stage_sum[name] = stage_sum.get(name, 0.0) + ms
+    stage_ms = {name: ms / reps for name, ms in stage_sum.items()}
+    # block build alone
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record()
+    for _ in range(reps):
+        ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
+    eb1.record()
+    torch.cuda.synchronize()
+    build_ms = eb0.elapsed_time(eb1) / reps
+
+    attn_names = [n for n in stage_ms if n != "pool_kernel"]
+    dom = max(attn_names, key=lambda n: stage_ms[n])
+    dom_flops = work["total"] if len(attn_names) == 1 else work.get("cmp")
+    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    n = wl.n_tokens
+    tflops = work["total"] / (ms_step * 1e-3) / 1e12
+
+    line = {
+        "metric": "SSA fwd tokens/s and TFLOP/s at 131072 voxel tokens; % bf16 MFMA peak",
+        "value": n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ssa-fwd-1024^3-12prims-131072tok-h16-d64-bf16", "n_tokens": n,
+                   "grid_res": wl.grid_res, "h_q": wl.h_q, "h_kv": wl.h_kv, "head_dim": wl.head_dim,
+                   "m_cmp": wl.m_cmp, "m_win": wl.m_win, "topk": wl.topk, "parallelism": "none"},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_tflop_per_step": work["total"] / 1e12,
+        "work": {k2: work[k2] for k2 in ("cmp", "sel", "win", "mean_sel_tokens", "mean_win_tokens", "nb", "nw")},
+        "build_ms": build_ms,
+        "stage_ms": stage_ms,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,6 +150,29 @@ ssa_status ssa_forward(const ssa_blocks *blocks, const ssa_attn *attn, const voi
                        void *k_cmp, void *v_cmp, int32_t *topk_idx, void *workspace,
                        size_t ws_bytes, void *hip_stream);
 
+/* Stages of ssa_forward, in launch order (indices into stage_ms below). */
+enum {
+  SSA_STAGE_POOL = 0,        /* mean pooling of keys / values                      */
+  SSA_STAGE_ATTN = 1,        /* attention branches (compressed + top-k, selected,   */
+                             /* window) and the gated sum                          */
+  SSA_STAGE_ATTN2 = 2,       /* a second attention kernel, when the plan has one    */
+  SSA_STAGE_ATTN3 = 3,       /* a third attention kernel, when the plan has one     */
+  SSA_STAGES = 8
+};
+
+/* Same as ssa_forward, but records a hipEvent on hip_stream around every
+ * kernel it launches, waits for the stream, and writes each stage's duration
+ * in milliseconds to stage_ms[0 .. SSA_STAGES) (0 for stages the plan does
+ * not launch).  For profiling and benchmarking; results are identical to
+ * ssa_forward.  *n_stages receives the number of stages launched. */
+ssa_status ssa_forward_timed(const ssa_blocks *blocks, const ssa_attn *attn, const void *q,
+                             const void *k, const void *v, const void *gates, void *out,
+                             void *k_cmp, void *v_cmp, int32_t *topk_idx, void *workspace,
+                             size_t ws_bytes, void *hip_stream, float *stage_ms, int32_t *n_stages);
+
+/* Name of the kernel that runs stage `stage` for this layout ("" if none). */
+const char *ssa_stage_name(const ssa_attn *attn, int32_t stage);
+
 /* Static text for a status code. */
 const char *ssa_status_string(ssa_status status);
 

@@ -133,12 +133,13 @@ def forward_workspace_bytes(blocks: Blocks, q, k, topk: int, scale=None) -> int:
 def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gates: torch.Tensor,
             topk: int, scale: float | None = None, return_pooled: bool = False,
             return_topk: bool = False, out: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None):
+            workspace: torch.Tensor | None = None, stage_times: dict | None = None):
     """SSA forward.  q [N, Hq, D], k/v [N, Hkv, D], gates [N, Hq, 3], all one dtype.
 
     Returns ``out`` [N, Hq, D]; with ``return_pooled`` / ``return_topk`` also
     the pooled keys/values [nb, Hkv, D] and the selected block ids
-    [N, Hkv, topk] in a dict.
+    [N, Hkv, topk] in a dict.  Passing a dict as ``stage_times`` runs the
+    timed variant (blocks until done) and fills it with {kernel name: ms}.
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("gates", gates)):
         if not t.is_cuda:
@@ -167,9 +168,16 @@ def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
     ws_bytes = int(L.ssa_forward_workspace(ctypes.byref(blocks.struct), ctypes.byref(a)))
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    B.check(L.ssa_forward(ctypes.byref(blocks.struct), ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v),
-                          _ptr(gates), _ptr(out), _ptr(kc), _ptr(vc), _ptr(tk), _ptr(workspace),
-                          ws_bytes, _stream(dev)))
+    args = (ctypes.byref(blocks.struct), ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(gates),
+            _ptr(out), _ptr(kc), _ptr(vc), _ptr(tk), _ptr(workspace), ws_bytes, _stream(dev))
+    if stage_times is None:
+        B.check(L.ssa_forward(*args))
+    else:
+        ms = (ctypes.c_float * B.SSA_STAGES)()
+        ns = ctypes.c_int32(0)
+        B.check(L.ssa_forward_timed(*args, ms, ctypes.byref(ns)))
+        for i in range(ns.value):
+            stage_times[L.ssa_stage_name(ctypes.byref(a), i).decode()] = float(ms[i])
     if not (return_pooled or return_topk):
         return out
     res = dict(out=out)

@@ -29,6 +29,7 @@ SSA_COUNT_MAX_BLK = 3
 SSA_COUNT_MAX_WIN = 4
 SSA_COUNT_KEY_BITS = 5
 SSA_COUNTS = 8
+SSA_STAGES = 8
 
 # every symbol include/ssa.h declares
 EXPORTED = (
@@ -36,6 +37,8 @@ EXPORTED = (
     "ssa_build_blocks",
     "ssa_forward_workspace",
     "ssa_forward",
+    "ssa_forward_timed",
+    "ssa_stage_name",
     "ssa_status_string",
     "ssa_last_error",
     "ssa_version",
@@ -106,6 +109,12 @@ def lib() -> ctypes.CDLL:
     L.ssa_forward.argtypes = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn), vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, sz, vp]
     L.ssa_forward.restype = ctypes.c_int
+    L.ssa_forward_timed.argtypes = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn), vp, vp, vp, vp,
+                                    vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float),
+                                    ctypes.POINTER(i32)]
+    L.ssa_forward_timed.restype = ctypes.c_int
+    L.ssa_stage_name.argtypes = [ctypes.POINTER(SsaAttn), i32]
+    L.ssa_stage_name.restype = ctypes.c_char_p
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
     L.ssa_last_error.argtypes = []

@@ -89,15 +89,43 @@ ssa_status check_attn(const ssa_attn* a) {
 
 int elt_bytes(ssa_dtype d) { return d == SSA_BF16 ? 2 : 4; }
 
-int64_t nb_capacity(const ssa_blocks* b) { return b->nb >= 0 ? b->nb : b->n_tokens; }
-
-size_t forward_ws_bytes(const ssa_blocks* b, const ssa_attn* a) {
-  const int64_t cap = nb_capacity(b) > 0 ? nb_capacity(b) : 1;
-  size_t s = 0;
-  s += 2 * align256(static_cast<size_t>(elt_bytes(a->dtype)) * a->h_kv * cap * a->head_dim);  // kbar, vbar
-  s += align256(sizeof(int32_t) * static_cast<size_t>(b->n_tokens) * a->h_kv * a->topk);     // topk fallback
-  return s + 256;
+// pooled-row capacity: the block count when known, else the token count;
+// rounded up to whole 32-block key tiles
+int64_t nb_capacity(const ssa_blocks* b) {
+  int64_t c = b->nb >= 0 ? b->nb : b->n_tokens;
+  if (c < 1) c = 1;
+  return (c + ssa::kKeyTile - 1) / ssa::kKeyTile * ssa::kKeyTile;
 }
+
+// the MFMA kernels cover bfloat16, head_dim 64, one query head per key/value head
+bool use_mfma_path(const ssa_attn* a) {
+  return a->dtype == SSA_BF16 && a->head_dim == 64 && a->h_q == a->h_kv;
+}
+
+struct FwdLayout {
+  size_t kbar, vbar, vbar_t, topk, tile_pre, fix, acc, total;
+};
+
+FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
+  const size_t cap = static_cast<size_t>(nb_capacity(b));
+  const size_t n = static_cast<size_t>(b->n_tokens);
+  const size_t pooled = align256(static_cast<size_t>(elt_bytes(a->dtype)) * a->h_kv * cap * a->head_dim);
+  FwdLayout L{};
+  size_t off = 0;
+  L.kbar = off; off += pooled;
+  L.vbar = off; off += pooled;
+  L.topk = off; off += align256(sizeof(int32_t) * n * a->h_kv * a->topk);
+  if (use_mfma_path(a)) {
+    L.vbar_t = off; off += pooled;
+    L.tile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    L.fix = off; off += align256(sizeof(int32_t) * (1 + n * a->h_kv));
+    L.acc = off; off += align256(sizeof(float) * n * a->h_q * a->head_dim);
+  }
+  L.total = off + 256;
+  return L;
+}
+
+size_t forward_ws_bytes(const ssa_blocks* b, const ssa_attn* a) { return forward_layout(b, a).total; }
 
 }  // namespace
 
@@ -176,9 +204,33 @@ size_t ssa_forward_workspace(const ssa_blocks* blocks, const ssa_attn* attn) {
   return forward_ws_bytes(blocks, attn);
 }
 
-ssa_status ssa_forward(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
-                       const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
-                       int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The kernels ssa_forward launches for a layout, in order.
+struct Stage {
+  const char* name;
+  hipError_t (*launch)(const ssa::FwdParams&, ssa_dtype, hipStream_t);
+};
+
+int forward_plan(const ssa_attn* attn, Stage* stages) {
+  stages[0] = Stage{"pool_kernel", ssa::launch_pool};
+  if (!use_mfma_path(attn)) {
+    stages[1] = Stage{"generic_fwd", ssa::launch_generic};
+    return 2;
+  }
+  stages[1] = Stage{"cmp_mfma_kernel", ssa::launch_cmp_mfma};
+  stages[2] = Stage{"topk_fixup_kernel", ssa::launch_topk_fixup};
+  stages[3] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
+  stages[4] = Stage{"sel_combine_kernel", ssa::launch_sel_combine};
+  return 5;
+}
+
+ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                        const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
+                        int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream,
+                        float* stage_ms, int32_t* n_stages) {
   if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
   ssa_status st = check_attn(attn);
   if (st != SSA_OK) return st;
@@ -193,9 +245,13 @@ ssa_status ssa_forward(const ssa_blocks* blocks, const ssa_attn* attn, const voi
   const size_t need = forward_ws_bytes(blocks, attn);
   if (!workspace || ws_bytes < need)
     return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, need);
+  if (stage_ms)
+    for (int i = 0; i < SSA_STAGES; ++i) stage_ms[i] = 0.f;
+  if (n_stages) *n_stages = 0;
   if (blocks->n_tokens == 0) return ok();
 
-  const int64_t cap = nb_capacity(blocks) > 0 ? nb_capacity(blocks) : 1;
+  const int64_t cap = nb_capacity(blocks);
+  const FwdLayout lay = forward_layout(blocks, attn);
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
   ssa::FwdParams p{};
   p.perm = blocks->perm;
@@ -217,18 +273,68 @@ ssa_status ssa_forward(const ssa_blocks* blocks, const ssa_attn* attn, const voi
   p.v = v;
   p.gates = gates;
   p.out = out;
-  const size_t pooled = align256(static_cast<size_t>(elt_bytes(attn->dtype)) * attn->h_kv * cap * attn->head_dim);
-  p.kbar = w;
-  p.vbar = w + pooled;
+  p.kbar = w + lay.kbar;
+  p.vbar = w + lay.vbar;
   p.k_cmp = k_cmp;
   p.v_cmp = v_cmp;
-  p.topk_idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + 2 * pooled);
+  p.topk_idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + lay.topk);
+  if (use_mfma_path(attn)) {
+    p.vbar_t = w + lay.vbar_t;
+    p.tile_pre = reinterpret_cast<int32_t*>(w + lay.tile_pre);
+    p.fix = reinterpret_cast<int32_t*>(w + lay.fix);
+    p.acc = reinterpret_cast<float*>(w + lay.acc);
+    p.max_tiles = static_cast<int32_t>(blocks->n_tokens / ssa::kQueryTile + blocks->batch + 1);
+  }
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = ssa::launch_pool(p, attn->dtype, stream);
-  if (e == hipSuccess) e = ssa::launch_generic(p, attn->dtype, stream);
+  Stage stages[SSA_STAGES];
+  const int ns = forward_plan(attn, stages);
+  hipEvent_t ev[SSA_STAGES + 1] = {};
+  hipError_t e = hipSuccess;
+  if (stage_ms) {
+    for (int i = 0; i <= ns && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    if (e == hipSuccess) e = hipEventRecord(ev[0], stream);
+  }
+  for (int i = 0; i < ns && e == hipSuccess; ++i) {
+    e = stages[i].launch(p, attn->dtype, stream);
+    if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[i + 1], stream);
+  }
+  if (stage_ms) {
+    if (e == hipSuccess) e = hipEventSynchronize(ev[ns]);
+    for (int i = 0; i < ns && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i <= ns; ++i)
+      if (ev[i]) hipEventDestroy(ev[i]);
+  }
   if (e != hipSuccess) return fail(SSA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  if (n_stages) *n_stages = ns;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ssa_status ssa_forward(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                       const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
+                       int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream) {
+  return forward_impl(blocks, attn, q, k, v, gates, out, k_cmp, v_cmp, topk_idx, workspace, ws_bytes,
+                      hip_stream, nullptr, nullptr);
+}
+
+ssa_status ssa_forward_timed(const ssa_blocks* blocks, const ssa_attn* attn, const void* q,
+                             const void* k, const void* v, const void* gates, void* out,
+                             void* k_cmp, void* v_cmp, int32_t* topk_idx, void* workspace,
+                             size_t ws_bytes, void* hip_stream, float* stage_ms, int32_t* n_stages) {
+  if (!stage_ms) return fail(SSA_ERR_INVALID_ARGUMENT, "stage_ms is null");
+  return forward_impl(blocks, attn, q, k, v, gates, out, k_cmp, v_cmp, topk_idx, workspace, ws_bytes,
+                      hip_stream, stage_ms, n_stages);
+}
+
+const char* ssa_stage_name(const ssa_attn* attn, int32_t stage) {
+  if (!attn || stage < 0 || stage >= SSA_STAGES) return "";
+  Stage stages[SSA_STAGES];
+  const int ns = forward_plan(attn, stages);
+  return stage < ns ? stages[stage].name : "";
 }
 
 }  // extern "C"

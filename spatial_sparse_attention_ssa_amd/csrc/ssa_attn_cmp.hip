@@ -1,0 +1,367 @@
+// Compressed-block attention with top-k block selection, on MFMA (bf16, D = 64,
+// one query head per key/value head).
+//
+// Direct3D-S2 page, "Method": every query attends to the mean-pooled blocks of
+// its sequence, and the same query-to-block scores choose the top-k blocks
+// for the selection branch.  With one query head per key/value group the
+// score order is the logit order (softmax is monotone), so the ranking uses
+// the float32 logits; ties go to the lower block id.
+//
+// Work split: a workgroup owns 128 consecutive sorted queries of one sequence
+// and one head (4 waves x 32 queries) and streams the sequence's pooled keys
+// and values through LDS in tiles of 32 blocks.  Each tile is a
+// v_mfma_f32_32x32x16_bf16 product S^T = Kbar Q^T; lane l then holds 16 block
+// logits of query l % 32 (lanes l and l ^ 32 split the row between them).
+//
+// Two passes over the keys:
+//  1. scan: per lane, the maximum of each tile's 16 logits (a "group max") is
+//     merged into a sorted list of the LK largest group maxima with v_med3
+//     (for a descending list L, inserting x gives L'[i] = med3(L[i-1], x, L[i])).
+//     The row maximum is max(L0 of both lanes).  The two lanes together hold
+//     2 * LK >= k distinct elements no smaller than
+//     tau = min(L[LK-1] of both lanes), so tau bounds the k-th largest logit
+//     from below.
+//  2. attend: recompute S, p = exp2((s - m) * scale * log2 e) with the exact
+//     row maximum m (no rescaling), O^T += Vbar^T P^T on MFMA, and append the
+//     logits >= tau with their block ids to a per-lane LDS list.  Afterwards
+//     each candidate's rank among the query's candidates (value descending,
+//     block ascending) places it in the output.  A lane whose list overflows
+//     sends its query to the exact fallback kernel below.
+#include <float.h>
+
+#include "ssa_internal.h"
+
+namespace ssa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kD = 64;
+constexpr int kKRow = kD + 8;          // LDS row of a key tile (bf16), padded against bank conflicts
+constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf16)
+constexpr int kCand = 16;              // candidate slots per lane
+
+struct CandSlot {
+  float v;
+  int j;
+};
+
+__device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// sorted position of sequence b's first token and one past its last
+__device__ __forceinline__ void seq_token_range(const FwdParams& p, int b, int* s0, int* s1) {
+  *s0 = p.win_off[p.seq_win_off[b]];
+  *s1 = p.win_off[p.seq_win_off[b + 1]];
+}
+
+// tile_pre[b] = number of 128-query tiles of sequences before b
+__global__ void tile_prefix_kernel(FwdParams p) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int run = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    p.tile_pre[b] = run;
+    int s0, s1;
+    seq_token_range(p, b, &s0, &s1);
+    run += (s1 - s0 + kQueryTile - 1) / kQueryTile;
+  }
+  p.tile_pre[p.batch] = run;
+  p.fix[0] = 0;
+}
+
+template <int LK>
+__global__ void __launch_bounds__(256, 2)
+cmp_mfma_kernel(FwdParams p) {
+  __shared__ __align__(16) uint16_t k_lds[kKeyTile * kKRow];
+  __shared__ __align__(16) uint16_t v_lds[kD * kVRow];
+  __shared__ __align__(16) CandSlot cand[4 * 64 * (kCand + 1)];  // per lane, padded stride
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int h = blockIdx.y;            // query head == key/value head
+  const int tile = blockIdx.x;
+  if (tile >= p.tile_pre[p.batch]) return;  // uniform over the workgroup
+
+  // tile -> sequence b and its query range
+  int lo = 0, hi = p.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tile_pre[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  int s0, s1;
+  seq_token_range(p, b, &s0, &s1);
+  const int q_begin = s0 + (tile - p.tile_pre[b]) * kQueryTile;
+  const int q_end = min(q_begin + kQueryTile, s1);
+  const int j0 = p.seq_blk_off[b], j1 = p.seq_blk_off[b + 1];
+  const int nbs = j1 - j0;
+
+  // this lane's query (column l % 32 of the wave's 32 queries)
+  const int qi = q_begin + wv * 32 + (lane & 31);
+  const bool q_valid = qi < q_end;
+  const int t = q_valid ? p.perm[qi] : 0;
+  const int half = lane >> 5;          // which 8-wide k slice / which half of the keys
+
+  // Q^T as the B operand: lane holds query (l % 32), d = 16 ks + 8 half + 0..7
+  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+  bf16x8 qb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (q_valid)
+      u = *reinterpret_cast<const u32x4*>(Q + (static_cast<int64_t>(t) * p.h_q + h) * kD + 16 * ks + 8 * half);
+    qb[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+
+  const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(h) * p.nb_cap * kD;
+  const uint16_t* VT = static_cast<const uint16_t*>(p.vbar_t) + static_cast<int64_t>(h) * p.nb_cap * kD;
+  const int kt0 = j0 / kKeyTile, kt1 = (j1 + kKeyTile - 1) / kKeyTile;
+
+  // cooperative tile staging: thread -> 16 bytes of the key tile / value tile
+  const int k_row = tid >> 3, k_chunk = tid & 7;      // key tile: 32 rows x 8 chunks
+  const int v_row = tid >> 2, v_chunk = tid & 3;      // value tile: 64 rows x 4 chunks
+  auto load_k = [&](int kt) {
+    return *reinterpret_cast<const u32x4*>(KB + (static_cast<int64_t>(kt) * kKeyTile + k_row) * kD + 8 * k_chunk);
+  };
+  auto load_v = [&](int kt) {
+    return *reinterpret_cast<const u32x4*>(VT + (static_cast<int64_t>(kt) * kD + v_row) * kKeyTile + 8 * v_chunk);
+  };
+  auto store_k = [&](u32x4 u) { *reinterpret_cast<u32x4*>(k_lds + k_row * kKRow + 8 * k_chunk) = u; };
+  auto store_v = [&](u32x4 u) { *reinterpret_cast<u32x4*>(v_lds + v_row * kVRow + 8 * v_chunk) = u; };
+
+  // S^T tile for the current key tile in LDS
+  auto qk = [&]() {
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = lds_b128(k_lds + (lane & 31) * kKRow + 16 * ks + 8 * half);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s, 0, 0, 0);
+    }
+    return s;
+  };
+  // block id held in accumulator register r of this lane for key tile kt
+  auto key_of = [&](int kt, int r) { return kt * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3); };
+
+  // ---------------- pass 1: group-max lists
+  float L[LK];
+#pragma unroll
+  for (int i = 0; i < LK; ++i) L[i] = -FLT_MAX;
+  u32x4 kreg = load_k(kt0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    __syncthreads();
+    store_k(kreg);
+    __syncthreads();
+    if (kt + 1 < kt1) kreg = load_k(kt + 1);
+    f32x16 s = qk();
+    const bool full = kt * kKeyTile >= j0 && (kt + 1) * kKeyTile <= j1;
+    float m = -FLT_MAX;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[r];
+      if (!full) {
+        const int j = key_of(kt, r);
+        if (j < j0 || j >= j1) x = -FLT_MAX;
+      }
+      m = fmaxf(m, x);
+    }
+#pragma unroll
+    for (int i = LK - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
+    L[0] = fmaxf(L[0], m);
+  }
+  const float row_max = fmaxf(L[0], __shfl_xor(L[0], 32));
+  const float tau = fminf(L[LK - 1], __shfl_xor(L[LK - 1], 32));
+
+  // ---------------- pass 2: probabilities, P V, candidates
+  const float c2 = p.scale * kLog2e;
+  const float mc = row_max * c2;
+  f32x16 o0 = {}, o1 = {};
+  float lsum = 0.f;
+  int cnt = 0;
+  CandSlot* my_cand = &cand[(wv * 64 + lane) * (kCand + 1)];
+  kreg = load_k(kt0);
+  u32x4 vreg = load_v(kt0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    __syncthreads();
+    store_k(kreg);
+    store_v(vreg);
+    __syncthreads();
+    if (kt + 1 < kt1) {
+      kreg = load_k(kt + 1);
+      vreg = load_v(kt + 1);
+    }
+    f32x16 s = qk();
+    const bool full = kt * kKeyTile >= j0 && (kt + 1) * kKeyTile <= j1;
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = key_of(kt, r);
+      const bool ok = full || (j >= j0 && j < j1);
+      const float x = ok ? fmaf(s[r], c2, -mc) : -FLT_MAX;
+      pr[r] = __builtin_amdgcn_exp2f(x);
+      lsum += pr[r];
+      const bool hit = q_valid && ok && s[r] >= tau;
+      if (__ballot(hit)) {
+        if (hit) {
+          if (cnt < kCand) my_cand[cnt] = CandSlot{s[r], j};
+          ++cnt;
+        }
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a0 = lds_b128(v_lds + (lane & 31) * kVRow + 16 * ks + 8 * half);
+      const bf16x8 a1 = lds_b128(v_lds + (32 + (lane & 31)) * kVRow + 16 * ks + 8 * half);
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb[ks], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb[ks], o1, 0, 0, 0);
+    }
+  }
+
+  // ---------------- o_cmp (times its gate) into the branch accumulator
+  const float l_q = lsum + __shfl_xor(lsum, 32);
+  if (q_valid) {
+    const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
+    const float f = bf16_bits_to_f32(gt[0]) / l_q;
+    float* dst = p.acc + (static_cast<int64_t>(t) * p.h_q + h) * kD;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int d = 8 * rb + 4 * half;
+      *reinterpret_cast<float4*>(dst + d) =
+          make_float4(o0[4 * rb] * f, o0[4 * rb + 1] * f, o0[4 * rb + 2] * f, o0[4 * rb + 3] * f);
+      *reinterpret_cast<float4*>(dst + 32 + d) =
+          make_float4(o1[4 * rb] * f, o1[4 * rb + 1] * f, o1[4 * rb + 2] * f, o1[4 * rb + 3] * f);
+    }
+  }
+
+  // ---------------- exact top-k among the candidates
+  wave_lds_sync();
+  const int cnt_other = __shfl_xor(cnt, 32);
+  const bool overflow = cnt > kCand || cnt_other > kCand;
+  const int k_eff = min(p.topk, nbs);
+  int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + h) * p.topk;
+  if (q_valid && overflow) {
+    if (half == 0) {
+      const int slot = atomicAdd(&p.fix[0], 1);
+      p.fix[1 + slot] = qi * p.h_kv + h;
+    }
+  } else if (q_valid) {
+    const CandSlot* other = &cand[(wv * 64 + (lane ^ 32)) * (kCand + 1)];
+    for (int i = 0; i < cnt; ++i) {
+      const CandSlot c = my_cand[i];
+      int rank = 0;
+      for (int e = 0; e < cnt; ++e) {
+        const CandSlot o = my_cand[e];
+        rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
+      }
+      for (int e = 0; e < cnt_other; ++e) {
+        const CandSlot o = other[e];
+        rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
+      }
+      if (rank < k_eff) out_sel[rank] = c.j;
+    }
+    if (half == 0)
+      for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
+  }
+}
+
+// Exact top-k for the (sorted position, group) pairs whose candidate list
+// overflowed: one wave per pair, each lane keeps a sorted list of its strided blocks'
+// logits, then the wave pops the best heads (value desc, block asc).
+template <int KMAX>
+__global__ void __launch_bounds__(256)
+topk_fixup_kernel(FwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int n_fix = p.fix[0];
+  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < n_fix; item += gridDim.x * 4) {
+    const int entry = p.fix[1 + item];
+    const int i = entry / p.h_kv, g = entry % p.h_kv;
+    const int t = p.perm[i];
+    const int tg = t * p.h_kv + g;
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.win_off[p.seq_win_off[mid]] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int j0 = p.seq_blk_off[lo], j1 = p.seq_blk_off[lo + 1];
+    float q[kD];
+#pragma unroll
+    for (int d = 0; d < kD; ++d) q[d] = bf16_bits_to_f32(Q[(static_cast<int64_t>(t) * p.h_q + g) * kD + d]);
+    const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(g) * p.nb_cap * kD;
+    float lv[KMAX];
+    int li[KMAX];
+#pragma unroll
+    for (int e = 0; e < KMAX; ++e) { lv[e] = -FLT_MAX; li[e] = 0x7FFFFFFF; }
+    for (int j = j0 + lane; j < j1; j += 64) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < kD / 8; ++c) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(KB + static_cast<int64_t>(j) * kD + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = fmaf(q[8 * c + 2 * e], __uint_as_float(u[e] << 16), s);
+          s = fmaf(q[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), s);
+        }
+      }
+      if (s > lv[KMAX - 1]) {
+        bool placed = false;
+#pragma unroll
+        for (int e = KMAX - 1; e >= 1; --e) {
+          if (!placed) {
+            if (s > lv[e - 1]) { lv[e] = lv[e - 1]; li[e] = li[e - 1]; }
+            else { lv[e] = s; li[e] = j; placed = true; }
+          }
+        }
+        if (!placed) { lv[0] = s; li[0] = j; }
+      }
+    }
+    const int k_eff = min(p.topk, j1 - j0);
+    int32_t* out_sel = p.topk_idx + static_cast<int64_t>(tg) * p.topk;
+    for (int r = 0; r < k_eff; ++r) {
+      float bv = lv[0];
+      int bi = li[0];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (li[0] == bi) {
+#pragma unroll
+        for (int e = 0; e < KMAX - 1; ++e) { lv[e] = lv[e + 1]; li[e] = li[e + 1]; }
+        lv[KMAX - 1] = -FLT_MAX;
+        li[KMAX - 1] = 0x7FFFFFFF;
+      }
+      if (lane == 0) out_sel[r] = bi;
+    }
+    if (lane == 0)
+      for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
+  const dim3 grid(p.max_tiles, p.h_q);
+  if (p.topk <= 16) cmp_mfma_kernel<8><<<grid, 256, 0, stream>>>(p);
+  else cmp_mfma_kernel<16><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  if (p.topk <= 16) topk_fixup_kernel<16><<<1024, 256, 0, stream>>>(p);
+  else topk_fixup_kernel<32><<<1024, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

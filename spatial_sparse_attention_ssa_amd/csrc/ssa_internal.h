@@ -100,15 +100,31 @@ struct FwdParams {
   const void* gates;
   void* out;
   // pooled keys / values, internal layout [h_kv][nb_cap][D] in the input dtype
+  // (nb_cap is a multiple of 32; rows nb..nb_cap are zero)
   void* kbar;
   void* vbar;
+  // pooled values for the MFMA path: [h_kv][nb_cap/32][D][32], keys of each
+  // 32-block tile in the order the MFMA B operand of P^T expects (null = skip)
+  void* vbar_t;
+  // MFMA path scratch
+  int32_t* tile_pre;  // [batch + 1] prefix of query tiles per sequence
+  int32_t* fix;       // [1 + n * h_kv] overflow counter, then (token * h_kv + group) entries
+  float* acc;         // [n][h_q][D] partial sum of the gated branches (input token order)
+  int32_t max_tiles;  // upper bound of query tiles
   // optional public outputs
   void* k_cmp;       // [nb][h_kv][D] or null
   void* v_cmp;
   int32_t* topk_idx; // [N][h_kv][topk]  (always valid: library workspace when the caller passes null)
 };
 
+constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile
+constexpr int kQueryTile = 128;  // queries per workgroup of the MFMA kernels (4 waves x 32)
+
 hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_sel_combine(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_generic(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 
 }  // namespace ssa

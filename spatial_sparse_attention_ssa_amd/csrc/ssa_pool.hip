@@ -31,12 +31,32 @@ __device__ __forceinline__ void store4(uint16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
+// Position of key jj (0..31) of a 32-key tile in the MFMA operand order: the
+// 32x32 accumulator gives lane group 0 the keys {0-3, 8-11} and lane group 1
+// the keys {4-7, 12-15} of each 16-key half; the permutation is its own
+// inverse.
+__device__ __forceinline__ int mfma_key_pos(int jj) {
+  const int lo = jj & 15;
+  const int perm = (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
+  return (jj & 16) | perm;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_vt(T* vt, int d, int nb_cap, int g, int j, int dd, float4 s) {
+  if (!vt) return;
+  const int64_t tile = static_cast<int64_t>(g) * (nb_cap / kKeyTile) + j / kKeyTile;
+  T* base = vt + tile * d * kKeyTile + mfma_key_pos(j % kKeyTile);
+  const float x[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Elt<T>::store(base + (dd + e) * kKeyTile, x[e]);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 pool_kernel(const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ perm,
             const int32_t* __restrict__ blk_off, const int32_t* __restrict__ counts, int hkv, int d,
-            int nb_cap, T* __restrict__ kbar, T* __restrict__ vbar, T* __restrict__ k_cmp,
-            T* __restrict__ v_cmp) {
+            int nb_cap, T* __restrict__ kbar, T* __restrict__ vbar, T* __restrict__ vbar_t,
+            T* __restrict__ k_cmp, T* __restrict__ v_cmp) {
   __shared__ float4 red[256];
   const int e_per_tok = hkv * d;
   const int c_per_tok = e_per_tok / 4;                 // 4-element chunks per row
@@ -72,11 +92,27 @@ pool_kernel(const T* __restrict__ k, const T* __restrict__ v, const int32_t* __r
           const int g = e / d, dd = e % d;
           T* dst = which ? vbar : kbar;
           store4(dst + (static_cast<int64_t>(g) * nb_cap + j) * d + dd, s);
+          if (which) store_vt(vbar_t, d, nb_cap, g, j, dd, s);
           T* pub = which ? v_cmp : k_cmp;
           if (pub) store4(pub + static_cast<int64_t>(j) * e_per_tok + e, s);
         }
         __syncthreads();
       }
+    }
+  }
+  // zero the rows between nb and nb_cap so padded key tiles hold finite values
+  const int pad_rows = nb_cap - nb;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+       i < static_cast<int64_t>(hkv) * pad_rows * d; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int g = static_cast<int>(i / (static_cast<int64_t>(pad_rows) * d));
+    const int rem = static_cast<int>(i % (static_cast<int64_t>(pad_rows) * d));
+    const int j = nb + rem / d, dd = rem % d;
+    const int64_t row = (static_cast<int64_t>(g) * nb_cap + j) * d + dd;
+    kbar[row] = T(0);
+    vbar[row] = T(0);
+    if (vbar_t) {
+      const int64_t tile = static_cast<int64_t>(g) * (nb_cap / kKeyTile) + j / kKeyTile;
+      vbar_t[(tile * d + dd) * kKeyTile + mfma_key_pos(j % kKeyTile)] = T(0);
     }
   }
 }
@@ -89,13 +125,13 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
     pool_kernel<uint16_t><<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(p.k), static_cast<const uint16_t*>(p.v), p.perm, p.blk_off,
         p.counts, p.h_kv, p.d, p.nb_cap, static_cast<uint16_t*>(p.kbar),
-        static_cast<uint16_t*>(p.vbar), static_cast<uint16_t*>(p.k_cmp),
-        static_cast<uint16_t*>(p.v_cmp));
+        static_cast<uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t),
+        static_cast<uint16_t*>(p.k_cmp), static_cast<uint16_t*>(p.v_cmp));
   } else {
     pool_kernel<float><<<grid, 256, 0, stream>>>(
         static_cast<const float*>(p.k), static_cast<const float*>(p.v), p.perm, p.blk_off,
         p.counts, p.h_kv, p.d, p.nb_cap, static_cast<float*>(p.kbar), static_cast<float*>(p.vbar),
-        static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp));
+        static_cast<float*>(p.vbar_t), static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp));
   }
   return hipGetLastError();
 }
