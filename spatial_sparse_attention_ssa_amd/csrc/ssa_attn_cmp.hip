@@ -15,18 +15,19 @@
 //
 // Two passes over the keys:
 //  1. scan: per lane, the maximum of each tile's 16 logits (a "group max") is
-//     merged into a sorted list of the LK largest group maxima with v_med3
+//     merged into a sorted list of the KMAX largest group maxima with v_med3
 //     (for a descending list L, inserting x gives L'[i] = med3(L[i-1], x, L[i])).
-//     The row maximum is max(L0 of both lanes).  The two lanes together hold
-//     2 * LK >= k distinct elements no smaller than
-//     tau = min(L[LK-1] of both lanes), so tau bounds the k-th largest logit
-//     from below.
+//     The row maximum is max(L0 of both lanes).  For every split a + b = KMAX
+//     the two lanes hold a + b distinct elements no smaller than
+//     min(L_A[a-1], L_B[b-1]); the largest such value, tau, bounds the KMAX-th
+//     (so also the k-th, k <= KMAX) largest logit from below.
 //  2. attend: recompute S, p = exp2((s - m) * scale * log2 e) with the exact
 //     row maximum m (no rescaling), O^T += Vbar^T P^T on MFMA, and append the
-//     logits >= tau with their block ids to a per-lane LDS list.  Afterwards
+//     logits >= tau with their block ids to the query's LDS list (its two
+//     lanes fill it from opposite ends).  Afterwards
 //     each candidate's rank among the query's candidates (value descending,
-//     block ascending) places it in the output.  A lane whose list overflows
-//     sends its query to the exact fallback kernel below.
+//     block ascending) places it in the output.  A query whose list overflows
+//     goes to the exact fallback kernel below.
 #include <float.h>
 
 #include "ssa_internal.h"
@@ -42,7 +43,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kD = 64;
 constexpr int kKRow = kD + 8;          // LDS row of a key tile (bf16), padded against bank conflicts
 constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf16)
-constexpr int kCand = 16;              // candidate slots per lane
 
 struct CandSlot {
   float v;
@@ -73,12 +73,13 @@ __global__ void tile_prefix_kernel(FwdParams p) {
   p.fix[0] = 0;
 }
 
-template <int LK>
+template <int KMAX>
 __global__ void __launch_bounds__(256, 2)
 cmp_mfma_kernel(FwdParams p) {
+  constexpr int kCap = 2 * KMAX;  // candidate slots per query, shared by its two lanes
   __shared__ __align__(16) uint16_t k_lds[kKeyTile * kKRow];
   __shared__ __align__(16) uint16_t v_lds[kD * kVRow];
-  __shared__ __align__(16) CandSlot cand[4 * 64 * (kCand + 1)];  // per lane, padded stride
+  __shared__ __align__(16) CandSlot cand[4 * 32 * (kCap + 1)];  // padded stride per query
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,11 +147,19 @@ cmp_mfma_kernel(FwdParams p) {
   };
   // block id held in accumulator register r of this lane for key tile kt
   auto key_of = [&](int kt, int r) { return kt * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3); };
-
-  // ---------------- pass 1: group-max lists
-  float L[LK];
+  // keys of a partial tile outside [j0, j1) get -FLT_MAX
+  auto mask = [&](int kt, f32x16& s) {
 #pragma unroll
-  for (int i = 0; i < LK; ++i) L[i] = -FLT_MAX;
+    for (int r = 0; r < 16; ++r) {
+      const int j = key_of(kt, r);
+      if (j < j0 || j >= j1) s[r] = -FLT_MAX;
+    }
+  };
+
+  // ---------------- pass 1: sorted list of this lane's KMAX largest group maxima
+  float L[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) L[i] = -FLT_MAX;
   u32x4 kreg = load_k(kt0);
   for (int kt = kt0; kt < kt1; ++kt) {
     __syncthreads();
@@ -158,23 +167,25 @@ cmp_mfma_kernel(FwdParams p) {
     __syncthreads();
     if (kt + 1 < kt1) kreg = load_k(kt + 1);
     f32x16 s = qk();
-    const bool full = kt * kKeyTile >= j0 && (kt + 1) * kKeyTile <= j1;
-    float m = -FLT_MAX;
+    if (kt * kKeyTile < j0 || (kt + 1) * kKeyTile > j1) mask(kt, s);
+    float m = fmaxf(s[0], fmaxf(s[1], s[2]));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[r];
-      if (!full) {
-        const int j = key_of(kt, r);
-        if (j < j0 || j >= j1) x = -FLT_MAX;
-      }
-      m = fmaxf(m, x);
-    }
+    for (int r = 3; r < 15; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+    m = fmaxf(m, s[15]);
 #pragma unroll
-    for (int i = LK - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
+    for (int i = KMAX - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
     L[0] = fmaxf(L[0], m);
   }
-  const float row_max = fmaxf(L[0], __shfl_xor(L[0], 32));
-  const float tau = fminf(L[LK - 1], __shfl_xor(L[LK - 1], 32));
+  // row maximum, and the best lower bound on the KMAX-th largest logit (hence
+  // on the k-th, k <= KMAX): for any split a + b = KMAX the two lanes hold a
+  // and b distinct elements >= min(L_this[a-1], L_other[b-1])
+  float Lo[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) Lo[i] = __shfl_xor(L[i], 32);
+  const float row_max = fmaxf(L[0], Lo[0]);
+  float tau = fmaxf(L[KMAX - 1], Lo[KMAX - 1]);
+#pragma unroll
+  for (int a = 1; a < KMAX; ++a) tau = fmaxf(tau, fminf(L[a - 1], Lo[KMAX - 1 - a]));
 
   // ---------------- pass 2: probabilities, P V, candidates
   const float c2 = p.scale * kLog2e;
@@ -182,7 +193,7 @@ cmp_mfma_kernel(FwdParams p) {
   f32x16 o0 = {}, o1 = {};
   float lsum = 0.f;
   int cnt = 0;
-  CandSlot* my_cand = &cand[(wv * 64 + lane) * (kCand + 1)];
+  CandSlot* qcand = &cand[(wv * 32 + (lane & 31)) * (kCap + 1)];
   kreg = load_k(kt0);
   u32x4 vreg = load_v(kt0);
   for (int kt = kt0; kt < kt1; ++kt) {
@@ -195,19 +206,19 @@ cmp_mfma_kernel(FwdParams p) {
       vreg = load_v(kt + 1);
     }
     f32x16 s = qk();
-    const bool full = kt * kKeyTile >= j0 && (kt + 1) * kKeyTile <= j1;
+    if (kt * kKeyTile < j0 || (kt + 1) * kKeyTile > j1) mask(kt, s);
     float pr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = key_of(kt, r);
-      const bool ok = full || (j >= j0 && j < j1);
-      const float x = ok ? fmaf(s[r], c2, -mc) : -FLT_MAX;
-      pr[r] = __builtin_amdgcn_exp2f(x);
+      pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
       lsum += pr[r];
-      const bool hit = q_valid && ok && s[r] >= tau;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool hit = q_valid && s[r] >= tau;
       if (__ballot(hit)) {
         if (hit) {
-          if (cnt < kCand) my_cand[cnt] = CandSlot{s[r], j};
+          if (cnt < kCap) qcand[half ? kCap - 1 - cnt : cnt] = CandSlot{s[r], key_of(kt, r)};
           ++cnt;
         }
       }
@@ -245,7 +256,7 @@ cmp_mfma_kernel(FwdParams p) {
   // ---------------- exact top-k among the candidates
   wave_lds_sync();
   const int cnt_other = __shfl_xor(cnt, 32);
-  const bool overflow = cnt > kCand || cnt_other > kCand;
+  const bool overflow = cnt + cnt_other > kCap;
   const int k_eff = min(p.topk, nbs);
   int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + h) * p.topk;
   if (q_valid && overflow) {
@@ -254,16 +265,19 @@ cmp_mfma_kernel(FwdParams p) {
       p.fix[1 + slot] = qi * p.h_kv + h;
     }
   } else if (q_valid) {
-    const CandSlot* other = &cand[(wv * 64 + (lane ^ 32)) * (kCand + 1)];
+    // the query's candidates: slots [0, c0) from lane half 0 and
+    // [kCap - c1, kCap) from lane half 1
+    const int c0 = half ? cnt_other : cnt, c1 = half ? cnt : cnt_other;
+    const int mine0 = half ? kCap - cnt : 0;
     for (int i = 0; i < cnt; ++i) {
-      const CandSlot c = my_cand[i];
+      const CandSlot c = qcand[mine0 + i];
       int rank = 0;
-      for (int e = 0; e < cnt; ++e) {
-        const CandSlot o = my_cand[e];
+      for (int e = 0; e < c0; ++e) {
+        const CandSlot o = qcand[e];
         rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
       }
-      for (int e = 0; e < cnt_other; ++e) {
-        const CandSlot o = other[e];
+      for (int e = kCap - c1; e < kCap; ++e) {
+        const CandSlot o = qcand[e];
         rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
       }
       if (rank < k_eff) out_sel[rank] = c.j;
@@ -353,8 +367,8 @@ topk_fixup_kernel(FwdParams p) {
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
   const dim3 grid(p.max_tiles, p.h_q);
-  if (p.topk <= 16) cmp_mfma_kernel<8><<<grid, 256, 0, stream>>>(p);
-  else cmp_mfma_kernel<16><<<grid, 256, 0, stream>>>(p);
+  if (p.topk <= 16) cmp_mfma_kernel<16><<<grid, 256, 0, stream>>>(p);
+  else cmp_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
