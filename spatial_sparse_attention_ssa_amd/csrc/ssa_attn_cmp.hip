@@ -9,7 +9,9 @@
 //
 // Work split: a workgroup owns 128 consecutive sorted queries of one sequence
 // and one head (4 waves x 32 queries) and streams the sequence's pooled keys
-// and values through LDS in tiles of 32 blocks.  Each tile is a
+// and values through a two-slot LDS ring in tiles of 32 blocks: one barrier
+// per tile, global loads issued two tiles ahead, loop unrolled by two so that
+// ring slots and register sets are compile-time constants.  Each tile is a
 // v_mfma_f32_32x32x16_bf16 product S^T = Kbar Q^T; lane l then holds 16 block
 // logits of query l % 32 (lanes l and l ^ 32 split the row between them).
 //
@@ -23,12 +25,14 @@
 //     (so also the k-th, k <= KMAX) largest logit from below.
 //  2. attend: recompute S, p = exp2((s - m) * scale * log2 e) with the exact
 //     row maximum m (no rescaling), O^T += Vbar^T P^T on MFMA, and append the
-//     logits >= tau with their block ids to the query's LDS list (its two
-//     lanes fill it from opposite ends).  Afterwards
+//     logits >= tau with their block ids to the query's LDS candidate list
+//     (its two lanes fill it from opposite ends).  Afterwards
 //     each candidate's rank among the query's candidates (value descending,
 //     block ascending) places it in the output.  A query whose list overflows
 //     goes to the exact fallback kernel below.
 #include <float.h>
+
+#include <type_traits>
 
 #include "ssa_internal.h"
 
@@ -73,13 +77,36 @@ __global__ void tile_prefix_kernel(FwdParams p) {
   p.fix[0] = 0;
 }
 
+// Runs step(rel, slot, mask) for rel = 0 .. n - 1 with ring slot rel & 1 as
+// a compile-time constant; only the first and last tile (the ones that can
+// be partial) take the masking path.
+template <typename Step>
+__device__ __forceinline__ void run_tiles(int n, Step&& step) {
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using M0 = std::false_type;
+  using M1 = std::true_type;
+  step(0, S0{}, M1{});
+  int rel = 1;
+  for (; rel + 2 < n; rel += 2) {
+    step(rel, S1{}, M0{});
+    step(rel + 1, S0{}, M0{});
+  }
+  if (rel < n) step(rel, S1{}, M1{});
+  if (rel + 1 < n) step(rel + 1, S0{}, M1{});
+}
+
 template <int KMAX>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 cmp_mfma_kernel(FwdParams p) {
-  constexpr int kCap = 2 * KMAX;  // candidate slots per query, shared by its two lanes
-  __shared__ __align__(16) uint16_t k_lds[kKeyTile * kKRow];
-  __shared__ __align__(16) uint16_t v_lds[kD * kVRow];
-  __shared__ __align__(16) CandSlot cand[4 * 32 * (kCap + 1)];  // padded stride per query
+  // candidate slots per query, shared by its two lanes (with the bound below
+  // a query rarely has more than KMAX + 6; overflow goes to the fallback)
+  constexpr int kCap = KMAX + KMAX / 2;
+  __shared__ __align__(16) uint16_t k_lds[2][kKeyTile * kKRow];
+  __shared__ __align__(16) uint16_t v_lds[2][kD * kVRow];
+  // per query kCap data slots 1..kCap plus a sink slot at each end that
+  // absorbs writes past the capacity
+  __shared__ __align__(16) CandSlot cand[4 * 32 * (kCap + 2)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,36 +149,35 @@ cmp_mfma_kernel(FwdParams p) {
   const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(h) * p.nb_cap * kD;
   const uint16_t* VT = static_cast<const uint16_t*>(p.vbar_t) + static_cast<int64_t>(h) * p.nb_cap * kD;
   const int kt0 = j0 / kKeyTile, kt1 = (j1 + kKeyTile - 1) / kKeyTile;
+  const int n_kt = kt1 - kt0;
 
   // cooperative tile staging: thread -> 16 bytes of the key tile / value tile
   const int k_row = tid >> 3, k_chunk = tid & 7;      // key tile: 32 rows x 8 chunks
   const int v_row = tid >> 2, v_chunk = tid & 3;      // value tile: 64 rows x 4 chunks
-  auto load_k = [&](int kt) {
-    return *reinterpret_cast<const u32x4*>(KB + (static_cast<int64_t>(kt) * kKeyTile + k_row) * kD + 8 * k_chunk);
-  };
-  auto load_v = [&](int kt) {
-    return *reinterpret_cast<const u32x4*>(VT + (static_cast<int64_t>(kt) * kD + v_row) * kKeyTile + 8 * v_chunk);
-  };
-  auto store_k = [&](u32x4 u) { *reinterpret_cast<u32x4*>(k_lds + k_row * kKRow + 8 * k_chunk) = u; };
-  auto store_v = [&](u32x4 u) { *reinterpret_cast<u32x4*>(v_lds + v_row * kVRow + 8 * v_chunk) = u; };
+  const uint16_t* kg = KB + (static_cast<int64_t>(kt0) * kKeyTile + k_row) * kD + 8 * k_chunk;
+  const uint16_t* vg = VT + (static_cast<int64_t>(kt0) * kD + v_row) * kKeyTile + 8 * v_chunk;
+  auto load_k = [&](int rel) { return *reinterpret_cast<const u32x4*>(kg + static_cast<int64_t>(rel) * kKeyTile * kD); };
+  auto load_v = [&](int rel) { return *reinterpret_cast<const u32x4*>(vg + static_cast<int64_t>(rel) * kKeyTile * kD); };
+  uint16_t* const ks_dst = &k_lds[0][k_row * kKRow + 8 * k_chunk];
+  uint16_t* const vs_dst = &v_lds[0][v_row * kVRow + 8 * v_chunk];
+  const uint16_t* const ka = &k_lds[0][(lane & 31) * kKRow + 8 * half];
+  const uint16_t* const va = &v_lds[0][(lane & 31) * kVRow + 8 * half];
 
-  // S^T tile for the current key tile in LDS
-  auto qk = [&]() {
+  // S^T of the key tile in ring slot `slot`
+  auto qk = [&](int slot) {
+    const uint16_t* kl = ka + slot * (kKeyTile * kKRow);
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 a = lds_b128(k_lds + (lane & 31) * kKRow + 16 * ks + 8 * half);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(kl + 16 * ks), qb[ks], s, 0, 0, 0);
     return s;
   };
-  // block id held in accumulator register r of this lane for key tile kt
-  auto key_of = [&](int kt, int r) { return kt * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3); };
   // keys of a partial tile outside [j0, j1) get -FLT_MAX
   auto mask = [&](int kt, f32x16& s) {
+    if (kt * kKeyTile >= j0 && (kt + 1) * kKeyTile <= j1) return;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = key_of(kt, r);
+      const int j = kt * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3);
       if (j < j0 || j >= j1) s[r] = -FLT_MAX;
     }
   };
@@ -160,21 +186,29 @@ cmp_mfma_kernel(FwdParams p) {
   float L[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) L[i] = -FLT_MAX;
-  u32x4 kreg = load_k(kt0);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    __syncthreads();
-    store_k(kreg);
-    __syncthreads();
-    if (kt + 1 < kt1) kreg = load_k(kt + 1);
-    f32x16 s = qk();
-    if (kt * kKeyTile < j0 || (kt + 1) * kKeyTile > j1) mask(kt, s);
-    float m = fmaxf(s[0], fmaxf(s[1], s[2]));
+  {
+    // ring: LDS slot (rel & 1) holds tile rel; register set (rel & 1) holds
+    // the tile two ahead of the one being stored
+    u32x4 kr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    *reinterpret_cast<u32x4*>(ks_dst) = load_k(0);
+    if (n_kt > 1) kr[1] = load_k(1);
+    if (n_kt > 2) kr[0] = load_k(2);
+    auto step = [&](int rel, auto slot_c, auto mask_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      __syncthreads();  // tile rel stored; slot of tile rel - 1 free
+      if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
+      if (rel + 3 < n_kt) kr[slot ^ 1] = load_k(rel + 3);
+      f32x16 s = qk(slot);
+      if (decltype(mask_c)::value) mask(kt0 + rel, s);
+      float m = fmaxf(s[0], fmaxf(s[1], s[2]));
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
-    m = fmaxf(m, s[15]);
+      for (int r = 3; r < 15; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+      m = fmaxf(m, s[15]);
 #pragma unroll
-    for (int i = KMAX - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
-    L[0] = fmaxf(L[0], m);
+      for (int i = KMAX - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
+      L[0] = fmaxf(L[0], m);
+    };
+    run_tiles(n_kt, step);
   }
   // row maximum, and the best lower bound on the KMAX-th largest logit (hence
   // on the k-th, k <= KMAX): for any split a + b = KMAX the two lanes hold a
@@ -191,53 +225,72 @@ cmp_mfma_kernel(FwdParams p) {
   const float c2 = p.scale * kLog2e;
   const float mc = row_max * c2;
   f32x16 o0 = {}, o1 = {};
-  float lsum = 0.f;
-  int cnt = 0;
-  CandSlot* qcand = &cand[(wv * 32 + (lane & 31)) * (kCap + 1)];
-  kreg = load_k(kt0);
-  u32x4 vreg = load_v(kt0);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    __syncthreads();
-    store_k(kreg);
-    store_v(vreg);
-    __syncthreads();
-    if (kt + 1 < kt1) {
-      kreg = load_k(kt + 1);
-      vreg = load_v(kt + 1);
-    }
-    f32x16 s = qk();
-    if (kt * kKeyTile < j0 || (kt + 1) * kKeyTile > j1) mask(kt, s);
-    float pr[16];
+  float lsum0 = 0.f, lsum1 = 0.f;
+  // the query's candidate list: lane half 0 writes slots 1, 2, ... upward,
+  // half 1 writes kCap, kCap - 1, ... downward; a write past the capacity
+  // lands in the sink slot (0 or kCap + 1) and the query goes to the fallback
+  const int qbase = (wv * 32 + (lane & 31)) * (kCap + 2);
+  CandSlot* const qcand = &cand[qbase];
+  int cpos = qbase + (half ? kCap : 1);
+  const int climit = qbase + (half ? 0 : kCap + 1);
+  const int cstep = half ? -1 : 1;
+  const float tau_eff = q_valid ? tau : __builtin_inff();  // columns without a query never hit
+  const int key_lane = 4 * half;
+  {
+    u32x4 kr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    u32x4 vr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    __syncthreads();  // every wave is done with pass 1's ring
+    *reinterpret_cast<u32x4*>(ks_dst) = load_k(0);
+    *reinterpret_cast<u32x4*>(vs_dst) = load_v(0);
+    if (n_kt > 1) { kr[1] = load_k(1); vr[1] = load_v(1); }
+    if (n_kt > 2) { kr[0] = load_k(2); vr[0] = load_v(2); }
+    auto step = [&](int rel, auto slot_c, auto mask_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      __syncthreads();
+      if (rel + 1 < n_kt) {
+        *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
+        *reinterpret_cast<u32x4*>(vs_dst + (slot ^ 1) * (kD * kVRow)) = vr[slot ^ 1];
+      }
+      if (rel + 3 < n_kt) {
+        kr[slot ^ 1] = load_k(rel + 3);
+        vr[slot ^ 1] = load_v(rel + 3);
+      }
+      const int kt = kt0 + rel;
+      f32x16 s = qk(slot);
+      if (decltype(mask_c)::value) mask(kt, s);
+      float pr[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
-      lsum += pr[r];
-    }
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
+        if (r & 1) lsum1 += pr[r]; else lsum0 += pr[r];
+      }
+      const int key0 = kt * kKeyTile + key_lane;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool hit = q_valid && s[r] >= tau;
-      if (__ballot(hit)) {
-        if (hit) {
-          if (cnt < kCap) qcand[half ? kCap - 1 - cnt : cnt] = CandSlot{s[r], key_of(kt, r)};
-          ++cnt;
+      for (int r = 0; r < 16; ++r) {
+        if (s[r] >= tau_eff) {
+          cand[cpos] = CandSlot{s[r], key0 + 8 * (r >> 2) + (r & 3)};
+          cpos = (cpos == climit) ? cpos : cpos + cstep;
         }
       }
-    }
-    bf16x8 pb[2];
+      bf16x8 pb[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+        for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+      const uint16_t* vl = va + slot * (kD * kVRow);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a0 = lds_b128(v_lds + (lane & 31) * kVRow + 16 * ks + 8 * half);
-      const bf16x8 a1 = lds_b128(v_lds + (32 + (lane & 31)) * kVRow + 16 * ks + 8 * half);
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb[ks], o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb[ks], o1, 0, 0, 0);
-    }
+      for (int ks = 0; ks < 2; ++ks) {
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 16 * ks), pb[ks], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow + 16 * ks), pb[ks], o1, 0, 0, 0);
+      }
+    };
+    run_tiles(n_kt, step);
   }
+  // appended so far (a pointer parked on the sink slot counts as overflow)
+  const int cnt = half ? qbase + kCap - cpos : cpos - (qbase + 1);
 
   // ---------------- o_cmp (times its gate) into the branch accumulator
+  const float lsum = lsum0 + lsum1;
   const float l_q = lsum + __shfl_xor(lsum, 32);
   if (q_valid) {
     const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
@@ -256,7 +309,7 @@ cmp_mfma_kernel(FwdParams p) {
   // ---------------- exact top-k among the candidates
   wave_lds_sync();
   const int cnt_other = __shfl_xor(cnt, 32);
-  const bool overflow = cnt + cnt_other > kCap;
+  const bool overflow = cnt + cnt_other > kCap - 1;  // kCap - 1: a lane parked on its sink also counts
   const int k_eff = min(p.topk, nbs);
   int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + h) * p.topk;
   if (q_valid && overflow) {
@@ -265,18 +318,18 @@ cmp_mfma_kernel(FwdParams p) {
       p.fix[1 + slot] = qi * p.h_kv + h;
     }
   } else if (q_valid) {
-    // the query's candidates: slots [0, c0) from lane half 0 and
-    // [kCap - c1, kCap) from lane half 1
+    // the query's candidates: slots [1, 1 + c0) from lane half 0 and
+    // [kCap + 1 - c1, kCap + 1) from lane half 1
     const int c0 = half ? cnt_other : cnt, c1 = half ? cnt : cnt_other;
-    const int mine0 = half ? kCap - cnt : 0;
+    const int mine0 = half ? kCap + 1 - cnt : 1;
     for (int i = 0; i < cnt; ++i) {
       const CandSlot c = qcand[mine0 + i];
       int rank = 0;
-      for (int e = 0; e < c0; ++e) {
+      for (int e = 1; e < 1 + c0; ++e) {
         const CandSlot o = qcand[e];
         rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
       }
-      for (int e = kCap - c1; e < kCap; ++e) {
+      for (int e = kCap + 1 - c1; e < kCap + 1; ++e) {
         const CandSlot o = qcand[e];
         rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
       }

@@ -8,10 +8,12 @@
 // G1 * o_sel, rounds once to bfloat16 and writes the output row.
 //
 // Four lanes serve one (token, head) pair, each owning 16 of the 64 dims; a
-// wave covers 16 pairs (one token's 16 heads when h_q = 16, so accumulator,
-// gate and output rows are read and written contiguously).  The lanes walk
-// the selected blocks' token runs (contiguous in sorted order) gathering key
-// and value rows through perm, with an online softmax per pair.
+// wave covers 16 tokens of one head.  Pairs are ordered head-major, so the
+// workgroups running at any time gather from one or two heads' key/value
+// rows (32 MB per head at 131072 tokens), which stay in the MI355X's
+// 256 MB Infinity Cache instead of streaming all heads from HBM.  The lanes
+// walk the selected blocks' token runs (contiguous in sorted order) gathering
+// key and value rows through perm, with an online softmax per pair.
 #include <float.h>
 
 #include "ssa_internal.h"
@@ -44,8 +46,8 @@ sel_combine_kernel(FwdParams p) {
   const int64_t pair = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 2;
   const int64_t n_pairs = static_cast<int64_t>(p.n) * p.h_q;
   const bool active0 = pair < n_pairs;
-  const int t = active0 ? static_cast<int>(pair / p.h_q) : 0;   // input token order
-  const int h = active0 ? static_cast<int>(pair % p.h_q) : 0;
+  const int h = active0 ? static_cast<int>(pair / p.n) : 0;
+  const int t = active0 ? static_cast<int>(pair % p.n) : 0;      // input token order
   const int g = h;  // one query head per group on this path
 
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);

@@ -337,6 +337,7 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
 __global__ void __launch_bounds__(256)
 seg_stats(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ win_off,
           int32_t* __restrict__ counts) {
+  __shared__ int red[2][4];
   const int nb = counts[SSA_COUNT_NB], nw = counts[SSA_COUNT_NW];
   const int m = nb > nw ? nb : nw;
   int mb = 0, mw = 0;
@@ -349,8 +350,13 @@ seg_stats(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ win_o
     mw = max(mw, __shfl_xor(mw, off));
   }
   if ((threadIdx.x & (kWave - 1)) == 0) {
-    atomicMax(&counts[SSA_COUNT_MAX_BLK], mb);
-    atomicMax(&counts[SSA_COUNT_MAX_WIN], mw);
+    red[0][threadIdx.x >> 6] = mb;
+    red[1][threadIdx.x >> 6] = mw;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // one atomic pair per workgroup
+    atomicMax(&counts[SSA_COUNT_MAX_BLK], max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3])));
+    atomicMax(&counts[SSA_COUNT_MAX_WIN], max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3])));
   }
 }
 
@@ -413,7 +419,7 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
   seg_write<<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
                                         out.counts, out.blk_off, out.win_off, out.win_blk_off,
                                         out.seq_blk_off, out.seq_win_off);
-  const int sgrid = min((n + 255) / 256, 1024);
+  const int sgrid = min((n + 255) / 256, 64);
   seg_stats<<<sgrid, 256, 0, stream>>>(out.blk_off, out.win_off, out.counts);
   return hipGetLastError();
 }
