@@ -11,7 +11,9 @@
 // and one head (4 waves x 32 queries) and streams the sequence's pooled keys
 // and values through a two-slot LDS ring in tiles of 32 blocks: one barrier
 // per tile, global loads issued two tiles ahead, loop unrolled by two so that
-// ring slots and register sets are compile-time constants.  Each tile is a
+// ring slots and register sets are compile-time constants, and a two-stage
+// software pipeline inside each wave (MFMAs of tile n next to the VALU work
+// of tile n - 1).  Each tile is a
 // v_mfma_f32_32x32x16_bf16 product S^T = Kbar Q^T; lane l then holds 16 block
 // logits of query l % 32 (lanes l and l ^ 32 split the row between them).
 //
@@ -48,11 +50,6 @@ constexpr int kD = 64;
 constexpr int kKRow = kD + 8;          // LDS row of a key tile (bf16), padded against bank conflicts
 constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf16)
 
-struct CandSlot {
-  float v;
-  int j;
-};
-
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -77,25 +74,6 @@ __global__ void tile_prefix_kernel(FwdParams p) {
   p.fix[0] = 0;
 }
 
-// Runs step(rel, slot, mask) for rel = 0 .. n - 1 with ring slot rel & 1 as
-// a compile-time constant; only the first and last tile (the ones that can
-// be partial) take the masking path.
-template <typename Step>
-__device__ __forceinline__ void run_tiles(int n, Step&& step) {
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using M0 = std::false_type;
-  using M1 = std::true_type;
-  step(0, S0{}, M1{});
-  int rel = 1;
-  for (; rel + 2 < n; rel += 2) {
-    step(rel, S1{}, M0{});
-    step(rel + 1, S0{}, M0{});
-  }
-  if (rel < n) step(rel, S1{}, M1{});
-  if (rel + 1 < n) step(rel + 1, S0{}, M1{});
-}
-
 template <int KMAX>
 __global__ void __launch_bounds__(256, 3)
 cmp_mfma_kernel(FwdParams p) {
@@ -105,8 +83,11 @@ cmp_mfma_kernel(FwdParams p) {
   __shared__ __align__(16) uint16_t k_lds[2][kKeyTile * kKRow];
   __shared__ __align__(16) uint16_t v_lds[2][kD * kVRow];
   // per query kCap data slots 1..kCap plus a sink slot at each end that
-  // absorbs writes past the capacity
-  __shared__ __align__(16) CandSlot cand[4 * 32 * (kCap + 2)];
+  // absorbs writes past the capacity: the logit, and the block id relative to
+  // the sequence's first key tile (sequences with 65536 or more blocks take
+  // the fallback for every query)
+  __shared__ float cand_v[4 * 32 * (kCap + 2)];
+  __shared__ uint16_t cand_j[4 * 32 * (kCap + 2)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,8 +154,8 @@ cmp_mfma_kernel(FwdParams p) {
     return s;
   };
   // keys of a partial tile outside [j0, j1) get -FLT_MAX
-  auto mask = [&](int kt, f32x16& s) {
-    if (kt * kKeyTile >= j0 && (kt + 1) * kKeyTile <= j1) return;
+  auto mask = [&](int rel, f32x16& s) {
+    const int kt = kt0 + rel;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = kt * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -182,33 +163,60 @@ cmp_mfma_kernel(FwdParams p) {
     }
   };
 
+  // Both passes run a two-stage software pipeline over the key tiles: step
+  // `rel` issues the MFMAs of tile rel while the VALU works on the logits of
+  // tile rel - 1, which are already in registers.  MFMA and VALU overlap only
+  // within one wave's instruction stream on this hardware, so each wave needs
+  // independent MFMA and VALU work side by side.  The first and last tile (the
+  // only ones that can be partial) take the masking path.
+
   // ---------------- pass 1: sorted list of this lane's KMAX largest group maxima
   float L[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) L[i] = -FLT_MAX;
+  auto list_insert = [&](const f32x16& s) {
+    float m = fmaxf(s[0], fmaxf(s[1], s[2]));
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+    m = fmaxf(m, s[15]);
+#pragma unroll
+    for (int i = KMAX - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
+    L[0] = fmaxf(L[0], m);
+  };
   {
-    // ring: LDS slot (rel & 1) holds tile rel; register set (rel & 1) holds
-    // the tile two ahead of the one being stored
+    // ring: LDS slot (rel & 1) holds key tile rel; register set (rel & 1)
+    // holds the tile two ahead of the one being stored
     u32x4 kr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     *reinterpret_cast<u32x4*>(ks_dst) = load_k(0);
     if (n_kt > 1) kr[1] = load_k(1);
     if (n_kt > 2) kr[0] = load_k(2);
-    auto step = [&](int rel, auto slot_c, auto mask_c) {
+    f32x16 s_prev;
+    auto step = [&](int rel, auto slot_c, auto valu_c) {
       constexpr int slot = decltype(slot_c)::value;
-      __syncthreads();  // tile rel stored; slot of tile rel - 1 free
+      constexpr int valu = decltype(valu_c)::value;  // 0: none, 1: masked, 2: interior
+      __syncthreads();  // key tile rel stored; the slot of tile rel - 1 is free
       if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
       if (rel + 3 < n_kt) kr[slot ^ 1] = load_k(rel + 3);
-      f32x16 s = qk(slot);
-      if (decltype(mask_c)::value) mask(kt0 + rel, s);
-      float m = fmaxf(s[0], fmaxf(s[1], s[2]));
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
-      m = fmaxf(m, s[15]);
-#pragma unroll
-      for (int i = KMAX - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
-      L[0] = fmaxf(L[0], m);
+      const f32x16 s_new = qk(slot);
+      if (valu == 1) mask(rel - 1, s_prev);
+      if (valu != 0) list_insert(s_prev);
+      s_prev = s_new;
     };
-    run_tiles(n_kt, step);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using V0 = std::integral_constant<int, 0>;
+    using V1 = std::integral_constant<int, 1>;
+    using V2 = std::integral_constant<int, 2>;
+    step(0, S0{}, V0{});
+    if (n_kt > 1) step(1, S1{}, V1{});
+    int rel = 2;
+    for (; rel + 1 < n_kt; rel += 2) {
+      step(rel, S0{}, V2{});
+      step(rel + 1, S1{}, V2{});
+    }
+    if (rel < n_kt) step(rel, S0{}, V2{});
+    mask(n_kt - 1, s_prev);
+    list_insert(s_prev);
   }
   // row maximum, and the best lower bound on the KMAX-th largest logit (hence
   // on the k-th, k <= KMAX): for any split a + b = KMAX the two lanes hold a
@@ -230,61 +238,90 @@ cmp_mfma_kernel(FwdParams p) {
   // half 1 writes kCap, kCap - 1, ... downward; a write past the capacity
   // lands in the sink slot (0 or kCap + 1) and the query goes to the fallback
   const int qbase = (wv * 32 + (lane & 31)) * (kCap + 2);
-  CandSlot* const qcand = &cand[qbase];
   int cpos = qbase + (half ? kCap : 1);
   const int climit = qbase + (half ? 0 : kCap + 1);
   const int cstep = half ? -1 : 1;
   const float tau_eff = q_valid ? tau : __builtin_inff();  // columns without a query never hit
   const int key_lane = 4 * half;
+  // probabilities, row sums and candidates of tile rel's logits; returns P^T
+  // as two bf16 B operands
+  auto softmax_tile = [&](int rel, const f32x16& s, bf16x8 (&pb)[2]) {
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
+      if (r & 1) lsum1 += pr[r]; else lsum0 += pr[r];
+    }
+    const int key0 = rel * kKeyTile + key_lane;   // relative to the first key tile
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (s[r] >= tau_eff) {
+        cand_v[cpos] = s[r];
+        cand_j[cpos] = static_cast<uint16_t>(key0 + 8 * (r >> 2) + (r & 3));
+        cpos = (cpos == climit) ? cpos : cpos + cstep;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+  };
+  auto pv = [&](int slot, const bf16x8 (&pb)[2]) {
+    const uint16_t* vl = va + slot * (kD * kVRow);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 16 * ks), pb[ks], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow + 16 * ks), pb[ks], o1, 0, 0, 0);
+    }
+  };
   {
+    // key slot (rel & 1) holds key tile rel (read by the MFMAs of step rel);
+    // value slot (rel & 1) holds value tile rel (read by step rel + 1)
     u32x4 kr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     u32x4 vr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     __syncthreads();  // every wave is done with pass 1's ring
     *reinterpret_cast<u32x4*>(ks_dst) = load_k(0);
-    *reinterpret_cast<u32x4*>(vs_dst) = load_v(0);
-    if (n_kt > 1) { kr[1] = load_k(1); vr[1] = load_v(1); }
-    if (n_kt > 2) { kr[0] = load_k(2); vr[0] = load_v(2); }
-    auto step = [&](int rel, auto slot_c, auto mask_c) {
+    if (n_kt > 1) kr[1] = load_k(1);
+    if (n_kt > 2) kr[0] = load_k(2);
+    vr[0] = load_v(0);
+    if (n_kt > 1) vr[1] = load_v(1);
+    f32x16 s_prev;
+    auto step = [&](int rel, auto slot_c, auto valu_c) {
       constexpr int slot = decltype(slot_c)::value;
-      __syncthreads();
-      if (rel + 1 < n_kt) {
-        *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
-        *reinterpret_cast<u32x4*>(vs_dst + (slot ^ 1) * (kD * kVRow)) = vr[slot ^ 1];
+      constexpr int valu = decltype(valu_c)::value;  // 0: none, 1: masked, 2: interior
+      __syncthreads();  // key tile rel and value tile rel - 1 stored; older slots free
+      if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
+      *reinterpret_cast<u32x4*>(vs_dst + slot * (kD * kVRow)) = vr[slot];
+      if (rel + 3 < n_kt) kr[slot ^ 1] = load_k(rel + 3);
+      if (rel + 2 < n_kt) vr[slot] = load_v(rel + 2);
+      const f32x16 s_new = qk(slot);
+      if (valu != 0) {
+        if (valu == 1) mask(rel - 1, s_prev);
+        bf16x8 pb[2];
+        softmax_tile(rel - 1, s_prev, pb);
+        pv(slot ^ 1, pb);
       }
-      if (rel + 3 < n_kt) {
-        kr[slot ^ 1] = load_k(rel + 3);
-        vr[slot ^ 1] = load_v(rel + 3);
-      }
-      const int kt = kt0 + rel;
-      f32x16 s = qk(slot);
-      if (decltype(mask_c)::value) mask(kt, s);
-      float pr[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
-        if (r & 1) lsum1 += pr[r]; else lsum0 += pr[r];
-      }
-      const int key0 = kt * kKeyTile + key_lane;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (s[r] >= tau_eff) {
-          cand[cpos] = CandSlot{s[r], key0 + 8 * (r >> 2) + (r & 3)};
-          cpos = (cpos == climit) ? cpos : cpos + cstep;
-        }
-      }
-      bf16x8 pb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
-      const uint16_t* vl = va + slot * (kD * kVRow);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 16 * ks), pb[ks], o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow + 16 * ks), pb[ks], o1, 0, 0, 0);
-      }
+      s_prev = s_new;
     };
-    run_tiles(n_kt, step);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using V0 = std::integral_constant<int, 0>;
+    using V1 = std::integral_constant<int, 1>;
+    using V2 = std::integral_constant<int, 2>;
+    step(0, S0{}, V0{});
+    if (n_kt > 1) step(1, S1{}, V1{});
+    int rel = 2;
+    for (; rel + 1 < n_kt; rel += 2) {
+      step(rel, S0{}, V2{});
+      step(rel + 1, S1{}, V2{});
+    }
+    if (rel < n_kt) step(rel, S0{}, V2{});
+    // last tile: its values were stored by the final step
+    __syncthreads();
+    mask(n_kt - 1, s_prev);
+    bf16x8 pb[2];
+    softmax_tile(n_kt - 1, s_prev, pb);
+    pv((n_kt - 1) & 1, pb);
   }
   // appended so far (a pointer parked on the sink slot counts as overflow)
   const int cnt = half ? qbase + kCap - cpos : cpos - (qbase + 1);
@@ -309,7 +346,9 @@ cmp_mfma_kernel(FwdParams p) {
   // ---------------- exact top-k among the candidates
   wave_lds_sync();
   const int cnt_other = __shfl_xor(cnt, 32);
-  const bool overflow = cnt + cnt_other > kCap - 1;  // kCap - 1: a lane parked on its sink also counts
+  // kCap - 1: a lane parked on its sink also counts; relative block ids
+  // must fit 16 bits
+  const bool overflow = cnt + cnt_other > kCap - 1 || n_kt * kKeyTile > 65536;
   const int k_eff = min(p.topk, nbs);
   int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + h) * p.topk;
   if (q_valid && overflow) {
@@ -321,19 +360,21 @@ cmp_mfma_kernel(FwdParams p) {
     // the query's candidates: slots [1, 1 + c0) from lane half 0 and
     // [kCap + 1 - c1, kCap + 1) from lane half 1
     const int c0 = half ? cnt_other : cnt, c1 = half ? cnt : cnt_other;
-    const int mine0 = half ? kCap + 1 - cnt : 1;
+    const int mine0 = qbase + (half ? kCap + 1 - cnt : 1);
+    const int jbase = kt0 * kKeyTile;
     for (int i = 0; i < cnt; ++i) {
-      const CandSlot c = qcand[mine0 + i];
+      const float cv = cand_v[mine0 + i];
+      const int cj = cand_j[mine0 + i];
       int rank = 0;
-      for (int e = 1; e < 1 + c0; ++e) {
-        const CandSlot o = qcand[e];
-        rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
+      for (int e = qbase + 1; e < qbase + 1 + c0; ++e) {
+        const float ov = cand_v[e];
+        rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
       }
-      for (int e = kCap + 1 - c1; e < kCap + 1; ++e) {
-        const CandSlot o = qcand[e];
-        rank += (o.v > c.v) || (o.v == c.v && o.j < c.j);
+      for (int e = qbase + kCap + 1 - c1; e < qbase + kCap + 1; ++e) {
+        const float ov = cand_v[e];
+        rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
       }
-      if (rank < k_eff) out_sel[rank] = c.j;
+      if (rank < k_eff) out_sel[rank] = jbase + cj;
     }
     if (half == 0)
       for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
