@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -137,6 +139,15 @@ def main():
     def step():
         b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
         ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd)
+
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+        # readings calibrate the same counters of the SSA kernels
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

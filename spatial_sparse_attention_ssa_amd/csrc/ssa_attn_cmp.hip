@@ -5,33 +5,46 @@
 // its sequence, and the same query-to-block scores choose the top-k blocks
 // for the selection branch.  With one query head per key/value group the
 // score order is the logit order (softmax is monotone), so the ranking uses
-// the float32 logits; ties go to the lower block id.
+// float32 logits; ties go to the lower block id.
 //
-// Work split: a workgroup owns 128 consecutive sorted queries of one sequence
-// and one head (4 waves x 32 queries) and streams the sequence's pooled keys
-// and values through a two-slot LDS ring in tiles of 32 blocks: one barrier
-// per tile, global loads issued two tiles ahead, loop unrolled by two so that
-// ring slots and register sets are compile-time constants, and a two-stage
-// software pipeline inside each wave (MFMAs of tile n next to the VALU work
-// of tile n - 1).  Each tile is a
-// v_mfma_f32_32x32x16_bf16 product S^T = Kbar Q^T; lane l then holds 16 block
-// logits of query l % 32 (lanes l and l ^ 32 split the row between them).
+// Work split: a workgroup owns 256 consecutive sorted queries of one sequence
+// and one head; each of its 4 waves owns 64 queries as two 32-query blocks A
+// and B.  The sequence's pooled keys and values stream through a two-slot LDS
+// ring in tiles of 32 blocks (one barrier per tile, global loads one tile
+// ahead).  A wave reads each tile's MFMA operands from LDS once into registers
+// and uses them for both query blocks, which halves the LDS traffic per MFMA
+// against one block per wave.  Each product is a v_mfma_f32_32x32x16_bf16
+// S^T = Kbar Q^T; lane l then holds 16 block logits of query l % 32 of a block
+// (lanes l and l ^ 32 split the row between them).  The two blocks form a
+// software pipeline inside the wave: the MFMAs of one block are issued next to
+// the VALU work of the other (MFMA and VALU overlap only within one wave's
+// instruction stream on this hardware).
 //
 // Two passes over the keys:
-//  1. scan: per lane, the maximum of each tile's 16 logits (a "group max") is
-//     merged into a sorted list of the KMAX largest group maxima with v_med3
-//     (for a descending list L, inserting x gives L'[i] = med3(L[i-1], x, L[i])).
-//     The row maximum is max(L0 of both lanes).  For every split a + b = KMAX
-//     the two lanes hold a + b distinct elements no smaller than
-//     min(L_A[a-1], L_B[b-1]); the largest such value, tau, bounds the KMAX-th
-//     (so also the k-th, k <= KMAX) largest logit from below.
-//  2. attend: recompute S, p = exp2((s - m) * scale * log2 e) with the exact
-//     row maximum m (no rescaling), O^T += Vbar^T P^T on MFMA, and append the
-//     logits >= tau with their block ids to the query's LDS candidate list
-//     (its two lanes fill it from opposite ends).  Afterwards
-//     each candidate's rank among the query's candidates (value descending,
-//     block ascending) places it in the output.  A query whose list overflows
-//     goes to the exact fallback kernel below.
+//  1. scan: per lane and block, the maximum of the lane's 16 logits of a tile
+//     (a "group max") is merged into a sorted list of the KMAX largest group
+//     maxima with v_med3 (for a descending list L, inserting x gives
+//     L'[i] = med3(L[i-1], x, L[i])).  The row maximum is max(L0 of both
+//     lanes).  For every split a + b = KMAX the two lanes hold a + b distinct
+//     elements no smaller than min(L_A[a-1], L_B[b-1]); the largest such value,
+//     tau, bounds the KMAX-th (so also the k-th, k <= KMAX) largest logit from
+//     below.
+//  2. attend: x = (s - tau') * scale * log2 e with tau' = tau lowered by a
+//     small relative slack (rounding differences between the passes); the
+//     sign bit of x says whether the logit can be in the top-k, and p = 2^x is
+//     the softmax numerator shifted by tau' instead of the row maximum (the
+//     shift cancels in the normalisation; a row whose maximum lies so far above
+//     tau' that 2^x could overflow uses the maximum and takes the fallback).
+//     O^T += Vbar^T P^T on MFMA with P truncated to bf16 (one v_perm_b32 per
+//     pair; the mean truncation loss is compensated by a constant factor), the
+//     row sum over the float32 p, and one v_alignbit per logit packs the 16
+//     sign bits of a tile; a tile with any candidate appends one word (tile,
+//     bit mask) to the lane's LDS list.
+//     There is no per-logit branch.
+// Afterwards each lane recomputes its candidates' logits in float32 from the
+// pooled keys, and each candidate's rank among the query's candidates (value
+// descending, block ascending) places it in the output.  A query whose lists
+// overflow goes to the exact fallback kernel below.
 #include <float.h>
 
 #include <type_traits>
@@ -49,6 +62,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kD = 64;
 constexpr int kKRow = kD + 8;          // LDS row of a key tile (bf16), padded against bank conflicts
 constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf16)
+constexpr int kKTileElems = kKeyTile * kKRow;
+constexpr int kVTileElems = kD * kVRow;
+constexpr int kBlockQ = 32;            // queries per MFMA column block
+constexpr int kGroupTiles = 1;         // key tiles per pass-1 group
+// bf16 P by truncation: the mean relative loss of truncating a float32 with
+// a log-uniform mantissa to 8 significant bits is 2^-8 * (1/ln 2) * (1/2);
+// p is scaled up by the inverse factor (an exponent offset of log2 of it) and
+// the row sum divided by it again, so P V and the row sum agree on average
+constexpr float kTruncLog2 = 0.0040711f;   // log2(1 / (1 - 2^-8 * 0.5 / ln 2))
+constexpr float kTruncInv = 0.99718215f;   // 1 - 2^-8 * 0.5 / ln 2
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -60,7 +83,7 @@ __device__ __forceinline__ void seq_token_range(const FwdParams& p, int b, int* 
   *s1 = p.win_off[p.seq_win_off[b + 1]];
 }
 
-// tile_pre[b] = number of 128-query tiles of sequences before b
+// tile_pre[b] = number of query tiles of sequences before b
 __global__ void tile_prefix_kernel(FwdParams p) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int run = 0;
@@ -75,23 +98,63 @@ __global__ void tile_prefix_kernel(FwdParams p) {
 }
 
 template <int KMAX>
-__global__ void __launch_bounds__(256, 3)
-cmp_mfma_kernel(FwdParams p) {
-  // candidate slots per query, shared by its two lanes (with the bound below
+struct CmpShape {
+  // candidate slots per query, shared by its two lanes (with the bound above
   // a query rarely has more than KMAX + 6; overflow goes to the fallback)
-  constexpr int kCap = KMAX + KMAX / 2;
-  __shared__ __align__(16) uint16_t k_lds[2][kKeyTile * kKRow];
-  __shared__ __align__(16) uint16_t v_lds[2][kD * kVRow];
-  // per query kCap data slots 1..kCap plus a sink slot at each end that
-  // absorbs writes past the capacity: the logit, and the block id relative to
-  // the sequence's first key tile (sequences with 65536 or more blocks take
-  // the fallback for every query)
-  __shared__ float cand_v[4 * 32 * (kCap + 2)];
-  __shared__ uint16_t cand_j[4 * 32 * (kCap + 2)];
+  static constexpr int kCap = KMAX + KMAX / 2 - 1;
+  // hit-tile words per lane and block (a lane typically has about KMAX / 2
+  // candidates)
+  static constexpr int kEnt = KMAX <= 16 ? 20 : 36;
+  static constexpr int kRingBytes = 2 * (kKTileElems + kVTileElems) * 2;
+  // candidate lists of one query block of every wave (the blocks take turns)
+  static constexpr int kCandSlots = 4 * kBlockQ * (kCap + 2);
+  static constexpr int kCandBytes = kCandSlots * 6;
+  static constexpr int kSmem = kRingBytes > kCandBytes ? kRingBytes : kCandBytes;
+};
+
+// Per-lane state of one 32-query block.
+template <int KMAX>
+struct QBlock {
+  bf16x8 qb[4];       // Q^T B operand: query (l % 32), d = 16 ks + 8 half + 0..7
+  const uint16_t* q_row;
+  int qi;             // sorted position
+  int t;              // token (input order)
+  bool valid;
+  float L[KMAX];      // pass 1: descending list of group maxima
+  float g;            // pass 1: running maximum of the open group
+  f32x16 s;           // logits of the tile in flight
+  f32x16 o0, o1;      // O^T, dims 0..31 and 32..63
+  float l0, l1;       // row-sum partials
+  float k0;           // exponent offset: x = s * c2 + k0
+  uint32_t f_or, f_and;
+  bool to_fix;        // the fallback computes this query's top-k
+  int ecnt;           // hit-tile words written
+};
+
+template <int KMAX>
+__global__ void __launch_bounds__(256, 2)
+cmp_mfma_kernel(FwdParams p) {
+  using Shape = CmpShape<KMAX>;
+  constexpr int kCap = Shape::kCap;
+  constexpr int kEnt = Shape::kEnt;
+  // the key/value ring while the passes run; afterwards the same bytes hold
+  // the candidate lists of one query block: per query kCap data slots
+  // 1..kCap plus a sink slot at each end that absorbs writes past the
+  // capacity (the logit, and the block id relative to the sequence's first
+  // key tile; sequences with 65536 or more blocks take the fallback)
+  __shared__ __align__(16) uint8_t smem[Shape::kSmem];
+  // hit-tile words: word e of block x of thread t at [(2 e + x) * 256 + t];
+  // word kEnt is a sink
+  __shared__ uint32_t ent[(kEnt + 1) * 2 * 256];
+  uint16_t* const k_lds = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const v_lds = k_lds + 2 * kKTileElems;
+  float* const cand_v = reinterpret_cast<float*>(smem);
+  uint16_t* const cand_j = reinterpret_cast<uint16_t*>(smem + Shape::kCandSlots * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  const int half = lane >> 5;          // which 8-wide k slice / which half of the keys
   const int h = blockIdx.y;            // query head == key/value head
   const int tile = blockIdx.x;
   if (tile >= p.tile_pre[p.batch]) return;  // uniform over the workgroup
@@ -110,21 +173,21 @@ cmp_mfma_kernel(FwdParams p) {
   const int j0 = p.seq_blk_off[b], j1 = p.seq_blk_off[b + 1];
   const int nbs = j1 - j0;
 
-  // this lane's query (column l % 32 of the wave's 32 queries)
-  const int qi = q_begin + wv * 32 + (lane & 31);
-  const bool q_valid = qi < q_end;
-  const int t = q_valid ? p.perm[qi] : 0;
-  const int half = lane >> 5;          // which 8-wide k slice / which half of the keys
-
-  // Q^T as the B operand: lane holds query (l % 32), d = 16 ks + 8 half + 0..7
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  bf16x8 qb[4];
+  QBlock<KMAX> blk[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (q_valid)
-      u = *reinterpret_cast<const u32x4*>(Q + (static_cast<int64_t>(t) * p.h_q + h) * kD + 16 * ks + 8 * half);
-    qb[ks] = __builtin_bit_cast(bf16x8, u);
+  for (int x = 0; x < 2; ++x) {
+    QBlock<KMAX>& B = blk[x];
+    B.qi = q_begin + wv * 64 + x * kBlockQ + (lane & 31);
+    B.valid = B.qi < q_end;
+    B.t = B.valid ? p.perm[B.qi] : 0;
+    B.q_row = Q + (static_cast<int64_t>(B.t) * p.h_q + h) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (B.valid) u = *reinterpret_cast<const u32x4*>(B.q_row + 16 * ks + 8 * half);
+      B.qb[ks] = __builtin_bit_cast(bf16x8, u);
+    }
   }
 
   const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(h) * p.nb_cap * kD;
@@ -139,246 +202,367 @@ cmp_mfma_kernel(FwdParams p) {
   const uint16_t* vg = VT + (static_cast<int64_t>(kt0) * kD + v_row) * kKeyTile + 8 * v_chunk;
   auto load_k = [&](int rel) { return *reinterpret_cast<const u32x4*>(kg + static_cast<int64_t>(rel) * kKeyTile * kD); };
   auto load_v = [&](int rel) { return *reinterpret_cast<const u32x4*>(vg + static_cast<int64_t>(rel) * kKeyTile * kD); };
-  uint16_t* const ks_dst = &k_lds[0][k_row * kKRow + 8 * k_chunk];
-  uint16_t* const vs_dst = &v_lds[0][v_row * kVRow + 8 * v_chunk];
-  const uint16_t* const ka = &k_lds[0][(lane & 31) * kKRow + 8 * half];
-  const uint16_t* const va = &v_lds[0][(lane & 31) * kVRow + 8 * half];
+  const int ks_dst = k_row * kKRow + 8 * k_chunk;
+  const int vs_dst = v_row * kVRow + 8 * v_chunk;
+  const int ka = (lane & 31) * kKRow + 8 * half;
+  const int va = (lane & 31) * kVRow + 8 * half;
 
-  // S^T of the key tile in ring slot `slot`
-  auto qk = [&](int slot) {
-    const uint16_t* kl = ka + slot * (kKeyTile * kKRow);
+  // MFMA A operands of key tile rel (slot rel & 1): rows = blocks, k = dims
+  auto read_k = [&](int rel, bf16x8 (&a)[4]) {
+    const uint16_t* kl = k_lds + (rel & 1) * kKTileElems + ka;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = lds_b128(kl + 16 * ks);
+  };
+  // MFMA A operands of value tile rel: rows = dims (0..31, 32..63), k = blocks
+  auto read_v = [&](int rel, bf16x8 (&a)[4]) {
+    const uint16_t* vl = v_lds + (rel & 1) * kVTileElems + va;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      a[2 * ks] = lds_b128(vl + 16 * ks);
+      a[2 * ks + 1] = lds_b128(vl + 32 * kVRow + 16 * ks);
+    }
+  };
+  auto qk = [&](const bf16x8 (&a)[4], const bf16x8 (&qb)[4]) {
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(kl + 16 * ks), qb[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qb[ks], s, 0, 0, 0);
     return s;
   };
-  // keys of a partial tile outside [j0, j1) get -FLT_MAX
+  // keys of tile rel outside [j0, j1) get -FLT_MAX; returns the in-range mask
+  // (bit 15 - r for accumulator entry r)
   auto mask = [&](int rel, f32x16& s) {
     const int kt = kt0 + rel;
+    uint32_t valid = 0u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = kt * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (j < j0 || j >= j1) s[r] = -FLT_MAX;
+      const bool ok = j >= j0 && j < j1;
+      if (!ok) s[r] = -FLT_MAX;
+      valid = (valid << 1) | (ok ? 1u : 0u);
+    }
+    return valid;
+  };
+
+  // Tile order of both passes: the first and the last tile are the only ones
+  // that can hold keys outside [j0, j1); they run in peeled steps with the
+  // masking code, the steps in between without it.
+  using kT = std::true_type;
+  using kF = std::false_type;
+  auto run_tiles = [&](auto step) {
+    step(0, kT{}, kF{}, kF{});
+    if (n_kt == 2) {
+      step(1, kT{}, kT{}, kT{});
+    } else if (n_kt > 2) {
+      step(1, kF{}, kT{}, kT{});
+      for (int rel = 2; rel < n_kt - 1; ++rel) step(rel, kF{}, kT{}, kF{});
+      step(n_kt - 1, kT{}, kT{}, kF{});
     }
   };
 
-  // Both passes run a two-stage software pipeline over the key tiles: step
-  // `rel` issues the MFMAs of tile rel while the VALU works on the logits of
-  // tile rel - 1, which are already in registers.  MFMA and VALU overlap only
-  // within one wave's instruction stream on this hardware, so each wave needs
-  // independent MFMA and VALU work side by side.  The first and last tile (the
-  // only ones that can be partial) take the masking path.
-
-  // ---------------- pass 1: sorted list of this lane's KMAX largest group maxima
-  float L[KMAX];
+  // ---------------- pass 1: sorted lists of the KMAX largest group maxima
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) L[i] = -FLT_MAX;
-  auto list_insert = [&](const f32x16& s) {
-    float m = fmaxf(s[0], fmaxf(s[1], s[2]));
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
-    m = fmaxf(m, s[15]);
+    for (int i = 0; i < KMAX; ++i) blk[x].L[i] = -FLT_MAX;
+  // a group is kGroupTiles consecutive tiles of one lane (16 logits each); its
+  // running maximum goes into the list when the group is complete
+  auto group_max = [&](QBlock<KMAX>& B, int rel, auto masked) {
+    if (decltype(masked)::value) mask(rel, B.s);
+    const f32x16& s = B.s;
+    float m = fmaxf(B.g, fmaxf(s[0], s[1]));
 #pragma unroll
-    for (int i = KMAX - 1; i >= 1; --i) L[i] = __builtin_amdgcn_fmed3f(L[i - 1], m, L[i]);
-    L[0] = fmaxf(L[0], m);
+    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+    B.g = m;
+  };
+  auto list_insert = [&](QBlock<KMAX>& B) {
+    const float m = B.g;
+#pragma unroll
+    for (int i = KMAX - 1; i >= 1; --i) B.L[i] = __builtin_amdgcn_fmed3f(B.L[i - 1], m, B.L[i]);
+    B.L[0] = fmaxf(B.L[0], m);
+    B.g = -FLT_MAX;
   };
   {
-    // ring: LDS slot (rel & 1) holds key tile rel; register set (rel & 1)
-    // holds the tile two ahead of the one being stored
-    u32x4 kr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    *reinterpret_cast<u32x4*>(ks_dst) = load_k(0);
-    if (n_kt > 1) kr[1] = load_k(1);
-    if (n_kt > 2) kr[0] = load_k(2);
-    f32x16 s_prev;
-    auto step = [&](int rel, auto slot_c, auto valu_c) {
-      constexpr int slot = decltype(slot_c)::value;
-      constexpr int valu = decltype(valu_c)::value;  // 0: none, 1: masked, 2: interior
-      __syncthreads();  // key tile rel stored; the slot of tile rel - 1 is free
-      if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
-      if (rel + 3 < n_kt) kr[slot ^ 1] = load_k(rel + 3);
-      const f32x16 s_new = qk(slot);
-      if (valu == 1) mask(rel - 1, s_prev);
-      if (valu != 0) list_insert(s_prev);
-      s_prev = s_new;
+    blk[0].g = blk[1].g = -FLT_MAX;
+    u32x4 kr = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(k_lds + ks_dst) = load_k(0);
+    if (n_kt > 1) kr = load_k(1);
+    // step rel: S of block A for tile rel next to block B's update for tile
+    // rel - 1, then S of block B next to block A's update
+    auto step = [&](int rel, auto mask_a, auto has_b, auto mask_b) {
+      __syncthreads();  // key tile rel stored; everyone is done with tile rel - 1
+      if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTileElems + ks_dst) = kr;
+      if (rel + 2 < n_kt) kr = load_k(rel + 2);
+      bf16x8 a[4];
+      read_k(rel, a);
+      const f32x16 sa = qk(a, blk[0].qb);
+      if (decltype(has_b)::value) {
+        group_max(blk[1], rel - 1, mask_b);
+        if ((rel - 1) % kGroupTiles == kGroupTiles - 1) list_insert(blk[1]);
+      }
+      blk[1].s = qk(a, blk[1].qb);
+      blk[0].s = sa;
+      group_max(blk[0], rel, mask_a);
+      if (rel % kGroupTiles == kGroupTiles - 1) list_insert(blk[0]);
     };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using V0 = std::integral_constant<int, 0>;
-    using V1 = std::integral_constant<int, 1>;
-    using V2 = std::integral_constant<int, 2>;
-    step(0, S0{}, V0{});
-    if (n_kt > 1) step(1, S1{}, V1{});
-    int rel = 2;
-    for (; rel + 1 < n_kt; rel += 2) {
-      step(rel, S0{}, V2{});
-      step(rel + 1, S1{}, V2{});
+    run_tiles(step);
+    group_max(blk[1], n_kt - 1, kT{});
+    // the last, partial groups
+    if (n_kt % kGroupTiles != 0) {
+      list_insert(blk[0]);
+      list_insert(blk[1]);
+    } else {
+      list_insert(blk[1]);
     }
-    if (rel < n_kt) step(rel, S0{}, V2{});
-    mask(n_kt - 1, s_prev);
-    list_insert(s_prev);
   }
-  // row maximum, and the best lower bound on the KMAX-th largest logit (hence
-  // on the k-th, k <= KMAX): for any split a + b = KMAX the two lanes hold a
-  // and b distinct elements >= min(L_this[a-1], L_other[b-1])
-  float Lo[KMAX];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) Lo[i] = __shfl_xor(L[i], 32);
-  const float row_max = fmaxf(L[0], Lo[0]);
-  float tau = fmaxf(L[KMAX - 1], Lo[KMAX - 1]);
-#pragma unroll
-  for (int a = 1; a < KMAX; ++a) tau = fmaxf(tau, fminf(L[a - 1], Lo[KMAX - 1 - a]));
 
-  // ---------------- pass 2: probabilities, P V, candidates
+  // ---------------- per-query constants for pass 2
   const float c2 = p.scale * kLog2e;
-  const float mc = row_max * c2;
-  f32x16 o0 = {}, o1 = {};
-  float lsum0 = 0.f, lsum1 = 0.f;
-  // the query's candidate list: lane half 0 writes slots 1, 2, ... upward,
-  // half 1 writes kCap, kCap - 1, ... downward; a write past the capacity
-  // lands in the sink slot (0 or kCap + 1) and the query goes to the fallback
-  const int qbase = (wv * 32 + (lane & 31)) * (kCap + 2);
-  int cpos = qbase + (half ? kCap : 1);
-  const int climit = qbase + (half ? 0 : kCap + 1);
-  const int cstep = half ? -1 : 1;
-  const float tau_eff = q_valid ? tau : __builtin_inff();  // columns without a query never hit
-  const int key_lane = 4 * half;
-  // probabilities, row sums and candidates of tile rel's logits; returns P^T
-  // as two bf16 B operands
-  auto softmax_tile = [&](int rel, const f32x16& s, bf16x8 (&pb)[2]) {
-    float pr[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
-      if (r & 1) lsum1 += pr[r]; else lsum0 += pr[r];
-    }
-    const int key0 = rel * kKeyTile + key_lane;   // relative to the first key tile
+  for (int x = 0; x < 2; ++x) {
+    QBlock<KMAX>& B = blk[x];
+    // row maximum, and the best lower bound on the KMAX-th largest logit
+    // (hence on the k-th, k <= KMAX): for any split a + b = KMAX the two
+    // lanes hold a and b distinct elements >= min(L_this[a-1], L_other[b-1])
+    float Lo[KMAX];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (s[r] >= tau_eff) {
-        cand_v[cpos] = s[r];
-        cand_j[cpos] = static_cast<uint16_t>(key0 + 8 * (r >> 2) + (r & 3));
-        cpos = (cpos == climit) ? cpos : cpos + cstep;
+    for (int i = 0; i < KMAX; ++i) Lo[i] = __shfl_xor(B.L[i], 32);
+    const float row_max = fmaxf(B.L[0], Lo[0]);
+    float tau = fmaxf(B.L[KMAX - 1], Lo[KMAX - 1]);
+#pragma unroll
+    for (int a = 1; a < KMAX; ++a) tau = fmaxf(tau, fminf(B.L[a - 1], Lo[KMAX - 1 - a]));
+    // x = s * c2 + k0: shifted by tau' (sign bit = candidate), or by the row
+    // maximum when fewer than KMAX group maxima exist (every real key is a
+    // candidate) or when 2^x could overflow (the fallback ranks the query)
+    B.k0 = 0.f;
+    B.f_or = 0u;
+    B.f_and = 0u;
+    B.to_fix = false;
+    if (B.valid) {
+      B.f_and = 0xFFFFu;
+      if (tau > -FLT_MAX) {
+        const float tp = tau - (fabsf(tau) + fabsf(row_max)) * (1.0f / 4096.0f);
+        if ((row_max - tp) * c2 <= 64.f) {
+          B.k0 = -tp * c2;
+        } else {
+          B.k0 = -row_max * c2;
+          B.f_and = 0u;
+          B.to_fix = true;
+        }
+      } else {
+        B.k0 = -row_max * c2;
+        B.f_or = 0xFFFFu;
       }
     }
+    B.k0 += kTruncLog2;  // after the sign decisions: the shift is a factor of p only
+    B.o0 = f32x16{};
+    B.o1 = f32x16{};
+    B.l0 = 0.f;
+    B.l1 = 0.f;
+    B.ecnt = 0;
+  }
+
+  // ---------------- pass 2: probabilities, P V, candidate tiles
+  // probabilities, row sums and the candidate word of block x's tile rel;
+  // returns P^T as two bf16 B operands (truncated: v_perm_b32 takes the high
+  // halves of two float32 values)
+  auto softmax_tile = [&](QBlock<KMAX>& B, int x, int rel, bf16x8 (&pb)[2], auto masked) {
+    uint32_t valid = 0xFFFFu;
+    if (decltype(masked)::value) valid = mask(rel, B.s);
+    float pr[16];
+    uint32_t bits = 0u;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int r = 0; r < 16; ++r) {
+      const float xr = fmaf(B.s[r], c2, B.k0);
+      pr[r] = __builtin_amdgcn_exp2f(xr);
+      bits = __builtin_amdgcn_alignbit(bits, __float_as_uint(xr), 31);
+    }
+    // bit 15 - r set: logit r is >= tau' (a clear sign bit; the truncation
+    // offset in k0 lowers tau' a little further, which keeps it a lower bound)
+    const uint32_t hit = (~bits | B.f_or) & valid & B.f_and;
+    ent[(2 * B.ecnt + x) * 256 + tid] = (static_cast<uint32_t>(rel) << 16) | hit;
+    B.ecnt = min(B.ecnt + (hit != 0u ? 1 : 0), kEnt);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
-  };
-  auto pv = [&](int slot, const bf16x8 (&pb)[2]) {
-    const uint16_t* vl = va + slot * (kD * kVRow);
+    for (int r = 0; r < 16; r += 2) {
+      B.l0 += pr[r];
+      B.l1 += pr[r + 1];
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 16 * ks), pb[ks], o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow + 16 * ks), pb[ks], o1, 0, 0, 0);
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        u[e] = __builtin_amdgcn_perm(__float_as_uint(pr[8 * ks + 2 * e + 1]), __float_as_uint(pr[8 * ks + 2 * e]),
+                                     0x07060302u);
+      pb[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  };
+  auto pv = [&](QBlock<KMAX>& B, const bf16x8 (&a)[4], const bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      B.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * ks], pb[ks], B.o0, 0, 0, 0);
+      B.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * ks + 1], pb[ks], B.o1, 0, 0, 0);
     }
   };
   {
-    // key slot (rel & 1) holds key tile rel (read by the MFMAs of step rel);
-    // value slot (rel & 1) holds value tile rel (read by step rel + 1)
-    u32x4 kr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    u32x4 vr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
     __syncthreads();  // every wave is done with pass 1's ring
-    *reinterpret_cast<u32x4*>(ks_dst) = load_k(0);
-    if (n_kt > 1) kr[1] = load_k(1);
-    if (n_kt > 2) kr[0] = load_k(2);
-    vr[0] = load_v(0);
-    if (n_kt > 1) vr[1] = load_v(1);
-    f32x16 s_prev;
-    auto step = [&](int rel, auto slot_c, auto valu_c) {
-      constexpr int slot = decltype(slot_c)::value;
-      constexpr int valu = decltype(valu_c)::value;  // 0: none, 1: masked, 2: interior
-      __syncthreads();  // key tile rel and value tile rel - 1 stored; older slots free
-      if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(ks_dst + (slot ^ 1) * (kKeyTile * kKRow)) = kr[slot ^ 1];
-      *reinterpret_cast<u32x4*>(vs_dst + slot * (kD * kVRow)) = vr[slot];
-      if (rel + 3 < n_kt) kr[slot ^ 1] = load_k(rel + 3);
-      if (rel + 2 < n_kt) vr[slot] = load_v(rel + 2);
-      const f32x16 s_new = qk(slot);
-      if (valu != 0) {
-        if (valu == 1) mask(rel - 1, s_prev);
-        bf16x8 pb[2];
-        softmax_tile(rel - 1, s_prev, pb);
-        pv(slot ^ 1, pb);
-      }
-      s_prev = s_new;
-    };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using V0 = std::integral_constant<int, 0>;
-    using V1 = std::integral_constant<int, 1>;
-    using V2 = std::integral_constant<int, 2>;
-    step(0, S0{}, V0{});
-    if (n_kt > 1) step(1, S1{}, V1{});
-    int rel = 2;
-    for (; rel + 1 < n_kt; rel += 2) {
-      step(rel, S0{}, V2{});
-      step(rel + 1, S1{}, V2{});
+    *reinterpret_cast<u32x4*>(k_lds + ks_dst) = load_k(0);
+    *reinterpret_cast<u32x4*>(v_lds + vs_dst) = load_v(0);
+    if (n_kt > 1) {
+      kr = load_k(1);
+      vr = load_v(1);
     }
-    if (rel < n_kt) step(rel, S0{}, V2{});
-    // last tile: its values were stored by the final step
-    __syncthreads();
-    mask(n_kt - 1, s_prev);
+    bf16x8 va_prev[4];
+    // step rel: S of block A for tile rel next to the softmax and P V of block
+    // B for tile rel - 1, then S of block B next to block A's softmax and P V
+    auto step = [&](int rel, auto mask_a, auto has_b, auto mask_b) {
+      __syncthreads();  // tiles rel stored; everyone is done with the tiles of rel - 1
+      if (rel + 1 < n_kt) {
+        *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTileElems + ks_dst) = kr;
+        *reinterpret_cast<u32x4*>(v_lds + ((rel + 1) & 1) * kVTileElems + vs_dst) = vr;
+      }
+      if (rel + 2 < n_kt) {
+        kr = load_k(rel + 2);
+        vr = load_v(rel + 2);
+      }
+      bf16x8 a[4];
+      read_k(rel, a);
+      const f32x16 sa = qk(a, blk[0].qb);
+      if (decltype(has_b)::value) {
+        bf16x8 pb[2];
+        softmax_tile(blk[1], 1, rel - 1, pb, mask_b);
+        pv(blk[1], va_prev, pb);
+      }
+      blk[1].s = qk(a, blk[1].qb);
+      blk[0].s = sa;
+      read_v(rel, va_prev);
+      bf16x8 pb[2];
+      softmax_tile(blk[0], 0, rel, pb, mask_a);
+      pv(blk[0], va_prev, pb);
+    };
+    run_tiles(step);
     bf16x8 pb[2];
-    softmax_tile(n_kt - 1, s_prev, pb);
-    pv((n_kt - 1) & 1, pb);
+    softmax_tile(blk[1], 1, n_kt - 1, pb, kT{});
+    pv(blk[1], va_prev, pb);
   }
-  // appended so far (a pointer parked on the sink slot counts as overflow)
-  const int cnt = half ? qbase + kCap - cpos : cpos - (qbase + 1);
 
   // ---------------- o_cmp (times its gate) into the branch accumulator
-  const float lsum = lsum0 + lsum1;
-  const float l_q = lsum + __shfl_xor(lsum, 32);
-  if (q_valid) {
-    const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
-    const float f = bf16_bits_to_f32(gt[0]) / l_q;
-    float* dst = p.acc + (static_cast<int64_t>(t) * p.h_q + h) * kD;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int d = 8 * rb + 4 * half;
-      *reinterpret_cast<float4*>(dst + d) =
-          make_float4(o0[4 * rb] * f, o0[4 * rb + 1] * f, o0[4 * rb + 2] * f, o0[4 * rb + 3] * f);
-      *reinterpret_cast<float4*>(dst + 32 + d) =
-          make_float4(o1[4 * rb] * f, o1[4 * rb + 1] * f, o1[4 * rb + 2] * f, o1[4 * rb + 3] * f);
+  for (int x = 0; x < 2; ++x) {
+    QBlock<KMAX>& B = blk[x];
+    const float lsum = B.l0 + B.l1;
+    const float l_q = (lsum + __shfl_xor(lsum, 32)) * kTruncInv;
+    if (B.valid) {
+      const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(B.t) * p.h_q + h) * 3;
+      const float f = bf16_bits_to_f32(gt[0]) / l_q;
+      float* dst = p.acc + (static_cast<int64_t>(B.t) * p.h_q + h) * kD;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int d = 8 * rb + 4 * half;
+        *reinterpret_cast<float4*>(dst + d) =
+            make_float4(B.o0[4 * rb] * f, B.o0[4 * rb + 1] * f, B.o0[4 * rb + 2] * f, B.o0[4 * rb + 3] * f);
+        *reinterpret_cast<float4*>(dst + 32 + d) =
+            make_float4(B.o1[4 * rb] * f, B.o1[4 * rb + 1] * f, B.o1[4 * rb + 2] * f, B.o1[4 * rb + 3] * f);
+      }
     }
   }
 
-  // ---------------- exact top-k among the candidates
-  wave_lds_sync();
-  const int cnt_other = __shfl_xor(cnt, 32);
-  // kCap - 1: a lane parked on its sink also counts; relative block ids
-  // must fit 16 bits
-  const bool overflow = cnt + cnt_other > kCap - 1 || n_kt * kKeyTile > 65536;
+  // ---------------- exact top-k, one query block at a time
+  __syncthreads();  // every wave is done with the ring; its bytes now hold candidate lists
+  const int qbase = (wv * kBlockQ + (lane & 31)) * (kCap + 2);
   const int k_eff = min(p.topk, nbs);
-  int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + h) * p.topk;
-  if (q_valid && overflow) {
-    if (half == 0) {
-      const int slot = atomicAdd(&p.fix[0], 1);
-      p.fix[1 + slot] = qi * p.h_kv + h;
+  const uint16_t* kb0 = KB + static_cast<int64_t>(kt0) * kKeyTile * kD;
+  auto finish = [&](QBlock<KMAX>& B, int x) {
+    // the query's candidate list: lane half 0 writes slots 1, 2, ... upward,
+    // half 1 writes kCap, kCap - 1, ... downward; a write past the capacity
+    // lands in the sink slot (0 or kCap + 1) and the query goes to the fallback
+    int cpos = qbase + (half ? kCap : 1);
+    const int climit = qbase + (half ? 0 : kCap + 1);
+    const int cstep = half ? -1 : 1;
+    int over = (B.ecnt >= kEnt || B.to_fix) ? 1 : 0;
+    if (!over) {
+      for (int e = 0; e < B.ecnt; ++e) {
+        const uint32_t word = ent[(2 * e + x) * 256 + tid];
+        const int base = static_cast<int>(word >> 16) * kKeyTile + 4 * half;
+        uint32_t m = word & 0xFFFFu;
+        while (m != 0u) {
+          const int bpos = 31 - __clz(m);
+          m ^= 1u << bpos;
+          const int r = 15 - bpos;
+          cand_j[cpos] = static_cast<uint16_t>(base + 8 * (r >> 2) + (r & 3));
+          cpos = (cpos == climit) ? cpos : cpos + cstep;
+        }
+      }
     }
-  } else if (q_valid) {
-    // the query's candidates: slots [1, 1 + c0) from lane half 0 and
-    // [kCap + 1 - c1, kCap + 1) from lane half 1
-    const int c0 = half ? cnt_other : cnt, c1 = half ? cnt : cnt_other;
+    // appended so far (a pointer parked on the sink slot counts as overflow)
+    const int cnt = half ? qbase + kCap - cpos : cpos - (qbase + 1);
+    over |= __shfl_xor(over, 32);
+    const int cnt_other = __shfl_xor(cnt, 32);
+    // kCap - 1: a lane parked on its sink also counts; relative block ids
+    // must fit 16 bits
+    const bool overflow = over || cnt + cnt_other > kCap - 1 || n_kt * kKeyTile > 65536;
+
+    // exact float32 logits of this lane's candidates
     const int mine0 = qbase + (half ? kCap + 1 - cnt : 1);
-    const int jbase = kt0 * kKeyTile;
-    for (int i = 0; i < cnt; ++i) {
-      const float cv = cand_v[mine0 + i];
-      const int cj = cand_j[mine0 + i];
-      int rank = 0;
-      for (int e = qbase + 1; e < qbase + 1 + c0; ++e) {
-        const float ov = cand_v[e];
-        rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
+    if (B.valid && !overflow && cnt > 0) {
+      float qf[kD];
+#pragma unroll
+      for (int c = 0; c < kD / 8; ++c) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(B.q_row + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
+          qf[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+        }
       }
-      for (int e = qbase + kCap + 1 - c1; e < qbase + kCap + 1; ++e) {
-        const float ov = cand_v[e];
-        rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
+      for (int i = 0; i < cnt; ++i) {
+        const uint16_t* kr = kb0 + static_cast<int64_t>(cand_j[mine0 + i]) * kD;
+        float sc = 0.f;
+#pragma unroll
+        for (int c = 0; c < kD / 8; ++c) {
+          const u32x4 u = *reinterpret_cast<const u32x4*>(kr + 8 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc = fmaf(qf[8 * c + 2 * e], __uint_as_float(u[e] << 16), sc);
+            sc = fmaf(qf[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), sc);
+          }
+        }
+        cand_v[mine0 + i] = sc;
       }
-      if (rank < k_eff) out_sel[rank] = jbase + cj;
     }
-    if (half == 0)
-      for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
-  }
+    wave_lds_sync();
+    int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(B.t) * p.h_kv + h) * p.topk;
+    if (B.valid && overflow) {
+      if (half == 0) {
+        const int slot = atomicAdd(&p.fix[0], 1);
+        p.fix[1 + slot] = B.qi * p.h_kv + h;
+      }
+    } else if (B.valid) {
+      // the query's candidates: slots [1, 1 + c0) from lane half 0 and
+      // [kCap + 1 - c1, kCap + 1) from lane half 1
+      const int c0 = half ? cnt_other : cnt, c1 = half ? cnt : cnt_other;
+      const int jbase = kt0 * kKeyTile;
+      for (int i = 0; i < cnt; ++i) {
+        const float cv = cand_v[mine0 + i];
+        const int cj = cand_j[mine0 + i];
+        int rank = 0;
+        for (int e = qbase + 1; e < qbase + 1 + c0; ++e) {
+          const float ov = cand_v[e];
+          rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
+        }
+        for (int e = qbase + kCap + 1 - c1; e < qbase + kCap + 1; ++e) {
+          const float ov = cand_v[e];
+          rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
+        }
+        if (rank < k_eff) out_sel[rank] = jbase + cj;
+      }
+      if (half == 0)
+        for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
+    }
+  };
+  finish(blk[0], 0);
+  wave_lds_sync();  // block A's lists are consumed (each wave owns its slots)
+  finish(blk[1], 1);
 }
 
 // Exact top-k for the (sorted position, group) pairs whose candidate list

@@ -118,7 +118,7 @@ struct FwdParams {
 };
 
 constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile
-constexpr int kQueryTile = 128;  // queries per workgroup of the compressed MFMA kernel (4 waves x 32)
+constexpr int kQueryTile = 256;  // queries per workgroup of the compressed MFMA kernel (4 waves x 64)
 
 hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
