@@ -29,6 +29,103 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 WORKLOAD_ID = 3
+WORKLOAD_NAME = "ssa-fwd-1024^3-12prims-131072tok-h16-d64-bf16"
+CALIB_BYTES = 1 << 30       # plain-copy calibration size for the HBM byte counters
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "spatial_sparse_attention_ssa_amd", "csrc")
+# the source file of each timed kernel (with the shared header, its content
+# hash tells whether stored counter readings still describe the kernel)
+KERNEL_SOURCES = {
+    "cmp_mfma_kernel": "ssa_attn_cmp.hip",
+    "topk_fixup_kernel": "ssa_attn_cmp.hip",
+    "win_mfma_kernel": "ssa_attn_win.hip",
+    "sel_combine_kernel": "ssa_attn_sel.hip",
+    "pool_kernel": "ssa_pool.hip",
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "ssa_internal.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(kernel: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}_131072tok_traffic.json")
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel's source changed since."""
+    path = traffic_path(kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def pool_bytes(wl, nb: int) -> float:
+    """Algorithmic HBM bytes of the pooling kernel: every token's K and V row
+    read once (gathered through perm, 4 B per token), pooled rows written."""
+    row = wl.h_kv * wl.head_dim * 2
+    return wl.n_tokens * (2 * row + 4) + 2 * nb * row
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, stats_csv: str | None, commands: dict):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (each with
+    --copy-calibration) into per-kernel HBM bytes per launch; writes
+    profiles/<kernel>_131072tok_traffic.json and prints a markdown table."""
+    import csv
+    from collections import defaultdict
+
+    def load(path, counter):
+        per = defaultdict(list)
+        copy_vals = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
+                if "copyBuffer" in name:
+                    copy_vals.append(val)
+                for k in KERNEL_SOURCES:
+                    if f"::{k}" in name or f" {k}" in name or name.startswith(k):
+                        per[k].append(val)
+        return per, max(copy_vals)
+
+    fetch, copy_f = load(fetch_csv, "FETCH_SIZE")
+    write, copy_w = load(write_csv, "WRITE_SIZE")
+    ff, fw = CALIB_BYTES / copy_f, CALIB_BYTES / copy_w
+    avg_ns = {}
+    if stats_csv:
+        with open(stats_csv) as fh:
+            for r in csv.DictReader(fh):
+                for k in KERNEL_SOURCES:
+                    if f"::{k}" in r["Name"]:
+                        avg_ns[k] = float(r["AverageNs"])
+    print(f"calibration: 1 GiB copy read {copy_f / 2**20:.1f} MiB by FETCH_SIZE (x{ff:.3f}), "
+          f"wrote {copy_w / 2**20:.1f} MiB by WRITE_SIZE (x{fw:.3f})")
+    print("| kernel | FETCH MB/launch (scaled) | WRITE MB/launch (scaled) | HBM MB/launch | avg us | GB/s |")
+    print("|---|---|---|---|---|---|")
+    for k in KERNEL_SOURCES:
+        if k not in fetch or k not in write:
+            continue
+        fb = sum(fetch[k]) / len(fetch[k]) * ff
+        wb = sum(write[k]) / len(write[k]) * fw
+        us = avg_ns.get(k, float("nan")) / 1e3
+        print(f"| {k} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | {us:.1f} | {(fb + wb) / (us * 1e3):.0f} |")
+        rec = {"kernel": k, "workload": WORKLOAD_NAME, "source_sha256": kernel_source_hash(k),
+               "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
+               "fetch_factor": ff, "write_factor": fw, "launches": len(fetch[k]), "commands": commands}
+        with open(traffic_path(k), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
 
 
 def algorithmic_flops(wl, blocks, topk, torch):
@@ -104,8 +201,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 256 MiB device copy (for scaling HBM byte counters)")
+                    help="also run one plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="only summarise two rocprofv3 --pmc runs into profiles/*_traffic.json")
+    ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        cmds = {"fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python bench.py "
+                         "--steps 1 --warmup 1 --no-cpu-baseline --copy-calibration",
+                "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- python bench.py "
+                         "--steps 1 --warmup 1 --no-cpu-baseline --copy-calibration"}
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel_stats, cmds)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -141,13 +248,16 @@ def main():
         ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd)
 
     if args.copy_calibration:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
-        # readings calibrate the same counters of the SSA kernels
-        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        # a plain copy of known size whose source is not cache-resident: its
+        # FETCH_SIZE / WRITE_SIZE counter readings calibrate the same counters
+        # of the SSA kernels
+        src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        evict = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)   # pushes src out of the caches
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, evict, dst
 
     for _ in range(args.warmup):
         step()
@@ -190,6 +300,7 @@ def main():
     achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
     n = wl.n_tokens
     tflops = work["total"] / (ms_step * 1e-3) / 1e12
+    pool_gbs = pool_bytes(wl, work["nb"]) / (stage_ms["pool_kernel"] * 1e-3) / 1e9
 
     line = {
         "metric": "SSA fwd tokens/s and TFLOP/s at 131072 voxel tokens; % bf16 MFMA peak",
@@ -204,7 +315,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "ssa-fwd-1024^3-12prims-131072tok-h16-d64-bf16", "n_tokens": n,
+        "config": {"workload": WORKLOAD_NAME, "n_tokens": n,
                    "grid_res": wl.grid_res, "h_q": wl.h_q, "h_kv": wl.h_kv, "head_dim": wl.head_dim,
                    "m_cmp": wl.m_cmp, "m_win": wl.m_win, "topk": wl.topk, "parallelism": "none"},
         "tflops": tflops,
@@ -213,8 +324,10 @@ def main():
         "work": {k2: work[k2] for k2 in ("cmp", "sel", "win", "mean_sel_tokens", "mean_win_tokens", "nb", "nw")},
         "build_ms": build_ms,
         "stage_ms": stage_ms,
+        "pool_hbm": {"achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pool_gbs / PEAK_HBM_GBS,
+                     "bytes": pool_bytes(wl, work["nb"])},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic(dom)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
