@@ -103,7 +103,7 @@ bool use_mfma_path(const ssa_attn* a) {
 }
 
 struct FwdLayout {
-  size_t kbar, vbar, vbar_t, topk, tile_pre, fix, acc, total;
+  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, total;
 };
 
 FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
@@ -117,6 +117,9 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
   L.topk = off; off += align256(sizeof(int32_t) * n * a->h_kv * a->topk);
   if (use_mfma_path(a)) {
     L.vbar_t = off; off += pooled;
+    const size_t sorted = align256(static_cast<size_t>(elt_bytes(a->dtype)) * a->h_kv * n * a->head_dim);
+    L.k_s = off; off += sorted;
+    L.v_s = off; off += sorted;
     L.tile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     L.fix = off; off += align256(sizeof(int32_t) * (1 + n * a->h_kv));
     L.acc = off; off += align256(sizeof(float) * n * a->h_q * a->head_dim);
@@ -280,6 +283,8 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
   p.topk_idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + lay.topk);
   if (use_mfma_path(attn)) {
     p.vbar_t = w + lay.vbar_t;
+    p.k_s = w + lay.k_s;
+    p.v_s = w + lay.v_s;
     p.tile_pre = reinterpret_cast<int32_t*>(w + lay.tile_pre);
     p.fix = reinterpret_cast<int32_t*>(w + lay.fix);
     p.acc = reinterpret_cast<float*>(w + lay.acc);

@@ -8,12 +8,15 @@
 // G1 * o_sel, rounds once to bfloat16 and writes the output row.
 //
 // Four lanes serve one (token, head) pair, each owning 16 of the 64 dims; a
-// wave covers 16 tokens of one head.  Pairs are ordered head-major, so the
-// workgroups running at any time gather from one or two heads' key/value
-// rows (32 MB per head at 131072 tokens), which stay in the MI355X's
-// 256 MB Infinity Cache instead of streaming all heads from HBM.  The lanes
-// walk the selected blocks' token runs (contiguous in sorted order) gathering
-// key and value rows through perm, with an online softmax per pair.
+// wave covers 16 pairs of one head (pairs are ordered head-major, so the rows
+// gathered at any time belong to one or two heads and stay in the Infinity
+// Cache).  Keys and values come from the head-major sorted copies, where a
+// block is a contiguous run of rows.  First the pair's lanes turn its block
+// list into a list of row positions in LDS (each lane expands every fourth
+// block; one prefix over the four lanes places them), then the lanes stream
+// the rows four at a time (16 loads in flight per lane) with an online
+// softmax.  Rows past the LDS list's capacity, which only very large
+// selections reach, are walked block by block afterwards.
 #include <float.h>
 
 #include "ssa_internal.h"
@@ -25,7 +28,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kD = 64;
-constexpr int kDL = 16;  // dims per lane
+constexpr int kDL = 16;      // dims per lane
+constexpr int kList = 64;    // row positions listed per pair
+constexpr int kStep = 1;     // rows per step
 
 __device__ __forceinline__ void load16(const uint16_t* p, float (&x)[kDL]) {
   const u32x4 a = *reinterpret_cast<const u32x4*>(p);
@@ -39,86 +44,177 @@ __device__ __forceinline__ void load16(const uint16_t* p, float (&x)[kDL]) {
   }
 }
 
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// 16 bf16 values of a row, packed
+struct Row16 {
+  u32x4 a, b;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    a = *reinterpret_cast<const u32x4*>(p);
+    b = *reinterpret_cast<const u32x4*>(p + 8);
+  }
+  __device__ __forceinline__ float dot(const float (&q)[kDL]) const {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s0 = fmaf(q[2 * e], bf_lo(a[e]), s0);
+      s1 = fmaf(q[2 * e + 1], bf_hi(a[e]), s1);
+      s0 = fmaf(q[8 + 2 * e], bf_lo(b[e]), s0);
+      s1 = fmaf(q[8 + 2 * e + 1], bf_hi(b[e]), s1);
+    }
+    return s0 + s1;
+  }
+  __device__ __forceinline__ void axpy(float w, float (&o)[kDL]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = fmaf(w, bf_lo(a[e]), o[2 * e]);
+      o[2 * e + 1] = fmaf(w, bf_hi(a[e]), o[2 * e + 1]);
+      o[8 + 2 * e] = fmaf(w, bf_lo(b[e]), o[8 + 2 * e]);
+      o[8 + 2 * e + 1] = fmaf(w, bf_hi(b[e]), o[8 + 2 * e + 1]);
+    }
+  }
+};
+
+// Online-softmax state of one lane (16 dims of one pair).
+struct SelState {
+  float m, l, o[kDL];
+  __device__ __forceinline__ void init() {
+    m = -FLT_MAX;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < kDL; ++e) o[e] = 0.f;
+  }
+  // logits s2[u] (already times scale * log2 e; -FLT_MAX = absent) and their
+  // value rows
+  template <int U>
+  __device__ __forceinline__ void add(const float (&s2)[U], const Row16 (&v)[U]) {
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, s2[u]);
+    if (mx > m) {
+      const float corr = __builtin_amdgcn_exp2f(m - mx);
+      l *= corr;
+#pragma unroll
+      for (int e = 0; e < kDL; ++e) o[e] *= corr;
+      m = mx;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pr = __builtin_amdgcn_exp2f(s2[u] - m);
+      l += pr;
+      v[u].axpy(pr, o);
+    }
+  }
+};
+
+// sum over the four lanes of a pair
+__device__ __forceinline__ float quad_sum(float s) {
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  return s;
+}
+
+template <int KMAX>
 __global__ void __launch_bounds__(256)
 sel_combine_kernel(FwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int sub = lane & 3;                       // which 16 dims
-  const int64_t pair = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 2;
-  const int64_t n_pairs = static_cast<int64_t>(p.n) * p.h_q;
-  const bool active0 = pair < n_pairs;
-  const int h = active0 ? static_cast<int>(pair / p.n) : 0;
-  const int t = active0 ? static_cast<int>(pair % p.n) : 0;      // input token order
-  const int g = h;  // one query head per group on this path
+  __shared__ int32_t rows[64 * kList];   // per pair (256 threads / 4): row positions
+  __shared__ int2 ranges[64 * KMAX];      // per pair: the selected blocks' row ranges
 
-  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  const uint16_t* K = static_cast<const uint16_t*>(p.k);
-  const uint16_t* V = static_cast<const uint16_t*>(p.v);
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 3;                       // which 16 dims / which rows to list
+  const int pl = threadIdx.x >> 2;                // pair within the workgroup
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 64 + pl;
+  const int64_t n_pairs = static_cast<int64_t>(p.n) * p.h_q;
+  const bool active = pair < n_pairs;
+  const int h = active ? static_cast<int>(pair / p.n) : 0;
+  const int t = active ? static_cast<int>(pair % p.n) : 0;      // input token order
+  const int g = h;  // one query head per group on this path
+  const int nb = p.counts[SSA_COUNT_NB];
   const float c2 = p.scale * kLog2e;
 
+  const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(g) * p.n * kD + kDL * sub;
+  const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(g) * p.n * kD + kDL * sub;
   float q[kDL];
-  load16(Q + (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub, q);
+  load16(static_cast<const uint16_t*>(p.q) + (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub, q);
   const int32_t* sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
 
-  // walk state: selection slot r, current sorted position and block end.
-  // Block ids outside [0, nb) end the walk (they never occur in valid output
-  // of the selection kernels; the check keeps a corrupt list memory-safe).
-  const int nb = p.counts[SSA_COUNT_NB];
-  int r = 0, pos = 0, end = 0;
-  bool active = active0;
-  if (active) {
-    const int j = sel[0];
-    if (j < 0 || j >= nb) active = false;
-    else { pos = p.blk_off[j]; end = p.blk_off[j + 1]; active = pos < end; }
+  // ---------------- the selected blocks' row ranges, all loads in flight at once
+  // Lane sub loads blocks sub, sub + 4, ... into LDS.  The list ends at the
+  // first block id outside [0, nb) (the padding -1; the check also keeps a
+  // corrupt list memory-safe): such a slot gets the range (-1, -1).
+  int2* const rng = ranges + pl * KMAX;
+#pragma unroll
+  for (int i = 0; i < KMAX / 4; ++i) {
+    const int r = sub + 4 * i;
+    const int id = (active && r < p.topk) ? sel[r] : -1;
+    const bool ok = id >= 0 && id < nb;
+    rng[r] = ok ? make_int2(p.blk_off[id], p.blk_off[id + 1]) : make_int2(-1, -1);
   }
-  float m = -FLT_MAX, l = 0.f, o[kDL];
-#pragma unroll
-  for (int e = 0; e < kDL; ++e) o[e] = 0.f;
-  while (__ballot(active)) {
-    float kx[kDL], vx[kDL];
-    float s = 0.f;
-    if (active) {
-      const int64_t tok = p.perm[pos];
-      load16(K + (tok * p.h_kv + g) * kD + kDL * sub, kx);
-      load16(V + (tok * p.h_kv + g) * kD + kDL * sub, vx);
-#pragma unroll
-      for (int e = 0; e < kDL; ++e) s = fmaf(q[e], kx[e], s);
+  wave_lds_sync();
+  // list: rows of block r start at the rows of blocks 0 .. r - 1; lane sub
+  // writes every fourth row of each block
+  int total = 0, k_eff = 0;
+  for (; k_eff < KMAX; ++k_eff) {
+    const int2 ab = rng[k_eff];
+    if (ab.x < 0) break;
+    for (int i = ab.x + sub; i < ab.y; i += 4) {
+      const int idx = total + (i - ab.x);
+      if (idx < kList) rows[pl * kList + idx] = i;
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    if (active) {
-      const float s2 = s * c2;
-      if (s2 > m) {
-        const float corr = __builtin_amdgcn_exp2f(m - s2);
-        l *= corr;
+    total += ab.y - ab.x;
+  }
+  wave_lds_sync();
+
+  // ---------------- stream the listed rows
+  SelState st;
+  st.init();
+  const int listed = min(total, kList);
+  for (int i0 = 0; i0 < listed; i0 += kStep) {
+    Row16 kr[kStep], vr[kStep];
 #pragma unroll
-        for (int e = 0; e < kDL; ++e) o[e] *= corr;
-        m = s2;
-      }
-      const float pr = __builtin_amdgcn_exp2f(s2 - m);
-      l += pr;
+    for (int u = 0; u < kStep; ++u) {
+      const int64_t row = rows[pl * kList + min(i0 + u, listed - 1)];
+      kr[u].load(KS + row * kD);
+      vr[u].load(VS + row * kD);
+    }
+    float s2[kStep];
 #pragma unroll
-      for (int e = 0; e < kDL; ++e) o[e] = fmaf(pr, vx[e], o[e]);
-      if (++pos >= end) {
-        ++r;
-        const int j = r < p.topk ? sel[r] : -1;
-        if (j < 0 || j >= nb) active = false;
-        else { pos = p.blk_off[j]; end = p.blk_off[j + 1]; active = pos < end; }
+    for (int u = 0; u < kStep; ++u) {
+      const float s = quad_sum(kr[u].dot(q));
+      s2[u] = i0 + u < listed ? s * c2 : -FLT_MAX;
+    }
+    st.add<kStep>(s2, vr);
+  }
+  // ---------------- rows past the list (only selections of more than kList rows)
+  if (total > kList) {
+    int seen = 0;
+    for (int r = 0; r < k_eff; ++r) {
+      const int2 ab = rng[r];
+      for (int i = ab.x; i < ab.y; ++i, ++seen) {
+        if (seen < kList) continue;
+        Row16 kr, vr[1];
+        kr.load(KS + static_cast<int64_t>(i) * kD);
+        vr[0].load(VS + static_cast<int64_t>(i) * kD);
+        float s2[1] = {quad_sum(kr.dot(q)) * c2};
+        st.add<1>(s2, vr);
       }
     }
   }
-  if (!active0) return;
-  const int64_t row = (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub;
+
+  if (!active) return;
+  const int64_t orow = (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub;
   const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
-  const float f = bf16_bits_to_f32(gt[1]) / l;
-  const float* acc = p.acc + row;
+  const float f = st.l > 0.f ? bf16_bits_to_f32(gt[1]) / st.l : 0.f;
+  const float* acc = p.acc + orow;
   uint16_t res[kDL];
 #pragma unroll
   for (int c = 0; c < kDL / 4; ++c) {
     const float4 a = *reinterpret_cast<const float4*>(acc + 4 * c);
-    res[4 * c] = f32_to_bf16_bits(fmaf(o[4 * c], f, a.x));
-    res[4 * c + 1] = f32_to_bf16_bits(fmaf(o[4 * c + 1], f, a.y));
-    res[4 * c + 2] = f32_to_bf16_bits(fmaf(o[4 * c + 2], f, a.z));
-    res[4 * c + 3] = f32_to_bf16_bits(fmaf(o[4 * c + 3], f, a.w));
+    res[4 * c] = f32_to_bf16_bits(fmaf(st.o[4 * c], f, a.x));
+    res[4 * c + 1] = f32_to_bf16_bits(fmaf(st.o[4 * c + 1], f, a.y));
+    res[4 * c + 2] = f32_to_bf16_bits(fmaf(st.o[4 * c + 2], f, a.z));
+    res[4 * c + 3] = f32_to_bf16_bits(fmaf(st.o[4 * c + 3], f, a.w));
   }
   u32x4 w0, w1;
 #pragma unroll
@@ -126,7 +222,7 @@ sel_combine_kernel(FwdParams p) {
     w0[e] = static_cast<uint32_t>(res[2 * e]) | (static_cast<uint32_t>(res[2 * e + 1]) << 16);
     w1[e] = static_cast<uint32_t>(res[8 + 2 * e]) | (static_cast<uint32_t>(res[8 + 2 * e + 1]) << 16);
   }
-  uint16_t* out = static_cast<uint16_t*>(p.out) + row;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + orow;
   *reinterpret_cast<u32x4*>(out) = w0;
   *reinterpret_cast<u32x4*>(out + 8) = w1;
 }
@@ -134,8 +230,10 @@ sel_combine_kernel(FwdParams p) {
 }  // namespace
 
 hipError_t launch_sel_combine(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  const int64_t threads = static_cast<int64_t>(p.n) * p.h_q * 4;
-  sel_combine_kernel<<<static_cast<int>((threads + 255) / 256), 256, 0, stream>>>(p);
+  const int64_t pairs = static_cast<int64_t>(p.n) * p.h_q;
+  const int grid = static_cast<int>((pairs + 63) / 64);
+  if (p.topk <= 16) sel_combine_kernel<16><<<grid, 256, 0, stream>>>(p);
+  else sel_combine_kernel<32><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -1,15 +1,17 @@
-// Window attention on MFMA (bf16, D = 64): every query attends to all tokens
-// of its own m_win^3 window (Direct3D-S2 page, "Method": the sparse 3D window
-// module splits tokens into non-overlapping windows and runs self-attention
-// inside each).  Adds G2 * o_win to the branch accumulator.
+// Window attention (bf16, D = 64, one query head per key/value head).
 //
-// Work split: one workgroup per (window, head) item (persistent grid).  A window's tokens are a
-// contiguous run of sorted positions; the workgroup gathers their key rows
-// (row-major) and value rows (transposed, in the MFMA operand order) into LDS
-// once, in chunks of up to kChunk tokens, and each of its 4 waves computes 32
-// queries at a time: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 over 32-key
-// tiles, an online softmax (running max, rescaled sum and O^T), and
-// O^T += V^T P^T.
+// Direct3D-S2 page, "Method": every query attends to all tokens of its own
+// m_win^3 window (the windows do not overlap).  Adds G2 * o_win to the float32
+// branch accumulator.
+//
+// Work split: one workgroup per (window, head) item (persistent grid, items
+// head-major).  Keys and values come from the head-major sorted copies made by
+// the pooling kernel, so a window is one contiguous run of rows.  The
+// workgroup stages the window's key rows (row-major) and value rows
+// (transposed, in the MFMA operand order) in LDS, in chunks of up to kChunk
+// tokens; each of its 4 waves computes 32 queries with
+// v_mfma_f32_32x32x16_bf16 (S^T = K Q^T over 32-key tiles), an online softmax
+// (running max, rescaled sum and O^T), and O^T += V^T P^T.
 #include <float.h>
 
 #include "ssa_internal.h"
@@ -46,122 +48,122 @@ win_mfma_kernel(FwdParams p) {
   const int wv = tid >> 6;
   const int half = lane >> 5;
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  const uint16_t* K = static_cast<const uint16_t*>(p.k);
-  const uint16_t* V = static_cast<const uint16_t*>(p.v);
   const float c2 = p.scale * kLog2e;
   const int nw = p.counts[SSA_COUNT_NW];
-  // (window, head) items, head-major so that concurrently running workgroups
-  // share one head's rows in the caches
   const int64_t n_items = static_cast<int64_t>(nw) * p.h_q;
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-  const int h = static_cast<int>(item / nw);
-  const int w = static_cast<int>(item % nw);
-  const int wa = p.win_off[w], wb = p.win_off[w + 1];
-  const int n_w = wb - wa;
+    const int h = static_cast<int>(item / nw);
+    const int w = static_cast<int>(item % nw);
+    const int wa = p.win_off[w], wb = p.win_off[w + 1];
+    const int n_w = wb - wa;
+    const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(h) * p.n * kD;
+    const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(h) * p.n * kD;
 
-  // query groups of 32 (round robin over the waves); every key chunk is
-  // staged once per group round, so windows up to kChunk tokens and 128
-  // queries are staged exactly once
-  for (int qg0 = 0; qg0 < n_w; qg0 += 128) {
-    const int qi = wa + qg0 + wv * 32 + (lane & 31);
-    const bool q_valid = qi < wb;
-    const int t = q_valid ? p.perm[qi] : 0;
-    bf16x8 qb[4];
+    // query groups of 32 (round robin over the waves); every key chunk is
+    // staged once per group round, so windows up to kChunk tokens and 128
+    // queries are staged exactly once
+    for (int qg0 = 0; qg0 < n_w; qg0 += 128) {
+      const int qi = wa + qg0 + wv * 32 + (lane & 31);
+      const bool q_valid = qi < wb;
+      const int t = q_valid ? p.perm[qi] : 0;
+      const uint16_t* q_row = Q + (static_cast<int64_t>(t) * p.h_q + h) * kD;
+      bf16x8 qb[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (q_valid)
-        u = *reinterpret_cast<const u32x4*>(Q + (static_cast<int64_t>(t) * p.h_q + h) * kD + 16 * ks + 8 * half);
-      qb[ks] = __builtin_bit_cast(bf16x8, u);
-    }
-    float m = -FLT_MAX, l = 0.f;
-    f32x16 o0 = {}, o1 = {};
-    for (int kc = 0; kc < n_w; kc += kChunk) {
-      const int nk = min(kChunk, n_w - kc);
-      const int nk32 = (nk + 31) & ~31;
-      __syncthreads();  // previous chunk fully consumed
-      // stage keys (row-major) and values (transposed) of this chunk
-      for (int e = tid; e < nk32 * 8; e += 256) {
-        const int row = e >> 3, c = e & 7;
-        u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-        if (row < nk) {
-          const int64_t tok = p.perm[wa + kc + row];
-          kr = *reinterpret_cast<const u32x4*>(K + (tok * p.h_kv + h) * kD + 8 * c);
-          vr = *reinterpret_cast<const u32x4*>(V + (tok * p.h_kv + h) * kD + 8 * c);
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 u = {0u, 0u, 0u, 0u};
+        if (q_valid) u = *reinterpret_cast<const u32x4*>(q_row + 16 * ks + 8 * half);
+        qb[ks] = __builtin_bit_cast(bf16x8, u);
+      }
+
+      // ---------------- window attention
+      float m = -FLT_MAX, l = 0.f;
+      f32x16 o0 = {}, o1 = {};
+      for (int kc = 0; kc < n_w; kc += kChunk) {
+        const int nk = min(kChunk, n_w - kc);
+        const int nk32 = (nk + 31) & ~31;
+        __syncthreads();  // previous chunk fully consumed
+        // stage keys (row-major) and values (transposed) of this chunk
+        for (int e = tid; e < nk32 * 8; e += 256) {
+          const int row = e >> 3, c = e & 7;
+          u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+          if (row < nk) {
+            const int64_t off = static_cast<int64_t>(wa + kc + row) * kD + 8 * c;
+            kr = *reinterpret_cast<const u32x4*>(KS + off);
+            vr = *reinterpret_cast<const u32x4*>(VS + off);
+          }
+          *reinterpret_cast<u32x4*>(k_lds + row * kKRow + 8 * c) = kr;
+          const int kp = mfma_key_pos(row);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int d = 8 * c + 2 * e2;
+            v_lds[d * kVRow + kp] = static_cast<uint16_t>(vr[e2] & 0xFFFFu);
+            v_lds[(d + 1) * kVRow + kp] = static_cast<uint16_t>(vr[e2] >> 16);
+          }
         }
-        *reinterpret_cast<u32x4*>(k_lds + row * kKRow + 8 * c) = kr;
-        const int kp = mfma_key_pos(row);
+        __syncthreads();
+        for (int kt = 0; kt < nk32; kt += kKeyTile) {
+          f32x16 s = {};
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int d = 8 * c + 2 * e2;
-          v_lds[d * kVRow + kp] = static_cast<uint16_t>(vr[e2] & 0xFFFFu);
-          v_lds[(d + 1) * kVRow + kp] = static_cast<uint16_t>(vr[e2] >> 16);
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = lds_b128(k_lds + (kt + (lane & 31)) * kKRow + 16 * ks + 8 * half);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s, 0, 0, 0);
+          }
+          if (kt + kKeyTile > nk) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kt + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) s[r] = -FLT_MAX;
+          }
+          float tmax = -FLT_MAX;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+          const float m_new = fmaxf(m, tmax);
+          const float corr = __builtin_amdgcn_exp2f((m - m_new) * c2);
+          const float mc = m_new * c2;
+          m = m_new;
+          float pr[16];
+          float ls = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
+            ls += pr[r];
+          }
+          l = l * corr + ls;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            o0[r] *= corr;
+            o1[r] *= corr;
+          }
+          bf16x8 pb[2];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint16_t* vl = v_lds + (lane & 31) * kVRow + kt + 16 * ks + 8 * half;
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl), pb[ks], o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow), pb[ks], o1, 0, 0, 0);
+          }
         }
       }
-      __syncthreads();
-      for (int kt = 0; kt < nk32; kt += kKeyTile) {
-        f32x16 s = {};
+      const float l_win = l + __shfl_xor(l, 32);
+      if (q_valid) {
+        const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
+        const float f = bf16_bits_to_f32(gt[2]) / l_win;
+        float* dst = p.acc + (static_cast<int64_t>(t) * p.h_q + h) * kD;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = lds_b128(k_lds + (kt + (lane & 31)) * kKRow + 16 * ks + 8 * half);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s, 0, 0, 0);
-        }
-        if (kt + kKeyTile > nk) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kt + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) s[r] = -FLT_MAX;
-        }
-        float tmax = -FLT_MAX;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);
-        const float corr = __builtin_amdgcn_exp2f((m - m_new) * c2);
-        const float mc = m_new * c2;
-        m = m_new;
-        float pr[16];
-        float ls = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
-          ls += pr[r];
-        }
-        l = l * corr + ls;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          o0[r] *= corr;
-          o1[r] *= corr;
-        }
-        bf16x8 pb[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint16_t* vl = v_lds + (lane & 31) * kVRow + kt + 16 * ks + 8 * half;
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl), pb[ks], o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow), pb[ks], o1, 0, 0, 0);
+        for (int rb = 0; rb < 4; ++rb) {
+          const int d = 8 * rb + 4 * half;
+          float4 a = *reinterpret_cast<float4*>(dst + d);
+          a.x += o0[4 * rb] * f; a.y += o0[4 * rb + 1] * f; a.z += o0[4 * rb + 2] * f; a.w += o0[4 * rb + 3] * f;
+          *reinterpret_cast<float4*>(dst + d) = a;
+          float4 c = *reinterpret_cast<float4*>(dst + 32 + d);
+          c.x += o1[4 * rb] * f; c.y += o1[4 * rb + 1] * f; c.z += o1[4 * rb + 2] * f; c.w += o1[4 * rb + 3] * f;
+          *reinterpret_cast<float4*>(dst + 32 + d) = c;
         }
       }
     }
-    const float l_q = l + __shfl_xor(l, 32);
-    if (q_valid) {
-      const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
-      const float f = bf16_bits_to_f32(gt[2]) / l_q;
-      float* dst = p.acc + (static_cast<int64_t>(t) * p.h_q + h) * kD;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int d = 8 * rb + 4 * half;
-        float4 a = *reinterpret_cast<float4*>(dst + d);
-        a.x += o0[4 * rb] * f; a.y += o0[4 * rb + 1] * f; a.z += o0[4 * rb + 2] * f; a.w += o0[4 * rb + 3] * f;
-        *reinterpret_cast<float4*>(dst + d) = a;
-        float4 c = *reinterpret_cast<float4*>(dst + 32 + d);
-        c.x += o1[4 * rb] * f; c.y += o1[4 * rb + 1] * f; c.z += o1[4 * rb + 2] * f; c.w += o1[4 * rb + 3] * f;
-        *reinterpret_cast<float4*>(dst + 32 + d) = c;
-      }
-    }
-  }
   }
 }
 

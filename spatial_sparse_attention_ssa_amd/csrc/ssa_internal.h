@@ -106,6 +106,10 @@ struct FwdParams {
   // pooled values for the MFMA path: [h_kv][nb_cap/32][D][32], keys of each
   // 32-block tile in the order the MFMA B operand of P^T expects (null = skip)
   void* vbar_t;
+  // keys / values in sorted token order, head-major [h_kv][N][D] (MFMA path;
+  // written by the pooling kernel; null = skip)
+  void* k_s;
+  void* v_s;
   // MFMA path scratch
   int32_t* tile_pre;  // [batch + 1] prefix of query tiles per sequence
   int32_t* fix;       // [1 + n * h_kv] overflow counter, then (token * h_kv + group) entries

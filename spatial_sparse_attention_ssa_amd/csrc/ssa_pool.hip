@@ -8,7 +8,8 @@
 // is rounded once to the input dtype.
 //
 // pool_kernel: one workgroup per block (grid-stride over the device-side
-// block count).  A token row (h_kv * D elements, contiguous in HBM) is split
+// block count).  On the MFMA path it also writes the key and value rows in
+// sorted order, head-major, for the window and selection kernels.  A token row (h_kv * D elements, contiguous in HBM) is split
 // into 16-byte chunks, one per thread; rows with fewer than 256 chunks run
 // several token slots side by side, summed afterwards in slot order through
 // LDS (deterministic).  Each thread keeps four row loads in flight.
@@ -58,9 +59,9 @@ template <> struct Chunk<float> {
 template <typename T>
 __global__ void __launch_bounds__(256)
 pool_kernel(const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ perm,
-            const int32_t* __restrict__ blk_off, const int32_t* __restrict__ counts, int hkv, int d,
+            const int32_t* __restrict__ blk_off, const int32_t* __restrict__ counts, int n, int hkv, int d,
             int nb_cap, T* __restrict__ kbar, T* __restrict__ vbar, T* __restrict__ k_cmp,
-            T* __restrict__ v_cmp) {
+            T* __restrict__ v_cmp, T* __restrict__ k_s, T* __restrict__ v_s) {
   constexpr int EC = Chunk<T>::kN;                      // elements per 16-byte chunk
   __shared__ float red[256 * EC];
   const int e_per_tok = hkv * d;
@@ -96,6 +97,19 @@ pool_kernel(const T* __restrict__ k, const T* __restrict__ v, const int32_t* __r
             if (p0 + u * slots < b) {
               Chunk<T>::add(ak, kx[u]);
               Chunk<T>::add(av, vx[u]);
+            }
+          }
+          if (k_s) {
+            // the rows in sorted order, head-major
+            const int e0 = EC * c;
+            const int64_t dst0 = (static_cast<int64_t>(e0 / d) * n) * d + e0 % d;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int pp = p0 + u * slots;
+              if (pp < b) {
+                *reinterpret_cast<u32x4*>(k_s + dst0 + static_cast<int64_t>(pp) * d) = kx[u];
+                *reinterpret_cast<u32x4*>(v_s + dst0 + static_cast<int64_t>(pp) * d) = vx[u];
+              }
             }
           }
         }
@@ -197,9 +211,9 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
   if (dtype == SSA_BF16) {
     pool_kernel<uint16_t><<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(p.k), static_cast<const uint16_t*>(p.v), p.perm, p.blk_off,
-        p.counts, p.h_kv, p.d, p.nb_cap, static_cast<uint16_t*>(p.kbar),
+        p.counts, p.n, p.h_kv, p.d, p.nb_cap, static_cast<uint16_t*>(p.kbar),
         static_cast<uint16_t*>(p.vbar), static_cast<uint16_t*>(p.k_cmp),
-        static_cast<uint16_t*>(p.v_cmp));
+        static_cast<uint16_t*>(p.v_cmp), static_cast<uint16_t*>(p.k_s), static_cast<uint16_t*>(p.v_s));
     if (p.vbar_t) {
       const int tiles = p.h_kv * (p.nb_cap / kKeyTile);
       vt_transpose_kernel<<<tiles < 4096 ? tiles : 4096, 256, 0, stream>>>(
@@ -209,8 +223,8 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
   } else {
     pool_kernel<float><<<grid, 256, 0, stream>>>(
         static_cast<const float*>(p.k), static_cast<const float*>(p.v), p.perm, p.blk_off,
-        p.counts, p.h_kv, p.d, p.nb_cap, static_cast<float*>(p.kbar), static_cast<float*>(p.vbar),
-        static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp));
+        p.counts, p.n, p.h_kv, p.d, p.nb_cap, static_cast<float*>(p.kbar), static_cast<float*>(p.vbar),
+        static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp), nullptr, nullptr);
   }
   return hipGetLastError();
 }
