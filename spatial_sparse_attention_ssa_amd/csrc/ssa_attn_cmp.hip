@@ -65,7 +65,7 @@ constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf
 constexpr int kKTileElems = kKeyTile * kKRow;
 constexpr int kVTileElems = kD * kVRow;
 constexpr int kBlockQ = 32;            // queries per MFMA column block
-constexpr int kGroupTiles = 1;         // key tiles per pass-1 group
+constexpr int kGroupTiles = 2;         // key tiles per pass-1 group
 // bf16 P by truncation: the mean relative loss of truncating a float32 with
 // a log-uniform mantissa to 8 significant bits is 2^-8 * (1/ln 2) * (1/2);
 // p is scaled up by the inverse factor (an exponent offset of log2 of it) and
@@ -101,7 +101,7 @@ template <int KMAX>
 struct CmpShape {
   // candidate slots per query, shared by its two lanes (with the bound above
   // a query rarely has more than KMAX + 6; overflow goes to the fallback)
-  static constexpr int kCap = KMAX + KMAX / 2 - 1;
+  static constexpr int kCap = KMAX + KMAX / 2 + 2;
   // hit-tile words per lane and block (a lane typically has about KMAX / 2
   // candidates)
   static constexpr int kEnt = KMAX <= 16 ? 20 : 36;
