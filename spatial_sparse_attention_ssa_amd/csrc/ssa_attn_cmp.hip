@@ -21,9 +21,9 @@
 // instruction stream on this hardware).
 //
 // Two passes over the keys:
-//  1. scan: per lane and block, the maximum of the lane's 16 logits of a tile
-//     (a "group max") is merged into a sorted list of the KMAX largest group
-//     maxima with v_med3 (for a descending list L, inserting x gives
+//  1. scan: per lane and block, the maximum of a group of the lane's logits
+//     (4 to 32 of them, chosen per sequence) is merged into a sorted list of
+//     the KMAX largest group maxima with v_med3 (for a descending list L, inserting x gives
 //     L'[i] = med3(L[i-1], x, L[i])).  The row maximum is max(L0 of both
 //     lanes).  For every split a + b = KMAX the two lanes hold a + b distinct
 //     elements no smaller than min(L_A[a-1], L_B[b-1]); the largest such value,
@@ -65,7 +65,6 @@ constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf
 constexpr int kKTileElems = kKeyTile * kKRow;
 constexpr int kVTileElems = kD * kVRow;
 constexpr int kBlockQ = 32;            // queries per MFMA column block
-constexpr int kGroupTiles = 2;         // key tiles per pass-1 group
 // bf16 P by truncation: the mean relative loss of truncating a float32 with
 // a log-uniform mantissa to 8 significant bits is 2^-8 * (1/ln 2) * (1/2);
 // p is scaled up by the inverse factor (an exponent offset of log2 of it) and
@@ -264,22 +263,45 @@ cmp_mfma_kernel(FwdParams p) {
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) blk[x].L[i] = -FLT_MAX;
-  // a group is kGroupTiles consecutive tiles of one lane (16 logits each); its
-  // running maximum goes into the list when the group is complete
-  auto group_max = [&](QBlock<KMAX>& B, int rel, auto masked) {
-    if (decltype(masked)::value) mask(rel, B.s);
-    const f32x16& s = B.s;
-    float m = fmaxf(B.g, fmaxf(s[0], s[1]));
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
-    B.g = m;
-  };
-  auto list_insert = [&](QBlock<KMAX>& B) {
-    const float m = B.g;
+  // Group size, per sequence: a group is a run of one lane's logits whose
+  // maximum goes into the list.  Larger groups cost fewer list updates but
+  // give a looser bound; each lane keeps at least ~48 groups:
+  //   glog 32: two tiles (16 logits each), glog 16: one tile,
+  //   glog 8: half a tile, glog 4: a quarter tile.
+  const int glog = n_kt >= 96 ? 32 : n_kt >= 48 ? 16 : n_kt >= 24 ? 8 : 4;
+  auto list_insert = [&](QBlock<KMAX>& B, float m) {
 #pragma unroll
     for (int i = KMAX - 1; i >= 1; --i) B.L[i] = __builtin_amdgcn_fmed3f(B.L[i - 1], m, B.L[i]);
     B.L[0] = fmaxf(B.L[0], m);
-    B.g = -FLT_MAX;
+  };
+  // the logits of tile rel of block B into its list (glog 32: into the open
+  // two-tile group, inserted after the odd tile)
+  auto group_update = [&](QBlock<KMAX>& B, int rel, auto masked) {
+    if (decltype(masked)::value) mask(rel, B.s);
+    const f32x16& s = B.s;
+    if (glog >= 16) {
+      float m = fmaxf(B.g, fmaxf(s[0], s[1]));
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+      if (glog == 16 || (rel & 1)) {
+        list_insert(B, m);
+        B.g = -FLT_MAX;
+      } else {
+        B.g = m;
+      }
+    } else if (glog == 8) {
+#pragma unroll
+      for (int q8 = 0; q8 < 2; ++q8) {
+        float m = fmaxf(s[8 * q8], s[8 * q8 + 1]);
+#pragma unroll
+        for (int r = 2; r < 8; r += 2) m = fmaxf(m, fmaxf(s[8 * q8 + r], s[8 * q8 + r + 1]));
+        list_insert(B, m);
+      }
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        list_insert(B, fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3])));
+    }
   };
   {
     blk[0].g = blk[1].g = -FLT_MAX;
@@ -295,23 +317,17 @@ cmp_mfma_kernel(FwdParams p) {
       bf16x8 a[4];
       read_k(rel, a);
       const f32x16 sa = qk(a, blk[0].qb);
-      if (decltype(has_b)::value) {
-        group_max(blk[1], rel - 1, mask_b);
-        if ((rel - 1) % kGroupTiles == kGroupTiles - 1) list_insert(blk[1]);
-      }
+      if (decltype(has_b)::value) group_update(blk[1], rel - 1, mask_b);
       blk[1].s = qk(a, blk[1].qb);
       blk[0].s = sa;
-      group_max(blk[0], rel, mask_a);
-      if (rel % kGroupTiles == kGroupTiles - 1) list_insert(blk[0]);
+      group_update(blk[0], rel, mask_a);
     };
     run_tiles(step);
-    group_max(blk[1], n_kt - 1, kT{});
-    // the last, partial groups
-    if (n_kt % kGroupTiles != 0) {
-      list_insert(blk[0]);
-      list_insert(blk[1]);
-    } else {
-      list_insert(blk[1]);
+    group_update(blk[1], n_kt - 1, kT{});
+    // an open two-tile group (odd tile count)
+    if (glog == 32 && (n_kt & 1)) {
+      list_insert(blk[0], blk[0].g);
+      list_insert(blk[1], blk[1].g);
     }
   }
 
