@@ -582,19 +582,24 @@ cmp_mfma_kernel(FwdParams p) {
 }
 
 // Exact top-k for the (sorted position, group) pairs whose candidate list
-// overflowed: one wave per pair, each lane keeps a sorted list of its strided blocks'
-// logits, then the wave pops the best heads (value desc, block asc).
+// overflowed: one workgroup per pair.  Each thread scores every 256th block
+// of the sequence in float32 and keeps a sorted list of its best KMAX (value
+// descending, block ascending); each wave then pops its KMAX best with wave
+// reductions, and wave 0 ranks the 4 x KMAX survivors.
 template <int KMAX>
 __global__ void __launch_bounds__(256)
 topk_fixup_kernel(FwdParams p) {
-  const int lane = threadIdx.x & 63;
+  __shared__ float wv_val[4 * KMAX];
+  __shared__ int wv_idx[4 * KMAX];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
   const int n_fix = p.fix[0];
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < n_fix; item += gridDim.x * 4) {
+  for (int item = blockIdx.x; item < n_fix; item += gridDim.x) {
     const int entry = p.fix[1 + item];
     const int i = entry / p.h_kv, g = entry % p.h_kv;
     const int t = p.perm[i];
-    const int tg = t * p.h_kv + g;
     int lo = 0, hi = p.batch - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -603,13 +608,20 @@ topk_fixup_kernel(FwdParams p) {
     const int j0 = p.seq_blk_off[lo], j1 = p.seq_blk_off[lo + 1];
     float q[kD];
 #pragma unroll
-    for (int d = 0; d < kD; ++d) q[d] = bf16_bits_to_f32(Q[(static_cast<int64_t>(t) * p.h_q + g) * kD + d]);
+    for (int c = 0; c < kD / 8; ++c) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(Q + (static_cast<int64_t>(t) * p.h_q + g) * kD + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
+        q[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+      }
+    }
     const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(g) * p.nb_cap * kD;
     float lv[KMAX];
     int li[KMAX];
 #pragma unroll
     for (int e = 0; e < KMAX; ++e) { lv[e] = -FLT_MAX; li[e] = 0x7FFFFFFF; }
-    for (int j = j0 + lane; j < j1; j += 64) {
+    for (int j = j0 + tid; j < j1; j += 256) {
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < kD / 8; ++c) {
@@ -620,6 +632,7 @@ topk_fixup_kernel(FwdParams p) {
           s = fmaf(q[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), s);
         }
       }
+      // blocks arrive in increasing id, so a tie keeps the earlier (lower) id ahead
       if (s > lv[KMAX - 1]) {
         bool placed = false;
 #pragma unroll
@@ -632,9 +645,8 @@ topk_fixup_kernel(FwdParams p) {
         if (!placed) { lv[0] = s; li[0] = j; }
       }
     }
-    const int k_eff = min(p.topk, j1 - j0);
-    int32_t* out_sel = p.topk_idx + static_cast<int64_t>(tg) * p.topk;
-    for (int r = 0; r < k_eff; ++r) {
+    // each wave pops its KMAX best (value descending, block ascending)
+    for (int r = 0; r < KMAX; ++r) {
       float bv = lv[0];
       int bi = li[0];
 #pragma unroll
@@ -649,10 +661,28 @@ topk_fixup_kernel(FwdParams p) {
         lv[KMAX - 1] = -FLT_MAX;
         li[KMAX - 1] = 0x7FFFFFFF;
       }
-      if (lane == 0) out_sel[r] = bi;
+      if (lane == 0) { wv_val[wv * KMAX + r] = bv; wv_idx[wv * KMAX + r] = bi; }
     }
-    if (lane == 0)
-      for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
+    __syncthreads();
+    // wave 0 ranks the survivors (an unused slot holds -FLT_MAX and the
+    // largest id, so it ranks after every real block)
+    const int k_eff = min(p.topk, j1 - j0);
+    int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
+    if (wv == 0) {
+      for (int e = lane; e < 4 * KMAX; e += 64) {
+        const float cv = wv_val[e];
+        const int ci = wv_idx[e];
+        int rank = 0;
+        for (int o = 0; o < 4 * KMAX; ++o) {
+          const float ov = wv_val[o];
+          const int oi = wv_idx[o];
+          rank += (ov > cv) || (ov == cv && oi < ci);
+        }
+        if (rank < k_eff) out_sel[rank] = ci;
+      }
+      for (int r = k_eff + lane; r < p.topk; r += 64) out_sel[r] = -1;
+    }
+    __syncthreads();  // the survivor arrays are reused by the next pair
   }
 }
 
@@ -667,8 +697,8 @@ hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t 
 }
 
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  if (p.topk <= 16) topk_fixup_kernel<16><<<1024, 256, 0, stream>>>(p);
-  else topk_fixup_kernel<32><<<1024, 256, 0, stream>>>(p);
+  if (p.topk <= 16) topk_fixup_kernel<16><<<2048, 256, 0, stream>>>(p);
+  else topk_fixup_kernel<32><<<2048, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
