@@ -97,13 +97,17 @@ int64_t nb_capacity(const ssa_blocks* b) {
   return (c + ssa::kKeyTile - 1) / ssa::kKeyTile * ssa::kKeyTile;
 }
 
-// the MFMA kernels cover bfloat16, head_dim 64, one query head per key/value head
+// the MFMA kernels cover bfloat16 with head_dim 64 and one query head per
+// key/value head, or head_dim 32 / 64 with 16 query heads per key/value head
+bool use_gqa_path(const ssa_attn* a) {
+  return a->dtype == SSA_BF16 && (a->head_dim == 32 || a->head_dim == 64) && a->h_q == 16 * a->h_kv;
+}
 bool use_mfma_path(const ssa_attn* a) {
-  return a->dtype == SSA_BF16 && a->head_dim == 64 && a->h_q == a->h_kv;
+  return (a->dtype == SSA_BF16 && a->head_dim == 64 && a->h_q == a->h_kv) || use_gqa_path(a);
 }
 
 struct FwdLayout {
-  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, total;
+  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, total;
 };
 
 FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
@@ -123,6 +127,10 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
     L.tile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     L.fix = off; off += align256(sizeof(int32_t) * (1 + n * a->h_kv));
     L.acc = off; off += align256(sizeof(float) * n * a->h_q * a->head_dim);
+    if (use_gqa_path(a)) {
+      L.norm = off; off += align256(sizeof(float) * n * a->h_q);
+      L.tile_pre2 = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    }
   }
   L.total = off + 256;
   return L;
@@ -223,6 +231,14 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
     stages[1] = Stage{"generic_fwd", ssa::launch_generic};
     return 2;
   }
+  if (use_gqa_path(attn)) {
+    stages[1] = Stage{"gqa_cmp_kernel", ssa::launch_gqa_cmp};
+    stages[2] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
+    stages[3] = Stage{"gqa_fixup_kernel", ssa::launch_gqa_fixup};
+    stages[4] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
+    stages[5] = Stage{"sel_combine_kernel", ssa::launch_sel_combine};
+    return 6;
+  }
   stages[1] = Stage{"cmp_mfma_kernel", ssa::launch_cmp_mfma};
   stages[2] = Stage{"topk_fixup_kernel", ssa::launch_topk_fixup};
   stages[3] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
@@ -289,6 +305,11 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
     p.fix = reinterpret_cast<int32_t*>(w + lay.fix);
     p.acc = reinterpret_cast<float*>(w + lay.acc);
     p.max_tiles = static_cast<int32_t>(blocks->n_tokens / ssa::kQueryTile + blocks->batch + 1);
+    if (use_gqa_path(attn)) {
+      p.norm = reinterpret_cast<float*>(w + lay.norm);
+      p.tile_pre2 = reinterpret_cast<int32_t*>(w + lay.tile_pre2);
+      p.max_tiles2 = static_cast<int32_t>(blocks->n_tokens / 16 + blocks->batch + 1);
+    }
   }
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);

@@ -688,8 +688,12 @@ topk_fixup_kernel(FwdParams p) {
 
 }  // namespace
 
-hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream) {
   tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
+}
+
+hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  tile_prefix_kernel_launch(p, stream);
   const dim3 grid(p.max_tiles, p.h_q);
   if (p.topk <= 16) cmp_mfma_kernel<16><<<grid, 256, 0, stream>>>(p);
   else cmp_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);

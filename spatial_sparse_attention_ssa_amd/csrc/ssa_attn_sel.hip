@@ -1,5 +1,5 @@
-// Selected-block attention and the gated sum (bf16, D = 64, one query head
-// per key/value head).
+// Selected-block attention and the gated sum (bf16, D = 32 or 64; query head
+// h reads key/value head g = h / (h_q / h_kv) and the selection of group g).
 //
 // Direct3D-S2 page, "Method": all tokens of the top-k selected blocks take
 // part in a second attention; the three branch outputs are summed with the
@@ -7,8 +7,8 @@
 // G0 * o_cmp + G2 * o_win to the float32 accumulator; this kernel adds
 // G1 * o_sel, rounds once to bfloat16 and writes the output row.
 //
-// Four lanes serve one (token, head) pair, each owning 16 of the 64 dims; a
-// wave covers 16 pairs of one head (pairs are ordered head-major, so the rows
+// D / 16 lanes serve one (token, head) pair, each owning 16 dims; a wave
+// covers 64 / (D / 16) pairs of one head (pairs are ordered head-major, so the rows
 // gathered at any time belong to one or two heads and stay in the Infinity
 // Cache).  Keys and values come from the head-major sorted copies, where a
 // block is a contiguous run of rows.  First the pair's lanes turn its block
@@ -27,7 +27,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kD = 64;
 constexpr int kDL = 16;      // dims per lane
 constexpr int kList = 64;    // row positions listed per pair
 constexpr int kStep = 1;     // rows per step
@@ -108,28 +107,32 @@ struct SelState {
   }
 };
 
-// sum over the four lanes of a pair
-__device__ __forceinline__ float quad_sum(float s) {
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
+// sum over the LP lanes of a pair
+template <int LP>
+__device__ __forceinline__ float pair_sum(float s) {
+#pragma unroll
+  for (int o = 1; o < LP; o <<= 1) s += __shfl_xor(s, o);
   return s;
 }
 
-template <int KMAX>
+template <int KMAX, int D>
 __global__ void __launch_bounds__(256)
 sel_combine_kernel(FwdParams p) {
-  __shared__ int32_t rows[64 * kList];   // per pair (256 threads / 4): row positions
-  __shared__ int2 ranges[64 * KMAX];      // per pair: the selected blocks' row ranges
+  constexpr int kD = D;
+  constexpr int LP = D / kDL;             // lanes per pair
+  constexpr int NP = 256 / LP;            // pairs per workgroup
+  __shared__ int32_t rows[NP * kList];    // per pair: row positions
+  __shared__ int2 ranges[NP * KMAX];      // per pair: the selected blocks' row ranges
 
   const int lane = threadIdx.x & 63;
-  const int sub = lane & 3;                       // which 16 dims / which rows to list
-  const int pl = threadIdx.x >> 2;                // pair within the workgroup
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 64 + pl;
+  const int sub = lane & (LP - 1);                // which 16 dims / which rows to list
+  const int pl = threadIdx.x / LP;                // pair within the workgroup
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * NP + pl;
   const int64_t n_pairs = static_cast<int64_t>(p.n) * p.h_q;
   const bool active = pair < n_pairs;
   const int h = active ? static_cast<int>(pair / p.n) : 0;
   const int t = active ? static_cast<int>(pair % p.n) : 0;      // input token order
-  const int g = h;  // one query head per group on this path
+  const int g = h / (p.h_q / p.h_kv);
   const int nb = p.counts[SSA_COUNT_NB];
   const float c2 = p.scale * kLog2e;
 
@@ -140,13 +143,13 @@ sel_combine_kernel(FwdParams p) {
   const int32_t* sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
 
   // ---------------- the selected blocks' row ranges, all loads in flight at once
-  // Lane sub loads blocks sub, sub + 4, ... into LDS.  The list ends at the
+  // Lane sub loads blocks sub, sub + LP, ... into LDS.  The list ends at the
   // first block id outside [0, nb) (the padding -1; the check also keeps a
   // corrupt list memory-safe): such a slot gets the range (-1, -1).
   int2* const rng = ranges + pl * KMAX;
 #pragma unroll
-  for (int i = 0; i < KMAX / 4; ++i) {
-    const int r = sub + 4 * i;
+  for (int i = 0; i < KMAX / LP; ++i) {
+    const int r = sub + LP * i;
     const int id = (active && r < p.topk) ? sel[r] : -1;
     const bool ok = id >= 0 && id < nb;
     rng[r] = ok ? make_int2(p.blk_off[id], p.blk_off[id + 1]) : make_int2(-1, -1);
@@ -158,7 +161,7 @@ sel_combine_kernel(FwdParams p) {
   for (; k_eff < KMAX; ++k_eff) {
     const int2 ab = rng[k_eff];
     if (ab.x < 0) break;
-    for (int i = ab.x + sub; i < ab.y; i += 4) {
+    for (int i = ab.x + sub; i < ab.y; i += LP) {
       const int idx = total + (i - ab.x);
       if (idx < kList) rows[pl * kList + idx] = i;
     }
@@ -181,7 +184,7 @@ sel_combine_kernel(FwdParams p) {
     float s2[kStep];
 #pragma unroll
     for (int u = 0; u < kStep; ++u) {
-      const float s = quad_sum(kr[u].dot(q));
+      const float s = pair_sum<LP>(kr[u].dot(q));
       s2[u] = i0 + u < listed ? s * c2 : -FLT_MAX;
     }
     st.add<kStep>(s2, vr);
@@ -196,7 +199,7 @@ sel_combine_kernel(FwdParams p) {
         Row16 kr, vr[1];
         kr.load(KS + static_cast<int64_t>(i) * kD);
         vr[0].load(VS + static_cast<int64_t>(i) * kD);
-        float s2[1] = {quad_sum(kr.dot(q)) * c2};
+        float s2[1] = {pair_sum<LP>(kr.dot(q)) * c2};
         st.add<1>(s2, vr);
       }
     }
@@ -231,9 +234,15 @@ sel_combine_kernel(FwdParams p) {
 
 hipError_t launch_sel_combine(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(p.n) * p.h_q;
-  const int grid = static_cast<int>((pairs + 63) / 64);
-  if (p.topk <= 16) sel_combine_kernel<16><<<grid, 256, 0, stream>>>(p);
-  else sel_combine_kernel<32><<<grid, 256, 0, stream>>>(p);
+  const int np = 256 / (p.d / kDL);
+  const int grid = static_cast<int>((pairs + np - 1) / np);
+  if (p.d == 32) {
+    if (p.topk <= 16) sel_combine_kernel<16, 32><<<grid, 256, 0, stream>>>(p);
+    else sel_combine_kernel<32, 32><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (p.topk <= 16) sel_combine_kernel<16, 64><<<grid, 256, 0, stream>>>(p);
+    else sel_combine_kernel<32, 64><<<grid, 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

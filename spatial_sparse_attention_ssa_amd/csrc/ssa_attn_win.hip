@@ -1,4 +1,5 @@
-// Window attention (bf16, D = 64, one query head per key/value head).
+// Window attention (bf16, D = 32 or 64; query head h reads key/value head
+// h / (h_q / h_kv)).
 //
 // Direct3D-S2 page, "Method": every query attends to all tokens of its own
 // m_win^3 window (the windows do not overlap).  Adds G2 * o_win to the float32
@@ -24,9 +25,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kD = 64;
 constexpr int kChunk = 256;            // window tokens staged in LDS at a time
-constexpr int kKRow = kD + 8;          // padded key row (bf16)
 constexpr int kVRow = kChunk + 8;      // padded transposed value row (bf16)
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
@@ -38,8 +37,14 @@ __device__ __forceinline__ int mfma_key_pos(int jj) {
   return (jj & ~15) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
 }
 
+template <int D>
 __global__ void __launch_bounds__(256, 2)
 win_mfma_kernel(FwdParams p) {
+  constexpr int kD = D;
+  constexpr int KSTEPS = D / 16;         // MFMA k steps over the dims
+  constexpr int VB = D / 32;             // 32-dim row blocks of O^T
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int kKRow = kD + 8;          // padded key row (bf16)
   __shared__ __align__(16) uint16_t k_lds[kChunk * kKRow];
   __shared__ __align__(16) uint16_t v_lds[kD * kVRow];
 
@@ -56,8 +61,9 @@ win_mfma_kernel(FwdParams p) {
     const int w = static_cast<int>(item % nw);
     const int wa = p.win_off[w], wb = p.win_off[w + 1];
     const int n_w = wb - wa;
-    const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(h) * p.n * kD;
-    const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(h) * p.n * kD;
+    const int kvh = h / (p.h_q / p.h_kv);
+    const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(kvh) * p.n * kD;
+    const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(kvh) * p.n * kD;
 
     // query groups of 32 (round robin over the waves); every key chunk is
     // staged once per group round, so windows up to kChunk tokens and 128
@@ -67,9 +73,9 @@ win_mfma_kernel(FwdParams p) {
       const bool q_valid = qi < wb;
       const int t = q_valid ? p.perm[qi] : 0;
       const uint16_t* q_row = Q + (static_cast<int64_t>(t) * p.h_q + h) * kD;
-      bf16x8 qb[4];
+      bf16x8 qb[KSTEPS];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KSTEPS; ++ks) {
         u32x4 u = {0u, 0u, 0u, 0u};
         if (q_valid) u = *reinterpret_cast<const u32x4*>(q_row + 16 * ks + 8 * half);
         qb[ks] = __builtin_bit_cast(bf16x8, u);
@@ -77,14 +83,16 @@ win_mfma_kernel(FwdParams p) {
 
       // ---------------- window attention
       float m = -FLT_MAX, l = 0.f;
-      f32x16 o0 = {}, o1 = {};
+      f32x16 o[VB];
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) o[vb] = f32x16{};
       for (int kc = 0; kc < n_w; kc += kChunk) {
         const int nk = min(kChunk, n_w - kc);
         const int nk32 = (nk + 31) & ~31;
         __syncthreads();  // previous chunk fully consumed
         // stage keys (row-major) and values (transposed) of this chunk
-        for (int e = tid; e < nk32 * 8; e += 256) {
-          const int row = e >> 3, c = e & 7;
+        for (int e = tid; e < nk32 * CPR; e += 256) {
+          const int row = e / CPR, c = e % CPR;
           u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
           if (row < nk) {
             const int64_t off = static_cast<int64_t>(wa + kc + row) * kD + 8 * c;
@@ -104,7 +112,7 @@ win_mfma_kernel(FwdParams p) {
         for (int kt = 0; kt < nk32; kt += kKeyTile) {
           f32x16 s = {};
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
+          for (int ks = 0; ks < KSTEPS; ++ks) {
             const bf16x8 a = lds_b128(k_lds + (kt + (lane & 31)) * kKRow + 16 * ks + 8 * half);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s, 0, 0, 0);
           }
@@ -130,10 +138,9 @@ win_mfma_kernel(FwdParams p) {
           }
           l = l * corr + ls;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            o0[r] *= corr;
-            o1[r] *= corr;
-          }
+          for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[vb][r] *= corr;
           bf16x8 pb[2];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
@@ -142,8 +149,9 @@ win_mfma_kernel(FwdParams p) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const uint16_t* vl = v_lds + (lane & 31) * kVRow + kt + 16 * ks + 8 * half;
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl), pb[ks], o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 32 * kVRow), pb[ks], o1, 0, 0, 0);
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+              o[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + vb * 32 * kVRow), pb[ks], o[vb], 0, 0, 0);
           }
         }
       }
@@ -153,15 +161,15 @@ win_mfma_kernel(FwdParams p) {
         const float f = bf16_bits_to_f32(gt[2]) / l_win;
         float* dst = p.acc + (static_cast<int64_t>(t) * p.h_q + h) * kD;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int d = 8 * rb + 4 * half;
-          float4 a = *reinterpret_cast<float4*>(dst + d);
-          a.x += o0[4 * rb] * f; a.y += o0[4 * rb + 1] * f; a.z += o0[4 * rb + 2] * f; a.w += o0[4 * rb + 3] * f;
-          *reinterpret_cast<float4*>(dst + d) = a;
-          float4 c = *reinterpret_cast<float4*>(dst + 32 + d);
-          c.x += o1[4 * rb] * f; c.y += o1[4 * rb + 1] * f; c.z += o1[4 * rb + 2] * f; c.w += o1[4 * rb + 3] * f;
-          *reinterpret_cast<float4*>(dst + 32 + d) = c;
-        }
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const int d = 32 * vb + 8 * rb + 4 * half;
+            float4 a = *reinterpret_cast<float4*>(dst + d);
+            a.x += o[vb][4 * rb] * f; a.y += o[vb][4 * rb + 1] * f;
+            a.z += o[vb][4 * rb + 2] * f; a.w += o[vb][4 * rb + 3] * f;
+            *reinterpret_cast<float4*>(dst + d) = a;
+          }
       }
     }
   }
@@ -172,7 +180,8 @@ win_mfma_kernel(FwdParams p) {
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   // persistent grid over (window, head) items; the window count is read on
   // the device, so the grid does not depend on it
-  win_mfma_kernel<<<2048, 256, 0, stream>>>(p);
+  if (p.d == 32) win_mfma_kernel<32><<<2048, 256, 0, stream>>>(p);
+  else win_mfma_kernel<64><<<2048, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

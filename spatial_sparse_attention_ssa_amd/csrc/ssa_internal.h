@@ -115,6 +115,11 @@ struct FwdParams {
   int32_t* fix;       // [1 + n * h_kv] overflow counter, then (token * h_kv + group) entries
   float* acc;         // [n][h_q][D] partial sum of the gated branches (input token order)
   int32_t max_tiles;  // upper bound of query tiles
+  // grouped-head path: log2 softmax normaliser per (token, query head), and
+  // the prefix of 16-token tiles per sequence
+  float* norm;        // [n][h_q]
+  int32_t* tile_pre2; // [batch + 1]
+  int32_t max_tiles2;
   // optional public outputs
   void* k_cmp;       // [nb][h_kv][D] or null
   void* v_cmp;
@@ -125,6 +130,10 @@ constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile
 constexpr int kQueryTile = 256;  // queries per workgroup of the compressed MFMA kernel (4 waves x 64)
 
 hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream);
+hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);

@@ -165,20 +165,21 @@ __device__ __forceinline__ int mfma_key_pos(int jj) {
   return (jj & 16) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
 }
 
-// vbar [h_kv][nb_cap][64] -> vbar_t [h_kv][nb_cap / 32][64][32] (bf16)
+// vbar [h_kv][nb_cap][D] -> vbar_t [h_kv][nb_cap / 32][D][32] (bf16)
+template <int D>
 __global__ void __launch_bounds__(256)
 vt_transpose_kernel(const uint16_t* __restrict__ vbar, uint16_t* __restrict__ vbar_t,
                     const int32_t* __restrict__ counts, int hkv, int nb_cap) {
-  constexpr int D = 64;
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
   __shared__ uint16_t tile_lds[kKeyTile][D + 2];
   const int n_tiles = (counts[SSA_COUNT_NB] + kKeyTile - 1) / kKeyTile;
   const int per_head = nb_cap / kKeyTile;
   for (int w = blockIdx.x; w < hkv * n_tiles; w += gridDim.x) {
     const int g = w / n_tiles, kt = w % n_tiles;
     const uint16_t* src = vbar + (static_cast<int64_t>(g) * nb_cap + static_cast<int64_t>(kt) * kKeyTile) * D;
-    // 32 rows x 64 dims: thread -> 8 consecutive dims of one row
-    {
-      const int row = threadIdx.x >> 3, c = threadIdx.x & 7;
+    // 32 rows x D dims: thread -> 8 consecutive dims of one row
+    if (threadIdx.x < kKeyTile * CPR) {
+      const int row = threadIdx.x / CPR, c = threadIdx.x % CPR;
       const u32x4 u = *reinterpret_cast<const u32x4*>(src + row * D + 8 * c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -187,8 +188,8 @@ vt_transpose_kernel(const uint16_t* __restrict__ vbar, uint16_t* __restrict__ vb
       }
     }
     __syncthreads();
-    // 64 dim rows x 32 positions: thread -> 8 consecutive positions of one dim
-    {
+    // D dim rows x 32 positions: thread -> 8 consecutive positions of one dim
+    if (threadIdx.x < D * 4) {
       const int dd = threadIdx.x >> 2, c = threadIdx.x & 3;
       u32x4 u;
 #pragma unroll
@@ -216,9 +217,13 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
         static_cast<uint16_t*>(p.v_cmp), static_cast<uint16_t*>(p.k_s), static_cast<uint16_t*>(p.v_s));
     if (p.vbar_t) {
       const int tiles = p.h_kv * (p.nb_cap / kKeyTile);
-      vt_transpose_kernel<<<tiles < 4096 ? tiles : 4096, 256, 0, stream>>>(
-          static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv,
-          p.nb_cap);
+      const int grid_t = tiles < 4096 ? tiles : 4096;
+      if (p.d == 32)
+        vt_transpose_kernel<32><<<grid_t, 256, 0, stream>>>(
+            static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv, p.nb_cap);
+      else
+        vt_transpose_kernel<64><<<grid_t, 256, 0, stream>>>(
+            static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv, p.nb_cap);
     }
   } else {
     pool_kernel<float><<<grid, 256, 0, stream>>>(

@@ -14,6 +14,7 @@ import torch
 import oracle
 from tests import _parity as P
 from workloads import make_custom, make_workload
+from workloads.tensors import bf16_bits_from_f32, bf16_bits_to_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +59,10 @@ def _check_pooled(got, ref, dtype):
     dict(seqs=[2100], h_q=8, h_kv=2, head_dim=32, topk=8, dtype="bf16"),
     dict(seqs=[700, 1300], h_q=2, h_kv=2, head_dim=32, topk=4, dtype="f32"),
     dict(seqs=[333, 64, 1], h_q=2, h_kv=1, head_dim=64, topk=32, dtype="bf16"),
+    # grouped heads, 16 query heads per key/value head (the MFMA group path)
+    dict(seqs=[900, 0, 701], h_q=16, h_kv=1, head_dim=32, topk=8, dtype="bf16"),
+    dict(seqs=[1203], h_q=32, h_kv=2, head_dim=64, topk=16, dtype="bf16"),
+    dict(seqs=[517, 35], h_q=32, h_kv=2, head_dim=32, topk=32, dtype="bf16"),
 ])
 def test_small_full(case):
     wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],
@@ -69,14 +74,11 @@ def test_tiny_fp32_workload_full():
     _full_compare(make_workload(1))
 
 
-def _sampled_compare(cfg, n_rows, branches=True):
-    wl = make_workload(cfg)
-    print(f"workload {cfg}: N={wl.n_tokens}", flush=True)
+def _sampled_check(wl, rows, branches=True, min_agree=0.99, tag=""):
     ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
     gb = P.gpu_build(wl)
     P.check_build(gb, ob)
     res = P.gpu_forward(wl, gb, return_topk=True)
-    rows = P.sample_rows(wl, n_rows, seed=cfg)
     kbar = oracle.pool_blocks(wl.k, ob, wl.dtype)
     vbar = oracle.pool_blocks(wl.v, ob, wl.dtype)
     ref = oracle.forward_rows(wl, ob, rows, kbar=kbar, vbar=vbar, with_branches=branches,
@@ -87,13 +89,19 @@ def _sampled_compare(cfg, n_rows, branches=True):
     mx, mean = P.check_outputs(got, ref["out"])
     G = wl.h_q // wl.h_kv
     gsel = res["topk"][tt, hh // G].cpu().numpy()
-    agree, gap = P.check_topk(gsel, ref["topk"], ref["scores"], ref["first_block"], min_agree=0.99)
+    agree, gap = P.check_topk(gsel, ref["topk"], ref["scores"], ref["first_block"], min_agree=min_agree)
     if branches:
         for i, name in enumerate(("o_cmp", "o_sel", "o_win")):
             o = P.gpu_forward(wl, gb, gates=P.one_hot_gates(wl, i))
             P.check_branch(P.host(o[tt, hh]), ref[name], name)
-    print(f"workload {cfg}: max|err| {mx:.2e} mean|err| {mean:.2e} topk agree {agree:.4f} gap {gap:.1e}")
-    return wl, gb, res
+    print(f"{tag}: max|err| {mx:.2e} mean|err| {mean:.2e} topk agree {agree:.4f} gap {gap:.1e}")
+    return ob, gb, res
+
+
+def _sampled_compare(cfg, n_rows, branches=True):
+    wl = make_workload(cfg)
+    print(f"workload {cfg}: N={wl.n_tokens}", flush=True)
+    _sampled_check(wl, P.sample_rows(wl, n_rows, seed=cfg), branches, tag=f"workload {cfg}")
 
 
 def test_workload2_sampled():
@@ -112,9 +120,11 @@ def test_varlen_workload5_sampled():
     _sampled_compare(5, 256, branches=False)
 
 
-def test_zero_queries_pick_first_blocks():
-    wl = make_custom([1200, 500], grid_res=64, n_prims=3, topk=16, h_q=4, h_kv=2, head_dim=64,
-                     dtype="bf16", seed=31)
+@pytest.mark.parametrize("h_q,h_kv,head_dim", [(4, 2, 64), (16, 1, 32), (32, 2, 64)])
+def test_zero_queries_pick_first_blocks(h_q, h_kv, head_dim):
+    # every score ties, so the lowest block ids of the sequence are chosen
+    wl = make_custom([1200, 500], grid_res=64, n_prims=3, topk=16, h_q=h_q, h_kv=h_kv,
+                     head_dim=head_dim, dtype="bf16", seed=31)
     wl.q[:] = 0
     ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
     gb = P.gpu_build(wl)
@@ -125,6 +135,36 @@ def test_zero_queries_pick_first_blocks():
         toks = ob.perm[ob.blk_off[j0]:ob.blk_off[j1]]
         expect = np.arange(j0, min(j0 + 16, j1))
         assert (sel[toks][:, :, :len(expect)] == expect).all()
+
+
+@pytest.mark.parametrize("head_dim", [32, 64])
+def test_gqa_top_blocks_in_one_lane(head_dim):
+    # Scattered voxels give about one token per block (over a thousand blocks
+    # in one sequence).  Keys of the blocks whose id is 5 mod 32 are pushed
+    # along one direction that every query shares, so the top k all come from
+    # the same column of 32-block key tiles: the grouped top-k kernel keeps
+    # only 8 blocks per column and token, and the exact fallback must decide.
+    rng = np.random.default_rng(7)
+    lin = rng.choice(64 ** 3, size=1500, replace=False)
+    coords = np.stack(np.unravel_index(lin, (64,) * 3), -1)
+    wl = make_custom(None, coords=coords, grid_res=64, topk=16, h_q=16, h_kv=1,
+                     head_dim=head_dim, dtype="bf16", seed=7)
+    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    nb = int(ob.seq_blk_off[1])
+    assert nb > 32 * 9
+    u = rng.standard_normal(head_dim).astype(np.float32)
+    u /= np.linalg.norm(u)
+    fav = np.flatnonzero(np.arange(nb) % 32 == 5)
+    toks = np.concatenate([ob.perm[ob.blk_off[j]:ob.blk_off[j + 1]] for j in fav])
+    k = wl.k.copy()
+    k[toks, 0] += 4.0 * u
+    q = 3.0 * u + 0.3 * wl.q
+    wl.k = bf16_bits_to_f32(bf16_bits_from_f32(k))
+    wl.q = bf16_bits_to_f32(bf16_bits_from_f32(q))
+    rows = P.sample_rows(wl, 320, seed=7)
+    _, _, res = _sampled_check(wl, rows, min_agree=P.TOPK_AGREE, tag=f"one-lane top-k D={head_dim}")
+    sel = res["topk"].cpu().numpy()
+    assert np.isin(sel[:, 0, :], fav).mean() > 0.99
 
 
 def test_dense_reduction():
