@@ -9,7 +9,9 @@ attention, gated sum).  Inputs are resident in HBM before timing starts.
 Workload: 131072 surface-band voxel tokens of a seeded union of 12 primitives
 on a 1024^3 grid; 16 query / 16 key-value heads, head dim 64, bfloat16;
 m_cmp = 4, m_win = 8, top-k = 16 (the 128k-token setting of the Direct3D-S2
-summary page, "Experiments").
+summary page, "Experiments").  ``--workload 4`` times the grouped-head
+workload instead (262144 tokens, 32 query / 2 key-value heads, head dim 32),
+for its kernel profile.
 
 Prints one JSON line (rank 0, N = 1 only).
 """
@@ -28,8 +30,16 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# the timed workload (default) and the grouped-head workload, which
+# ``--workload 4`` times for its kernel profile
+WORKLOADS = {
+    3: dict(name="ssa-fwd-1024^3-12prims-131072tok-h16-d64-bf16", tag="131072tok",
+            metric="SSA fwd tokens/s and TFLOP/s at 131072 voxel tokens; % bf16 MFMA peak"),
+    4: dict(name="ssa-fwd-1024^3-16prims-262144tok-h32kv2-d32-bf16", tag="262144tok",
+            metric="SSA fwd tokens/s and TFLOP/s at 262144 voxel tokens, 32 query / 2 key-value heads; "
+                   "% bf16 MFMA peak"),
+}
 WORKLOAD_ID = 3
-WORKLOAD_NAME = "ssa-fwd-1024^3-12prims-131072tok-h16-d64-bf16"
 CALIB_BYTES = 1 << 30       # plain-copy calibration size for the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "spatial_sparse_attention_ssa_amd", "csrc")
@@ -41,6 +51,9 @@ KERNEL_SOURCES = {
     "win_mfma_kernel": "ssa_attn_win.hip",
     "sel_combine_kernel": "ssa_attn_sel.hip",
     "pool_kernel": "ssa_pool.hip",
+    "gqa_cmp_kernel": "ssa_attn_gqa.hip",
+    "gqa_topk_kernel": "ssa_attn_gqa.hip",
+    "gqa_fixup_kernel": "ssa_attn_gqa.hip",
 }
 
 
@@ -53,14 +66,14 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()
 
 
-def traffic_path(kernel: str) -> str:
-    return os.path.join(PROFILES, f"{kernel}_131072tok_traffic.json")
+def traffic_path(kernel: str, wid: int = WORKLOAD_ID) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{WORKLOADS[wid]['tag']}_traffic.json")
 
 
-def stored_traffic(kernel: str):
+def stored_traffic(kernel: str, wid: int = WORKLOAD_ID):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when there is none or the kernel's source changed since."""
-    path = traffic_path(kernel)
+    path = traffic_path(kernel, wid)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -77,10 +90,10 @@ def pool_bytes(wl, nb: int) -> float:
     return wl.n_tokens * (2 * row + 4) + 2 * nb * row
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, stats_csv: str | None, commands: dict):
+def summarize_counters(fetch_csv: str, write_csv: str, stats_csv: str | None, commands: dict, wid: int):
     """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (each with
     --copy-calibration) into per-kernel HBM bytes per launch; writes
-    profiles/<kernel>_131072tok_traffic.json and prints a markdown table."""
+    profiles/<kernel>_<tokens>tok_traffic.json and prints a markdown table."""
     import csv
     from collections import defaultdict
 
@@ -120,10 +133,10 @@ def summarize_counters(fetch_csv: str, write_csv: str, stats_csv: str | None, co
         wb = sum(write[k]) / len(write[k]) * fw
         us = avg_ns.get(k, float("nan")) / 1e3
         print(f"| {k} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | {us:.1f} | {(fb + wb) / (us * 1e3):.0f} |")
-        rec = {"kernel": k, "workload": WORKLOAD_NAME, "source_sha256": kernel_source_hash(k),
+        rec = {"kernel": k, "workload": WORKLOADS[wid]["name"], "source_sha256": kernel_source_hash(k),
                "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
                "fetch_factor": ff, "write_factor": fw, "launches": len(fetch[k]), "commands": commands}
-        with open(traffic_path(k), "w") as fh:
+        with open(traffic_path(k, wid), "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
 
@@ -205,13 +218,18 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only summarise two rocprofv3 --pmc runs into profiles/*_traffic.json")
     ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=sorted(WORKLOADS),
+                    help="3: the 131072-token workload (default); 4: the grouped-head 262144-token "
+                         "workload, for its kernel profile")
     args = ap.parse_args()
+    wid = args.workload
     if args.summarize_counters:
-        cmds = {"fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python bench.py "
-                         "--steps 1 --warmup 1 --no-cpu-baseline --copy-calibration",
-                "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- python bench.py "
-                         "--steps 1 --warmup 1 --no-cpu-baseline --copy-calibration"}
-        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel_stats, cmds)
+        extra = "" if wid == WORKLOAD_ID else f" --workload {wid}"
+        cmds = {c.lower(): f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python bench.py "
+                           f"--steps 1 --warmup 1 --no-cpu-baseline --copy-calibration{extra}"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")}
+        cmds = {"fetch": cmds["fetch_size"], "write": cmds["write_size"]}
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel_stats, cmds, wid)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -225,7 +243,7 @@ def main():
     from workloads import make_workload
 
     dev = torch.device("cuda:0")
-    wl = make_workload(WORKLOAD_ID)
+    wl = make_workload(wid)
     bf = torch.bfloat16
     up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
     coords, cu = up(wl.coords, torch.int32), up(wl.cu_seqlens, torch.int32)
@@ -294,16 +312,16 @@ def main():
     torch.cuda.synchronize()
     build_ms = eb0.elapsed_time(eb1) / reps
 
-    attn_names = [n for n in stage_ms if n != "pool_kernel"]
-    dom = max(attn_names, key=lambda n: stage_ms[n])
-    dom_flops = work["total"] if len(attn_names) == 1 else work.get("cmp")
-    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    # roofline of the compressed-attention kernel, which does the compressed
+    # branch's algorithmic flops (the largest kernel on both workloads)
+    dom = "gqa_cmp_kernel" if "gqa_cmp_kernel" in stage_ms else "cmp_mfma_kernel"
+    achieved = work["cmp"] / (stage_ms[dom] * 1e-3) / 1e12
     n = wl.n_tokens
     tflops = work["total"] / (ms_step * 1e-3) / 1e12
     pool_gbs = pool_bytes(wl, work["nb"]) / (stage_ms["pool_kernel"] * 1e-3) / 1e9
 
     line = {
-        "metric": "SSA fwd tokens/s and TFLOP/s at 131072 voxel tokens; % bf16 MFMA peak",
+        "metric": WORKLOADS[wid]["metric"],
         "value": n / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -315,7 +333,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAME, "n_tokens": n,
+        "config": {"workload": WORKLOADS[wid]["name"], "n_tokens": n,
                    "grid_res": wl.grid_res, "h_q": wl.h_q, "h_kv": wl.h_kv, "head_dim": wl.head_dim,
                    "m_cmp": wl.m_cmp, "m_win": wl.m_win, "topk": wl.topk, "parallelism": "none"},
         "tflops": tflops,
@@ -327,7 +345,7 @@ def main():
         "pool_hbm": {"achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pool_gbs / PEAK_HBM_GBS,
                      "bytes": pool_bytes(wl, work["nb"])},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic(dom)},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic(dom, wid)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
