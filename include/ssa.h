@@ -140,7 +140,10 @@ size_t ssa_forward_workspace(const ssa_blocks *blocks, const ssa_attn *attn);
  *   topk_idx      optional [N, h_kv, topk] int32 selected block ids per token
  *                 and key/value group, highest score first, ties to the lower
  *                 block id, -1 padded when the sequence has fewer blocks
- *                 (NULL = skip)
+ *                 (NULL = skip).  A block's score is its compressed-attention
+ *                 probability summed over the group's query heads (LSRM
+ *                 article, sparse-attention section: the query heads of a
+ *                 group share one selection).
  *   workspace     device scratch of at least ssa_forward_workspace() bytes.
  * Attention never crosses sequences; the selection is non-causal and forces
  * no block.  Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim, topk, dtype
