@@ -13,7 +13,9 @@ the query-to-block attention scores pick the top-k blocks, whose tokens take
 part in a second attention; a third attention runs inside non-overlapping
 m_win^3 windows; the three outputs are summed with predicted per-token gates.
 Grouped-query sharing of the selection follows LSRM's 32-query / 2-KV-head
-layout (LSRM article, "Stage 1").
+layout (LSRM article, "Stage 1").  The backward pass gives the gradients of
+that output with respect to the queries, keys, values and gates, with the
+top-k choice held fixed.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed
 forms, library routines, brute force and hand-worked cases.
@@ -29,6 +31,8 @@ from .ssa_oracle import (  # noqa: F401
     topk_blocks,
     forward,
     forward_rows,
+    backward,
+    softmax_attention_grad,
     token_window_and_seq,
     round_to,
 )

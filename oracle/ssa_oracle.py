@@ -1,4 +1,5 @@
-"""Float64 numpy oracle of the SSA forward pass (test infrastructure only).
+"""Float64 numpy oracle of the SSA forward and backward passes (test
+infrastructure only).
 
 Page references: "Direct3D-S2 page" is the hyper.ai summary of arXiv
 2505.17412; "LSRM page" is the article on LSRM (Meta Reality Labs / NVIDIA).
@@ -21,6 +22,10 @@ Readings taken where the pages are silent (each listed in the design notes):
   k_eff = min(k, blocks in the sequence).  No block is forced, no causality.
 * Softmax scale 1/sqrt(D) in every branch.  Gates are used as given, in the
   order (compressed, selected, window).
+* Backward: the top-k choice is held fixed (it is piecewise constant in Q and
+  K, so it has no gradient), and the one rounding of the pooled blocks to the
+  input dtype is differentiated as the identity; a pooled row's gradient is
+  shared equally by the block's tokens (the derivative of a mean).
 """
 
 from __future__ import annotations
@@ -50,6 +55,9 @@ def bf16_round(x) -> np.ndarray:
 
 
 def round_to(x, dtype: str) -> np.ndarray:
+    """Round to the dtype's values ("f64": no rounding, for exact derivative checks)."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     if dtype == "bf16":
         return bf16_round(x)
     if dtype == "f32":
@@ -303,3 +311,94 @@ def forward(wl, blocks: Blocks | None = None, with_branches=False):
         for name in ("o_cmp", "o_sel", "o_win"):
             full[name] = res[name].reshape(N, H, D)
     return full
+
+
+# ----------------------------------------------------------------------------
+# Backward pass
+# ----------------------------------------------------------------------------
+
+def softmax_attention_grad(q, k, v, do, scale: float):
+    """Gradients of o = softmax(scale * k q) v for one query, given do = dL/do.
+
+    With p the probabilities: dp_j = do . v_j is the gradient of p_j, the
+    softmax turns it into the logit gradient ds_j = p_j (dp_j - sum_i p_i dp_i),
+    and the logits scale * q . k_j give dq = scale * sum_j ds_j k_j and
+    dk_j = scale * ds_j q; dv_j = p_j do.  Returns (dq [D], dk [n, D],
+    dv [n, D], o [D]).
+    """
+    o, p = softmax_attention(q, k, v, scale)
+    dp = v @ do
+    ds = p * (dp - p @ dp)
+    return scale * (ds @ k), scale * np.outer(ds, q), np.outer(p, do), o
+
+
+def backward(wl, dout, blocks: Blocks | None = None, rows=None):
+    """Gradients of L = sum(dout * O), O the SSA output before its rounding.
+
+    O[t, h] = G0 o_cmp + G1 o_sel + G2 o_win (Direct3D-S2 page, "Method"), so
+    branch x sees the output gradient G_x * dout[t, h] and the gate gets
+    dout[t, h] . o_x.  The compressed branch's key / value gradients land on
+    the pooled rows and are then shared by each block's tokens, divided by the
+    token count (the pooling is a mean).  The top-k choice is held fixed.
+
+    ``rows`` (default: every (token, head)) restricts the sum to those rows;
+    the returned dq and dgates rows are then exact for them, while dk / dv hold
+    only their contributions.  Returns float64 dq [N, H, D], dk / dv
+    [N, Hkv, D], dgates [N, H, 3], dkbar / dvbar [nb, Hkv, D].
+    """
+    if blocks is None:
+        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    H, Hkv, D, K = wl.h_q, wl.h_kv, wl.head_dim, wl.topk
+    G = H // Hkv
+    N = wl.n_tokens
+    scale = 1.0 / math.sqrt(D)
+    kbar = pool_blocks(wl.k, blocks, wl.dtype)
+    vbar = pool_blocks(wl.v, blocks, wl.dtype)
+    pos_of_tok = np.empty(len(blocks.perm), dtype=np.int64)
+    pos_of_tok[blocks.perm] = np.arange(len(blocks.perm))
+
+    def f64(a):
+        return np.asarray(a, dtype=np.float64)
+
+    k64, v64 = f64(wl.k), f64(wl.v)
+    dq = np.zeros((N, H, D))
+    dk = np.zeros((N, Hkv, D))
+    dv = np.zeros((N, Hkv, D))
+    dkbar = np.zeros((blocks.nb, Hkv, D))
+    dvbar = np.zeros((blocks.nb, Hkv, D))
+    dgates = np.zeros((N, H, 3))
+    if rows is None:
+        rows = [(t, h) for t in range(N) for h in range(H)]
+    for t, h in rows:
+        i = int(pos_of_tok[t])
+        b, w = _token_rows(blocks, i)
+        g = h // G
+        j0, j1 = int(blocks.seq_blk_off[b]), int(blocks.seq_blk_off[b + 1])
+        # the selection, as in the forward
+        score = np.zeros(j1 - j0)
+        for hh in range(g * G, (g + 1) * G):
+            score += softmax_attention(f64(wl.q[t, hh]), kbar[j0:j1, g], vbar[j0:j1, g], scale)[1]
+        chosen = topk_blocks(score, K)
+        sel = blocks.perm[np.concatenate([np.arange(blocks.blk_off[j0 + c], blocks.blk_off[j0 + c + 1])
+                                          for c in chosen])]
+        win = blocks.perm[blocks.win_off[w]:blocks.win_off[w + 1]]
+        q, do, gt = f64(wl.q[t, h]), f64(dout[t, h]), f64(wl.gates[t, h])
+        # (a) compressed branch: gradients of the pooled rows
+        dq_c, dkb, dvb, o_c = softmax_attention_grad(q, kbar[j0:j1, g], vbar[j0:j1, g], gt[0] * do, scale)
+        dkbar[j0:j1, g] += dkb
+        dvbar[j0:j1, g] += dvb
+        # (b) selected tokens and (c) window tokens (each a set of distinct tokens)
+        dq_s, dks, dvs, o_s = softmax_attention_grad(q, k64[sel, g], v64[sel, g], gt[1] * do, scale)
+        dk[sel, g] += dks
+        dv[sel, g] += dvs
+        dq_w, dkw, dvw, o_w = softmax_attention_grad(q, k64[win, g], v64[win, g], gt[2] * do, scale)
+        dk[win, g] += dkw
+        dv[win, g] += dvw
+        dq[t, h] = dq_c + dq_s + dq_w
+        dgates[t, h] = (do @ o_c, do @ o_s, do @ o_w)
+    # the pooling is a mean: each token of block j gets 1 / n_j of its gradient
+    for j in range(blocks.nb):
+        toks = blocks.perm[blocks.blk_off[j]:blocks.blk_off[j + 1]]
+        dk[toks] += dkbar[j] / len(toks)
+        dv[toks] += dvbar[j] / len(toks)
+    return dict(dq=dq, dk=dk, dv=dv, dgates=dgates, dkbar=dkbar, dvbar=dvbar)
