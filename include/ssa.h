@@ -160,7 +160,7 @@ enum {
                              /* window) and the gated sum                          */
   SSA_STAGE_ATTN2 = 2,       /* a second attention kernel, when the plan has one    */
   SSA_STAGE_ATTN3 = 3,       /* a third attention kernel, when the plan has one     */
-  SSA_STAGES = 8
+  SSA_STAGES = 12
 };
 
 /* Same as ssa_forward, but records a hipEvent on hip_stream around every
@@ -175,6 +175,58 @@ ssa_status ssa_forward_timed(const ssa_blocks *blocks, const ssa_attn *attn, con
 
 /* Name of the kernel that runs stage `stage` for this layout ("" if none). */
 const char *ssa_stage_name(const ssa_attn *attn, int32_t stage);
+
+/* ---------------------------------------------------------------- training */
+
+/* SSA forward that also saves what ssa_backward reads.  Same computation and
+ * output as ssa_forward (Direct3D-S2 page, "Method"), plus:
+ *   topk_idx  required [N, h_kv, topk] int32 (as in ssa_forward).
+ *   lse       required [3, N, h_q] float32: for branch x (0 compressed,
+ *             1 selected, 2 window) and query (t, h), the natural log of the
+ *             softmax denominator, log sum_j exp(scale * q . k_j) over the
+ *             branch's keys.
+ * Workspace: ssa_forward_workspace() bytes.  Errors as ssa_forward. */
+ssa_status ssa_forward_train(const ssa_blocks *blocks, const ssa_attn *attn, const void *q,
+                             const void *k, const void *v, const void *gates, void *out,
+                             int32_t *topk_idx, float *lse, void *workspace, size_t ws_bytes,
+                             void *hip_stream);
+
+/* Workspace bytes ssa_backward needs for these blocks and this layout. */
+size_t ssa_backward_workspace(const ssa_blocks *blocks, const ssa_attn *attn);
+
+/* Gradients of L = sum(dout * out), out being the ssa_forward output of the
+ * same inputs (Direct3D-S2 page, "Method": out = G0 o_cmp + G1 o_sel + G2
+ * o_win, three softmax attentions of the query over the sequence's pooled
+ * blocks, the tokens of its top-k blocks and the tokens of its window).
+ * The top-k choice is held fixed: it is piecewise constant in q and k, so it
+ * has no gradient.  The pooled rows are block means, so each token of block
+ * j receives 1 / n_j of its pooled row's gradient; their one rounding to the
+ * dtype counts as the identity.
+ *   q, k, v, gates  the forward's inputs (layouts as in ssa_forward)
+ *   dout      [N, h_q, D]  gradient of the output
+ *   topk_idx, lse  as written by ssa_forward_train for these inputs
+ *   dq        [N, h_q, D]  out
+ *   dk, dv    [N, h_kv, D] out
+ *   dgates    optional [N, h_q, 3] out: dout . o_x per branch (NULL = skip)
+ *   workspace device scratch of at least ssa_backward_workspace() bytes.
+ * All tensors in dtype except lse (float32).  Sums run in float32; the
+ * selected branch's key / value gradients are summed in an order that may
+ * differ from run to run (float rounding only).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (as ssa_forward), WORKSPACE, DEVICE. */
+ssa_status ssa_backward(const ssa_blocks *blocks, const ssa_attn *attn, const void *q, const void *k,
+                        const void *v, const void *gates, const void *dout, const int32_t *topk_idx,
+                        const float *lse, void *dq, void *dk, void *dv, void *dgates,
+                        void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* Same as ssa_backward, with per-stage times as in ssa_forward_timed. */
+ssa_status ssa_backward_timed(const ssa_blocks *blocks, const ssa_attn *attn, const void *q,
+                              const void *k, const void *v, const void *gates, const void *dout,
+                              const int32_t *topk_idx, const float *lse, void *dq, void *dk,
+                              void *dv, void *dgates, void *workspace, size_t ws_bytes,
+                              void *hip_stream, float *stage_ms, int32_t *n_stages);
+
+/* Name of backward stage `stage` for this layout ("" if none). */
+const char *ssa_backward_stage_name(const ssa_attn *attn, int32_t stage);
 
 /* Static text for a status code. */
 const char *ssa_status_string(ssa_status status);

@@ -341,10 +341,10 @@ def backward(wl, dout, blocks: Blocks | None = None, rows=None):
     the pooled rows and are then shared by each block's tokens, divided by the
     token count (the pooling is a mean).  The top-k choice is held fixed.
 
-    ``rows`` (default: every (token, head)) restricts the sum to those rows;
-    the returned dq and dgates rows are then exact for them, while dk / dv hold
-    only their contributions.  Returns float64 dq [N, H, D], dk / dv
-    [N, Hkv, D], dgates [N, H, 3], dkbar / dvbar [nb, Hkv, D].
+    Without ``rows``: float64 dq [N, H, D], dk / dv [N, Hkv, D], dgates
+    [N, H, 3] and dkbar / dvbar [nb, Hkv, D].  With ``rows`` (a list of
+    (token, head)): only dq [len(rows), D] and dgates [len(rows), 3] of those
+    rows, which depend on nothing else.
     """
     if blocks is None:
         blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
@@ -360,16 +360,19 @@ def backward(wl, dout, blocks: Blocks | None = None, rows=None):
     def f64(a):
         return np.asarray(a, dtype=np.float64)
 
-    k64, v64 = f64(wl.k), f64(wl.v)
-    dq = np.zeros((N, H, D))
-    dk = np.zeros((N, Hkv, D))
-    dv = np.zeros((N, Hkv, D))
-    dkbar = np.zeros((blocks.nb, Hkv, D))
-    dvbar = np.zeros((blocks.nb, Hkv, D))
-    dgates = np.zeros((N, H, 3))
-    if rows is None:
+    full = rows is None
+    if full:
         rows = [(t, h) for t in range(N) for h in range(H)]
-    for t, h in rows:
+        dq = np.zeros((N, H, D))
+        dgates = np.zeros((N, H, 3))
+        dk = np.zeros((N, Hkv, D))
+        dv = np.zeros((N, Hkv, D))
+        dkbar = np.zeros((blocks.nb, Hkv, D))
+        dvbar = np.zeros((blocks.nb, Hkv, D))
+    else:
+        dq = np.zeros((len(rows), D))
+        dgates = np.zeros((len(rows), 3))
+    for n_row, (t, h) in enumerate(rows):
         i = int(pos_of_tok[t])
         b, w = _token_rows(blocks, i)
         g = h // G
@@ -385,17 +388,23 @@ def backward(wl, dout, blocks: Blocks | None = None, rows=None):
         q, do, gt = f64(wl.q[t, h]), f64(dout[t, h]), f64(wl.gates[t, h])
         # (a) compressed branch: gradients of the pooled rows
         dq_c, dkb, dvb, o_c = softmax_attention_grad(q, kbar[j0:j1, g], vbar[j0:j1, g], gt[0] * do, scale)
-        dkbar[j0:j1, g] += dkb
-        dvbar[j0:j1, g] += dvb
         # (b) selected tokens and (c) window tokens (each a set of distinct tokens)
-        dq_s, dks, dvs, o_s = softmax_attention_grad(q, k64[sel, g], v64[sel, g], gt[1] * do, scale)
-        dk[sel, g] += dks
-        dv[sel, g] += dvs
-        dq_w, dkw, dvw, o_w = softmax_attention_grad(q, k64[win, g], v64[win, g], gt[2] * do, scale)
-        dk[win, g] += dkw
-        dv[win, g] += dvw
-        dq[t, h] = dq_c + dq_s + dq_w
-        dgates[t, h] = (do @ o_c, do @ o_s, do @ o_w)
+        dq_s, dks, dvs, o_s = softmax_attention_grad(q, f64(wl.k[sel, g]), f64(wl.v[sel, g]), gt[1] * do, scale)
+        dq_w, dkw, dvw, o_w = softmax_attention_grad(q, f64(wl.k[win, g]), f64(wl.v[win, g]), gt[2] * do, scale)
+        if full:
+            dkbar[j0:j1, g] += dkb
+            dvbar[j0:j1, g] += dvb
+            dk[sel, g] += dks
+            dv[sel, g] += dvs
+            dk[win, g] += dkw
+            dv[win, g] += dvw
+            dq[t, h] = dq_c + dq_s + dq_w
+            dgates[t, h] = (do @ o_c, do @ o_s, do @ o_w)
+        else:
+            dq[n_row] = dq_c + dq_s + dq_w
+            dgates[n_row] = (do @ o_c, do @ o_s, do @ o_w)
+    if not full:
+        return dict(dq=dq, dgates=dgates)
     # the pooling is a mean: each token of block j gets 1 / n_j of its gradient
     for j in range(blocks.nb):
         toks = blocks.perm[blocks.blk_off[j]:blocks.blk_off[j + 1]]

@@ -7,6 +7,9 @@ runs in the library's HIP kernels.
     blocks = build_blocks(coords, cu_seqlens, grid_res=1024, m_cmp=4, m_win=8)
     out = forward(blocks, q, k, v, gates, topk=16)
 
+    saved = forward_train(blocks, q, k, v, gates, topk=16)      # out + saved state
+    grads = backward(blocks, q, k, v, gates, saved, dout)       # dq, dk, dv, dgates
+
 Method: Direct3D-S2 (hyper.ai summary of arXiv 2505.17412, "Method"):
 mean-pooled compressed attention, top-k spatial block selection and
 non-overlapping window attention over 3D-blocked sparse voxel tokens, summed
@@ -22,8 +25,8 @@ import torch
 
 from . import _binding as B
 
-__all__ = ["Blocks", "build_blocks", "forward", "forward_workspace_bytes", "SsaError",
-           "library_path", "version"]
+__all__ = ["Blocks", "build_blocks", "forward", "forward_workspace_bytes", "forward_train", "backward",
+           "backward_workspace_bytes", "SsaError", "library_path", "version"]
 
 SsaError = B.SsaError
 
@@ -185,4 +188,88 @@ def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
         res["k_cmp"], res["v_cmp"] = kc[:blocks.nb], vc[:blocks.nb]
     if return_topk:
         res["topk"] = tk[:n]
+    return res
+
+
+def _check_inputs(blocks, q, k, v, gates):
+    for name, t in (("q", q), ("k", k), ("v", v), ("gates", gates)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    n = blocks.n_tokens
+    if q.shape[0] != n or k.shape[0] != n or v.shape[0] != n or gates.shape[0] != n:
+        raise ValueError("token count of q/k/v/gates differs from the blocks")
+    if k.shape != v.shape or gates.shape != (n, q.shape[1], 3) or k.shape[2] != q.shape[2]:
+        raise ValueError("shape mismatch among q, k, v, gates")
+    return tuple(t.contiguous() for t in (q, k, v, gates))
+
+
+def forward_train(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  gates: torch.Tensor, topk: int, scale: float | None = None,
+                  workspace: torch.Tensor | None = None) -> dict:
+    """SSA forward that also keeps what ``backward`` needs.
+
+    Returns a dict: ``out`` [N, Hq, D], ``topk`` [N, Hkv, topk] int32 and
+    ``lse`` [3, N, Hq] float32 (natural-log softmax denominators of the
+    compressed, selected and window branches), plus ``topk_k`` and ``scale``.
+    """
+    q, k, v, gates = _check_inputs(blocks, q, k, v, gates)
+    L = B.lib()
+    a = _attn(q, k, topk, scale)
+    dev = q.device
+    n, hq, d = q.shape
+    out = torch.empty_like(q)
+    tk = torch.empty((max(n, 1), k.shape[1], topk), dtype=torch.int32, device=dev)
+    lse = torch.empty((3, max(n, 1), hq), dtype=torch.float32, device=dev)
+    ws_bytes = int(L.ssa_forward_workspace(ctypes.byref(blocks.struct), ctypes.byref(a)))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    B.check(L.ssa_forward_train(ctypes.byref(blocks.struct), ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(gates), _ptr(out), _ptr(tk), _ptr(lse), _ptr(workspace), ws_bytes,
+                                _stream(dev)))
+    return dict(out=out, topk=tk, lse=lse, topk_k=int(topk), scale=scale)
+
+
+def backward_workspace_bytes(blocks: Blocks, q, k, topk: int, scale=None) -> int:
+    a = _attn(q, k, topk, scale)
+    return int(B.lib().ssa_backward_workspace(ctypes.byref(blocks.struct), ctypes.byref(a)))
+
+
+def backward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gates: torch.Tensor,
+             saved: dict, dout: torch.Tensor, want_dgates: bool = True,
+             workspace: torch.Tensor | None = None, stage_times: dict | None = None) -> dict:
+    """Gradients of sum(dout * out) for the forward that produced ``saved``.
+
+    Returns a dict with ``dq`` [N, Hq, D], ``dk`` / ``dv`` [N, Hkv, D] and,
+    with ``want_dgates``, ``dgates`` [N, Hq, 3], all in the input dtype.
+    """
+    q, k, v, gates = _check_inputs(blocks, q, k, v, gates)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_cuda:
+        raise ValueError("dout must be a GPU tensor shaped and typed like q")
+    dout = dout.contiguous()
+    L = B.lib()
+    a = _attn(q, k, saved["topk_k"], saved["scale"])
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty_like(gates) if want_dgates else None
+    ws_bytes = int(L.ssa_backward_workspace(ctypes.byref(blocks.struct), ctypes.byref(a)))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    args = (ctypes.byref(blocks.struct), ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(dout),
+            _ptr(saved["topk"]), _ptr(saved["lse"]), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(workspace),
+            ws_bytes, _stream(dev))
+    if stage_times is None:
+        B.check(L.ssa_backward(*args))
+    else:
+        ms = (ctypes.c_float * B.SSA_STAGES)()
+        ns = ctypes.c_int32(0)
+        B.check(L.ssa_backward_timed(*args, ms, ctypes.byref(ns)))
+        for i in range(ns.value):
+            stage_times[L.ssa_backward_stage_name(ctypes.byref(a), i).decode()] = float(ms[i])
+    res = dict(dq=dq, dk=dk, dv=dv)
+    if want_dgates:
+        res["dgates"] = dg
     return res

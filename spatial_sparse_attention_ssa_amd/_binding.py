@@ -29,7 +29,7 @@ SSA_COUNT_MAX_BLK = 3
 SSA_COUNT_MAX_WIN = 4
 SSA_COUNT_KEY_BITS = 5
 SSA_COUNTS = 8
-SSA_STAGES = 8
+SSA_STAGES = 12
 
 # every symbol include/ssa.h declares
 EXPORTED = (
@@ -39,6 +39,11 @@ EXPORTED = (
     "ssa_forward",
     "ssa_forward_timed",
     "ssa_stage_name",
+    "ssa_forward_train",
+    "ssa_backward_workspace",
+    "ssa_backward",
+    "ssa_backward_timed",
+    "ssa_backward_stage_name",
     "ssa_status_string",
     "ssa_last_error",
     "ssa_version",
@@ -115,6 +120,19 @@ def lib() -> ctypes.CDLL:
     L.ssa_forward_timed.restype = ctypes.c_int
     L.ssa_stage_name.argtypes = [ctypes.POINTER(SsaAttn), i32]
     L.ssa_stage_name.restype = ctypes.c_char_p
+    L.ssa_forward_train.argtypes = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn), vp, vp, vp, vp, vp,
+                                    vp, vp, vp, sz, vp]
+    L.ssa_forward_train.restype = ctypes.c_int
+    L.ssa_backward_workspace.argtypes = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn)]
+    L.ssa_backward_workspace.restype = sz
+    bwd = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+           vp, vp, sz, vp]
+    L.ssa_backward.argtypes = bwd
+    L.ssa_backward.restype = ctypes.c_int
+    L.ssa_backward_timed.argtypes = bwd + [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    L.ssa_backward_timed.restype = ctypes.c_int
+    L.ssa_backward_stage_name.argtypes = [ctypes.POINTER(SsaAttn), i32]
+    L.ssa_backward_stage_name.restype = ctypes.c_char_p
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
     L.ssa_last_error.argtypes = []

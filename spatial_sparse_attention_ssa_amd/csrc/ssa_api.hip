@@ -249,7 +249,7 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
 ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
                         const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
                         int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream,
-                        float* stage_ms, int32_t* n_stages) {
+                        float* stage_ms, int32_t* n_stages, float* lse = nullptr) {
   if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
   ssa_status st = check_attn(attn);
   if (st != SSA_OK) return st;
@@ -297,6 +297,7 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
   p.k_cmp = k_cmp;
   p.v_cmp = v_cmp;
   p.topk_idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + lay.topk);
+  p.lse = lse;
   if (use_mfma_path(attn)) {
     p.vbar_t = w + lay.vbar_t;
     p.k_s = w + lay.k_s;
@@ -356,10 +357,200 @@ ssa_status ssa_forward_timed(const ssa_blocks* blocks, const ssa_attn* attn, con
                       hip_stream, stage_ms, n_stages);
 }
 
+ssa_status ssa_forward_train(const ssa_blocks* blocks, const ssa_attn* attn, const void* q,
+                             const void* k, const void* v, const void* gates, void* out,
+                             int32_t* topk_idx, float* lse, void* workspace, size_t ws_bytes,
+                             void* hip_stream) {
+  if (!topk_idx || !lse) return fail(SSA_ERR_INVALID_ARGUMENT, "topk_idx and lse must be non-null");
+  return forward_impl(blocks, attn, q, k, v, gates, out, nullptr, nullptr, topk_idx, workspace, ws_bytes,
+                      hip_stream, nullptr, nullptr, lse);
+}
+
 const char* ssa_stage_name(const ssa_attn* attn, int32_t stage) {
   if (!attn || stage < 0 || stage >= SSA_STAGES) return "";
   Stage stages[SSA_STAGES];
   const int ns = forward_plan(attn, stages);
+  return stage < ns ? stages[stage].name : "";
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- backward
+
+namespace {
+
+struct BwdLayout {
+  size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_cnt, sel_off, sel_list, total;
+};
+
+BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
+  const size_t cap = static_cast<size_t>(nb_capacity(b));
+  const size_t n = static_cast<size_t>(b->n_tokens);
+  const size_t eb = static_cast<size_t>(elt_bytes(a->dtype));
+  const size_t D = static_cast<size_t>(a->head_dim);
+  const size_t pooled = align256(eb * a->h_kv * cap * D);
+  const size_t sorted = align256(eb * a->h_kv * n * D);
+  BwdLayout L{};
+  size_t off = 0;
+  L.kbar = off; off += pooled;
+  L.vbar = off; off += pooled;
+  L.k_s = off; off += sorted;
+  L.v_s = off; off += sorted;
+  L.delta = off; off += align256(sizeof(float) * 3 * n * a->h_q);
+  L.dq_acc = off; off += align256(sizeof(float) * n * a->h_q * D);
+  L.dk_acc = off; off += align256(sizeof(float) * a->h_kv * n * D);
+  L.dv_acc = off; off += align256(sizeof(float) * a->h_kv * n * D);
+  L.dkbar = off; off += align256(sizeof(float) * a->h_kv * cap * D);
+  L.dvbar = off; off += align256(sizeof(float) * a->h_kv * cap * D);
+  L.sel_cnt = off; off += align256(sizeof(int32_t) * a->h_kv * cap);
+  L.sel_off = off; off += align256(sizeof(int32_t) * (a->h_kv * cap + 1));
+  L.sel_list = off; off += align256(sizeof(int32_t) * n * a->h_kv * a->topk);
+  L.total = off + 256;
+  return L;
+}
+
+struct BStage {
+  const char* name;
+  hipError_t (*launch)(const ssa::BwdParams&, ssa_dtype, hipStream_t);
+};
+
+int backward_plan(const ssa_attn* /*attn*/, BStage* stages) {
+  int n = 0;
+  stages[n++] = BStage{"pool_kernel", ssa::launch_bwd_pool};
+  stages[n++] = BStage{"sel_index", ssa::launch_bwd_sel_index};
+  stages[n++] = BStage{"cmp_dq_kernel", ssa::launch_bwd_cmp_dq};
+  stages[n++] = BStage{"cmp_dkv_kernel", ssa::launch_bwd_cmp_dkv};
+  stages[n++] = BStage{"win_dq_kernel", ssa::launch_bwd_win_dq};
+  stages[n++] = BStage{"win_dkv_kernel", ssa::launch_bwd_win_dkv};
+  stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
+  stages[n++] = BStage{"sel_dkv_kernel", ssa::launch_bwd_sel_dkv};
+  stages[n++] = BStage{"bwd_finalize_kernel", ssa::launch_bwd_finalize};
+  return n;
+}
+
+ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                         const void* v, const void* gates, const void* dout, const int32_t* topk_idx,
+                         const float* lse, void* dq, void* dk, void* dv, void* dgates, void* workspace,
+                         size_t ws_bytes, void* hip_stream, float* stage_ms, int32_t* n_stages) {
+  if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
+  ssa_status st = check_attn(attn);
+  if (st != SSA_OK) return st;
+  if (blocks->n_tokens < 0 || blocks->n_tokens > 0x7FFFFFFE || blocks->batch < 1)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "blocks were not built (n_tokens %lld, batch %d)",
+                static_cast<long long>(blocks->n_tokens), blocks->batch);
+  if (!blocks->perm || !blocks->blk_off || !blocks->win_off || !blocks->seq_blk_off ||
+      !blocks->seq_win_off || !blocks->counts)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "a device buffer of blocks is null");
+  if (blocks->n_tokens > 0 &&
+      (!q || !k || !v || !gates || !dout || !topk_idx || !lse || !dq || !dk || !dv))
+    return fail(SSA_ERR_INVALID_ARGUMENT, "q, k, v, gates, dout, topk_idx, lse, dq, dk and dv must be non-null");
+  const BwdLayout lay = backward_layout(blocks, attn);
+  if (!workspace || ws_bytes < lay.total)
+    return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, lay.total);
+  if (stage_ms)
+    for (int i = 0; i < SSA_STAGES; ++i) stage_ms[i] = 0.f;
+  if (n_stages) *n_stages = 0;
+  if (blocks->n_tokens == 0) return ok();
+
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255));
+  ssa::BwdParams bp{};
+  ssa::FwdParams& p = bp.f;
+  p.perm = blocks->perm;
+  p.blk_off = blocks->blk_off;
+  p.win_off = blocks->win_off;
+  p.seq_blk_off = blocks->seq_blk_off;
+  p.seq_win_off = blocks->seq_win_off;
+  p.counts = blocks->counts;
+  p.n = static_cast<int32_t>(blocks->n_tokens);
+  p.batch = blocks->batch;
+  p.nb_cap = static_cast<int32_t>(nb_capacity(blocks));
+  p.h_q = attn->h_q;
+  p.h_kv = attn->h_kv;
+  p.d = attn->head_dim;
+  p.topk = attn->topk;
+  p.scale = attn->scale > 0.f ? attn->scale : 1.0f / sqrtf(static_cast<float>(attn->head_dim));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gates = gates;
+  p.kbar = w + lay.kbar;
+  p.vbar = w + lay.vbar;
+  p.k_s = w + lay.k_s;
+  p.v_s = w + lay.v_s;
+  p.topk_idx = const_cast<int32_t*>(topk_idx);
+  bp.dout = dout;
+  bp.lse = lse;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dgates = dgates;
+  bp.delta = reinterpret_cast<float*>(w + lay.delta);
+  bp.dq_acc = reinterpret_cast<float*>(w + lay.dq_acc);
+  bp.dk_acc = reinterpret_cast<float*>(w + lay.dk_acc);
+  bp.dv_acc = reinterpret_cast<float*>(w + lay.dv_acc);
+  bp.dkbar = reinterpret_cast<float*>(w + lay.dkbar);
+  bp.dvbar = reinterpret_cast<float*>(w + lay.dvbar);
+  bp.sel_cnt = reinterpret_cast<int32_t*>(w + lay.sel_cnt);
+  bp.sel_off = reinterpret_cast<int32_t*>(w + lay.sel_off);
+  bp.sel_list = reinterpret_cast<int32_t*>(w + lay.sel_list);
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  BStage stages[SSA_STAGES];
+  const int ns = backward_plan(attn, stages);
+  hipEvent_t ev[SSA_STAGES + 1] = {};
+  hipError_t e = hipSuccess;
+  if (stage_ms) {
+    for (int i = 0; i <= ns && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    if (e == hipSuccess) e = hipEventRecord(ev[0], stream);
+  }
+  for (int i = 0; i < ns && e == hipSuccess; ++i) {
+    e = stages[i].launch(bp, attn->dtype, stream);
+    if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[i + 1], stream);
+  }
+  if (stage_ms) {
+    if (e == hipSuccess) e = hipEventSynchronize(ev[ns]);
+    for (int i = 0; i < ns && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i <= ns; ++i)
+      if (ev[i]) hipEventDestroy(ev[i]);
+  }
+  if (e != hipSuccess) return fail(SSA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  if (n_stages) *n_stages = ns;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssa_backward_workspace(const ssa_blocks* blocks, const ssa_attn* attn) {
+  if (!blocks || !attn || blocks->n_tokens < 0 || attn->h_kv < 1 || attn->h_q < 1 || attn->head_dim < 1 ||
+      attn->topk < 1)
+    return 0;
+  return backward_layout(blocks, attn).total;
+}
+
+ssa_status ssa_backward(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                        const void* v, const void* gates, const void* dout, const int32_t* topk_idx,
+                        const float* lse, void* dq, void* dk, void* dv, void* dgates, void* workspace,
+                        size_t ws_bytes, void* hip_stream) {
+  return backward_impl(blocks, attn, q, k, v, gates, dout, topk_idx, lse, dq, dk, dv, dgates, workspace,
+                       ws_bytes, hip_stream, nullptr, nullptr);
+}
+
+ssa_status ssa_backward_timed(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                              const void* v, const void* gates, const void* dout, const int32_t* topk_idx,
+                              const float* lse, void* dq, void* dk, void* dv, void* dgates,
+                              void* workspace, size_t ws_bytes, void* hip_stream, float* stage_ms,
+                              int32_t* n_stages) {
+  if (!stage_ms) return fail(SSA_ERR_INVALID_ARGUMENT, "stage_ms is null");
+  return backward_impl(blocks, attn, q, k, v, gates, dout, topk_idx, lse, dq, dk, dv, dgates, workspace,
+                       ws_bytes, hip_stream, stage_ms, n_stages);
+}
+
+const char* ssa_backward_stage_name(const ssa_attn* attn, int32_t stage) {
+  if (!attn || stage < 0 || stage >= SSA_STAGES) return "";
+  BStage stages[SSA_STAGES];
+  const int ns = backward_plan(attn, stages);
   return stage < ns ? stages[stage].name : "";
 }
 

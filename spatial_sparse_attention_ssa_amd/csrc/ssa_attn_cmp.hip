@@ -467,11 +467,13 @@ cmp_mfma_kernel(FwdParams p) {
   for (int x = 0; x < 2; ++x) {
     QBlock<KMAX>& B = blk[x];
     const float lsum = B.l0 + B.l1;
-    const float l_q = (lsum + __shfl_xor(lsum, 32)) * kTruncInv;
+    const float lsum_q = lsum + __shfl_xor(lsum, 32);
+    const float l_q = lsum_q * kTruncInv;
     if (B.valid) {
-      const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(B.t) * p.h_q + h) * 3;
+      const int64_t row = static_cast<int64_t>(B.t) * p.h_q + h;
+      const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + row * 3;
       const float f = bf16_bits_to_f32(gt[0]) / l_q;
-      float* dst = p.acc + (static_cast<int64_t>(B.t) * p.h_q + h) * kD;
+      float* dst = p.acc + row * kD;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int d = 8 * rb + 4 * half;
@@ -479,6 +481,11 @@ cmp_mfma_kernel(FwdParams p) {
             make_float4(B.o0[4 * rb] * f, B.o0[4 * rb + 1] * f, B.o0[4 * rb + 2] * f, B.o0[4 * rb + 3] * f);
         *reinterpret_cast<float4*>(dst + 32 + d) =
             make_float4(B.o1[4 * rb] * f, B.o1[4 * rb + 1] * f, B.o1[4 * rb + 2] * f, B.o1[4 * rb + 3] * f);
+      }
+      if (p.lse && half == 0) {
+        // p_j = 2^(s_j scale log2e + k0), so the denominator of the logits is
+        // lsum_q * 2^-k0
+        p.lse[row] = (__log2f(lsum_q) - B.k0) * kLn2;
       }
     }
   }

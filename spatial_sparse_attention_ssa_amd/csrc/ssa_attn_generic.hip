@@ -113,14 +113,16 @@ struct Acc {
 #pragma unroll
     for (int e = 0; e < D; ++e) o[e] = fmaf(p, vrow[e], o[e]);
   }
-  // merged result for component (lane mod D)
-  __device__ __forceinline__ float finish() {
+  // merged result for component (lane mod D); *lse2 receives the log2 of
+  // the softmax denominator of the log2-unit logits
+  __device__ __forceinline__ float finish(float* lse2) {
     const float mm = wave_max(m);
     const float f = (l > 0.f) ? exp2f(m - mm) : 0.f;
     l *= f;
 #pragma unroll
     for (int e = 0; e < D; ++e) o[e] *= f;
     const float ll = wave_sum(l);
+    *lse2 = mm + log2f(ll);
     return wave_reduce_scatter<D>(o) / ll;
   }
 };
@@ -287,7 +289,8 @@ generic_fwd(FwdParams p) {
       load_row<D>(VB + static_cast<int64_t>(j) * D, row2);
       acc.add(c2 * dot<D>(q, row), row2);
     }
-    const float o_cmp = acc.finish();
+    float lse_c, lse_s, lse_w;
+    const float o_cmp = acc.finish(&lse_c);
 
     acc.init();
     for (int f = lane; f < n_sel; f += 64) {
@@ -299,7 +302,7 @@ generic_fwd(FwdParams p) {
       load_row<D>(V + (tok * p.h_kv + g) * D, row2);
       acc.add(c2 * dot<D>(q, row), row2);
     }
-    const float o_sel = acc.finish();
+    const float o_sel = acc.finish(&lse_s);
 
     acc.init();
     for (int pos = wa + lane; pos < wb; pos += 64) {
@@ -308,13 +311,20 @@ generic_fwd(FwdParams p) {
       load_row<D>(V + (tok * p.h_kv + g) * D, row2);
       acc.add(c2 * dot<D>(q, row), row2);
     }
-    const float o_win = acc.finish();
+    const float o_win = acc.finish(&lse_w);
 
     if (lane < D) {
       const T* gt = static_cast<const T*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
       const float o = Elt<T>::load(gt) * o_cmp + Elt<T>::load(gt + 1) * o_sel +
                       Elt<T>::load(gt + 2) * o_win;
       Elt<T>::store(static_cast<T*>(p.out) + (static_cast<int64_t>(t) * p.h_q + h) * D + lane, o);
+      if (p.lse && lane == 0) {
+        const int64_t nrow = static_cast<int64_t>(p.n) * p.h_q;
+        const int64_t row = static_cast<int64_t>(t) * p.h_q + h;
+        p.lse[row] = lse_c * kLn2;
+        p.lse[nrow + row] = lse_s * kLn2;
+        p.lse[2 * nrow + row] = lse_w * kLn2;
+      }
     }
   }
 }

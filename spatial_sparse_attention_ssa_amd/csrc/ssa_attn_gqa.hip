@@ -249,7 +249,11 @@ gqa_cmp_kernel(FwdParams p) {
     const float lq = l[x] + __shfl_xor(l[x], 32);
     if (!valid[x]) continue;
     const int64_t row = static_cast<int64_t>(t[x]) * p.h_q + h;
-    if (half == 0) p.norm[row] = m[x] * c2 + __log2f(lq);
+    const float c = m[x] * c2 + __log2f(lq);
+    if (half == 0) {
+      p.norm[row] = c;
+      if (p.lse) p.lse[row] = c * kLn2;
+    }
     const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + row * 3;
     const float f = bf16_bits_to_f32(gt[0]) / lq;
     float* dst = p.acc + row * D;

@@ -207,6 +207,8 @@ sel_combine_kernel(FwdParams p) {
 
   if (!active) return;
   const int64_t orow = (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub;
+  if (p.lse && sub == 0)
+    p.lse[static_cast<int64_t>(p.n) * p.h_q + static_cast<int64_t>(t) * p.h_q + h] = (st.m + __log2f(st.l)) * kLn2;
   const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
   const float f = st.l > 0.f ? bf16_bits_to_f32(gt[1]) / st.l : 0.f;
   const float* acc = p.acc + orow;

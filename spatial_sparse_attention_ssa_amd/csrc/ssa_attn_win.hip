@@ -157,9 +157,10 @@ win_mfma_kernel(FwdParams p) {
       }
       const float l_win = l + __shfl_xor(l, 32);
       if (q_valid) {
-        const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
+        const int64_t row = static_cast<int64_t>(t) * p.h_q + h;
+        const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + row * 3;
         const float f = bf16_bits_to_f32(gt[2]) / l_win;
-        float* dst = p.acc + (static_cast<int64_t>(t) * p.h_q + h) * kD;
+        float* dst = p.acc + row * kD;
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
@@ -170,6 +171,8 @@ win_mfma_kernel(FwdParams p) {
             a.z += o[vb][4 * rb + 2] * f; a.w += o[vb][4 * rb + 3] * f;
             *reinterpret_cast<float4*>(dst + d) = a;
           }
+        if (p.lse && half == 0)
+          p.lse[2 * static_cast<int64_t>(p.n) * p.h_q + row] = (m * c2 + __log2f(l_win)) * kLn2;
       }
     }
   }

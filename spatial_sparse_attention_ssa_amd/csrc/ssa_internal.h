@@ -33,6 +33,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Four float32 values rounded to bfloat16 and stored as 8 bytes.
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
+  uint2 w;
+  w.x = static_cast<uint32_t>(f32_to_bf16_bits(a)) | (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
+  w.y = static_cast<uint32_t>(f32_to_bf16_bits(c)) | (static_cast<uint32_t>(f32_to_bf16_bits(d)) << 16);
+  *reinterpret_cast<uint2*>(dst) = w;
+}
+
 // Element access for the two storage types: float, or bfloat16 carried as
 // its 16-bit pattern.
 template <typename T> struct Elt;
@@ -124,6 +134,29 @@ struct FwdParams {
   void* k_cmp;       // [nb][h_kv][D] or null
   void* v_cmp;
   int32_t* topk_idx; // [N][h_kv][topk]  (always valid: library workspace when the caller passes null)
+  // training: the state the backward reads (null = plain forward)
+  float* lse;        // [3][n][h_q] natural-log softmax denominators of the
+                     // (compressed, selected, window) branches, input token order
+};
+
+// Backward pass: the forward's parameters plus the gradients and scratch.
+struct BwdParams {
+  FwdParams f;          // blocks, layout, inputs, pooled rows, sorted K / V copies
+  const void* dout;     // [n][h_q][D] gradient of the output
+  const float* lse;     // [3][n][h_q] natural-log softmax denominators (saved by the forward)
+  void* dq;             // [n][h_q][D] out
+  void* dk;             // [n][h_kv][D] out
+  void* dv;
+  void* dgates;         // [n][h_q][3] out, or null
+  float* delta;         // [3][n][h_q] Delta_x = sum_j P_j (dout . v_j), i.e. dout . o_x
+  float* dq_acc;        // [n][h_q][D]
+  float* dk_acc;        // [h_kv][n][D], sorted token order
+  float* dv_acc;
+  float* dkbar;         // [h_kv][nb_cap][D] gradients of the pooled rows
+  float* dvbar;
+  int32_t* sel_cnt;     // [h_kv * nb_cap] selections per (group, block), then fill cursors
+  int32_t* sel_off;     // [h_kv * nb_cap + 1] exclusive offsets into sel_list
+  int32_t* sel_list;    // [n * h_kv * topk] the selecting token (input index) of every entry
 };
 
 constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile
@@ -134,6 +167,17 @@ void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream);
 hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+
+// backward stages (ssa_bwd.hip)
+hipError_t launch_bwd_pool(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_sel_index(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_cmp_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_cmp_dkv(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_win_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_win_dkv(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_sel_dkv(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_sel_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_finalize(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);

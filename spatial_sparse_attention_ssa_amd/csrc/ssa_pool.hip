@@ -229,7 +229,8 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
     pool_kernel<float><<<grid, 256, 0, stream>>>(
         static_cast<const float*>(p.k), static_cast<const float*>(p.v), p.perm, p.blk_off,
         p.counts, p.n, p.h_kv, p.d, p.nb_cap, static_cast<float*>(p.kbar), static_cast<float*>(p.vbar),
-        static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp), nullptr, nullptr);
+        static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp), static_cast<float*>(p.k_s),
+        static_cast<float*>(p.v_s));
   }
   return hipGetLastError();
 }

@@ -112,9 +112,9 @@ def test_row_subset_gives_the_same_rows():
     full = oracle.backward(wl, dout)
     rows = [(0, 1), (17, 3), (wl.n_tokens - 1, 0)]
     part = oracle.backward(wl, dout, rows=rows)
-    for t, h in rows:
-        np.testing.assert_array_equal(part["dq"][t, h], full["dq"][t, h])
-        np.testing.assert_array_equal(part["dgates"][t, h], full["dgates"][t, h])
+    for r, (t, h) in enumerate(rows):
+        np.testing.assert_array_equal(part["dq"][r], full["dq"][t, h])
+        np.testing.assert_array_equal(part["dgates"][r], full["dgates"][t, h])
 
 
 def test_zero_output_gradient_gives_zero_gradients():
