@@ -380,8 +380,12 @@ const char* ssa_stage_name(const ssa_attn* attn, int32_t stage) {
 namespace {
 
 struct BwdLayout {
-  size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_cnt, sel_off, sel_list, total;
+  size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_cnt, sel_off, sel_list, kbar_t,
+      qtile_pre, btile_pre, total;
 };
+
+// the compressed branch's backward runs on MFMA for bfloat16 (D = 32 or 64)
+bool use_mfma_backward(const ssa_attn* a) { return a->dtype == SSA_BF16; }
 
 BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
   const size_t cap = static_cast<size_t>(nb_capacity(b));
@@ -405,6 +409,11 @@ BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
   L.sel_cnt = off; off += align256(sizeof(int32_t) * a->h_kv * cap);
   L.sel_off = off; off += align256(sizeof(int32_t) * (a->h_kv * cap + 1));
   L.sel_list = off; off += align256(sizeof(int32_t) * n * a->h_kv * a->topk);
+  if (use_mfma_backward(a)) {
+    L.kbar_t = off; off += pooled;
+    L.qtile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    L.btile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+  }
   L.total = off + 256;
   return L;
 }
@@ -414,12 +423,17 @@ struct BStage {
   hipError_t (*launch)(const ssa::BwdParams&, ssa_dtype, hipStream_t);
 };
 
-int backward_plan(const ssa_attn* /*attn*/, BStage* stages) {
+int backward_plan(const ssa_attn* attn, BStage* stages) {
   int n = 0;
   stages[n++] = BStage{"pool_kernel", ssa::launch_bwd_pool};
   stages[n++] = BStage{"sel_index", ssa::launch_bwd_sel_index};
-  stages[n++] = BStage{"cmp_dq_kernel", ssa::launch_bwd_cmp_dq};
-  stages[n++] = BStage{"cmp_dkv_kernel", ssa::launch_bwd_cmp_dkv};
+  if (use_mfma_backward(attn)) {
+    stages[n++] = BStage{"cmp_dq_mfma_kernel", ssa::launch_bwd_cmp_dq_mfma};
+    stages[n++] = BStage{"cmp_dkv_mfma_kernel", ssa::launch_bwd_cmp_dkv_mfma};
+  } else {
+    stages[n++] = BStage{"cmp_dq_kernel", ssa::launch_bwd_cmp_dq};
+    stages[n++] = BStage{"cmp_dkv_kernel", ssa::launch_bwd_cmp_dkv};
+  }
   stages[n++] = BStage{"win_dq_kernel", ssa::launch_bwd_win_dq};
   stages[n++] = BStage{"win_dkv_kernel", ssa::launch_bwd_win_dkv};
   stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
@@ -493,6 +507,13 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
   bp.sel_cnt = reinterpret_cast<int32_t*>(w + lay.sel_cnt);
   bp.sel_off = reinterpret_cast<int32_t*>(w + lay.sel_off);
   bp.sel_list = reinterpret_cast<int32_t*>(w + lay.sel_list);
+  if (use_mfma_backward(attn)) {
+    bp.kbar_t = w + lay.kbar_t;
+    bp.qtile_pre = reinterpret_cast<int32_t*>(w + lay.qtile_pre);
+    bp.btile_pre = reinterpret_cast<int32_t*>(w + lay.btile_pre);
+    bp.max_qtiles = static_cast<int32_t>(blocks->n_tokens / 128 + blocks->batch + 1);
+    bp.max_btiles = p.nb_cap / 128 + 2 * blocks->batch + 2;
+  }
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   BStage stages[SSA_STAGES];

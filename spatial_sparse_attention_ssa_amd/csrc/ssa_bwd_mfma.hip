@@ -1,0 +1,426 @@
+// Compressed-branch backward on MFMA (bf16, D = 32 or 64, any group size).
+//
+// Direct3D-S2 page, "Method": the compressed branch is a softmax attention
+// of every query over the mean-pooled blocks of its sequence.  With P the
+// probabilities (from the log-sum-exp the forward saved), dP = dO Vbar^T and
+// Delta = rowsum(P * dP):
+//   dq    = G0 scale (P * (dP - Delta)) Kbar
+//   dKbar = scale sum over the sequence's (query, head) rows of G0 P (dP - Delta) q
+//   dVbar = sum over the same rows of G0 P dO
+// Both kernels use v_mfma_f32_32x32x16_bf16 on 32 x 32 tiles.
+//
+// cmp_dq_mfma_kernel (query-major): a workgroup owns 128 sorted queries of
+//   one sequence and one query head, a wave 32 of them.  Pooled key / value
+//   rows and the transposed key tile stream through a two-slot LDS ring, 32
+//   blocks per tile.  Per tile: S^T = Kbar Q^T and dP^T = Vbar dO^T, then
+//   P and P * dP in registers, and dq^T accumulates as A - Delta B with
+//   A = Kbar^T (P * dP)^T and B = Kbar^T P^T, so Delta (summed on the fly)
+//   comes from the same float32 P as the rest.  Writes dq_acc (first writer),
+//   Delta and the gate gradient.
+//
+// cmp_dkv_mfma_kernel (block-major): a workgroup owns 128 blocks of one
+//   sequence and one key/value group, a wave one 32-block tile whose pooled
+//   rows stay in registers as MFMA operands.  The sequence's (query, head)
+//   rows stream through LDS 32 at a time, row-major (for S = Q Kbar^T and
+//   dP = dO Vbar^T) and transposed in MFMA operand order (for
+//   dVbar^T += dO^T (G0 P)^T and dKbar^T += Q^T (G0 P (dP - Delta))^T).
+#include <float.h>
+
+#include "ssa_internal.h"
+
+namespace ssa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQT = 128;  // sorted queries per workgroup of the dq kernel (4 waves x 32)
+constexpr int kBT = 4;    // 32-block tiles per workgroup of the dkv kernel (one per wave)
+constexpr int kTRow = kKeyTile + 8;  // padded row (bf16) of a transposed 32-wide tile
+
+__device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Position of row r of a 32-row tile in the k order of the MFMA operand that
+// the 32x32 accumulator feeds: lane half 0 holds rows {0-3, 8-11} of each
+// 16-row half, lane half 1 rows {4-7, 12-15}.  Its own inverse.
+__device__ __forceinline__ int mfma_pos(int r) {
+  const int lo = r & 15;
+  return (r & 16) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = static_cast<__bf16>(x[i]);
+  return b;
+}
+
+__device__ __forceinline__ void seq_bounds(const FwdParams& f, int b, int* s0, int* s1, int* j0, int* j1) {
+  *s0 = f.win_off[f.seq_win_off[b]];
+  *s1 = f.win_off[f.seq_win_off[b + 1]];
+  *j0 = f.seq_blk_off[b];
+  *j1 = f.seq_blk_off[b + 1];
+}
+
+// the sequence b with pre[b] <= tile < pre[b + 1]
+__device__ __forceinline__ int find_seq(const int32_t* pre, int batch, int tile) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void bwd_tile_prefix_kernel(BwdParams p) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int rq = 0, rb = 0;
+  for (int b = 0; b < p.f.batch; ++b) {
+    p.qtile_pre[b] = rq;
+    p.btile_pre[b] = rb;
+    int s0, s1, j0, j1;
+    seq_bounds(p.f, b, &s0, &s1, &j0, &j1);
+    rq += (s1 - s0 + kQT - 1) / kQT;
+    if (j1 > j0) {
+      const int tiles = (j1 + kKeyTile - 1) / kKeyTile - j0 / kKeyTile;
+      rb += (tiles + kBT - 1) / kBT;
+    }
+  }
+  p.qtile_pre[p.f.batch] = rq;
+  p.btile_pre[p.f.batch] = rb;
+}
+
+// ------------------------------------------------------------ dq (query-major)
+
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+cmp_dq_mfma_kernel(BwdParams p) {
+  constexpr int KS = D / 16;          // MFMA k steps over the dims
+  constexpr int VB = D / 32;          // 32-dim row blocks of dq^T
+  constexpr int kKRow = D + 8;        // padded key / value row (bf16)
+  constexpr int kRowCh = kKeyTile * D / 8;   // 16-byte chunks of a 32-row tile
+  constexpr int kKT = kKeyTile * kKRow;
+  constexpr int kTT = D * kTRow;
+  __shared__ __align__(16) uint16_t k_lds[2 * kKT];
+  __shared__ __align__(16) uint16_t v_lds[2 * kKT];
+  __shared__ __align__(16) uint16_t t_lds[2 * kTT];
+
+  const FwdParams& f = p.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int half = lane >> 5;
+  const int h = blockIdx.y;
+  const int g = h / (f.h_q / f.h_kv);
+  const int tile = blockIdx.x;
+  if (tile >= p.qtile_pre[f.batch]) return;
+  const int b = find_seq(p.qtile_pre, f.batch, tile);
+  int s0, s1, j0, j1;
+  seq_bounds(f, b, &s0, &s1, &j0, &j1);
+  const int qi = s0 + (tile - p.qtile_pre[b]) * kQT + wv * 32 + (lane & 31);
+  const bool valid = qi < s1;
+  const int t = valid ? f.perm[qi] : 0;
+  const int64_t qrow = static_cast<int64_t>(t) * f.h_q + h;
+  const uint16_t* Q = static_cast<const uint16_t*>(f.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
+  // B operands: the lane's query and output-gradient rows
+  bf16x8 qb[KS], db[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (valid) {
+      a = *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * ks + 8 * half);
+      c = *reinterpret_cast<const u32x4*>(dO + qrow * D + 16 * ks + 8 * half);
+    }
+    qb[ks] = __builtin_bit_cast(bf16x8, a);
+    db[ks] = __builtin_bit_cast(bf16x8, c);
+  }
+  const float c2 = f.scale * kLog2e;
+  const float l2 = valid ? p.lse[qrow] * kLog2e : 0.f;
+  const int kt0 = j0 / kKeyTile;
+  const int n_kt = (j1 + kKeyTile - 1) / kKeyTile - kt0;
+
+  // staging: thread tid moves chunk tid of the key rows, of the value rows
+  // and of the transposed key tile (D = 32: threads below 128 only)
+  const uint16_t* KB = static_cast<const uint16_t*>(f.kbar) + static_cast<int64_t>(g) * f.nb_cap * D;
+  const uint16_t* VBR = static_cast<const uint16_t*>(f.vbar) + static_cast<int64_t>(g) * f.nb_cap * D;
+  const uint16_t* KT = static_cast<const uint16_t*>(p.kbar_t) + static_cast<int64_t>(g) * f.nb_cap * D;
+  const bool stager = tid < kRowCh;
+  const int r_row = tid / (D / 8), r_c = tid % (D / 8);   // key / value rows: row, 8-dim chunk
+  const int t_dim = tid >> 2, t_c = tid & 3;              // transposed tile: dim, 8-position chunk
+  const int64_t src_r = static_cast<int64_t>(r_row) * D + 8 * r_c;
+  const int64_t src_t = static_cast<int64_t>(t_dim) * kKeyTile + 8 * t_c;
+  const int dst_r = r_row * kKRow + 8 * r_c;
+  const int dst_t = t_dim * kTRow + 8 * t_c;
+  u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u}, rt = {0u, 0u, 0u, 0u};
+  auto load = [&](int kt) {
+    if (stager) {
+      const int64_t base = static_cast<int64_t>(kt) * kKeyTile * D;
+      rk = *reinterpret_cast<const u32x4*>(KB + base + src_r);
+      rv = *reinterpret_cast<const u32x4*>(VBR + base + src_r);
+      rt = *reinterpret_cast<const u32x4*>(KT + base + src_t);
+    }
+  };
+  auto store = [&](int slot) {
+    if (stager) {
+      *reinterpret_cast<u32x4*>(k_lds + slot * kKT + dst_r) = rk;
+      *reinterpret_cast<u32x4*>(v_lds + slot * kKT + dst_r) = rv;
+      *reinterpret_cast<u32x4*>(t_lds + slot * kTT + dst_t) = rt;
+    }
+  };
+
+  f32x16 aa[VB], ab[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) {
+    aa[vb] = f32x16{};
+    ab[vb] = f32x16{};
+  }
+  float dl = 0.f;
+  load(kt0);
+  store(0);
+  if (n_kt > 1) load(kt0 + 1);
+  for (int rel = 0; rel < n_kt; ++rel) {
+    __syncthreads();  // tile rel stored; every wave is done with tile rel - 1
+    if (rel + 1 < n_kt) store((rel + 1) & 1);
+    if (rel + 2 < n_kt) load(kt0 + rel + 2);
+    const int slot = rel & 1;
+    const uint16_t* kl = k_lds + slot * kKT + (lane & 31) * kKRow + 8 * half;
+    const uint16_t* vl = v_lds + slot * kKT + (lane & 31) * kKRow + 8 * half;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(kl + 16 * ks), qb[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 16 * ks), db[ks], dp, 0, 0, 0);
+    }
+    // entry r is block jb + 8 (r / 4) + 4 half + r % 4 of this query
+    const int jb = (kt0 + rel) * kKeyTile + 4 * half;
+    float pr[16], pd[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = jb + 8 * (r >> 2) + (r & 3);
+      const float x = (j >= j0 && j < j1) ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2)) : 0.f;
+      pr[r] = x;
+      pd[r] = x * dp[r];
+      dl += pd[r];
+    }
+    const uint16_t* tl = t_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pdb = pack8(pd + 8 * ks);
+      const bf16x8 pb = pack8(pr + 8 * ks);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const bf16x8 a = lds_b128(tl + vb * 32 * kTRow + 16 * ks);
+        aa[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pdb, aa[vb], 0, 0, 0);
+        ab[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ab[vb], 0, 0, 0);
+      }
+    }
+  }
+  dl += __shfl_xor(dl, 32);
+  if (!valid) return;
+  const float gs = bf16_bits_to_f32(static_cast<const uint16_t*>(f.gates)[qrow * 3]) * f.scale;
+  float* dst = p.dq_acc + qrow * D;
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int d = 32 * vb + 8 * rb + 4 * half;
+      float4 o;
+      o.x = gs * fmaf(-dl, ab[vb][4 * rb], aa[vb][4 * rb]);
+      o.y = gs * fmaf(-dl, ab[vb][4 * rb + 1], aa[vb][4 * rb + 1]);
+      o.z = gs * fmaf(-dl, ab[vb][4 * rb + 2], aa[vb][4 * rb + 2]);
+      o.w = gs * fmaf(-dl, ab[vb][4 * rb + 3], aa[vb][4 * rb + 3]);
+      *reinterpret_cast<float4*>(dst + d) = o;
+    }
+  if (half == 0) {
+    p.delta[qrow] = dl;
+    if (p.dgates) static_cast<uint16_t*>(p.dgates)[qrow * 3] = f32_to_bf16_bits(dl);
+  }
+}
+
+// ------------------------------------------------------------ dKbar, dVbar (block-major)
+
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+cmp_dkv_mfma_kernel(BwdParams p) {
+  constexpr int KS = D / 16;
+  constexpr int VB = D / 32;
+  constexpr int kRRow = D + 8;                 // padded row-major query row (bf16)
+  constexpr int kRowCh = kKeyTile * D / 8;     // 16-byte chunks of a 32-row tile
+  constexpr int kRT = kKeyTile * kRRow;
+  constexpr int kTT = D * kTRow;
+  __shared__ __align__(16) uint16_t q_lds[2 * kRT];
+  __shared__ __align__(16) uint16_t d_lds[2 * kRT];
+  __shared__ __align__(16) uint16_t qt_lds[2 * kTT];
+  __shared__ __align__(16) uint16_t dt_lds[2 * kTT];
+  __shared__ float4 st_lds[2 * kKeyTile];      // per row: log2 lse, Delta, G0
+
+  const FwdParams& f = p.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int half = lane >> 5;
+  const int g = blockIdx.y;
+  const int G = f.h_q / f.h_kv;
+  const int tile = blockIdx.x;
+  if (tile >= p.btile_pre[f.batch]) return;
+  const int b = find_seq(p.btile_pre, f.batch, tile);
+  int s0, s1, j0, j1;
+  seq_bounds(f, b, &s0, &s1, &j0, &j1);
+  const int kt = j0 / kKeyTile + (tile - p.btile_pre[b]) * kBT + wv;
+  const bool wave_on = kt < (j1 + kKeyTile - 1) / kKeyTile;
+  const int j = kt * kKeyTile + (lane & 31);
+  const bool jok = wave_on && j >= j0 && j < j1;
+  // B operands: the lane's pooled key and value rows
+  bf16x8 kb[KS], vb[KS];
+  {
+    const uint16_t* KB = static_cast<const uint16_t*>(f.kbar) + (static_cast<int64_t>(g) * f.nb_cap + j) * D;
+    const uint16_t* VBR = static_cast<const uint16_t*>(f.vbar) + (static_cast<int64_t>(g) * f.nb_cap + j) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (wave_on) {
+        a = *reinterpret_cast<const u32x4*>(KB + 16 * ks + 8 * half);
+        c = *reinterpret_cast<const u32x4*>(VBR + 16 * ks + 8 * half);
+      }
+      kb[ks] = __builtin_bit_cast(bf16x8, a);
+      vb[ks] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+  const float c2 = f.scale * kLog2e;
+  const int R = (s1 - s0) * G;               // (query, head of the group) rows of the sequence
+  const int n_rt = (R + kKeyTile - 1) / kKeyTile;
+  const uint16_t* Q = static_cast<const uint16_t*>(f.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
+  const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
+
+  // staging: thread tid moves chunk tid of the query rows and of the
+  // output-gradient rows; threads below 32 also the row's statistics
+  const bool stager = tid < kRowCh;
+  const int r_row = tid / (D / 8), r_c = tid % (D / 8);
+  const int pos = mfma_pos(r_row);
+  u32x4 rq = {0u, 0u, 0u, 0u}, rd = {0u, 0u, 0u, 0u};
+  float4 rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
+  auto load = [&](int rt) {
+    if (stager) {
+      const int rr = rt * kKeyTile + r_row;
+      rq = u32x4{0u, 0u, 0u, 0u};
+      rd = u32x4{0u, 0u, 0u, 0u};
+      if (rr < R) {
+        const int64_t qrow = static_cast<int64_t>(f.perm[s0 + rr / G]) * f.h_q + g * G + rr % G;
+        rq = *reinterpret_cast<const u32x4*>(Q + qrow * D + 8 * r_c);
+        rd = *reinterpret_cast<const u32x4*>(dO + qrow * D + 8 * r_c);
+      }
+    }
+    if (tid < kKeyTile) {
+      const int rr = rt * kKeyTile + tid;
+      rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);   // a missing row has P = 0
+      if (rr < R) {
+        const int64_t qrow = static_cast<int64_t>(f.perm[s0 + rr / G]) * f.h_q + g * G + rr % G;
+        rs = make_float4(p.lse[qrow] * kLog2e, p.delta[qrow], bf16_bits_to_f32(gates[qrow * 3]), 0.f);
+      }
+    }
+  };
+  auto store = [&](int slot) {
+    if (stager) {
+      *reinterpret_cast<u32x4*>(q_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rq;
+      *reinterpret_cast<u32x4*>(d_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rd;
+      uint16_t* qt = qt_lds + slot * kTT + (8 * r_c) * kTRow + pos;
+      uint16_t* dt = dt_lds + slot * kTT + (8 * r_c) * kTRow + pos;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qt[(2 * e) * kTRow] = static_cast<uint16_t>(rq[e] & 0xFFFFu);
+        qt[(2 * e + 1) * kTRow] = static_cast<uint16_t>(rq[e] >> 16);
+        dt[(2 * e) * kTRow] = static_cast<uint16_t>(rd[e] & 0xFFFFu);
+        dt[(2 * e + 1) * kTRow] = static_cast<uint16_t>(rd[e] >> 16);
+      }
+    }
+    if (tid < kKeyTile) st_lds[slot * kKeyTile + tid] = rs;
+  };
+
+  f32x16 dk[VB], dv[VB];
+#pragma unroll
+  for (int x = 0; x < VB; ++x) {
+    dk[x] = f32x16{};
+    dv[x] = f32x16{};
+  }
+  if (n_rt > 0) {
+    load(0);
+    store(0);
+  }
+  if (n_rt > 1) load(1);
+  for (int rt = 0; rt < n_rt; ++rt) {
+    __syncthreads();  // tile rt stored; every wave is done with tile rt - 1
+    if (rt + 1 < n_rt) store((rt + 1) & 1);
+    if (rt + 2 < n_rt) load(rt + 2);
+    if (!wave_on) continue;
+    const int slot = rt & 1;
+    const uint16_t* ql = q_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
+    const uint16_t* dl = d_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ql + 16 * ks), kb[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dl + 16 * ks), vb[ks], dp, 0, 0, 0);
+    }
+    // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile, for this block
+    float pg[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float4 st = st_lds[slot * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3)];
+      const float x = st.z * __builtin_amdgcn_exp2f(fmaf(s[r], c2, -st.x));
+      pg[r] = x;
+      ds[r] = x * (dp[r] - st.y);
+    }
+    const uint16_t* qt = qt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
+    const uint16_t* dt = dt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pb = pack8(pg + 8 * ks);
+      const bf16x8 sb = pack8(ds + 8 * ks);
+#pragma unroll
+      for (int x = 0; x < VB; ++x) {
+        dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dt + x * 32 * kTRow + 16 * ks), pb, dv[x], 0, 0, 0);
+        dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qt + x * 32 * kTRow + 16 * ks), sb, dk[x], 0, 0, 0);
+      }
+    }
+  }
+  if (!jok) return;
+  const int64_t o = (static_cast<int64_t>(g) * f.nb_cap + j) * D;
+#pragma unroll
+  for (int x = 0; x < VB; ++x)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int d = 32 * x + 8 * rb + 4 * half;
+      *reinterpret_cast<float4*>(p.dkbar + o + d) =
+          make_float4(f.scale * dk[x][4 * rb], f.scale * dk[x][4 * rb + 1], f.scale * dk[x][4 * rb + 2],
+                      f.scale * dk[x][4 * rb + 3]);
+      *reinterpret_cast<float4*>(p.dvbar + o + d) =
+          make_float4(dv[x][4 * rb], dv[x][4 * rb + 1], dv[x][4 * rb + 2], dv[x][4 * rb + 3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  hipError_t e = launch_tile_transpose(p.f.kbar, p.kbar_t, p.f.counts, p.f.h_kv, p.f.nb_cap, p.f.d, stream);
+  if (e != hipSuccess) return e;
+  bwd_tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
+  const dim3 grid(p.max_qtiles, p.f.h_q);
+  if (p.f.d == 32) cmp_dq_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
+  else cmp_dq_mfma_kernel<64><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_cmp_dkv_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  const dim3 grid(p.max_btiles, p.f.h_kv);
+  if (p.f.d == 32) cmp_dkv_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
+  else cmp_dkv_mfma_kernel<64><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

@@ -157,6 +157,12 @@ struct BwdParams {
   int32_t* sel_cnt;     // [h_kv * nb_cap] selections per (group, block), then fill cursors
   int32_t* sel_off;     // [h_kv * nb_cap + 1] exclusive offsets into sel_list
   int32_t* sel_list;    // [n * h_kv * topk] the selecting token (input index) of every entry
+  // MFMA kernels of the compressed branch (bf16)
+  void* kbar_t;         // [h_kv][nb_cap / 32][D][32] pooled keys, each 32-block tile transposed
+  int32_t* qtile_pre;   // [batch + 1] prefix of 128-query tiles per sequence
+  int32_t* btile_pre;   // [batch + 1] prefix of 128-block chunks per sequence
+  int32_t max_qtiles;   // grid bounds of the two
+  int32_t max_btiles;
 };
 
 constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile
@@ -168,7 +174,12 @@ hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype dtype, hipStream_t strea
 hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 
-// backward stages (ssa_bwd.hip)
+// [h_kv][nb_cap][D] -> [h_kv][nb_cap / 32][D][32] per 32-block tile, rows in
+// the order of the MFMA operands (ssa_pool.hip)
+hipError_t launch_tile_transpose(const void* src, void* dst, const int32_t* counts, int hkv, int nb_cap, int d,
+                                 hipStream_t stream);
+
+// backward stages (ssa_bwd.hip, ssa_bwd_mfma.hip)
 hipError_t launch_bwd_pool(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_sel_index(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_cmp_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
@@ -178,6 +189,8 @@ hipError_t launch_bwd_win_dkv(const BwdParams& p, ssa_dtype dtype, hipStream_t s
 hipError_t launch_bwd_sel_dkv(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_sel_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_finalize(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_cmp_dkv_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
