@@ -435,9 +435,15 @@ int backward_plan(const ssa_attn* attn, BStage* stages) {
     stages[n++] = BStage{"cmp_dkv_kernel", ssa::launch_bwd_cmp_dkv};
   }
   stages[n++] = BStage{"win_dq_kernel", ssa::launch_bwd_win_dq};
-  stages[n++] = BStage{"win_dkv_kernel", ssa::launch_bwd_win_dkv};
+  if (use_mfma_backward(attn))
+    stages[n++] = BStage{"kv_grad_mfma_kernel<window>", ssa::launch_bwd_kv_win_mfma};
+  else
+    stages[n++] = BStage{"win_dkv_kernel", ssa::launch_bwd_win_dkv};
   stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
-  stages[n++] = BStage{"sel_dkv_kernel", ssa::launch_bwd_sel_dkv};
+  if (use_mfma_backward(attn))
+    stages[n++] = BStage{"kv_grad_mfma_kernel<selected>", ssa::launch_bwd_kv_sel_mfma};
+  else
+    stages[n++] = BStage{"sel_dkv_kernel", ssa::launch_bwd_sel_dkv};
   stages[n++] = BStage{"bwd_finalize_kernel", ssa::launch_bwd_finalize};
   return n;
 }

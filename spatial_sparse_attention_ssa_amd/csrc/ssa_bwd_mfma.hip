@@ -24,6 +24,17 @@
 //   rows stream through LDS 32 at a time, row-major (for S = Q Kbar^T and
 //   dP = dO Vbar^T) and transposed in MFMA operand order (for
 //   dVbar^T += dO^T (G0 P)^T and dKbar^T += Q^T (G0 P (dP - Delta))^T).
+//
+// kv_grad_mfma_kernel: the same block-major product for the token keys of
+//   the other two branches.  Selected branch: one workgroup per (group,
+//   block), the rows being every (query, head) whose top-k list holds the
+//   block (the inverted lists); window branch: one workgroup per (group,
+//   window), the rows being the window's own (query, head) pairs.  The key
+//   tile is up to 32 tokens of the block or window (sorted copies, in
+//   registers); each wave streams its own share of the rows (A operands
+//   straight from memory, the transposed copies through a wave-private LDS
+//   area), and the four partial tiles are summed in LDS, in wave order, at
+//   the end.
 #include <float.h>
 
 #include "ssa_internal.h"
@@ -404,7 +415,206 @@ cmp_dkv_mfma_kernel(BwdParams p) {
     }
 }
 
+// ------------------------------------------------------------ token keys of the selected / window branch
+
+enum KvMode { kSelected = 1, kWindow = 2 };   // the branch index of each
+
+template <int D, int MODE>
+__global__ void __launch_bounds__(256, 2)
+kv_grad_mfma_kernel(BwdParams p) {
+  constexpr int KS = D / 16;
+  constexpr int VB = D / 32;
+  constexpr int kTT = D * kTRow;
+  constexpr int kRed = kKeyTile * D;            // one partial tile (floats)
+  __shared__ __align__(16) uint16_t qt_lds[4 * kTT];   // per wave: Q^T of its row tile
+  __shared__ __align__(16) uint16_t dt_lds[4 * kTT];   // per wave: dO^T
+  __shared__ float4 st_lds[4 * kKeyTile];              // per wave: log2 lse, Delta, gate per row
+  __shared__ float red_k[kRed];
+  __shared__ float red_v[kRed];
+
+  const FwdParams& f = p.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int half = lane >> 5;
+  const int G = f.h_q / f.h_kv;
+  const float c2 = f.scale * kLog2e;
+  const int64_t nrow = static_cast<int64_t>(f.n) * f.h_q;
+  const float* lse = p.lse + MODE * nrow;
+  const float* dlt = p.delta + MODE * nrow;
+  const uint16_t* Q = static_cast<const uint16_t*>(f.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
+  const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
+  uint16_t* qt = qt_lds + wv * kTT;
+  uint16_t* dt = dt_lds + wv * kTT;
+  float4* st = st_lds + wv * kKeyTile;
+  const int n_units = MODE == kSelected ? f.counts[SSA_COUNT_NB] : f.counts[SSA_COUNT_NW];
+  const int64_t n_items = static_cast<int64_t>(n_units) * f.h_kv;
+
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int g = static_cast<int>(item / n_units);
+    const int u = static_cast<int>(item % n_units);
+    int a, bnd, e0, R;
+    if (MODE == kSelected) {
+      const int64_t slot = static_cast<int64_t>(g) * f.nb_cap + u;
+      e0 = p.sel_off[slot];
+      R = (p.sel_off[slot + 1] - e0) * G;
+      a = f.blk_off[u];
+      bnd = f.blk_off[u + 1];
+    } else {
+      a = f.win_off[u];
+      bnd = f.win_off[u + 1];
+      e0 = a;
+      R = (bnd - a) * G;
+    }
+    if (R == 0) continue;
+    const int n_rt = (R + kKeyTile - 1) / kKeyTile;
+    // (query, head) of row rr of this item
+    auto row_of = [&](int rr) -> int64_t {
+      const int t = MODE == kSelected ? p.sel_list[e0 + rr / G] : f.perm[e0 + rr / G];
+      return static_cast<int64_t>(t) * f.h_q + g * G + rr % G;
+    };
+    for (int k0 = a; k0 < bnd; k0 += kKeyTile) {
+      // B operands: the lane's key / value token of this tile
+      const int i = k0 + (lane & 31);
+      const bool iok = i < bnd;
+      bf16x8 kb[KS], vb[KS];
+      {
+        const int64_t krow = (static_cast<int64_t>(g) * f.n + i) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+          if (iok) {
+            x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(f.k_s) + krow + 16 * ks + 8 * half);
+            y = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(f.v_s) + krow + 16 * ks + 8 * half);
+          }
+          kb[ks] = __builtin_bit_cast(bf16x8, x);
+          vb[ks] = __builtin_bit_cast(bf16x8, y);
+        }
+      }
+      f32x16 dk[VB], dv[VB];
+#pragma unroll
+      for (int x = 0; x < VB; ++x) {
+        dk[x] = f32x16{};
+        dv[x] = f32x16{};
+      }
+      // rows of tile rt: this lane loads row 32 rt + lane % 32 (its 16 dims
+      // per k step and lane half), prefetched one tile ahead
+      u32x4 nq[KS], nd[KS];
+      float4 ns = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
+      auto load = [&](int rt) {
+        const int rr = rt * kKeyTile + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) nq[ks] = nd[ks] = u32x4{0u, 0u, 0u, 0u};
+        ns = make_float4(FLT_MAX, 0.f, 0.f, 0.f);   // a missing row has P = 0
+        if (rr < R) {
+          const int64_t qrow = row_of(rr);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            nq[ks] = *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * ks + 8 * half);
+            nd[ks] = *reinterpret_cast<const u32x4*>(dO + qrow * D + 16 * ks + 8 * half);
+          }
+          ns = make_float4(lse[qrow] * kLog2e, dlt[qrow], bf16_bits_to_f32(gates[qrow * 3 + MODE]), 0.f);
+        }
+      };
+      if (wv < n_rt) load(wv);
+      for (int rt = wv; rt < n_rt; rt += 4) {
+        // the transposed copies and the row statistics, wave-private
+        const int pos = mfma_pos(lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d0 = 16 * ks + 8 * half + 2 * e;
+            qt[d0 * kTRow + pos] = static_cast<uint16_t>(nq[ks][e] & 0xFFFFu);
+            qt[(d0 + 1) * kTRow + pos] = static_cast<uint16_t>(nq[ks][e] >> 16);
+            dt[d0 * kTRow + pos] = static_cast<uint16_t>(nd[ks][e] & 0xFFFFu);
+            dt[(d0 + 1) * kTRow + pos] = static_cast<uint16_t>(nd[ks][e] >> 16);
+          }
+        if (half == 0) st[lane] = ns;
+        wave_lds_sync();
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, nq[ks]), kb[ks], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, nd[ks]), vb[ks], dp, 0, 0, 0);
+        }
+        if (rt + 4 < n_rt) load(rt + 4);   // in flight during the rest of this tile
+        const uint16_t* qtl = qt + (lane & 31) * kTRow + 8 * half;
+        const uint16_t* dtl = dt + (lane & 31) * kTRow + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float pg[8], ds[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * ks + i;
+            const float4 sr = st[8 * (r >> 2) + 4 * half + (r & 3)];
+            const float x = sr.z * __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sr.x));
+            pg[i] = x;
+            ds[i] = x * (dp[r] - sr.y);
+          }
+          const bf16x8 pb = pack8(pg);
+          const bf16x8 sb = pack8(ds);
+#pragma unroll
+          for (int x = 0; x < VB; ++x) {
+            dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dtl + x * 32 * kTRow + 16 * ks), pb, dv[x], 0, 0, 0);
+            dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qtl + x * 32 * kTRow + 16 * ks), sb, dk[x], 0, 0, 0);
+          }
+        }
+        wave_lds_sync();  // the wave-private area is rewritten by the next row tile
+      }
+      // sum the four waves' partial tiles, [token][dim], in wave order
+      // (a fixed order keeps the result identical from run to run)
+      for (int w = 0; w < 4; ++w) {
+        __syncthreads();
+        if (wv == w) {
+#pragma unroll
+          for (int x = 0; x < VB; ++x)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int e = (lane & 31) * D + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+              red_k[e] = w == 0 ? dk[x][r] : red_k[e] + dk[x][r];
+              red_v[e] = w == 0 ? dv[x][r] : red_v[e] + dv[x][r];
+            }
+        }
+      }
+      __syncthreads();
+      // add to the token rows (the window branch writes them first)
+      const int n_tok = min(kKeyTile, bnd - k0);
+      for (int e = tid; e < n_tok * (D / 4); e += 256) {
+        const int tok = e / (D / 4), d = 4 * (e % (D / 4));
+        const int64_t o = (static_cast<int64_t>(g) * f.n + k0 + tok) * D + d;
+        float4 rk = make_float4(f.scale * red_k[tok * D + d], f.scale * red_k[tok * D + d + 1],
+                                f.scale * red_k[tok * D + d + 2], f.scale * red_k[tok * D + d + 3]);
+        float4 rv = make_float4(red_v[tok * D + d], red_v[tok * D + d + 1], red_v[tok * D + d + 2],
+                                red_v[tok * D + d + 3]);
+        if (MODE == kSelected) {
+          const float4 ck = *reinterpret_cast<const float4*>(p.dk_acc + o);
+          const float4 cv = *reinterpret_cast<const float4*>(p.dv_acc + o);
+          rk.x += ck.x; rk.y += ck.y; rk.z += ck.z; rk.w += ck.w;
+          rv.x += cv.x; rv.y += cv.y; rv.z += cv.z; rv.w += cv.w;
+        }
+        *reinterpret_cast<float4*>(p.dk_acc + o) = rk;
+        *reinterpret_cast<float4*>(p.dv_acc + o) = rv;
+      }
+      __syncthreads();  // the reduction buffers are reused by the next tile
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  if (p.f.d == 32) kv_grad_mfma_kernel<32, kSelected><<<8192, 256, 0, stream>>>(p);
+  else kv_grad_mfma_kernel<64, kSelected><<<8192, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  if (p.f.d == 32) kv_grad_mfma_kernel<32, kWindow><<<4096, 256, 0, stream>>>(p);
+  else kv_grad_mfma_kernel<64, kWindow><<<4096, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   hipError_t e = launch_tile_transpose(p.f.kbar, p.kbar_t, p.f.counts, p.f.h_kv, p.f.nb_cap, p.f.d, stream);
