@@ -209,9 +209,8 @@ size_t ssa_backward_workspace(const ssa_blocks *blocks, const ssa_attn *attn);
  *   dk, dv    [N, h_kv, D] out
  *   dgates    optional [N, h_q, 3] out: dout . o_x per branch (NULL = skip)
  *   workspace device scratch of at least ssa_backward_workspace() bytes.
- * All tensors in dtype except lse (float32).  Sums run in float32; the
- * selected branch's key / value gradients are summed in an order that may
- * differ from run to run (float rounding only).
+ * All tensors in dtype except lse (float32).  Sums run in float32 in a
+ * fixed order, so repeated calls give identical results.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (as ssa_forward), WORKSPACE, DEVICE. */
 ssa_status ssa_backward(const ssa_blocks *blocks, const ssa_attn *attn, const void *q, const void *k,
                         const void *v, const void *gates, const void *dout, const int32_t *topk_idx,

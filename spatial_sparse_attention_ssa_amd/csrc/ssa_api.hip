@@ -380,9 +380,24 @@ const char* ssa_stage_name(const ssa_attn* attn, int32_t stage) {
 namespace {
 
 struct BwdLayout {
-  size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_cnt, sel_off, sel_list, kbar_t,
-      qtile_pre, btile_pre, total;
+  size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_keys, sel_vals, sel_keys_tmp,
+      sel_vals_tmp, sel_hist, sel_off, kbar_t, qtile_pre, btile_pre, dkbar_part, dvbar_part, total;
 };
+
+// 128-block chunks (an upper bound) and the row splits that give the
+// pooled-row gradient kernel about 8192 workgroups
+int32_t max_block_chunks(const ssa_blocks* b) { return static_cast<int32_t>(nb_capacity(b) / 128 + 2 * b->batch + 2); }
+int32_t dkv_row_splits(const ssa_blocks* b, const ssa_attn* a) {
+  const int64_t wg = static_cast<int64_t>(max_block_chunks(b)) * a->h_kv;
+  const int64_t s = (8192 + wg - 1) / wg;
+  return static_cast<int32_t>(s < 1 ? 1 : (s > 32 ? 32 : s));
+}
+
+// bits of the inverted-list sort keys: group * nb_cap + block, plus the
+// padding key h_kv * nb_cap
+int sel_key_bits(const ssa_blocks* b, const ssa_attn* a) {
+  return ceil_log2(static_cast<int64_t>(a->h_kv) * nb_capacity(b) + 1);
+}
 
 // the compressed branch's backward runs on MFMA for bfloat16 (D = 32 or 64)
 bool use_mfma_backward(const ssa_attn* a) { return a->dtype == SSA_BF16; }
@@ -406,13 +421,22 @@ BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
   L.dv_acc = off; off += align256(sizeof(float) * a->h_kv * n * D);
   L.dkbar = off; off += align256(sizeof(float) * a->h_kv * cap * D);
   L.dvbar = off; off += align256(sizeof(float) * a->h_kv * cap * D);
-  L.sel_cnt = off; off += align256(sizeof(int32_t) * a->h_kv * cap);
+  const size_t m = n * a->h_kv * a->topk;
+  L.sel_keys = off; off += align256(sizeof(uint32_t) * m);
+  L.sel_vals = off; off += align256(sizeof(int32_t) * m);
+  L.sel_keys_tmp = off; off += align256(sizeof(uint32_t) * m);
+  L.sel_vals_tmp = off; off += align256(sizeof(int32_t) * m);
+  L.sel_hist = off; off += align256(ssa::sort_pairs_hist_bytes(static_cast<int64_t>(m)));
   L.sel_off = off; off += align256(sizeof(int32_t) * (a->h_kv * cap + 1));
-  L.sel_list = off; off += align256(sizeof(int32_t) * n * a->h_kv * a->topk);
   if (use_mfma_backward(a)) {
     L.kbar_t = off; off += pooled;
     L.qtile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     L.btile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    const size_t splits = static_cast<size_t>(dkv_row_splits(b, a));
+    if (splits > 1) {
+      L.dkbar_part = off; off += align256(sizeof(float) * splits * a->h_kv * cap * D);
+      L.dvbar_part = off; off += align256(sizeof(float) * splits * a->h_kv * cap * D);
+    }
   }
   L.total = off + 256;
   return L;
@@ -464,6 +488,10 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
   if (blocks->n_tokens > 0 &&
       (!q || !k || !v || !gates || !dout || !topk_idx || !lse || !dq || !dk || !dv))
     return fail(SSA_ERR_INVALID_ARGUMENT, "q, k, v, gates, dout, topk_idx, lse, dq, dk and dv must be non-null");
+  if (blocks->n_tokens * attn->h_kv * attn->topk > 0x7FFFFFFF)
+    return fail(SSA_ERR_UNSUPPORTED, "n_tokens * h_kv * topk exceeds 2^31 - 1 top-k entries");
+  if (sel_key_bits(blocks, attn) > 32)
+    return fail(SSA_ERR_UNSUPPORTED, "h_kv * blocks exceeds 2^32");
   const BwdLayout lay = backward_layout(blocks, attn);
   if (!workspace || ws_bytes < lay.total)
     return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, lay.total);
@@ -510,15 +538,27 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
   bp.dv_acc = reinterpret_cast<float*>(w + lay.dv_acc);
   bp.dkbar = reinterpret_cast<float*>(w + lay.dkbar);
   bp.dvbar = reinterpret_cast<float*>(w + lay.dvbar);
-  bp.sel_cnt = reinterpret_cast<int32_t*>(w + lay.sel_cnt);
+  bp.sel_keys = reinterpret_cast<uint32_t*>(w + lay.sel_keys);
+  bp.sel_vals = reinterpret_cast<int32_t*>(w + lay.sel_vals);
+  bp.sel_keys_tmp = reinterpret_cast<uint32_t*>(w + lay.sel_keys_tmp);
+  bp.sel_vals_tmp = reinterpret_cast<int32_t*>(w + lay.sel_vals_tmp);
+  bp.sel_hist = reinterpret_cast<uint32_t*>(w + lay.sel_hist);
+  bp.sel_key_bits = sel_key_bits(blocks, attn);
+  const bool in_tmp = ssa::sort_pairs_lands_in_tmp(bp.sel_key_bits);
+  bp.sel_list = in_tmp ? bp.sel_vals_tmp : bp.sel_vals;
+  bp.sel_sorted_keys = in_tmp ? bp.sel_keys_tmp : bp.sel_keys;
   bp.sel_off = reinterpret_cast<int32_t*>(w + lay.sel_off);
-  bp.sel_list = reinterpret_cast<int32_t*>(w + lay.sel_list);
   if (use_mfma_backward(attn)) {
     bp.kbar_t = w + lay.kbar_t;
     bp.qtile_pre = reinterpret_cast<int32_t*>(w + lay.qtile_pre);
     bp.btile_pre = reinterpret_cast<int32_t*>(w + lay.btile_pre);
     bp.max_qtiles = static_cast<int32_t>(blocks->n_tokens / 128 + blocks->batch + 1);
-    bp.max_btiles = p.nb_cap / 128 + 2 * blocks->batch + 2;
+    bp.max_btiles = max_block_chunks(blocks);
+    bp.row_splits = dkv_row_splits(blocks, attn);
+    if (bp.row_splits > 1) {
+      bp.dkbar_part = reinterpret_cast<float*>(w + lay.dkbar_part);
+      bp.dvbar_part = reinterpret_cast<float*>(w + lay.dvbar_part);
+    }
   }
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);

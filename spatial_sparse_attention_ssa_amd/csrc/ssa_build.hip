@@ -114,6 +114,56 @@ __global__ void __launch_bounds__(1024) scan_exclusive_u32(uint32_t* __restrict_
   }
 }
 
+// Exclusive scan of many values: per-chunk sums, one scan of the sums, then
+// each chunk rescanned with its offset (chunks of kScanChunk values, 16 per
+// thread, contiguous).
+constexpr int kScanChunk = 4096;
+
+__global__ void __launch_bounds__(256) scan_chunk_sums(const uint32_t* __restrict__ data, int m,
+                                                       uint32_t* __restrict__ sums) {
+  __shared__ uint32_t part[256];
+  const int base = blockIdx.x * kScanChunk + threadIdx.x * 16;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (base + i < m) s += data[base + i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sums[blockIdx.x] = part[0];
+}
+
+__global__ void __launch_bounds__(256) scan_chunk_apply(uint32_t* __restrict__ data, int m,
+                                                        const uint32_t* __restrict__ sums) {
+  __shared__ uint32_t part[256];
+  const int tid = threadIdx.x;
+  const int base = blockIdx.x * kScanChunk + tid * 16;
+  uint32_t v[16];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = base + i < m ? data[base + i] : 0u;
+    s += v[i];
+  }
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t x = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  uint32_t run = sums[blockIdx.x] + part[tid] - s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (base + i < m) data[base + i] = run;
+    run += v[i];
+  }
+}
+
 __global__ void __launch_bounds__(256)
 radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t n,
@@ -383,6 +433,46 @@ void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out) {
   out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * 256 * ntiles);
   out->tile_cnt = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * 2 * ntiles);
   out->tile_base = reinterpret_cast<int32_t*>(p);
+}
+
+bool sort_pairs_lands_in_tmp(int key_bits) {
+  return ((key_bits + kRadixBits - 1) / kRadixBits) % 2 == 1;
+}
+
+size_t sort_pairs_hist_bytes(int64_t n) {
+  const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
+  const int64_t m = 256 * (ntiles > 0 ? ntiles : 1);
+  // tile histograms, then the chunk sums of their scan
+  return align256(sizeof(uint32_t) * m) + sizeof(uint32_t) * ((m + kScanChunk - 1) / kScanChunk);
+}
+
+hipError_t launch_sort_pairs(uint32_t* keys, int32_t* vals, uint32_t* keys_tmp, int32_t* vals_tmp, int32_t n,
+                             int key_bits, uint32_t* tile_hist, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int ntiles = (n + kSortTile - 1) / kSortTile;
+  const int passes = (key_bits + kRadixBits - 1) / kRadixBits;
+  uint32_t* sums = tile_hist + align256(sizeof(uint32_t) * 256 * static_cast<size_t>(ntiles)) / sizeof(uint32_t);
+  uint32_t* kin = keys;
+  int32_t* vin = vals;
+  uint32_t* kout = keys_tmp;
+  int32_t* vout = vals_tmp;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = pass * kRadixBits;
+    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, tile_hist, ntiles);
+    const int m = 256 * ntiles;
+    if (m <= 8 * kScanChunk) {
+      scan_exclusive_u32<<<1, 1024, 0, stream>>>(tile_hist, m);
+    } else {
+      const int chunks = (m + kScanChunk - 1) / kScanChunk;
+      scan_chunk_sums<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
+      scan_exclusive_u32<<<1, 1024, 0, stream>>>(sums, chunks);
+      scan_chunk_apply<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
+    }
+    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, tile_hist, ntiles);
+    uint32_t* tk = kin; kin = kout; kout = tk;
+    int32_t* tv = vin; vin = vout; vout = tv;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,

@@ -22,8 +22,10 @@
 // These kernels work for both storage types and any group size with plain
 // VALU arithmetic: D / 16 lanes share one row (16 dims each) and combine
 // their partial dot products with lane shuffles.  Stages, in launch order:
-//   sel_count/scan/fill  for every (group, block), the tokens whose selection
-//                        holds it (an inverted top-k list)
+//   sel_keys + sort      for every (group, block), the tokens whose selection
+//                        holds it (an inverted top-k list): a stable radix sort
+//                        of the top-k entries by (group, block), so each list
+//                        lists its tokens in increasing order
 //   cmp_dq_kernel        compressed branch: Delta, dgates, dq (first writer of dq_acc)
 //   cmp_dkv_kernel       pooled-row gradients, block-major
 //   win_dq_kernel        window branch: Delta, dgates, dq (adds)
@@ -119,71 +121,36 @@ __device__ __forceinline__ void put_delta(const BwdParams& p, int x, int64_t qro
 
 // ------------------------------------------------------------ inverted top-k lists
 
+// key of entry e = (token * h_kv + group) * topk + rank: group * nb_cap +
+// block, or h_kv * nb_cap (past every list) for a padding slot
 __global__ void __launch_bounds__(256)
-sel_clear_kernel(BwdParams p) {
-  const int64_t m = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < m;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p.sel_cnt[e] = 0;
-}
-
-__global__ void __launch_bounds__(256)
-sel_count_kernel(BwdParams p) {
+sel_keys_kernel(BwdParams p) {
   const int64_t m = static_cast<int64_t>(p.f.n) * p.f.h_kv * p.f.topk;
   const int nb = p.f.counts[SSA_COUNT_NB];
+  const uint32_t none = static_cast<uint32_t>(p.f.h_kv) * static_cast<uint32_t>(p.f.nb_cap);
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < m;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int j = p.f.topk_idx[e];
-    if (j < 0 || j >= nb) continue;
-    const int g = static_cast<int>((e / p.f.topk) % p.f.h_kv);
-    atomicAdd(&p.sel_cnt[static_cast<int64_t>(g) * p.f.nb_cap + j], 1);
-  }
-}
-
-// exclusive prefix of the counts (one workgroup of 1024 threads, each owning
-// a contiguous chunk); the counts are then reset to serve as fill cursors
-__global__ void __launch_bounds__(1024)
-sel_scan_kernel(BwdParams p) {
-  __shared__ int32_t part[1024];
-  const int64_t m = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap;
-  const int tid = threadIdx.x;
-  const int64_t chunk = (m + 1023) / 1024;
-  const int64_t a = tid * chunk;
-  const int64_t b = a + chunk < m ? a + chunk : m;
-  int32_t sum = 0;
-  for (int64_t e = a; e < b; ++e) sum += p.sel_cnt[e];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = part[tid] - sum;
-  for (int64_t e = a; e < b; ++e) {
-    const int32_t c = p.sel_cnt[e];
-    p.sel_off[e] = run;
-    run += c;
-    p.sel_cnt[e] = 0;
-  }
-  if (tid == 1023) p.sel_off[m] = part[1023];
-}
-
-__global__ void __launch_bounds__(256)
-sel_fill_kernel(BwdParams p) {
-  const int64_t m = static_cast<int64_t>(p.f.n) * p.f.h_kv * p.f.topk;
-  const int nb = p.f.counts[SSA_COUNT_NB];
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < m;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int j = p.f.topk_idx[e];
-    if (j < 0 || j >= nb) continue;
     const int64_t tg = e / p.f.topk;
-    const int g = static_cast<int>(tg % p.f.h_kv);
-    const int t = static_cast<int>(tg / p.f.h_kv);
-    const int64_t slot = static_cast<int64_t>(g) * p.f.nb_cap + j;
-    const int pos = atomicAdd(&p.sel_cnt[slot], 1);
-    p.sel_list[p.sel_off[slot] + pos] = t;
+    const uint32_t g = static_cast<uint32_t>(tg % p.f.h_kv);
+    p.sel_keys[e] = (j >= 0 && j < nb) ? g * static_cast<uint32_t>(p.f.nb_cap) + static_cast<uint32_t>(j) : none;
+    p.sel_vals[e] = static_cast<int32_t>(tg / p.f.h_kv);
+  }
+}
+
+// start of every list: the first sorted key >= the list's key
+__global__ void __launch_bounds__(256)
+sel_offsets_kernel(BwdParams p) {
+  const int64_t m = static_cast<int64_t>(p.f.n) * p.f.h_kv * p.f.topk;
+  const int64_t nl = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap;
+  for (int64_t key = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; key <= nl;
+       key += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    int64_t lo = 0, hi = m;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (static_cast<int64_t>(p.sel_sorted_keys[mid]) < key) lo = mid + 1; else hi = mid;
+    }
+    p.sel_off[key] = static_cast<int32_t>(lo);
   }
 }
 
@@ -591,12 +558,12 @@ hipError_t launch_bwd_pool(const BwdParams& p, ssa_dtype dtype, hipStream_t stre
 hipError_t launch_bwd_sel_index(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   const int64_t m = static_cast<int64_t>(p.f.n) * p.f.h_kv * p.f.topk;
   const int grid = static_cast<int>(std::min<int64_t>((m + 255) / 256, 8192));
-  const int64_t mc = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap;
-  const int grid_c = static_cast<int>(std::min<int64_t>((mc + 255) / 256, 8192));
-  sel_clear_kernel<<<grid_c, 256, 0, stream>>>(p);
-  sel_count_kernel<<<grid, 256, 0, stream>>>(p);
-  sel_scan_kernel<<<1, 1024, 0, stream>>>(p);
-  sel_fill_kernel<<<grid, 256, 0, stream>>>(p);
+  sel_keys_kernel<<<grid, 256, 0, stream>>>(p);
+  hipError_t e = launch_sort_pairs(p.sel_keys, p.sel_vals, p.sel_keys_tmp, p.sel_vals_tmp,
+                                   static_cast<int32_t>(m), p.sel_key_bits, p.sel_hist, stream);
+  if (e != hipSuccess) return e;
+  const int64_t nl = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap + 1;
+  sel_offsets_kernel<<<static_cast<int>(std::min<int64_t>((nl + 255) / 256, 8192)), 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@
 //   rows stream through LDS 32 at a time, row-major (for S = Q Kbar^T and
 //   dP = dO Vbar^T) and transposed in MFMA operand order (for
 //   dVbar^T += dO^T (G0 P)^T and dKbar^T += Q^T (G0 P (dP - Delta))^T).
+//   When there are few block tiles (grouped heads: few key/value groups, many
+//   rows), the rows are split over several workgroups whose partial tiles are
+//   summed afterwards in split order.
 //
 // kv_grad_mfma_kernel: the same block-major product for the token keys of
 //   the other two branches.  Selected branch: one workgroup per (group,
@@ -36,6 +39,8 @@
 //   area), and the four partial tiles are summed in LDS, in wave order, at
 //   the end.
 #include <float.h>
+
+#include <algorithm>
 
 #include "ssa_internal.h"
 
@@ -304,7 +309,11 @@ cmp_dkv_mfma_kernel(BwdParams p) {
   }
   const float c2 = f.scale * kLog2e;
   const int R = (s1 - s0) * G;               // (query, head of the group) rows of the sequence
-  const int n_rt = (R + kKeyTile - 1) / kKeyTile;
+  // this workgroup's share of the row tiles (split z of row_splits)
+  const int n_all = (R + kKeyTile - 1) / kKeyTile;
+  const int per = (n_all + p.row_splits - 1) / p.row_splits;
+  const int rt0 = min(n_all, static_cast<int>(blockIdx.z) * per);
+  const int n_rt = min(n_all, rt0 + per) - rt0;
   const uint16_t* Q = static_cast<const uint16_t*>(f.q);
   const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
   const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
@@ -317,6 +326,7 @@ cmp_dkv_mfma_kernel(BwdParams p) {
   u32x4 rq = {0u, 0u, 0u, 0u}, rd = {0u, 0u, 0u, 0u};
   float4 rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
   auto load = [&](int rt) {
+    rt += rt0;
     if (stager) {
       const int rr = rt * kKeyTile + r_row;
       rq = u32x4{0u, 0u, 0u, 0u};
@@ -401,18 +411,40 @@ cmp_dkv_mfma_kernel(BwdParams p) {
     }
   }
   if (!jok) return;
+  const int64_t part = p.row_splits > 1 ? static_cast<int64_t>(blockIdx.z) * f.h_kv * f.nb_cap * D : 0;
+  float* ok = (p.row_splits > 1 ? p.dkbar_part : p.dkbar) + part;
+  float* ov = (p.row_splits > 1 ? p.dvbar_part : p.dvbar) + part;
   const int64_t o = (static_cast<int64_t>(g) * f.nb_cap + j) * D;
 #pragma unroll
   for (int x = 0; x < VB; ++x)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int d = 32 * x + 8 * rb + 4 * half;
-      *reinterpret_cast<float4*>(p.dkbar + o + d) =
+      *reinterpret_cast<float4*>(ok + o + d) =
           make_float4(f.scale * dk[x][4 * rb], f.scale * dk[x][4 * rb + 1], f.scale * dk[x][4 * rb + 2],
                       f.scale * dk[x][4 * rb + 3]);
-      *reinterpret_cast<float4*>(p.dvbar + o + d) =
+      *reinterpret_cast<float4*>(ov + o + d) =
           make_float4(dv[x][4 * rb], dv[x][4 * rb + 1], dv[x][4 * rb + 2], dv[x][4 * rb + 3]);
     }
+}
+
+// the pooled-row gradients: the row splits' partial sums, in split order
+__global__ void __launch_bounds__(256)
+dkv_split_sum_kernel(BwdParams p) {
+  const int64_t per = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap * p.f.d;
+  for (int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; e < per;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x * 4) {
+    float4 k = *reinterpret_cast<const float4*>(p.dkbar_part + e);
+    float4 v = *reinterpret_cast<const float4*>(p.dvbar_part + e);
+    for (int z = 1; z < p.row_splits; ++z) {
+      const float4 a = *reinterpret_cast<const float4*>(p.dkbar_part + z * per + e);
+      const float4 c = *reinterpret_cast<const float4*>(p.dvbar_part + z * per + e);
+      k.x += a.x; k.y += a.y; k.z += a.z; k.w += a.w;
+      v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+    }
+    *reinterpret_cast<float4*>(p.dkbar + e) = k;
+    *reinterpret_cast<float4*>(p.dvbar + e) = v;
+  }
 }
 
 // ------------------------------------------------------------ token keys of the selected / window branch
@@ -627,9 +659,13 @@ hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 }
 
 hipError_t launch_bwd_cmp_dkv_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  const dim3 grid(p.max_btiles, p.f.h_kv);
+  const dim3 grid(p.max_btiles, p.f.h_kv, p.row_splits);
   if (p.f.d == 32) cmp_dkv_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
   else cmp_dkv_mfma_kernel<64><<<grid, 256, 0, stream>>>(p);
+  if (p.row_splits > 1) {
+    const int64_t n4 = static_cast<int64_t>(p.f.h_kv) * p.f.nb_cap * p.f.d / 4;
+    dkv_split_sum_kernel<<<static_cast<int>(std::min<int64_t>((n4 + 255) / 256, 8192)), 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -87,6 +87,14 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
                         const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
                         hipStream_t stream);
 
+// Stable LSD radix sort of (key, value) pairs by the low `key_bits` bits of
+// the keys, 8 bits per pass, ping-ponging between (keys, vals) and the tmp
+// pair: the result lands in the tmp pair when the pass count is odd.
+bool sort_pairs_lands_in_tmp(int key_bits);
+size_t sort_pairs_hist_bytes(int64_t n);
+hipError_t launch_sort_pairs(uint32_t* keys, int32_t* vals, uint32_t* keys_tmp, int32_t* vals_tmp, int32_t n,
+                             int key_bits, uint32_t* tile_hist, hipStream_t stream);
+
 // ---------------------------------------------------------------- forward
 
 struct FwdParams {
@@ -154,15 +162,27 @@ struct BwdParams {
   float* dv_acc;
   float* dkbar;         // [h_kv][nb_cap][D] gradients of the pooled rows
   float* dvbar;
-  int32_t* sel_cnt;     // [h_kv * nb_cap] selections per (group, block), then fill cursors
-  int32_t* sel_off;     // [h_kv * nb_cap + 1] exclusive offsets into sel_list
-  int32_t* sel_list;    // [n * h_kv * topk] the selecting token (input index) of every entry
+  // inverted top-k lists: every (token, group, rank) entry keyed by
+  // group * nb_cap + block, stably sorted, so that each list holds its
+  // selecting tokens in increasing order
+  uint32_t* sel_keys;   // [n * h_kv * topk] keys (input of the sort)
+  int32_t* sel_vals;    // [n * h_kv * topk] selecting token (input of the sort)
+  uint32_t* sel_keys_tmp;
+  int32_t* sel_vals_tmp;
+  uint32_t* sel_hist;   // radix sort tile histograms
+  int32_t sel_key_bits;
+  int32_t* sel_off;     // [h_kv * nb_cap + 1] start of each list in sel_list
+  int32_t* sel_list;    // the sorted tokens (one of the two value buffers)
+  const uint32_t* sel_sorted_keys;   // the sorted keys (one of the two key buffers)
   // MFMA kernels of the compressed branch (bf16)
   void* kbar_t;         // [h_kv][nb_cap / 32][D][32] pooled keys, each 32-block tile transposed
   int32_t* qtile_pre;   // [batch + 1] prefix of 128-query tiles per sequence
   int32_t* btile_pre;   // [batch + 1] prefix of 128-block chunks per sequence
   int32_t max_qtiles;   // grid bounds of the two
   int32_t max_btiles;
+  int32_t row_splits;   // the pooled-row gradients are summed over this many row ranges
+  float* dkbar_part;    // [row_splits][h_kv][nb_cap][D] partial sums (row_splits > 1)
+  float* dvbar_part;
 };
 
 constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile

@@ -99,6 +99,16 @@ def test_zero_output_gradient():
         assert not grads[nm].float().abs().max().item(), nm
 
 
+def test_backward_run_to_run_bit_identical():
+    wl = make_workload(2)
+    gb = P.gpu_build(wl)
+    dout = _dout(wl, 2)
+    _, a = _gpu_grads(wl, gb, dout)
+    _, b = _gpu_grads(wl, gb, dout)
+    for nm in ("dq", "dk", "dv", "dgates"):
+        assert torch.equal(a[nm], b[nm]), nm
+
+
 def _sequence_sums(wl, grads, dout):
     """sum_t dK[t, g] = 0 and sum_t dV[t, g] = sum_{t, h in g} (G0 + G1 + G2) dO,
     per sequence and group, relative to the size of the summands."""
