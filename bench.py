@@ -11,7 +11,9 @@ on a 1024^3 grid; 16 query / 16 key-value heads, head dim 64, bfloat16;
 m_cmp = 4, m_win = 8, top-k = 16 (the 128k-token setting of the Direct3D-S2
 summary page, "Experiments").  ``--workload 4`` times the grouped-head
 workload instead (262144 tokens, 32 query / 2 key-value heads, head dim 32),
-for its kernel profile.
+for its kernel profile; ``--workload 5`` times a training step (block build,
+forward that saves its log-sum-exps, backward giving dq, dk, dv and the gate
+gradients for a seeded output gradient) on the varlen batch of 8 sequences.
 
 Prints one JSON line (rank 0, N = 1 only).
 """
@@ -38,7 +40,11 @@ WORKLOADS = {
     4: dict(name="ssa-fwd-1024^3-16prims-262144tok-h32kv2-d32-bf16", tag="262144tok",
             metric="SSA fwd tokens/s and TFLOP/s at 262144 voxel tokens, 32 query / 2 key-value heads; "
                    "% bf16 MFMA peak"),
+    5: dict(name="ssa-fwd+bwd-varlen-8seq-469315tok-h16-d64-bf16", tag="varlen",
+            metric="SSA fwd+bwd (dq, dk, dv, dgates given dout) tokens/s and TFLOP/s on the varlen batch of "
+                   "8 sequences; % bf16 MFMA peak"),
 }
+TRAIN_WORKLOADS = (5,)
 WORKLOAD_ID = 3
 CALIB_BYTES = 1 << 30       # plain-copy calibration size for the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
@@ -54,6 +60,9 @@ KERNEL_SOURCES = {
     "gqa_cmp_kernel": "ssa_attn_gqa.hip",
     "gqa_topk_kernel": "ssa_attn_gqa.hip",
     "gqa_fixup_kernel": "ssa_attn_gqa.hip",
+    "cmp_dq_mfma_kernel": "ssa_bwd_mfma.hip",
+    "cmp_dkv_mfma_kernel": "ssa_bwd_mfma.hip",
+    "kv_grad_mfma_kernel": "ssa_bwd_mfma.hip",
 }
 
 
@@ -170,10 +179,11 @@ def algorithmic_flops(wl, blocks, topk, torch):
                 nb=int(h["counts"][0]), nw=int(h["counts"][1]))
 
 
-def cpu_baseline(wl, target_s: float):
+def cpu_baseline(wl, target_s: float, train: bool = False):
     """Time the oracle on a bounded sample of the same workload (test
     infrastructure, single thread): the full block build and pooling once,
-    then sampled (token, head) rows, extrapolated to all rows."""
+    then sampled (token, head) rows (forward, and with ``train`` also their
+    backward), extrapolated to all rows."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -184,6 +194,7 @@ def cpu_baseline(wl, target_s: float):
         kbar = oracle.pool_blocks(wl.k, ob, wl.dtype)
         vbar = oracle.pool_blocks(wl.v, ob, wl.dtype)
         t_fixed = time.perf_counter() - t0
+        dout = np.broadcast_to(np.ones((1, 1, wl.head_dim), np.float32), wl.q.shape)
         rng = np.random.default_rng(7)
         rows_done, t_rows = 0, 0.0
         budget = max(target_s - t_fixed, 2.0)
@@ -191,17 +202,20 @@ def cpu_baseline(wl, target_s: float):
             rows = list(zip(rng.integers(0, wl.n_tokens, 16).tolist(), rng.integers(0, wl.h_q, 16).tolist()))
             t1 = time.perf_counter()
             oracle.forward_rows(wl, ob, rows, kbar=kbar, vbar=vbar)
+            if train:
+                oracle.backward(wl, dout, blocks=ob, rows=rows)
             t_rows += time.perf_counter() - t1
             rows_done += len(rows)
     per_row = t_rows / rows_done
     t_step = t_fixed + per_row * wl.n_tokens * wl.h_q
+    what = "forward + backward" if train else "forward"
     return {
         "value": wl.n_tokens / t_step,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
         "sample": (f"float64 numpy oracle, one thread: full block build + pooling ({t_fixed:.1f} s), "
-                   f"then {rows_done} random (token, head) rows ({t_rows:.1f} s); per-step time "
+                   f"then the {what} of {rows_done} random (token, head) rows ({t_rows:.1f} s); per-step time "
                    f"extrapolated to all {wl.n_tokens * wl.h_q} rows = {t_step:.0f} s"),
     }
 
@@ -220,7 +234,7 @@ def main():
     ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=sorted(WORKLOADS),
                     help="3: the 131072-token workload (default); 4: the grouped-head 262144-token "
-                         "workload, for its kernel profile")
+                         "workload, for its kernel profile; 5: forward + backward on the varlen batch")
     args = ap.parse_args()
     wid = args.workload
     if args.summarize_counters:
@@ -261,9 +275,23 @@ def main():
                          device=dev)
     out = torch.empty_like(q)
 
+    train = wid in TRAIN_WORKLOADS
+    if train:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 * wid + 4)
+        dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(bf)
+        ws_bwd = torch.empty(ssa.backward_workspace_bytes(blocks0, q, k, wl.topk), dtype=torch.uint8, device=dev)
+
     def step():
-        b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
-        ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd)
+        if not train:
+            b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
+            ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd)
+            return
+        # the backward's workspace is sized from the block count, so the
+        # training step builds with the counts synced
+        b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=True)
+        saved = ssa.forward_train(b, q, k, v, gates, wl.topk, workspace=ws_fwd)
+        ssa.backward(b, q, k, v, gates, saved, dout, workspace=ws_bwd)
 
     if args.copy_calibration:
         # a plain copy of known size whose source is not cache-resident: its
@@ -300,6 +328,11 @@ def main():
         st = {}
         b = ssa.build_blocks(coords, cu, wl.grid_res, wl.m_cmp, wl.m_win, sync=False)
         ssa.forward(b, q, k, v, gates, wl.topk, out=out, workspace=ws_fwd, stage_times=st)
+        if train:
+            saved = ssa.forward_train(blocks0, q, k, v, gates, wl.topk, workspace=ws_fwd)
+            bst = {}
+            ssa.backward(blocks0, q, k, v, gates, saved, dout, workspace=ws_bwd, stage_times=bst)
+            st.update({"bwd:" + name: ms for name, ms in bst.items()})
         for name, ms in st.items():
             stage_sum[name] = stage_sum.get(name, 0.0) + ms
     stage_ms = {name: ms / reps for name, ms in stage_sum.items()}
@@ -312,12 +345,22 @@ def main():
     torch.cuda.synchronize()
     build_ms = eb0.elapsed_time(eb1) / reps
 
-    # roofline of the compressed-attention kernel, which does the compressed
-    # branch's algorithmic flops (the largest kernel on both workloads)
-    dom = "gqa_cmp_kernel" if "gqa_cmp_kernel" in stage_ms else "cmp_mfma_kernel"
-    achieved = work["cmp"] / (stage_ms[dom] * 1e-3) / 1e12
     n = wl.n_tokens
-    tflops = work["total"] / (ms_step * 1e-3) / 1e12
+    if not train:
+        # roofline of the compressed-attention kernel, which does the
+        # compressed branch's algorithmic flops (the largest kernel)
+        dom = "gqa_cmp_kernel" if "gqa_cmp_kernel" in stage_ms else "cmp_mfma_kernel"
+        achieved = work["cmp"] / (stage_ms[dom] * 1e-3) / 1e12
+        total_flops = work["total"]
+    else:
+        # backward algorithmic work: per (query head, key) pair of every branch
+        # 8 D flops (dP = dO V^T, dq = dS K, dk = dS^T q, dv = P^T dO); the
+        # pooled-row gradient kernel does the compressed branch's dk and dv
+        # part, 4 D per pair (its recomputed S and dP are not counted)
+        dom = "bwd:cmp_dkv_mfma_kernel"
+        achieved = work["cmp"] / (stage_ms[dom] * 1e-3) / 1e12
+        total_flops = 3.0 * work["total"]
+    tflops = total_flops / (ms_step * 1e-3) / 1e12
     pool_gbs = pool_bytes(wl, work["nb"]) / (stage_ms["pool_kernel"] * 1e-3) / 1e9
 
     line = {
@@ -338,17 +381,18 @@ def main():
                    "m_cmp": wl.m_cmp, "m_win": wl.m_win, "topk": wl.topk, "parallelism": "none"},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-        "algorithmic_tflop_per_step": work["total"] / 1e12,
+        "algorithmic_tflop_per_step": total_flops / 1e12,
         "work": {k2: work[k2] for k2 in ("cmp", "sel", "win", "mean_sel_tokens", "mean_win_tokens", "nb", "nw")},
         "build_ms": build_ms,
         "stage_ms": stage_ms,
         "pool_hbm": {"achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pool_gbs / PEAK_HBM_GBS,
                      "bytes": pool_bytes(wl, work["nb"])},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic(dom, wid)},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": stored_traffic(dom.split(":")[-1], wid)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, train=train)
     print(json.dumps(line), flush=True)
 
 
