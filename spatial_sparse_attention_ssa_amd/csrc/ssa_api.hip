@@ -458,11 +458,13 @@ int backward_plan(const ssa_attn* attn, BStage* stages) {
     stages[n++] = BStage{"cmp_dq_kernel", ssa::launch_bwd_cmp_dq};
     stages[n++] = BStage{"cmp_dkv_kernel", ssa::launch_bwd_cmp_dkv};
   }
-  stages[n++] = BStage{"win_dq_kernel", ssa::launch_bwd_win_dq};
-  if (use_mfma_backward(attn))
+  if (use_mfma_backward(attn)) {
+    stages[n++] = BStage{"win_dq_mfma_kernel", ssa::launch_bwd_win_dq_mfma};
     stages[n++] = BStage{"kv_grad_mfma_kernel<window>", ssa::launch_bwd_kv_win_mfma};
-  else
+  } else {
+    stages[n++] = BStage{"win_dq_kernel", ssa::launch_bwd_win_dq};
     stages[n++] = BStage{"win_dkv_kernel", ssa::launch_bwd_win_dkv};
+  }
   stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
   if (use_mfma_backward(attn))
     stages[n++] = BStage{"kv_grad_mfma_kernel<selected>", ssa::launch_bwd_kv_sel_mfma};

@@ -447,6 +447,151 @@ dkv_split_sum_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------ window branch dq
+
+// dq of the window branch on MFMA: one workgroup per (window, query head)
+// item (persistent grid, items head-major).  The window's key and value rows
+// (row-major) and its keys transposed in MFMA operand order are staged in LDS
+// kWinChunk tokens at a time; each wave owns 32 of the window's queries and
+// accumulates A = K^T (P * dP)^T and B = K^T P^T as in the compressed
+// branch's dq kernel.  Adds to dq_acc; writes Delta and the gate gradient.
+constexpr int kWinChunk = 128;
+
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+win_dq_mfma_kernel(BwdParams p) {
+  constexpr int KS = D / 16;
+  constexpr int VB = D / 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int kKRow = D + 8;               // padded key / value row (bf16)
+  constexpr int kCRow = kWinChunk + 8;       // padded transposed row
+  __shared__ __align__(16) uint16_t k_lds[kWinChunk * kKRow];
+  __shared__ __align__(16) uint16_t v_lds[kWinChunk * kKRow];
+  __shared__ __align__(16) uint16_t t_lds[D * kCRow];
+
+  const FwdParams& f = p.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int half = lane >> 5;
+  const float c2 = f.scale * kLog2e;
+  const int nw = f.counts[SSA_COUNT_NW];
+  const int64_t nrow = static_cast<int64_t>(f.n) * f.h_q;
+  const int64_t n_items = static_cast<int64_t>(nw) * f.h_q;
+  const uint16_t* Q = static_cast<const uint16_t*>(f.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int h = static_cast<int>(item / nw);
+    const int w = static_cast<int>(item % nw);
+    const int wa = f.win_off[w], wb = f.win_off[w + 1];
+    const int n_w = wb - wa;
+    const int g = h / (f.h_q / f.h_kv);
+    const uint16_t* KS_ = static_cast<const uint16_t*>(f.k_s) + (static_cast<int64_t>(g) * f.n + wa) * D;
+    const uint16_t* VS_ = static_cast<const uint16_t*>(f.v_s) + (static_cast<int64_t>(g) * f.n + wa) * D;
+    for (int qg0 = 0; qg0 < n_w; qg0 += 128) {
+      const int qi = wa + qg0 + wv * 32 + (lane & 31);
+      const bool valid = qi < wb;
+      const int t = valid ? f.perm[qi] : 0;
+      const int64_t qrow = static_cast<int64_t>(t) * f.h_q + h;
+      bf16x8 qb[KS], db[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (valid) {
+          a = *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * ks + 8 * half);
+          c = *reinterpret_cast<const u32x4*>(dO + qrow * D + 16 * ks + 8 * half);
+        }
+        qb[ks] = __builtin_bit_cast(bf16x8, a);
+        db[ks] = __builtin_bit_cast(bf16x8, c);
+      }
+      const float l2 = valid ? p.lse[2 * nrow + qrow] * kLog2e : 0.f;
+      f32x16 aa[VB], ab[VB];
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        aa[vb] = f32x16{};
+        ab[vb] = f32x16{};
+      }
+      float dl = 0.f;
+      for (int kc = 0; kc < n_w; kc += kWinChunk) {
+        const int nk = min(kWinChunk, n_w - kc);
+        const int nk32 = (nk + 31) & ~31;
+        __syncthreads();  // the previous chunk is consumed
+        for (int e = tid; e < nk32 * CPR; e += 256) {
+          const int row = e / CPR, c = e % CPR;
+          u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+          if (row < nk) {
+            const int64_t off = static_cast<int64_t>(kc + row) * D + 8 * c;
+            kr = *reinterpret_cast<const u32x4*>(KS_ + off);
+            vr = *reinterpret_cast<const u32x4*>(VS_ + off);
+          }
+          *reinterpret_cast<u32x4*>(k_lds + row * kKRow + 8 * c) = kr;
+          *reinterpret_cast<u32x4*>(v_lds + row * kKRow + 8 * c) = vr;
+          const int kp = (row & ~31) | mfma_pos(row & 31);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int d = 8 * c + 2 * e2;
+            t_lds[d * kCRow + kp] = static_cast<uint16_t>(kr[e2] & 0xFFFFu);
+            t_lds[(d + 1) * kCRow + kp] = static_cast<uint16_t>(kr[e2] >> 16);
+          }
+        }
+        __syncthreads();
+        for (int kt = 0; kt < nk32; kt += kKeyTile) {
+          const uint16_t* kl = k_lds + (kt + (lane & 31)) * kKRow + 8 * half;
+          const uint16_t* vl = v_lds + (kt + (lane & 31)) * kKRow + 8 * half;
+          f32x16 s = {}, dp = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(kl + 16 * ks), qb[ks], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + 16 * ks), db[ks], dp, 0, 0, 0);
+          }
+          float pr[16], pd[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            const float x = key < nk ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2)) : 0.f;
+            pr[r] = x;
+            pd[r] = x * dp[r];
+            dl += pd[r];
+          }
+          const uint16_t* tl = t_lds + (lane & 31) * kCRow + kt + 8 * half;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 pdb = pack8(pd + 8 * ks);
+            const bf16x8 pb = pack8(pr + 8 * ks);
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb) {
+              const bf16x8 a = lds_b128(tl + vb * 32 * kCRow + 16 * ks);
+              aa[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pdb, aa[vb], 0, 0, 0);
+              ab[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ab[vb], 0, 0, 0);
+            }
+          }
+        }
+      }
+      dl += __shfl_xor(dl, 32);
+      if (valid) {
+        const float gs = bf16_bits_to_f32(static_cast<const uint16_t*>(f.gates)[qrow * 3 + 2]) * f.scale;
+        float* dst = p.dq_acc + qrow * D;
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const int d = 32 * vb + 8 * rb + 4 * half;
+            float4 o = *reinterpret_cast<const float4*>(dst + d);
+            o.x = fmaf(gs, fmaf(-dl, ab[vb][4 * rb], aa[vb][4 * rb]), o.x);
+            o.y = fmaf(gs, fmaf(-dl, ab[vb][4 * rb + 1], aa[vb][4 * rb + 1]), o.y);
+            o.z = fmaf(gs, fmaf(-dl, ab[vb][4 * rb + 2], aa[vb][4 * rb + 2]), o.z);
+            o.w = fmaf(gs, fmaf(-dl, ab[vb][4 * rb + 3], aa[vb][4 * rb + 3]), o.w);
+            *reinterpret_cast<float4*>(dst + d) = o;
+          }
+        if (half == 0) {
+          p.delta[2 * nrow + qrow] = dl;
+          if (p.dgates) static_cast<uint16_t*>(p.dgates)[qrow * 3 + 2] = f32_to_bf16_bits(dl);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ token keys of the selected / window branch
 
 enum KvMode { kSelected = 1, kWindow = 2 };   // the branch index of each
@@ -645,6 +790,12 @@ hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   if (p.f.d == 32) kv_grad_mfma_kernel<32, kWindow><<<4096, 256, 0, stream>>>(p);
   else kv_grad_mfma_kernel<64, kWindow><<<4096, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_win_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  if (p.f.d == 32) win_dq_mfma_kernel<32><<<4096, 256, 0, stream>>>(p);
+  else win_dq_mfma_kernel<64><<<4096, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

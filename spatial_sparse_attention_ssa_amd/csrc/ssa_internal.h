@@ -211,6 +211,7 @@ hipError_t launch_bwd_sel_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t st
 hipError_t launch_bwd_finalize(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_cmp_dkv_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_win_dq_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
