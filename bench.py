@@ -63,6 +63,9 @@ KERNEL_SOURCES = {
     "cmp_dq_mfma_kernel": "ssa_bwd_mfma.hip",
     "cmp_dkv_mfma_kernel": "ssa_bwd_mfma.hip",
     "kv_grad_mfma_kernel": "ssa_bwd_mfma.hip",
+    "win_dq_mfma_kernel": "ssa_bwd_mfma.hip",
+    "win_dkv_mfma_kernel": "ssa_bwd_mfma.hip",
+    "rows_prep_kernel": "ssa_bwd_mfma.hip",
 }
 
 

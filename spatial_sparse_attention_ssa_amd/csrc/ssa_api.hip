@@ -381,8 +381,14 @@ namespace {
 
 struct BwdLayout {
   size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_keys, sel_vals, sel_keys_tmp,
-      sel_vals_tmp, sel_hist, sel_off, kbar_t, qtile_pre, btile_pre, dkbar_part, dvbar_part, total;
+      sel_vals_tmp, sel_hist, sel_off, kbar_t, qtile_pre, btile_pre, dkbar_part, dvbar_part, q_rows, do_rows,
+      q_rt, do_rt, st_rows, total;
 };
+
+// the sorted (query, head) rows of one group, rounded up to whole 32-row tiles
+int64_t rows_capacity(const ssa_blocks* b, const ssa_attn* a) {
+  return (b->n_tokens * (a->h_q / a->h_kv) + 31) / 32 * 32;
+}
 
 // 128-block chunks (an upper bound) and the row splits that give the
 // pooled-row gradient kernel about 8192 workgroups
@@ -432,6 +438,12 @@ BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
     L.kbar_t = off; off += pooled;
     L.qtile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     L.btile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    const size_t rows = static_cast<size_t>(a->h_kv) * static_cast<size_t>(rows_capacity(b, a));
+    L.q_rows = off; off += align256(eb * rows * D);
+    L.do_rows = off; off += align256(eb * rows * D);
+    L.q_rt = off; off += align256(eb * rows * D);
+    L.do_rt = off; off += align256(eb * rows * D);
+    L.st_rows = off; off += align256(4 * sizeof(float) * 2 * rows);
     const size_t splits = static_cast<size_t>(dkv_row_splits(b, a));
     if (splits > 1) {
       L.dkbar_part = off; off += align256(sizeof(float) * splits * a->h_kv * cap * D);
@@ -452,24 +464,23 @@ int backward_plan(const ssa_attn* attn, BStage* stages) {
   stages[n++] = BStage{"pool_kernel", ssa::launch_bwd_pool};
   stages[n++] = BStage{"sel_index", ssa::launch_bwd_sel_index};
   if (use_mfma_backward(attn)) {
+    // the three dq kernels (which also give Delta), then the key / value
+    // gradients over the sorted rows
     stages[n++] = BStage{"cmp_dq_mfma_kernel", ssa::launch_bwd_cmp_dq_mfma};
+    stages[n++] = BStage{"win_dq_mfma_kernel", ssa::launch_bwd_win_dq_mfma};
+    stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
+    stages[n++] = BStage{"rows_prep_kernel", ssa::launch_bwd_rows_prep};
     stages[n++] = BStage{"cmp_dkv_mfma_kernel", ssa::launch_bwd_cmp_dkv_mfma};
+    stages[n++] = BStage{"win_dkv_mfma_kernel", ssa::launch_bwd_kv_win_mfma};
+    stages[n++] = BStage{"kv_grad_mfma_kernel", ssa::launch_bwd_kv_sel_mfma};
   } else {
     stages[n++] = BStage{"cmp_dq_kernel", ssa::launch_bwd_cmp_dq};
     stages[n++] = BStage{"cmp_dkv_kernel", ssa::launch_bwd_cmp_dkv};
-  }
-  if (use_mfma_backward(attn)) {
-    stages[n++] = BStage{"win_dq_mfma_kernel", ssa::launch_bwd_win_dq_mfma};
-    stages[n++] = BStage{"kv_grad_mfma_kernel<window>", ssa::launch_bwd_kv_win_mfma};
-  } else {
     stages[n++] = BStage{"win_dq_kernel", ssa::launch_bwd_win_dq};
     stages[n++] = BStage{"win_dkv_kernel", ssa::launch_bwd_win_dkv};
-  }
-  stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
-  if (use_mfma_backward(attn))
-    stages[n++] = BStage{"kv_grad_mfma_kernel<selected>", ssa::launch_bwd_kv_sel_mfma};
-  else
+    stages[n++] = BStage{"sel_dq_kernel", ssa::launch_bwd_sel_dq};
     stages[n++] = BStage{"sel_dkv_kernel", ssa::launch_bwd_sel_dkv};
+  }
   stages[n++] = BStage{"bwd_finalize_kernel", ssa::launch_bwd_finalize};
   return n;
 }
@@ -557,6 +568,12 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
     bp.max_qtiles = static_cast<int32_t>(blocks->n_tokens / 128 + blocks->batch + 1);
     bp.max_btiles = max_block_chunks(blocks);
     bp.row_splits = dkv_row_splits(blocks, attn);
+    bp.rows_cap = static_cast<int32_t>(rows_capacity(blocks, attn));
+    bp.q_rows = w + lay.q_rows;
+    bp.do_rows = w + lay.do_rows;
+    bp.q_rt = w + lay.q_rt;
+    bp.do_rt = w + lay.do_rt;
+    bp.st_rows = reinterpret_cast<float4*>(w + lay.st_rows);
     if (bp.row_splits > 1) {
       bp.dkbar_part = reinterpret_cast<float*>(w + lay.dkbar_part);
       bp.dvbar_part = reinterpret_cast<float*>(w + lay.dvbar_part);

@@ -258,28 +258,234 @@ cmp_dq_mfma_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------ dKbar, dVbar (block-major)
+// ------------------------------------------------------------ sorted (query, head) rows
 
+// Row R = i * G + hh of group g is query head g * G + hh of the token at
+// sorted position i.  rows_prep_kernel writes, per group, the rows of Q and
+// dO in that order (row-major), the same rows as 32-row tiles transposed in
+// MFMA operand order ([D][32], row r at position mfma_pos(r)), and per row
+// (log2 lse, Delta, gate) of the compressed and the window branch.  The
+// block- and window-major gradient kernels then stage whole 16-byte chunks.
 template <int D>
-__global__ void __launch_bounds__(256, 2)
-cmp_dkv_mfma_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256)
+rows_prep_kernel(BwdParams p) {
+  constexpr int CPR = D / 8;
+  __shared__ uint16_t tq[kKeyTile][D + 2];
+  __shared__ uint16_t td[kKeyTile][D + 2];
+  const FwdParams& f = p.f;
+  const int tid = threadIdx.x;
+  const int G = f.h_q / f.h_kv;
+  const int64_t n_rows = static_cast<int64_t>(f.n) * G;
+  const int ntile = p.rows_cap / kKeyTile;
+  const int64_t nrow = static_cast<int64_t>(f.n) * f.h_q;
+  const uint16_t* Q = static_cast<const uint16_t*>(f.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
+  const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
+  for (int64_t item = blockIdx.x; item < static_cast<int64_t>(f.h_kv) * ntile; item += gridDim.x) {
+    const int g = static_cast<int>(item / ntile);
+    const int T = static_cast<int>(item % ntile);
+    const int64_t rbase = static_cast<int64_t>(g) * p.rows_cap + static_cast<int64_t>(T) * kKeyTile;
+    if (tid < kKeyTile * CPR) {
+      const int row = tid / CPR, c = tid % CPR;
+      const int64_t R = static_cast<int64_t>(T) * kKeyTile + row;
+      u32x4 uq = {0u, 0u, 0u, 0u}, ud = {0u, 0u, 0u, 0u};
+      if (R < n_rows) {
+        const int64_t qrow = static_cast<int64_t>(f.perm[R / G]) * f.h_q + g * G + R % G;
+        uq = *reinterpret_cast<const u32x4*>(Q + qrow * D + 8 * c);
+        ud = *reinterpret_cast<const u32x4*>(dO + qrow * D + 8 * c);
+      }
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.q_rows) + (rbase + row) * D + 8 * c) = uq;
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.do_rows) + (rbase + row) * D + 8 * c) = ud;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tq[row][8 * c + 2 * e] = static_cast<uint16_t>(uq[e] & 0xFFFFu);
+        tq[row][8 * c + 2 * e + 1] = static_cast<uint16_t>(uq[e] >> 16);
+        td[row][8 * c + 2 * e] = static_cast<uint16_t>(ud[e] & 0xFFFFu);
+        td[row][8 * c + 2 * e + 1] = static_cast<uint16_t>(ud[e] >> 16);
+      }
+    }
+    if (tid < kKeyTile) {
+      const int64_t R = static_cast<int64_t>(T) * kKeyTile + tid;
+      float4 s0 = make_float4(FLT_MAX, 0.f, 0.f, 0.f), s2 = s0;   // a padding row has P = 0
+      if (R < n_rows) {
+        const int64_t qrow = static_cast<int64_t>(f.perm[R / G]) * f.h_q + g * G + R % G;
+        s0 = make_float4(p.lse[qrow] * kLog2e, p.delta[qrow], bf16_bits_to_f32(gates[qrow * 3]), 0.f);
+        s2 = make_float4(p.lse[2 * nrow + qrow] * kLog2e, p.delta[2 * nrow + qrow],
+                         bf16_bits_to_f32(gates[qrow * 3 + 2]), 0.f);
+      }
+      p.st_rows[rbase + tid] = s0;
+      p.st_rows[static_cast<int64_t>(f.h_kv) * p.rows_cap + rbase + tid] = s2;
+    }
+    __syncthreads();
+    if (tid < D * 4) {
+      const int dd = tid >> 2, c = tid & 3;
+      u32x4 uq, ud;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r0 = mfma_pos(8 * c + 2 * e), r1 = mfma_pos(8 * c + 2 * e + 1);
+        uq[e] = static_cast<uint32_t>(tq[r0][dd]) | (static_cast<uint32_t>(tq[r1][dd]) << 16);
+        ud[e] = static_cast<uint32_t>(td[r0][dd]) | (static_cast<uint32_t>(td[r1][dd]) << 16);
+      }
+      const int64_t o = ((static_cast<int64_t>(g) * ntile + T) * D + dd) * kKeyTile + 8 * c;
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.q_rt) + o) = uq;
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.do_rt) + o) = ud;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ key gradients over sorted rows
+
+// One workgroup, four waves, each wave one 32-key tile (its key and value
+// rows in registers as MFMA B operands).  The rows [r_lo, r_hi) of group g
+// (sorted row space, tiles aligned to 32; rows outside the range get P = 0)
+// stream through a two-slot LDS ring: row-major (A operands of S = Q K^T and
+// dP = dO V^T) and transposed (A operands of dV^T += dO^T (gate P)^T and
+// dK^T += Q^T (gate P (dP - Delta))^T).  Tiles [t_beg, t_end) of the range
+// are this workgroup's share.  Writes scale * dK and dV rows of the valid
+// keys to dk_row / dv_row (null: nothing to write).
+template <int D>
+__device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wave_on, const uint16_t* k_row,
+                                              const uint16_t* v_row, int64_t r_lo, int64_t r_hi, int t_beg,
+                                              int t_end, const float4* st, float* dk_row, float* dv_row,
+                                              uint16_t* q_lds, uint16_t* d_lds, uint16_t* qt_lds,
+                                              uint16_t* dt_lds, float4* st_lds) {
   constexpr int KS = D / 16;
   constexpr int VB = D / 32;
-  constexpr int kRRow = D + 8;                 // padded row-major query row (bf16)
-  constexpr int kRowCh = kKeyTile * D / 8;     // 16-byte chunks of a 32-row tile
+  constexpr int kRRow = D + 8;
   constexpr int kRT = kKeyTile * kRRow;
   constexpr int kTT = D * kTRow;
-  __shared__ __align__(16) uint16_t q_lds[2 * kRT];
-  __shared__ __align__(16) uint16_t d_lds[2 * kRT];
-  __shared__ __align__(16) uint16_t qt_lds[2 * kTT];
-  __shared__ __align__(16) uint16_t dt_lds[2 * kTT];
-  __shared__ float4 st_lds[2 * kKeyTile];      // per row: log2 lse, Delta, G0
-
+  constexpr int CPR = D / 8;
   const FwdParams& f = p.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
   const int half = lane >> 5;
+  const float c2 = f.scale * kLog2e;
+  bf16x8 kb[KS], vb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (k_row) {
+      a = *reinterpret_cast<const u32x4*>(k_row + 16 * ks + 8 * half);
+      c = *reinterpret_cast<const u32x4*>(v_row + 16 * ks + 8 * half);
+    }
+    kb[ks] = __builtin_bit_cast(bf16x8, a);
+    vb[ks] = __builtin_bit_cast(bf16x8, c);
+  }
+  const int ntile = p.rows_cap / kKeyTile;
+  const uint16_t* QR = static_cast<const uint16_t*>(p.q_rows) + static_cast<int64_t>(g) * p.rows_cap * D;
+  const uint16_t* DR = static_cast<const uint16_t*>(p.do_rows) + static_cast<int64_t>(g) * p.rows_cap * D;
+  const uint16_t* QT = static_cast<const uint16_t*>(p.q_rt) + static_cast<int64_t>(g) * ntile * D * kKeyTile;
+  const uint16_t* DT = static_cast<const uint16_t*>(p.do_rt) + static_cast<int64_t>(g) * ntile * D * kKeyTile;
+  // staging: thread tid moves chunk tid of each of the four tiles
+  const bool stager = tid < kKeyTile * CPR;
+  const int r_row = tid / CPR, r_c = tid % CPR;    // row-major: row, 8-dim chunk
+  const int t_dim = tid >> 2, t_c = tid & 3;       // transposed: dim, 8-position chunk
+  u32x4 rq = {0u, 0u, 0u, 0u}, rd = rq, tq = rq, td = rq;
+  float4 rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
+  auto load = [&](int T) {
+    if (stager) {
+      const int64_t ro = (static_cast<int64_t>(T) * kKeyTile + r_row) * D + 8 * r_c;
+      const int64_t to = (static_cast<int64_t>(T) * D + t_dim) * kKeyTile + 8 * t_c;
+      rq = *reinterpret_cast<const u32x4*>(QR + ro);
+      rd = *reinterpret_cast<const u32x4*>(DR + ro);
+      tq = *reinterpret_cast<const u32x4*>(QT + to);
+      td = *reinterpret_cast<const u32x4*>(DT + to);
+    }
+    if (tid < kKeyTile) {
+      const int64_t R = static_cast<int64_t>(T) * kKeyTile + tid;
+      rs = (R >= r_lo && R < r_hi) ? st[R] : make_float4(FLT_MAX, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&](int slot) {
+    if (stager) {
+      *reinterpret_cast<u32x4*>(q_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rq;
+      *reinterpret_cast<u32x4*>(d_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rd;
+      *reinterpret_cast<u32x4*>(qt_lds + slot * kTT + t_dim * kTRow + 8 * t_c) = tq;
+      *reinterpret_cast<u32x4*>(dt_lds + slot * kTT + t_dim * kTRow + 8 * t_c) = td;
+    }
+    if (tid < kKeyTile) st_lds[slot * kKeyTile + tid] = rs;
+  };
+
+  f32x16 dk[VB], dv[VB];
+#pragma unroll
+  for (int x = 0; x < VB; ++x) {
+    dk[x] = f32x16{};
+    dv[x] = f32x16{};
+  }
+  const int n_rt = t_end - t_beg;
+  if (n_rt > 0) {
+    load(t_beg);
+    store(0);
+  }
+  if (n_rt > 1) load(t_beg + 1);
+  for (int rt = 0; rt < n_rt; ++rt) {
+    __syncthreads();  // tile rt stored; every wave is done with tile rt - 1
+    if (rt + 1 < n_rt) store((rt + 1) & 1);
+    if (rt + 2 < n_rt) load(t_beg + rt + 2);
+    if (!wave_on) continue;
+    const int slot = rt & 1;
+    const uint16_t* ql = q_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
+    const uint16_t* dl = d_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ql + 16 * ks), kb[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dl + 16 * ks), vb[ks], dp, 0, 0, 0);
+    }
+    const uint16_t* qt = qt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
+    const uint16_t* dt = dt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile, for this key
+      float pg[8], ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * ks + i;
+        const float4 sr = st_lds[slot * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3)];
+        const float x = sr.z * __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sr.x));
+        pg[i] = x;
+        ds[i] = x * (dp[r] - sr.y);
+      }
+      const bf16x8 pb = pack8(pg);
+      const bf16x8 sb = pack8(ds);
+#pragma unroll
+      for (int x = 0; x < VB; ++x) {
+        dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dt + x * 32 * kTRow + 16 * ks), pb, dv[x], 0, 0, 0);
+        dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qt + x * 32 * kTRow + 16 * ks), sb, dk[x], 0, 0, 0);
+      }
+    }
+  }
+  if (!dk_row) return;
+#pragma unroll
+  for (int x = 0; x < VB; ++x)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int d = 32 * x + 8 * rb + 4 * half;
+      *reinterpret_cast<float4*>(dk_row + d) =
+          make_float4(f.scale * dk[x][4 * rb], f.scale * dk[x][4 * rb + 1], f.scale * dk[x][4 * rb + 2],
+                      f.scale * dk[x][4 * rb + 3]);
+      *reinterpret_cast<float4*>(dv_row + d) =
+          make_float4(dv[x][4 * rb], dv[x][4 * rb + 1], dv[x][4 * rb + 2], dv[x][4 * rb + 3]);
+    }
+}
+
+#define SSA_ROWS_LDS(D)                                                   \
+  __shared__ __align__(16) uint16_t q_lds[2 * kKeyTile * ((D) + 8)];    \
+  __shared__ __align__(16) uint16_t d_lds[2 * kKeyTile * ((D) + 8)];    \
+  __shared__ __align__(16) uint16_t qt_lds[2 * (D) * kTRow];            \
+  __shared__ __align__(16) uint16_t dt_lds[2 * (D) * kTRow];            \
+  __shared__ float4 st_lds[2 * kKeyTile]
+
+// Pooled-row gradients: a workgroup owns 128 blocks (a 32-block tile per
+// wave) of one sequence and group, over split z of the sequence's rows.
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+cmp_dkv_mfma_kernel(BwdParams p) {
+  SSA_ROWS_LDS(D);
+  const FwdParams& f = p.f;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const int G = f.h_q / f.h_kv;
   const int tile = blockIdx.x;
@@ -291,141 +497,57 @@ cmp_dkv_mfma_kernel(BwdParams p) {
   const bool wave_on = kt < (j1 + kKeyTile - 1) / kKeyTile;
   const int j = kt * kKeyTile + (lane & 31);
   const bool jok = wave_on && j >= j0 && j < j1;
-  // B operands: the lane's pooled key and value rows
-  bf16x8 kb[KS], vb[KS];
-  {
-    const uint16_t* KB = static_cast<const uint16_t*>(f.kbar) + (static_cast<int64_t>(g) * f.nb_cap + j) * D;
-    const uint16_t* VBR = static_cast<const uint16_t*>(f.vbar) + (static_cast<int64_t>(g) * f.nb_cap + j) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-      if (wave_on) {
-        a = *reinterpret_cast<const u32x4*>(KB + 16 * ks + 8 * half);
-        c = *reinterpret_cast<const u32x4*>(VBR + 16 * ks + 8 * half);
-      }
-      kb[ks] = __builtin_bit_cast(bf16x8, a);
-      vb[ks] = __builtin_bit_cast(bf16x8, c);
-    }
-  }
-  const float c2 = f.scale * kLog2e;
-  const int R = (s1 - s0) * G;               // (query, head of the group) rows of the sequence
-  // this workgroup's share of the row tiles (split z of row_splits)
-  const int n_all = (R + kKeyTile - 1) / kKeyTile;
+  const int64_t krow = (static_cast<int64_t>(g) * f.nb_cap + j) * D;
+  const int64_t r_lo = static_cast<int64_t>(s0) * G, r_hi = static_cast<int64_t>(s1) * G;
+  const int T0 = static_cast<int>(r_lo / kKeyTile);
+  const int n_all = static_cast<int>((r_hi + kKeyTile - 1) / kKeyTile) - T0;
   const int per = (n_all + p.row_splits - 1) / p.row_splits;
-  const int rt0 = min(n_all, static_cast<int>(blockIdx.z) * per);
-  const int n_rt = min(n_all, rt0 + per) - rt0;
-  const uint16_t* Q = static_cast<const uint16_t*>(f.q);
-  const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
-  const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
-
-  // staging: thread tid moves chunk tid of the query rows and of the
-  // output-gradient rows; threads below 32 also the row's statistics
-  const bool stager = tid < kRowCh;
-  const int r_row = tid / (D / 8), r_c = tid % (D / 8);
-  const int pos = mfma_pos(r_row);
-  u32x4 rq = {0u, 0u, 0u, 0u}, rd = {0u, 0u, 0u, 0u};
-  float4 rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
-  auto load = [&](int rt) {
-    rt += rt0;
-    if (stager) {
-      const int rr = rt * kKeyTile + r_row;
-      rq = u32x4{0u, 0u, 0u, 0u};
-      rd = u32x4{0u, 0u, 0u, 0u};
-      if (rr < R) {
-        const int64_t qrow = static_cast<int64_t>(f.perm[s0 + rr / G]) * f.h_q + g * G + rr % G;
-        rq = *reinterpret_cast<const u32x4*>(Q + qrow * D + 8 * r_c);
-        rd = *reinterpret_cast<const u32x4*>(dO + qrow * D + 8 * r_c);
-      }
-    }
-    if (tid < kKeyTile) {
-      const int rr = rt * kKeyTile + tid;
-      rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);   // a missing row has P = 0
-      if (rr < R) {
-        const int64_t qrow = static_cast<int64_t>(f.perm[s0 + rr / G]) * f.h_q + g * G + rr % G;
-        rs = make_float4(p.lse[qrow] * kLog2e, p.delta[qrow], bf16_bits_to_f32(gates[qrow * 3]), 0.f);
-      }
-    }
-  };
-  auto store = [&](int slot) {
-    if (stager) {
-      *reinterpret_cast<u32x4*>(q_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rq;
-      *reinterpret_cast<u32x4*>(d_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rd;
-      uint16_t* qt = qt_lds + slot * kTT + (8 * r_c) * kTRow + pos;
-      uint16_t* dt = dt_lds + slot * kTT + (8 * r_c) * kTRow + pos;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qt[(2 * e) * kTRow] = static_cast<uint16_t>(rq[e] & 0xFFFFu);
-        qt[(2 * e + 1) * kTRow] = static_cast<uint16_t>(rq[e] >> 16);
-        dt[(2 * e) * kTRow] = static_cast<uint16_t>(rd[e] & 0xFFFFu);
-        dt[(2 * e + 1) * kTRow] = static_cast<uint16_t>(rd[e] >> 16);
-      }
-    }
-    if (tid < kKeyTile) st_lds[slot * kKeyTile + tid] = rs;
-  };
-
-  f32x16 dk[VB], dv[VB];
-#pragma unroll
-  for (int x = 0; x < VB; ++x) {
-    dk[x] = f32x16{};
-    dv[x] = f32x16{};
-  }
-  if (n_rt > 0) {
-    load(0);
-    store(0);
-  }
-  if (n_rt > 1) load(1);
-  for (int rt = 0; rt < n_rt; ++rt) {
-    __syncthreads();  // tile rt stored; every wave is done with tile rt - 1
-    if (rt + 1 < n_rt) store((rt + 1) & 1);
-    if (rt + 2 < n_rt) load(rt + 2);
-    if (!wave_on) continue;
-    const int slot = rt & 1;
-    const uint16_t* ql = q_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
-    const uint16_t* dl = d_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ql + 16 * ks), kb[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dl + 16 * ks), vb[ks], dp, 0, 0, 0);
-    }
-    // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile, for this block
-    float pg[16], ds[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float4 st = st_lds[slot * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3)];
-      const float x = st.z * __builtin_amdgcn_exp2f(fmaf(s[r], c2, -st.x));
-      pg[r] = x;
-      ds[r] = x * (dp[r] - st.y);
-    }
-    const uint16_t* qt = qt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
-    const uint16_t* dt = dt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = pack8(pg + 8 * ks);
-      const bf16x8 sb = pack8(ds + 8 * ks);
-#pragma unroll
-      for (int x = 0; x < VB; ++x) {
-        dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dt + x * 32 * kTRow + 16 * ks), pb, dv[x], 0, 0, 0);
-        dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qt + x * 32 * kTRow + 16 * ks), sb, dk[x], 0, 0, 0);
-      }
-    }
-  }
-  if (!jok) return;
+  const int t_beg = T0 + min(n_all, static_cast<int>(blockIdx.z) * per);
+  const int t_end = T0 + min(n_all, static_cast<int>(blockIdx.z + 1) * per);
   const int64_t part = p.row_splits > 1 ? static_cast<int64_t>(blockIdx.z) * f.h_kv * f.nb_cap * D : 0;
   float* ok = (p.row_splits > 1 ? p.dkbar_part : p.dkbar) + part;
   float* ov = (p.row_splits > 1 ? p.dvbar_part : p.dvbar) + part;
-  const int64_t o = (static_cast<int64_t>(g) * f.nb_cap + j) * D;
-#pragma unroll
-  for (int x = 0; x < VB; ++x)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int d = 32 * x + 8 * rb + 4 * half;
-      *reinterpret_cast<float4*>(ok + o + d) =
-          make_float4(f.scale * dk[x][4 * rb], f.scale * dk[x][4 * rb + 1], f.scale * dk[x][4 * rb + 2],
-                      f.scale * dk[x][4 * rb + 3]);
-      *reinterpret_cast<float4*>(ov + o + d) =
-          make_float4(dv[x][4 * rb], dv[x][4 * rb + 1], dv[x][4 * rb + 2], dv[x][4 * rb + 3]);
-    }
+  rows_dkv_body<D>(p, g, wave_on, wave_on ? static_cast<const uint16_t*>(f.kbar) + krow : nullptr,
+                   static_cast<const uint16_t*>(f.vbar) + krow, r_lo, r_hi, t_beg, t_end,
+                   p.st_rows + static_cast<int64_t>(g) * p.rows_cap, jok ? ok + krow : nullptr,
+                   ov + krow, q_lds, d_lds, qt_lds, dt_lds, st_lds);
+}
+
+// Window tokens' key / value gradients (first writer of dk_acc / dv_acc): a
+// workgroup owns 128 tokens (a 32-token tile per wave) of one window and
+// group, over all the window's rows; persistent grid over (group, window,
+// 128-token chunk).
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+win_dkv_mfma_kernel(BwdParams p) {
+  SSA_ROWS_LDS(D);
+  const FwdParams& f = p.f;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int G = f.h_q / f.h_kv;
+  const int nw = f.counts[SSA_COUNT_NW];
+  const int cmax = (f.counts[SSA_COUNT_MAX_WIN] + 4 * kKeyTile - 1) / (4 * kKeyTile);
+  const int64_t per_g = static_cast<int64_t>(nw) * cmax;
+  for (int64_t item = blockIdx.x; item < per_g * f.h_kv; item += gridDim.x) {
+    const int g = static_cast<int>(item / per_g);
+    const int w = static_cast<int>((item % per_g) / cmax);
+    const int c = static_cast<int>(item % cmax);
+    const int wa = f.win_off[w], wb = f.win_off[w + 1];
+    if (wa + 4 * kKeyTile * c >= wb) continue;
+    const int i0 = wa + 4 * kKeyTile * c + kKeyTile * wv;
+    const bool wave_on = i0 < wb;
+    const int i = i0 + (lane & 31);
+    const bool iok = wave_on && i < wb;
+    const int64_t krow = (static_cast<int64_t>(g) * f.n + i) * D;
+    const int64_t r_lo = static_cast<int64_t>(wa) * G, r_hi = static_cast<int64_t>(wb) * G;
+    const int T0 = static_cast<int>(r_lo / kKeyTile);
+    const int T1 = static_cast<int>((r_hi + kKeyTile - 1) / kKeyTile);
+    rows_dkv_body<D>(p, g, wave_on, iok ? static_cast<const uint16_t*>(f.k_s) + krow : nullptr,
+                     static_cast<const uint16_t*>(f.v_s) + krow, r_lo, r_hi, T0, T1,
+                     p.st_rows + (static_cast<int64_t>(f.h_kv) + g) * p.rows_cap,
+                     iok ? p.dk_acc + krow : nullptr, p.dv_acc + krow, q_lds, d_lds, qt_lds, dt_lds, st_lds);
+    __syncthreads();  // the ring is reused by the next item
+  }
 }
 
 // the pooled-row gradients: the row splits' partial sums, in split order
@@ -788,8 +910,16 @@ hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 }
 
 hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  if (p.f.d == 32) kv_grad_mfma_kernel<32, kWindow><<<4096, 256, 0, stream>>>(p);
-  else kv_grad_mfma_kernel<64, kWindow><<<4096, 256, 0, stream>>>(p);
+  if (p.f.d == 32) win_dkv_mfma_kernel<32><<<4096, 256, 0, stream>>>(p);
+  else win_dkv_mfma_kernel<64><<<4096, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rows_prep(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(p.f.h_kv) * (p.rows_cap / kKeyTile);
+  const int grid = static_cast<int>(std::min<int64_t>(items, 8192));
+  if (p.f.d == 32) rows_prep_kernel<32><<<grid, 256, 0, stream>>>(p);
+  else rows_prep_kernel<64><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -180,6 +180,14 @@ struct BwdParams {
   int32_t* btile_pre;   // [batch + 1] prefix of 128-block chunks per sequence
   int32_t max_qtiles;   // grid bounds of the two
   int32_t max_btiles;
+  // (query, head) rows of each group in sorted order: row R = i * G + hh is
+  // query head g * G + hh of the token at sorted position i
+  int32_t rows_cap;     // n * G rounded up to 32
+  void* q_rows;         // [h_kv][rows_cap][D] Q rows (bf16)
+  void* do_rows;        // [h_kv][rows_cap][D] dO rows
+  void* q_rt;           // [h_kv][rows_cap / 32][D][32] the same, 32-row tiles transposed
+  void* do_rt;
+  float4* st_rows;      // [2][h_kv][rows_cap] (log2 lse, Delta, gate) of the compressed / window branch
   int32_t row_splits;   // the pooled-row gradients are summed over this many row ranges
   float* dkbar_part;    // [row_splits][h_kv][nb_cap][D] partial sums (row_splits > 1)
   float* dvbar_part;
@@ -214,6 +222,7 @@ hipError_t launch_bwd_cmp_dkv_mfma(const BwdParams& p, ssa_dtype dtype, hipStrea
 hipError_t launch_bwd_win_dq_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_bwd_rows_prep(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
