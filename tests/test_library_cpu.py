@@ -134,3 +134,52 @@ def test_binding_raises_without_gpu_tensors():
     with pytest.raises(ValueError):
         ssa.build_blocks(torch.zeros((4, 3), dtype=torch.int32), torch.tensor([0, 4], dtype=torch.int32),
                          8, 2, 4)
+
+
+def _bwd(L, attn, blocks=True, ptr=0x1000, lse=True, ws=None, ws_bytes=0, timed=False):
+    st = _fake_blocks()
+    p = ctypes.c_void_p(ptr)
+    args = (ctypes.byref(st) if blocks else None, ctypes.byref(attn), p, p, p, p, p, p,
+            p if lse else None, p, p, p, None, ws, ws_bytes, None)
+    if timed:
+        return L.ssa_backward_timed(*args, None, None)
+    return L.ssa_backward(*args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), B.SSA_ERR_UNSUPPORTED),
+    (dict(topk=0), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(h_q=16, h_kv=3), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.SSA_ERR_INVALID_ARGUMENT),
+])
+def test_backward_rejects_bad_layout(kw, status):
+    L = _lib()
+    assert _bwd(L, _attn(**kw)) == status
+    assert L.ssa_last_error()
+
+
+def test_backward_rejects_null_inputs_and_small_workspace():
+    L = _lib()
+    assert _bwd(L, _attn(), blocks=False) == B.SSA_ERR_INVALID_ARGUMENT
+    assert _bwd(L, _attn(), ptr=0) == B.SSA_ERR_INVALID_ARGUMENT
+    assert _bwd(L, _attn(), lse=False) == B.SSA_ERR_INVALID_ARGUMENT
+    assert _bwd(L, _attn()) == B.SSA_ERR_WORKSPACE
+    assert _bwd(L, _attn(), timed=True) == B.SSA_ERR_INVALID_ARGUMENT   # no stage_ms
+    st = _fake_blocks(n=1000, nb=50)
+    a = _attn()
+    need = L.ssa_backward_workspace(ctypes.byref(st), ctypes.byref(a))
+    # float32 dq accumulator plus the sorted-order dk / dv accumulators at least
+    assert need >= 4 * 1000 * 16 * 64 * 3
+    assert L.ssa_backward_stage_name(ctypes.byref(a), 0) == b"pool_kernel"
+    assert L.ssa_backward_stage_name(ctypes.byref(a), 99) == b""
+
+
+def test_forward_train_needs_its_outputs():
+    L = _lib()
+    st = _fake_blocks()
+    p = ctypes.c_void_p(0x1000)
+    a = _attn()
+    assert L.ssa_forward_train(ctypes.byref(st), ctypes.byref(a), p, p, p, p, p, None, p, p, 1 << 40,
+                               None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert L.ssa_forward_train(ctypes.byref(st), ctypes.byref(a), p, p, p, p, p, p, None, p, 1 << 40,
+                               None) == B.SSA_ERR_INVALID_ARGUMENT
