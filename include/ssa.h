@@ -50,11 +50,17 @@ typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
 
 /* Grid and block geometry.  grid_res (R), m_cmp and m_win are powers of two
  * with m_cmp <= m_win <= R <= 1024.  Blocks are the m_cmp^3 cells and windows
- * the m_win^3 cells of the grid, both aligned to the origin. */
+ * the m_win^3 cells of the grid, both aligned to the origin
+ * (Direct3D-S2 page, "Method": non-overlapping windows).  win_shift = 0
+ * keeps them so; a win_shift that is a multiple of m_cmp in (0, m_win) moves
+ * the window origin to -win_shift on every axis (the shifted windows of the
+ * same page's sparse VAE; m_win / 2 is the usual choice).  Blocks do not
+ * move, since the shift is a whole number of blocks. */
 typedef struct {
   int32_t grid_res;
   int32_t m_cmp;
   int32_t m_win;
+  int32_t win_shift;
 } ssa_geometry;
 
 /* Device-side counters written by ssa_build_blocks (int32 each). */

@@ -75,7 +75,7 @@ def _log2_exact(v: int) -> int:
     return v.bit_length() - 1
 
 
-def block_keys(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int):
+def block_keys(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int, shift: int = 0):
     """Hierarchical block key of every token (input order), plus validity.
 
     key = ((seq * Rw^3 + lin(w)) * r^3 + lin(s)) with w = floor(c / m_win),
@@ -83,20 +83,28 @@ def block_keys(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int):
     lin(x, y, z) = (x * n + y) * n + z.  Sorting by this key groups tokens by
     sequence, then window, then block (Direct3D-S2 page, "Method": blocking by
     3D coordinate; non-overlapping windows).
+
+    ``shift`` (a multiple of m_cmp below m_win) moves the window origin by
+    -shift on every axis, as in shifted-window attention (Direct3D-S2 page,
+    "Method", the sparse VAE's shifted windows): the coordinates are taken as
+    c + shift on a grid with one more window per axis.  Blocks stay the same
+    cells, since shift is a whole number of blocks.
     """
     coords = np.asarray(coords, dtype=np.int64).reshape(-1, 3)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     n = coords.shape[0]
     if m_win % m_cmp:
         raise ValueError("m_win must be a multiple of m_cmp")
-    Rw = grid_res // m_win
+    if shift % m_cmp or not 0 <= shift < m_win:
+        raise ValueError("shift must be a multiple of m_cmp in [0, m_win)")
+    Rw = grid_res // m_win + (1 if shift else 0)
     r = m_win // m_cmp
     seq = np.zeros(n, dtype=np.int64)
     for b in range(len(cu) - 1):
         seq[cu[b]:cu[b + 1]] = b
     valid = np.all((coords >= 0) & (coords < grid_res), axis=1)
-    w = coords // m_win
-    s = (coords // m_cmp) % r
+    w = (coords + shift) // m_win
+    s = ((coords + shift) // m_cmp) % r
     lin_w = (w[:, 0] * Rw + w[:, 1]) * Rw + w[:, 2]
     lin_s = (s[:, 0] * r + s[:, 1]) * r + s[:, 2]
     key = (seq * Rw ** 3 + lin_w) * r ** 3 + lin_s
@@ -124,9 +132,9 @@ class Blocks:
         return len(self.win_off) - 1
 
 
-def build_blocks(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int) -> Blocks:
+def build_blocks(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int, shift: int = 0) -> Blocks:
     """Stable sort of tokens by block key and the CSR segments over it."""
-    key, valid = block_keys(coords, cu_seqlens, grid_res, m_cmp, m_win)
+    key, valid = block_keys(coords, cu_seqlens, grid_res, m_cmp, m_win, shift)
     n = len(key)
     r3 = (m_win // m_cmp) ** 3
     perm = np.argsort(key, kind="stable")
@@ -144,7 +152,7 @@ def build_blocks(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int) -> B
     blk_id_of_pos = np.cumsum(new_blk) - 1
     win_blk_off = np.append(blk_id_of_pos[win_start], len(blk_start))
     # sequence of each block / window (the key's top part)
-    Rw3 = (grid_res // m_win) ** 3
+    Rw3 = (grid_res // m_win + (1 if shift else 0)) ** 3
     seq_of_blk = ks[blk_start] // (Rw3 * r3)
     seq_of_win = ks[win_start] // (Rw3 * r3)
     B = len(cu_seqlens) - 1
@@ -296,7 +304,8 @@ def forward(wl, blocks: Blocks | None = None, with_branches=False):
     and optionally the per-branch outputs.
     """
     if blocks is None:
-        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win,
+                              getattr(wl, "win_shift", 0))
     kbar = pool_blocks(wl.k, blocks, wl.dtype)
     vbar = pool_blocks(wl.v, blocks, wl.dtype)
     N, H, Hkv = wl.n_tokens, wl.h_q, wl.h_kv
@@ -347,7 +356,8 @@ def backward(wl, dout, blocks: Blocks | None = None, rows=None):
     rows, which depend on nothing else.
     """
     if blocks is None:
-        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win,
+                              getattr(wl, "win_shift", 0))
     H, Hkv, D, K = wl.h_q, wl.h_kv, wl.head_dim, wl.topk
     G = H // Hkv
     N = wl.n_tokens

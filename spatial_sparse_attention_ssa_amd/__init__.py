@@ -82,10 +82,13 @@ class Blocks:
 
 
 def build_blocks(coords: torch.Tensor, cu_seqlens: torch.Tensor, grid_res: int, m_cmp: int,
-                 m_win: int, sync: bool = True, workspace: torch.Tensor | None = None) -> Blocks:
+                 m_win: int, sync: bool = True, workspace: torch.Tensor | None = None,
+                 win_shift: int = 0) -> Blocks:
     """Sort tokens by 3D block key and build the block / window segments.
 
     coords: int32 [N, 3] on the GPU; cu_seqlens: int32 [B + 1] on the GPU.
+    ``win_shift`` (a multiple of m_cmp below m_win) moves the window origin
+    to -win_shift on every axis (shifted windows).
     """
     if coords.dtype != torch.int32 or cu_seqlens.dtype != torch.int32:
         raise TypeError("coords and cu_seqlens must be int32")
@@ -97,7 +100,7 @@ def build_blocks(coords: torch.Tensor, cu_seqlens: torch.Tensor, grid_res: int, 
     n = int(coords.shape[0])
     batch = int(cu_seqlens.shape[0]) - 1
     dev = coords.device
-    geo = B.SsaGeometry(grid_res, m_cmp, m_win)
+    geo = B.SsaGeometry(grid_res, m_cmp, m_win, win_shift)
     i32 = dict(dtype=torch.int32, device=dev)
     perm = torch.empty(max(n, 1), **i32)
     blk_off = torch.empty(n + 1, **i32)

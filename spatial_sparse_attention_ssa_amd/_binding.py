@@ -51,7 +51,8 @@ EXPORTED = (
 
 
 class SsaGeometry(ctypes.Structure):
-    _fields_ = [("grid_res", ctypes.c_int32), ("m_cmp", ctypes.c_int32), ("m_win", ctypes.c_int32)]
+    _fields_ = [("grid_res", ctypes.c_int32), ("m_cmp", ctypes.c_int32), ("m_win", ctypes.c_int32),
+                ("win_shift", ctypes.c_int32)]
 
 
 class SsaBlocks(ctypes.Structure):

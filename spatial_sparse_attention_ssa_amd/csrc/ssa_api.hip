@@ -54,6 +54,9 @@ ssa_status check_geometry(const ssa_geometry* geo) {
   if (geo->m_cmp > geo->m_win || geo->m_win > geo->grid_res)
     return fail(SSA_ERR_INVALID_ARGUMENT, "need m_cmp <= m_win <= grid_res (got %d, %d, %d)",
                 geo->m_cmp, geo->m_win, geo->grid_res);
+  if (geo->win_shift < 0 || geo->win_shift >= geo->m_win || geo->win_shift % geo->m_cmp)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "win_shift %d must be a multiple of m_cmp (%d) in [0, m_win = %d)",
+                geo->win_shift, geo->m_cmp, geo->m_win);
   return SSA_OK;
 }
 
@@ -61,8 +64,10 @@ ssa::KeyLayout key_layout(const ssa_geometry* geo, int32_t batch) {
   ssa::KeyLayout kl;
   kl.l_win = ilog2(geo->m_win);
   kl.l_cmp = ilog2(geo->m_cmp);
-  kl.l_rw = ilog2(geo->grid_res) - kl.l_win;
+  // a shifted window grid has one more window per axis
+  kl.l_rw = ilog2(geo->grid_res) - kl.l_win + (geo->win_shift ? 1 : 0);
   kl.l_r = kl.l_win - kl.l_cmp;
+  kl.shift = geo->win_shift;
   kl.seq_bits = ceil_log2(batch);
   kl.key_bits = kl.seq_bits + 3 * (kl.l_rw + kl.l_r);
   kl.grid_res = geo->grid_res;

@@ -69,6 +69,7 @@ keys_kernel(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, 
   if (bad) atomicAdd(&counts[SSA_COUNT_INVALID], 1);
   const uint32_t rmask = (1u << kl.l_r) - 1u;
   uint64_t key = static_cast<uint64_t>(lo);
+  for (int a = 0; a < 3; ++a) c[a] += kl.shift;   // shifted windows: cells of c + shift
   for (int a = 0; a < 3; ++a) key = (key << kl.l_rw) | static_cast<uint32_t>(c[a] >> kl.l_win);
   for (int a = 0; a < 3; ++a) key = (key << kl.l_r) | (static_cast<uint32_t>(c[a] >> kl.l_cmp) & rmask);
   keys[t] = static_cast<uint32_t>(key);

@@ -66,6 +66,7 @@ struct KeyLayout {
   int seq_bits;  // ceil(log2(B))
   int key_bits;  // seq_bits + 3 * (l_rw + l_r)
   int grid_res;
+  int shift;     // window origin at -shift per axis (a multiple of m_cmp), 0 = unshifted
 };
 
 struct BuildWorkspace {

@@ -33,7 +33,11 @@ def to_dev(a, dtype):
 
 def gpu_build(wl, sync=True):
     return ssa.build_blocks(to_dev(wl.coords, torch.int32), to_dev(wl.cu_seqlens, torch.int32),
-                            wl.grid_res, wl.m_cmp, wl.m_win, sync=sync)
+                            wl.grid_res, wl.m_cmp, wl.m_win, sync=sync, win_shift=wl.win_shift)
+
+
+def oracle_blocks(wl):
+    return oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win, wl.win_shift)
 
 
 def gpu_forward(wl, blocks, gates=None, **kw):

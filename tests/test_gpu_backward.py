@@ -57,7 +57,7 @@ def _compare(name, got, ref, dtype):
 
 
 def _full_compare(wl, seed, one_hot=False):
-    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    ob = P.oracle_blocks(wl)
     gb = P.gpu_build(wl)
     dout = _dout(wl, seed)
     ref_fwd = oracle.forward(wl, blocks=ob)
@@ -88,6 +88,12 @@ def test_small_backward_full(case):
     wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],
                      h_kv=case["h_kv"], head_dim=case["head_dim"], dtype=case["dtype"], seed=23)
     _full_compare(wl, seed=5, one_hot=case["h_q"] == 4 and case["h_kv"] == 4)
+
+
+def test_shifted_windows_backward_full():
+    wl = make_custom([800, 333], grid_res=64, n_prims=3, topk=8, h_q=4, h_kv=4, head_dim=64,
+                     dtype="bf16", seed=29, win_shift=4)
+    _full_compare(wl, seed=6)
 
 
 def test_zero_output_gradient():
@@ -132,7 +138,7 @@ def _sequence_sums(wl, grads, dout):
 def test_large_workload_backward(cfg, n_rows):
     wl = make_workload(cfg)
     print(f"workload {cfg}: N={wl.n_tokens}", flush=True)
-    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    ob = P.oracle_blocks(wl)
     gb = P.gpu_build(wl)
     dout = _dout(wl, cfg)
     saved, grads = _gpu_grads(wl, gb, dout)

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _oracle_blocks(wl):
-    return oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    return P.oracle_blocks(wl)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -30,9 +30,9 @@ def test_named_workload_build_bit_exact(cfg):
     P.check_build(gb, _oracle_blocks(wl))
 
 
-def _custom(coords, cu, R=64, m_cmp=4, m_win=8):
+def _custom(coords, cu, R=64, m_cmp=4, m_win=8, win_shift=0):
     return make_custom(None, coords=np.asarray(coords), cu_seqlens=cu, grid_res=R, m_cmp=m_cmp,
-                       m_win=m_win, h_q=1, h_kv=1, head_dim=32)
+                       m_win=m_win, h_q=1, h_kv=1, head_dim=32, win_shift=win_shift)
 
 
 @pytest.mark.parametrize("case", ["one_block", "voxel_blocks", "duplicates", "empty_seqs",
@@ -60,6 +60,24 @@ def test_adversarial_build(case):
     else:
         coords = rng.integers(0, 16, size=(4097, 3))
         wl = _custom(coords, [0, 4097], R=16, m_cmp=4, m_win=16)
+    gb = P.gpu_build(wl)
+    P.check_build(gb, _oracle_blocks(wl))
+
+
+@pytest.mark.parametrize("R,m_cmp,m_win,shift", [(64, 4, 8, 4), (32, 2, 8, 2), (32, 2, 8, 6), (1024, 4, 8, 4)])
+def test_shifted_window_build_bit_exact(R, m_cmp, m_win, shift):
+    rng = np.random.default_rng(R + shift)
+    n = 20000
+    coords = rng.integers(0, R, size=(n, 3))
+    cuts = np.sort(rng.integers(0, n, size=3))
+    wl = _custom(coords, np.concatenate([[0], cuts, [n]]), R=R, m_cmp=m_cmp, m_win=m_win, win_shift=shift)
+    gb = P.gpu_build(wl)
+    P.check_build(gb, _oracle_blocks(wl))
+
+
+def test_shifted_window_build_of_the_headline_geometry():
+    wl = make_workload(3, with_tensors=False)
+    wl.win_shift = wl.m_win // 2
     gb = P.gpu_build(wl)
     P.check_build(gb, _oracle_blocks(wl))
 

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _full_compare(wl, branches=True):
-    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    ob = P.oracle_blocks(wl)
     gb = P.gpu_build(wl)
     P.check_build(gb, ob)
     res = P.gpu_forward(wl, gb, return_topk=True, return_pooled=True)
@@ -70,12 +70,29 @@ def test_small_full(case):
     _full_compare(wl)
 
 
+@pytest.mark.parametrize("case", [
+    dict(seqs=[1500, 0, 700], h_q=4, h_kv=4, head_dim=64, topk=16),
+    dict(seqs=[900, 400], h_q=16, h_kv=1, head_dim=32, topk=8),
+])
+def test_shifted_windows_full(case):
+    # window origin at -m_win / 2 on every axis (shifted windows)
+    wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],
+                     h_kv=case["h_kv"], head_dim=case["head_dim"], dtype="bf16", seed=41, win_shift=4)
+    _full_compare(wl)
+
+
+def test_shifted_windows_headline_sampled():
+    wl = make_workload(3)
+    wl.win_shift = wl.m_win // 2
+    _sampled_check(wl, P.sample_rows(wl, 200, seed=33), tag="workload 3, shifted windows")
+
+
 def test_tiny_fp32_workload_full():
     _full_compare(make_workload(1))
 
 
 def _sampled_check(wl, rows, branches=True, min_agree=0.99, tag=""):
-    ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
+    ob = P.oracle_blocks(wl)
     gb = P.gpu_build(wl)
     P.check_build(gb, ob)
     res = P.gpu_forward(wl, gb, return_topk=True)

@@ -53,7 +53,8 @@ def _build(L, n=100, batch=1, geo=(64, 4, 8), ws=None, ws_bytes=0, out=True, coo
                               ctypes.byref(st) if out else None, 1, ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("geo", [(63, 4, 8), (64, 3, 8), (64, 8, 4), (2048, 4, 8), (64, 4, 128)])
+@pytest.mark.parametrize("geo", [(63, 4, 8), (64, 3, 8), (64, 8, 4), (2048, 4, 8), (64, 4, 128),
+                                 (64, 4, 8, 2), (64, 4, 8, 8), (64, 4, 8, -4), (64, 8, 8, 4)])
 def test_build_rejects_bad_geometry(geo):
     L = _lib()
     assert _build(L, geo=geo) == B.SSA_ERR_INVALID_ARGUMENT

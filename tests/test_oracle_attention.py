@@ -137,6 +137,23 @@ def test_window_branch_dense_per_window():
             np.testing.assert_allclose(res["o_win"][toks, h], ref, rtol=1e-10, atol=1e-12)
 
 
+def test_shifted_window_branch_is_dense_per_shifted_cell():
+    # windows start at -4 on every axis: group the tokens by ((c + 4) // 8)
+    # independently and compare with dense attention inside each group
+    wl = make_custom([500], grid_res=32, m_cmp=4, m_win=8, topk=2, h_q=2, h_kv=1, head_dim=8,
+                     dtype="f32", seed=12, win_shift=4)
+    res = oracle.forward(wl, with_branches=True)
+    cells = {}
+    for t, c in enumerate(wl.coords):
+        cells.setdefault(tuple((int(x) + 4) // 8 for x in c), []).append(t)
+    assert len(cells) == res["blocks"].nw
+    for toks in cells.values():
+        toks = np.array(toks)
+        for h in range(2):
+            ref = _dense(wl.q[toks, h], wl.k[toks, 0], wl.v[toks, 0])
+            np.testing.assert_allclose(res["o_win"][toks, h], ref, rtol=1e-10, atol=1e-12)
+
+
 # ---------------------------------------------------------------- closed forms
 
 def test_constant_values_give_constant_output():

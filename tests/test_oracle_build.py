@@ -25,14 +25,15 @@ def _random_tokens(rng, n, R, n_seq, dup_frac=0.1):
     return coords.astype(np.int32), cu
 
 
-def _brute_force(coords, cu, R, m_cmp, m_win):
+def _brute_force(coords, cu, R, m_cmp, m_win, shift=0):
     """Group by (seq, window cell, block cell) with plain Python; order groups
-    by (seq, window cell in x,y,z order, block cell in x,y,z order)."""
+    by (seq, window cell in x,y,z order, block cell in x,y,z order).  With
+    ``shift`` the window cells start at -shift on every axis."""
     groups = {}
     for b in range(len(cu) - 1):
         for t in range(cu[b], cu[b + 1]):
             c = tuple(int(x) for x in coords[t])
-            wcell = tuple(x // m_win for x in c)
+            wcell = tuple((x + shift) // m_win for x in c)
             bcell = tuple(x // m_cmp for x in c)
             groups.setdefault((b, wcell, bcell), []).append(t)
     keys = sorted(groups)
@@ -71,6 +72,44 @@ def test_brute_force_partition(seed):
     assert b.win_off.tolist() == [int(np.sum(sizes[:j])) for j in wstarts] + [n]
     B = len(cu) - 1
     assert b.seq_blk_off.tolist() == [sum(1 for s in seq_of_blk if s < q) for q in range(B + 1)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_brute_force_partition_with_shifted_windows(seed):
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.choice([8, 16, 32]))
+    m_cmp = int(rng.choice([1, 2, 4]))
+    m_win = min(m_cmp * int(rng.choice([2, 4])), R)
+    shift = m_cmp * int(rng.integers(1, m_win // m_cmp)) if m_win > m_cmp else 0
+    n = int(rng.integers(1, 300))
+    coords, cu = _random_tokens(rng, n, R, int(rng.integers(1, 5)))
+    b = oracle.build_blocks(coords, cu, R, m_cmp, m_win, shift)
+    perm, sizes, win_of_blk, seq_of_blk = _brute_force(coords, cu, R, m_cmp, m_win, shift)
+    assert b.perm.tolist() == perm
+    assert np.diff(b.blk_off).tolist() == sizes
+    wstarts = [0] + [j for j in range(1, len(sizes)) if win_of_blk[j] != win_of_blk[j - 1]]
+    assert b.win_blk_off.tolist() == wstarts + [len(sizes)]
+
+
+def test_shifted_windows_equal_translated_tokens():
+    # windows shifted by s on a grid R are the unshifted windows of the tokens
+    # moved by +s on a grid large enough to hold them; blocks do not move
+    rng = np.random.default_rng(9)
+    coords, cu = _random_tokens(rng, 400, 32, 3)
+    a = oracle.build_blocks(coords, cu, 32, 4, 8, 4)
+    t = oracle.build_blocks(coords + 4, cu, 64, 4, 8, 0)
+    for name in ("perm", "blk_off", "win_off", "win_blk_off", "seq_blk_off", "seq_win_off"):
+        assert np.array_equal(getattr(a, name), getattr(t, name)), name
+    z = oracle.build_blocks(coords, cu, 32, 4, 8, 0)
+    as_sets = lambda bl: sorted(tuple(sorted(bl.perm[bl.blk_off[j]:bl.blk_off[j + 1]])) for j in range(bl.nb))
+    assert as_sets(a) == as_sets(z)
+
+
+def test_bad_shift_is_rejected():
+    coords, cu = np.zeros((2, 3), np.int32), [0, 2]
+    for shift in (2, 8, -4):
+        with pytest.raises(ValueError):
+            oracle.build_blocks(coords, cu, 16, 4, 8, shift)
 
 
 def test_invariants_on_surface_band():
