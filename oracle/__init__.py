@@ -29,6 +29,7 @@ from .ssa_oracle import (  # noqa: F401
     pool_blocks,
     softmax_attention,
     topk_blocks,
+    geometric_topk,
     forward,
     forward_rows,
     backward,

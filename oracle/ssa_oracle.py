@@ -22,6 +22,11 @@ Readings taken where the pages are silent (each listed in the design notes):
   k_eff = min(k, blocks in the sequence).  No block is forced, no causality.
 * Softmax scale 1/sqrt(D) in every branch.  Gates are used as given, in the
   order (compressed, selected, window).
+* Geometric routing (the optional 3D-aware selection): the distance from a
+  query voxel to a block is the smallest squared distance between the query's
+  voxel centre and the centres of the block's voxels; the k nearest blocks of
+  the sequence are selected, ties to the lower block id.  The compressed
+  branch is still computed; only the selection changes.
 * Backward: the top-k choice is held fixed (it is piecewise constant in Q and
   K, so it has no gradient), and the one rounding of the pooled blocks to the
   input dtype is differentiated as the identity; a pooled row's gradient is
@@ -210,6 +215,25 @@ def softmax_attention(q, k, v, scale: float):
     return p @ v, p
 
 
+def geometric_topk(coords, blocks: Blocks, t: int, j0: int, j1: int, k: int):
+    """The k blocks of [j0, j1) nearest to token t, nearest first.
+
+    LSRM article, "3D-aware block routing": a voxel token stands at its
+    voxel's centre, and a query selects the blocks whose points lie closest to
+    it in Euclidean distance (the shortest distance from the query to the
+    block's point set).  Distances between voxel centres are compared as exact
+    integer squared distances; ties go to the lower block id.
+    """
+    c = np.asarray(coords[t], dtype=np.int64)
+    d = np.empty(j1 - j0, dtype=np.int64)
+    for j in range(j0, j1):
+        toks = blocks.perm[blocks.blk_off[j]:blocks.blk_off[j + 1]]
+        diff = np.asarray(coords[toks], dtype=np.int64) - c
+        d[j - j0] = int((diff * diff).sum(axis=1).min())
+    order = np.lexsort((np.arange(j1 - j0), d))
+    return order[:min(k, j1 - j0)]
+
+
 def topk_blocks(score, k: int):
     """Indices of the k largest scores, largest first; ties to the lower index."""
     score = np.asarray(score, dtype=np.float64)
@@ -272,8 +296,12 @@ def forward_rows(wl, blocks: Blocks, rows, kbar=None, vbar=None, with_branches=F
             score += p_hh
             if hh == h:
                 o_cmp = o_hh
-        # (b) top-k blocks; attention over all their tokens
-        chosen = topk_blocks(score, K)
+        # (b) top-k blocks (by score, or by distance with geometric routing);
+        # attention over all their tokens
+        if getattr(wl, "routing", "score") == "geometric":
+            chosen = geometric_topk(wl.coords, blocks, t, j0, j1, K)
+        else:
+            chosen = topk_blocks(score, K)
         if with_scores:
             scores.append(score)
             firsts.append(j0)
@@ -388,10 +416,13 @@ def backward(wl, dout, blocks: Blocks | None = None, rows=None):
         g = h // G
         j0, j1 = int(blocks.seq_blk_off[b]), int(blocks.seq_blk_off[b + 1])
         # the selection, as in the forward
-        score = np.zeros(j1 - j0)
-        for hh in range(g * G, (g + 1) * G):
-            score += softmax_attention(f64(wl.q[t, hh]), kbar[j0:j1, g], vbar[j0:j1, g], scale)[1]
-        chosen = topk_blocks(score, K)
+        if getattr(wl, "routing", "score") == "geometric":
+            chosen = geometric_topk(wl.coords, blocks, t, j0, j1, K)
+        else:
+            score = np.zeros(j1 - j0)
+            for hh in range(g * G, (g + 1) * G):
+                score += softmax_attention(f64(wl.q[t, hh]), kbar[j0:j1, g], vbar[j0:j1, g], scale)[1]
+            chosen = topk_blocks(score, K)
         sel = blocks.perm[np.concatenate([np.arange(blocks.blk_off[j0 + c], blocks.blk_off[j0 + c + 1])
                                           for c in chosen])]
         win = blocks.perm[blocks.win_off[w]:blocks.win_off[w + 1]]

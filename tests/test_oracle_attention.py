@@ -259,3 +259,53 @@ def test_sequences_do_not_interact():
     np.testing.assert_array_equal(r2["out"][300:], r1["out"])
     nb = r1["blocks"].nb
     np.testing.assert_array_equal(r2["topk"][300:], r1["topk"] + nb)
+
+
+# ---------------------------------------------------------------- geometric routing
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_geometric_routing_brute_force(seed):
+    # every block's distance from scipy's pairwise distances, ranked with the
+    # block id as the tie break
+    from scipy.spatial.distance import cdist
+    rng = np.random.default_rng(seed)
+    coords = rng.integers(0, 24, size=(300, 3)).astype(np.int32)
+    b = oracle.build_blocks(coords, [0, 300], 32, 4, 8)
+    dist = cdist(coords.astype(np.float64), coords.astype(np.float64), "sqeuclidean")
+    blk_of = np.empty(300, np.int64)
+    for j in range(b.nb):
+        blk_of[b.perm[b.blk_off[j]:b.blk_off[j + 1]]] = j
+    for t in rng.integers(0, 300, size=40):
+        per_block = np.full(b.nb, np.inf)
+        np.minimum.at(per_block, blk_of, dist[t])
+        expect = sorted(range(b.nb), key=lambda j: (per_block[j], j))[:7]
+        got = oracle.geometric_topk(coords, b, int(t), 0, b.nb, 7)
+        assert got.tolist() == expect
+        assert got[0] == blk_of[t]          # the query's own block is nearest (distance 0)
+
+
+def test_geometric_routing_is_translation_invariant():
+    rng = np.random.default_rng(4)
+    coords = rng.integers(0, 16, size=(200, 3)).astype(np.int32)
+    a = oracle.build_blocks(coords, [0, 200], 32, 4, 8)
+    moved = coords + np.array([8, 16, 8], np.int32)
+    c = oracle.build_blocks(moved, [0, 200], 32, 4, 8)
+    for t in range(0, 200, 7):
+        assert np.array_equal(oracle.geometric_topk(coords, a, t, 0, a.nb, 5),
+                              oracle.geometric_topk(moved, c, t, 0, c.nb, 5))
+
+
+def test_geometric_routing_forward_uses_the_nearest_blocks():
+    wl = make_custom([400, 150], grid_res=32, topk=3, h_q=2, h_kv=1, head_dim=8, dtype="f32", seed=5,
+                     routing="geometric")
+    res = oracle.forward(wl, with_branches=True)
+    b = res["blocks"]
+    for t in (0, 77, 399, 549):
+        seq = 0 if t < 400 else 1
+        j0, j1 = int(b.seq_blk_off[seq]), int(b.seq_blk_off[seq + 1])
+        chosen = oracle.geometric_topk(wl.coords, b, t, j0, j1, 3) + j0
+        assert res["topk"][t, 0].tolist() == chosen.tolist()
+        toks = np.concatenate([b.perm[b.blk_off[j]:b.blk_off[j + 1]] for j in chosen])
+        for h in range(2):
+            np.testing.assert_allclose(res["o_sel"][t, h], _dense(wl.q[t:t + 1, h], wl.k[toks, 0], wl.v[toks, 0])[0],
+                                       rtol=1e-10, atol=1e-12)

@@ -41,6 +41,7 @@ class Workload:
     v: np.ndarray | None = None      # float32 [N, Hkv, D]
     gates: np.ndarray | None = None  # float32 [N, Hq, 3]  order: compressed, selected, window
     win_shift: int = 0               # window origin at -win_shift per axis (0: unshifted)
+    routing: str = "score"           # block selection: "score" or "geometric"
 
     @property
     def n_tokens(self) -> int:
@@ -136,7 +137,7 @@ def make_workload(cfg_id: int, with_tensors: bool = True) -> Workload:
 
 def make_custom(seq_tokens, *, grid_res=64, n_prims=3, m_cmp=4, m_win=8, topk=4,
                 h_q=2, h_kv=2, head_dim=32, dtype="bf16", seed=0, gates="sigmoid",
-                coords=None, cu_seqlens=None, win_shift=0) -> Workload:
+                coords=None, cu_seqlens=None, win_shift=0, routing="score") -> Workload:
     """A small workload: one surface-band shape per entry of ``seq_tokens``.
 
     ``coords``/``cu_seqlens`` may be given directly instead (adversarial
@@ -158,7 +159,7 @@ def make_custom(seq_tokens, *, grid_res=64, n_prims=3, m_cmp=4, m_win=8, topk=4,
         cu_seqlens = np.asarray(cu_seqlens, dtype=np.int32)
     wl = Workload(name="custom", grid_res=grid_res, m_cmp=m_cmp, m_win=m_win, topk=topk,
                   h_q=h_q, h_kv=h_kv, head_dim=head_dim, dtype=dtype, coords=coords,
-                  cu_seqlens=cu_seqlens, win_shift=win_shift)
+                  cu_seqlens=cu_seqlens, win_shift=win_shift, routing=routing)
     wl.q, wl.k, wl.v, wl.gates = _draw_tensors(len(coords), h_q, h_kv, head_dim, dtype,
                                                gates, seed * 1000 + 2)
     return wl
