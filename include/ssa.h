@@ -93,7 +93,23 @@ typedef struct {
   int32_t nb, nw;       /* host copies of the counts when synced, else -1                              */
   int32_t max_blk_tokens, max_win_tokens; /* host copies when synced, else -1                          */
   ssa_geometry geo;     /* filled by ssa_build_blocks                                                  */
+  const int32_t *coords;/* the [N, 3] coordinates given to ssa_build_blocks (set by it); read by the   */
+                        /* forward with geometric routing, so they must stay valid for such calls      */
 } ssa_blocks;
+
+/* Block selection rule (ssa_attn.routing). */
+typedef enum {
+  /* top-k blocks by compressed-attention probability, summed over the
+   * group's query heads (Direct3D-S2 page, "Method"; LSRM article) */
+  SSA_ROUTE_SCORE = 0,
+  /* top-k blocks by geometric distance (LSRM article, "3D-aware block
+   * routing"): the smallest squared distance between the query's voxel
+   * centre and the centres of the block's voxels, ties to the lower block id;
+   * the same for every key/value group.  bfloat16 layouts of the MFMA path
+   * only (D = 64 with one query head per key/value head, or 16 query heads
+   * per key/value head) */
+  SSA_ROUTE_GEOMETRIC = 1
+} ssa_routing;
 
 /* Attention layout.  h_q query heads over h_kv key/value heads (h_q % h_kv
  * == 0; query head h uses key/value head h / (h_q / h_kv)).  head_dim D in
@@ -106,6 +122,7 @@ typedef struct {
   int32_t topk;
   float scale;
   ssa_dtype dtype;
+  int32_t routing;      /* ssa_routing; 0 = by score */
 } ssa_attn;
 
 /* Workspace bytes ssa_build_blocks needs for N tokens in B sequences. */

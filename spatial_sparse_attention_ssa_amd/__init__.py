@@ -58,6 +58,7 @@ class Blocks:
     seq_win_off: torch.Tensor
     counts: torch.Tensor
     struct: B.SsaBlocks
+    coords: torch.Tensor | None = None   # kept alive: geometric routing reads it
 
     @property
     def n_tokens(self) -> int:
@@ -118,34 +119,43 @@ def build_blocks(coords: torch.Tensor, cu_seqlens: torch.Tensor, grid_res: int, 
     B.check(L.ssa_build_blocks(_ptr(coords), _ptr(cu_seqlens), n, batch, ctypes.byref(geo),
                                ctypes.byref(st), 1 if sync else 0, _ptr(workspace), ws_bytes,
                                _stream(dev)))
-    return Blocks(perm[:n], blk_off, win_off, win_blk_off, seq_blk_off, seq_win_off, counts, st)
+    return Blocks(perm[:n], blk_off, win_off, win_blk_off, seq_blk_off, seq_win_off, counts, st, coords)
 
 
 _DTYPES = {torch.bfloat16: B.SSA_BF16, torch.float32: B.SSA_F32}
 
 
-def _attn(q, k, topk, scale):
+_ROUTING = {"score": B.SSA_ROUTE_SCORE, "geometric": B.SSA_ROUTE_GEOMETRIC}
+
+
+def _attn(q, k, topk, scale, routing="score"):
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    if routing not in _ROUTING:
+        raise ValueError(f"routing must be one of {sorted(_ROUTING)}")
     return B.SsaAttn(h_q=int(q.shape[1]), h_kv=int(k.shape[1]), head_dim=int(q.shape[2]),
-                     topk=int(topk), scale=float(scale) if scale else 0.0, dtype=_DTYPES[q.dtype])
+                     topk=int(topk), scale=float(scale) if scale else 0.0, dtype=_DTYPES[q.dtype],
+                     routing=_ROUTING[routing])
 
 
-def forward_workspace_bytes(blocks: Blocks, q, k, topk: int, scale=None) -> int:
-    a = _attn(q, k, topk, scale)
+def forward_workspace_bytes(blocks: Blocks, q, k, topk: int, scale=None, routing: str = "score") -> int:
+    a = _attn(q, k, topk, scale, routing)
     return int(B.lib().ssa_forward_workspace(ctypes.byref(blocks.struct), ctypes.byref(a)))
 
 
 def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gates: torch.Tensor,
             topk: int, scale: float | None = None, return_pooled: bool = False,
             return_topk: bool = False, out: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None, stage_times: dict | None = None):
+            workspace: torch.Tensor | None = None, stage_times: dict | None = None,
+            routing: str = "score"):
     """SSA forward.  q [N, Hq, D], k/v [N, Hkv, D], gates [N, Hq, 3], all one dtype.
 
     Returns ``out`` [N, Hq, D]; with ``return_pooled`` / ``return_topk`` also
     the pooled keys/values [nb, Hkv, D] and the selected block ids
     [N, Hkv, topk] in a dict.  Passing a dict as ``stage_times`` runs the
     timed variant (blocks until done) and fills it with {kernel name: ms}.
+    ``routing="geometric"`` selects the blocks nearest to each query voxel
+    instead of the best-scored ones.
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("gates", gates)):
         if not t.is_cuda:
@@ -159,7 +169,7 @@ def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
         raise ValueError("shape mismatch among q, k, v, gates")
     q, k, v, gates = (t.contiguous() for t in (q, k, v, gates))
     L = B.lib()
-    a = _attn(q, k, topk, scale)
+    a = _attn(q, k, topk, scale, routing)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -210,7 +220,7 @@ def _check_inputs(blocks, q, k, v, gates):
 
 def forward_train(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   gates: torch.Tensor, topk: int, scale: float | None = None,
-                  workspace: torch.Tensor | None = None) -> dict:
+                  workspace: torch.Tensor | None = None, routing: str = "score") -> dict:
     """SSA forward that also keeps what ``backward`` needs.
 
     Returns a dict: ``out`` [N, Hq, D], ``topk`` [N, Hkv, topk] int32 and
@@ -219,7 +229,7 @@ def forward_train(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     """
     q, k, v, gates = _check_inputs(blocks, q, k, v, gates)
     L = B.lib()
-    a = _attn(q, k, topk, scale)
+    a = _attn(q, k, topk, scale, routing)
     dev = q.device
     n, hq, d = q.shape
     out = torch.empty_like(q)

@@ -22,6 +22,9 @@ SSA_ERR_DEVICE = 4
 SSA_F32 = 0
 SSA_BF16 = 1
 
+SSA_ROUTE_SCORE = 0
+SSA_ROUTE_GEOMETRIC = 1
+
 SSA_COUNT_NB = 0
 SSA_COUNT_NW = 1
 SSA_COUNT_INVALID = 2
@@ -71,6 +74,7 @@ class SsaBlocks(ctypes.Structure):
         ("max_blk_tokens", ctypes.c_int32),
         ("max_win_tokens", ctypes.c_int32),
         ("geo", SsaGeometry),
+        ("coords", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +86,7 @@ class SsaAttn(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int),
+        ("routing", ctypes.c_int32),
     ]
 
 

@@ -89,6 +89,8 @@ ssa_status check_attn(const ssa_attn* a) {
   if (a->h_q / a->h_kv > 32)
     return fail(SSA_ERR_UNSUPPORTED, "group size %d > 32 not supported", a->h_q / a->h_kv);
   if (!isfinite(a->scale)) return fail(SSA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (a->routing != SSA_ROUTE_SCORE && a->routing != SSA_ROUTE_GEOMETRIC)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "unknown routing %d", a->routing);
   return SSA_OK;
 }
 
@@ -112,7 +114,7 @@ bool use_mfma_path(const ssa_attn* a) {
 }
 
 struct FwdLayout {
-  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, total;
+  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, blk_cell, total;
 };
 
 FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
@@ -135,6 +137,9 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
     if (use_gqa_path(a)) {
       L.norm = off; off += align256(sizeof(float) * n * a->h_q);
       L.tile_pre2 = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    }
+    if (a->routing == SSA_ROUTE_GEOMETRIC) {
+      L.blk_cell = off; off += align256(4 * sizeof(int32_t) * cap);
     }
   }
   L.total = off + 256;
@@ -197,6 +202,7 @@ ssa_status ssa_build_blocks(const int32_t* coords, const int32_t* cu_seqlens, in
   out->n_tokens = n_tokens;
   out->batch = batch;
   out->geo = *geo;
+  out->coords = coords;
   out->nb = out->nw = out->max_blk_tokens = out->max_win_tokens = -1;
   if (sync_counts) {
     int32_t h[SSA_COUNTS];
@@ -236,19 +242,20 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
     stages[1] = Stage{"generic_fwd", ssa::launch_generic};
     return 2;
   }
+  int n = 1;
   if (use_gqa_path(attn)) {
-    stages[1] = Stage{"gqa_cmp_kernel", ssa::launch_gqa_cmp};
-    stages[2] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
-    stages[3] = Stage{"gqa_fixup_kernel", ssa::launch_gqa_fixup};
-    stages[4] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
-    stages[5] = Stage{"sel_combine_kernel", ssa::launch_sel_combine};
-    return 6;
+    stages[n++] = Stage{"gqa_cmp_kernel", ssa::launch_gqa_cmp};
+    stages[n++] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
+    stages[n++] = Stage{"gqa_fixup_kernel", ssa::launch_gqa_fixup};
+  } else {
+    stages[n++] = Stage{"cmp_mfma_kernel", ssa::launch_cmp_mfma};
+    stages[n++] = Stage{"topk_fixup_kernel", ssa::launch_topk_fixup};
   }
-  stages[1] = Stage{"cmp_mfma_kernel", ssa::launch_cmp_mfma};
-  stages[2] = Stage{"topk_fixup_kernel", ssa::launch_topk_fixup};
-  stages[3] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
-  stages[4] = Stage{"sel_combine_kernel", ssa::launch_sel_combine};
-  return 5;
+  // geometric routing replaces the score-ranked lists
+  if (attn->routing == SSA_ROUTE_GEOMETRIC) stages[n++] = Stage{"geo_topk_kernel", ssa::launch_geo_topk};
+  stages[n++] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
+  stages[n++] = Stage{"sel_combine_kernel", ssa::launch_sel_combine};
+  return n;
 }
 
 ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
@@ -266,6 +273,12 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
     return fail(SSA_ERR_INVALID_ARGUMENT, "a device buffer of blocks is null");
   if (blocks->n_tokens > 0 && (!q || !k || !v || !gates || !out))
     return fail(SSA_ERR_INVALID_ARGUMENT, "q, k, v, gates and out must be non-null");
+  if (attn->routing == SSA_ROUTE_GEOMETRIC) {
+    if (!use_mfma_path(attn))
+      return fail(SSA_ERR_UNSUPPORTED, "geometric routing needs a bfloat16 layout of the MFMA path");
+    if (blocks->n_tokens > 0 && !blocks->coords)
+      return fail(SSA_ERR_INVALID_ARGUMENT, "geometric routing needs the blocks' coordinates");
+  }
   const size_t need = forward_ws_bytes(blocks, attn);
   if (!workspace || ws_bytes < need)
     return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, need);
@@ -315,6 +328,11 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
       p.norm = reinterpret_cast<float*>(w + lay.norm);
       p.tile_pre2 = reinterpret_cast<int32_t*>(w + lay.tile_pre2);
       p.max_tiles2 = static_cast<int32_t>(blocks->n_tokens / 16 + blocks->batch + 1);
+    }
+    if (attn->routing == SSA_ROUTE_GEOMETRIC) {
+      p.coords = blocks->coords;
+      p.blk_cell = reinterpret_cast<int4*>(w + lay.blk_cell);
+      p.l_cmp = ilog2(blocks->geo.m_cmp);
     }
   }
 

@@ -146,6 +146,10 @@ struct FwdParams {
   // training: the state the backward reads (null = plain forward)
   float* lse;        // [3][n][h_q] natural-log softmax denominators of the
                      // (compressed, selected, window) branches, input token order
+  // geometric routing
+  const int32_t* coords;   // [n][3] token coordinates (input order)
+  int4* blk_cell;          // [nb_cap] the m_cmp^3 cell of each block
+  int32_t l_cmp;           // log2(m_cmp)
 };
 
 // Backward pass: the forward's parameters plus the gradients and scratch.
@@ -202,6 +206,7 @@ void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream);
 hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_geo_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 
 // [h_kv][nb_cap][D] -> [h_kv][nb_cap / 32][D][32] per 32-block tile, rows in
 // the order of the MFMA operands (ssa_pool.hip)

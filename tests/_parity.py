@@ -43,6 +43,7 @@ def oracle_blocks(wl):
 def gpu_forward(wl, blocks, gates=None, **kw):
     dt = torch_dtype(wl)
     g = wl.gates if gates is None else gates
+    kw.setdefault("routing", wl.routing)
     return ssa.forward(blocks, to_dev(wl.q, dt), to_dev(wl.k, dt), to_dev(wl.v, dt), to_dev(g, dt),
                        wl.topk, **kw)
 

@@ -43,7 +43,7 @@ def _gpu_grads(wl, gb, dout, gates=None):
     dt = P.torch_dtype(wl)
     q, k, v = P.to_dev(wl.q, dt), P.to_dev(wl.k, dt), P.to_dev(wl.v, dt)
     g = P.to_dev(wl.gates if gates is None else gates, dt)
-    saved = ssa.forward_train(gb, q, k, v, g, wl.topk)
+    saved = ssa.forward_train(gb, q, k, v, g, wl.topk, routing=wl.routing)
     grads = ssa.backward(gb, q, k, v, g, saved, P.to_dev(dout, dt))
     return saved, grads
 
@@ -94,6 +94,12 @@ def test_shifted_windows_backward_full():
     wl = make_custom([800, 333], grid_res=64, n_prims=3, topk=8, h_q=4, h_kv=4, head_dim=64,
                      dtype="bf16", seed=29, win_shift=4)
     _full_compare(wl, seed=6)
+
+
+def test_geometric_routing_backward_full():
+    wl = make_custom([700, 300], grid_res=64, n_prims=3, topk=8, h_q=4, h_kv=4, head_dim=64,
+                     dtype="bf16", seed=31, routing="geometric")
+    _full_compare(wl, seed=7)
 
 
 def test_zero_output_gradient():

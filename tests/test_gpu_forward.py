@@ -87,6 +87,45 @@ def test_shifted_windows_headline_sampled():
     _sampled_check(wl, P.sample_rows(wl, 200, seed=33), tag="workload 3, shifted windows")
 
 
+@pytest.mark.parametrize("case", [
+    dict(seqs=[1500, 0, 700], h_q=4, h_kv=4, head_dim=64, topk=16),
+    dict(seqs=[900, 400], h_q=16, h_kv=1, head_dim=32, topk=8),
+    dict(seqs=[600], h_q=32, h_kv=2, head_dim=64, topk=32),
+])
+def test_geometric_routing_full(case):
+    # the k blocks nearest to each query voxel (exact integer distances): the
+    # lists must equal the oracle's, order included
+    wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],
+                     h_kv=case["h_kv"], head_dim=case["head_dim"], dtype="bf16", seed=43, routing="geometric")
+    ob = P.oracle_blocks(wl)
+    gb = P.gpu_build(wl)
+    res = P.gpu_forward(wl, gb, return_topk=True, routing="geometric")
+    N, H = wl.n_tokens, wl.h_q
+    rows = [(t, h) for t in range(N) for h in range(H)]
+    ref = oracle.forward_rows(wl, ob, rows, with_branches=True)
+    G = H // wl.h_kv
+    gsel = res["topk"].cpu().numpy()[[t for t, _ in rows], [h // G for _, h in rows]]
+    assert np.array_equal(gsel, ref["topk"])
+    P.check_outputs(P.host(res["out"]).reshape(N * H, -1), ref["out"])
+    o = P.host(P.gpu_forward(wl, gb, gates=P.one_hot_gates(wl, 1), routing="geometric")).reshape(N * H, -1)
+    P.check_branch(o, ref["o_sel"], "o_sel")
+
+
+def test_geometric_routing_headline_sampled():
+    wl = make_workload(3)
+    wl.routing = "geometric"
+    ob = P.oracle_blocks(wl)
+    gb = P.gpu_build(wl)
+    res = P.gpu_forward(wl, gb, return_topk=True, routing="geometric")
+    rows = P.sample_rows(wl, 64, seed=34)
+    ref = oracle.forward_rows(wl, ob, rows)
+    gsel = res["topk"].cpu().numpy()[[t for t, _ in rows], [h for _, h in rows]]
+    assert np.array_equal(gsel, ref["topk"])
+    tt = torch.tensor([t for t, _ in rows], device=P.DEV)
+    hh = torch.tensor([h for _, h in rows], device=P.DEV)
+    P.check_outputs(P.host(res["out"][tt, hh]), ref["out"])
+
+
 def test_tiny_fp32_workload_full():
     _full_compare(make_workload(1))
 

@@ -109,6 +109,10 @@ def _fwd(L, attn, blocks=True, ws=None, ws_bytes=0, ptr=0x100000):
     (dict(h_q=64, h_kv=1), B.SSA_ERR_UNSUPPORTED),
     (dict(dtype=7), B.SSA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("inf")), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(routing=5), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(routing=1, dtype=B.SSA_F32), B.SSA_ERR_UNSUPPORTED),
+    (dict(routing=1, h_q=8, h_kv=2), B.SSA_ERR_UNSUPPORTED),
+    (dict(routing=1), B.SSA_ERR_INVALID_ARGUMENT),     # the blocks carry no coordinates
 ])
 def test_forward_rejects_bad_layout(kw, status):
     L = _lib()
