@@ -72,6 +72,13 @@ constexpr int kBlockQ = 32;            // queries per MFMA column block
 constexpr float kTruncLog2 = 0.0040711f;   // log2(1 / (1 - 2^-8 * 0.5 / ln 2))
 constexpr float kTruncInv = 0.99718215f;   // 1 - 2^-8 * 0.5 / ln 2
 
+// float -> uint32 with the same order (finite values; -0 and +0 both map to
+// the image of +0)
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -105,9 +112,13 @@ struct CmpShape {
   // candidates)
   static constexpr int kEnt = KMAX <= 16 ? 20 : 36;
   static constexpr int kRingBytes = 2 * (kKTileElems + kVTileElems) * 2;
-  // candidate lists of one query block of every wave (the blocks take turns)
-  static constexpr int kCandSlots = 4 * kBlockQ * (kCap + 2);
-  static constexpr int kCandBytes = kCandSlots * 6;
+  // candidate lists of one query block of every wave (the blocks take turns):
+  // per query kSlots 64-bit keys (kSlots even, so a query's keys start on a
+  // 16-byte boundary)
+  static constexpr int kSlots = kCap + 2;
+  static_assert(kSlots % 2 == 0, "a query's key row must be whole 16-byte words");
+  static constexpr int kCandSlots = 4 * kBlockQ * kSlots;
+  static constexpr int kCandBytes = kCandSlots * 8;
   static constexpr int kSmem = kRingBytes > kCandBytes ? kRingBytes : kCandBytes;
 };
 
@@ -139,16 +150,18 @@ cmp_mfma_kernel(FwdParams p) {
   // the key/value ring while the passes run; afterwards the same bytes hold
   // the candidate lists of one query block: per query kCap data slots
   // 1..kCap plus a sink slot at each end that absorbs writes past the
-  // capacity (the logit, and the block id relative to the sequence's first
-  // key tile; sequences with 65536 or more blocks take the fallback)
+  // capacity.  A slot is one 64-bit key whose unsigned order is the ranking
+  // order: the high word is the logit mapped to an order-preserving integer,
+  // the low word the complement of the block id relative to the sequence's
+  // first key tile (sequences with 65536 or more blocks take the fallback);
+  // an unused slot is 0, below every key.
   __shared__ __align__(16) uint8_t smem[Shape::kSmem];
   // hit-tile words: word e of block x of thread t at [(2 e + x) * 256 + t];
   // word kEnt is a sink
   __shared__ uint32_t ent[(kEnt + 1) * 2 * 256];
   uint16_t* const k_lds = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const v_lds = k_lds + 2 * kKTileElems;
-  float* const cand_v = reinterpret_cast<float*>(smem);
-  uint16_t* const cand_j = reinterpret_cast<uint16_t*>(smem + Shape::kCandSlots * 4);
+  uint64_t* const cand_key = reinterpret_cast<uint64_t*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -428,9 +441,13 @@ cmp_mfma_kernel(FwdParams p) {
       kr = load_k(1);
       vr = load_v(1);
     }
-    bf16x8 va_prev[4];
-    // step rel: S of block A for tile rel next to the softmax and P V of block
-    // B for tile rel - 1, then S of block B next to block A's softmax and P V
+    bf16x8 va_prev[4];   // value tile rel - 1 (MFMA A operands)
+    bf16x8 pa[2];        // P^T of block A for tile rel - 1
+    // step rel: block A's P V for tile rel - 1 and its S for tile rel issue
+    // next to block B's softmax for tile rel - 1; block B's P V for tile
+    // rel - 1 and its S for tile rel issue next to block A's softmax for tile
+    // rel.  No MFMA of a step waits for the VALU work of the same step, so the
+    // two kinds can interleave.
     auto step = [&](int rel, auto mask_a, auto has_b, auto mask_b) {
       __syncthreads();  // tiles rel stored; everyone is done with the tiles of rel - 1
       if (rel + 1 < n_kt) {
@@ -443,6 +460,7 @@ cmp_mfma_kernel(FwdParams p) {
       }
       bf16x8 a[4];
       read_k(rel, a);
+      if (decltype(has_b)::value) pv(blk[0], va_prev, pa);
       const f32x16 sa = qk(a, blk[0].qb);
       if (decltype(has_b)::value) {
         bf16x8 pb[2];
@@ -452,11 +470,11 @@ cmp_mfma_kernel(FwdParams p) {
       blk[1].s = qk(a, blk[1].qb);
       blk[0].s = sa;
       read_v(rel, va_prev);
-      bf16x8 pb[2];
-      softmax_tile(blk[0], 0, rel, pb, mask_a);
-      pv(blk[0], va_prev, pb);
+      softmax_tile(blk[0], 0, rel, pa, mask_a);
+      if (decltype(has_b)::value) interleave_mfma_valu<16, 10>();
     };
     run_tiles(step);
+    pv(blk[0], va_prev, pa);
     bf16x8 pb[2];
     softmax_tile(blk[1], 1, n_kt - 1, pb, kT{});
     pv(blk[1], va_prev, pb);
@@ -492,10 +510,19 @@ cmp_mfma_kernel(FwdParams p) {
 
   // ---------------- exact top-k, one query block at a time
   __syncthreads();  // every wave is done with the ring; its bytes now hold candidate lists
-  const int qbase = (wv * kBlockQ + (lane & 31)) * (kCap + 2);
+  constexpr int kSlots = Shape::kSlots;
+  const int qbase = (wv * kBlockQ + (lane & 31)) * kSlots;
   const int k_eff = min(p.topk, nbs);
   const uint16_t* kb0 = KB + static_cast<int64_t>(kt0) * kKeyTile * kD;
   auto finish = [&](QBlock<KMAX>& B, int x) {
+    // clear the query's slots (each lane half clears one half of them)
+    {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      uint64_t* const row = cand_key + qbase + half * (kSlots / 2);
+#pragma unroll
+      for (int e = 0; e < kSlots / 2; e += 2) *reinterpret_cast<u32x4*>(row + e) = z;
+    }
+    wave_lds_sync();
     // the query's candidate list: lane half 0 writes slots 1, 2, ... upward,
     // half 1 writes kCap, kCap - 1, ... downward; a write past the capacity
     // lands in the sink slot (0 or kCap + 1) and the query goes to the fallback
@@ -512,7 +539,7 @@ cmp_mfma_kernel(FwdParams p) {
           const int bpos = 31 - __clz(m);
           m ^= 1u << bpos;
           const int r = 15 - bpos;
-          cand_j[cpos] = static_cast<uint16_t>(base + 8 * (r >> 2) + (r & 3));
+          reinterpret_cast<uint32_t*>(cand_key + cpos)[0] = ~static_cast<uint32_t>(base + 8 * (r >> 2) + (r & 3));
           cpos = (cpos == climit) ? cpos : cpos + cstep;
         }
       }
@@ -525,7 +552,7 @@ cmp_mfma_kernel(FwdParams p) {
     // must fit 16 bits
     const bool overflow = over || cnt + cnt_other > kCap - 1 || n_kt * kKeyTile > 65536;
 
-    // exact float32 logits of this lane's candidates
+    // exact float32 logits of this lane's candidates into the high key words
     const int mine0 = qbase + (half ? kCap + 1 - cnt : 1);
     if (B.valid && !overflow && cnt > 0) {
       float qf[kD];
@@ -539,7 +566,8 @@ cmp_mfma_kernel(FwdParams p) {
         }
       }
       for (int i = 0; i < cnt; ++i) {
-        const uint16_t* kr = kb0 + static_cast<int64_t>(cand_j[mine0 + i]) * kD;
+        uint32_t* const slot = reinterpret_cast<uint32_t*>(cand_key + mine0 + i);
+        const uint16_t* kr = kb0 + static_cast<int64_t>(~slot[0]) * kD;
         float sc = 0.f;
 #pragma unroll
         for (int c = 0; c < kD / 8; ++c) {
@@ -550,7 +578,7 @@ cmp_mfma_kernel(FwdParams p) {
             sc = fmaf(qf[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), sc);
           }
         }
-        cand_v[mine0 + i] = sc;
+        slot[1] = ordered_bits(sc);
       }
     }
     wave_lds_sync();
@@ -561,23 +589,21 @@ cmp_mfma_kernel(FwdParams p) {
         p.fix[1 + slot] = B.qi * p.h_kv + h;
       }
     } else if (B.valid) {
-      // the query's candidates: slots [1, 1 + c0) from lane half 0 and
-      // [kCap + 1 - c1, kCap + 1) from lane half 1
-      const int c0 = half ? cnt_other : cnt, c1 = half ? cnt : cnt_other;
+      // a candidate's rank is the number of the query's keys above its own
+      uint64_t keys[kSlots];
+#pragma unroll
+      for (int e = 0; e < kSlots; e += 2) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(cand_key + qbase + e);
+        keys[e] = (static_cast<uint64_t>(u[1]) << 32) | u[0];
+        keys[e + 1] = (static_cast<uint64_t>(u[3]) << 32) | u[2];
+      }
       const int jbase = kt0 * kKeyTile;
       for (int i = 0; i < cnt; ++i) {
-        const float cv = cand_v[mine0 + i];
-        const int cj = cand_j[mine0 + i];
+        const uint64_t ck = cand_key[mine0 + i];
         int rank = 0;
-        for (int e = qbase + 1; e < qbase + 1 + c0; ++e) {
-          const float ov = cand_v[e];
-          rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
-        }
-        for (int e = qbase + kCap + 1 - c1; e < qbase + kCap + 1; ++e) {
-          const float ov = cand_v[e];
-          rank += (ov > cv) || (ov == cv && cand_j[e] < cj);
-        }
-        if (rank < k_eff) out_sel[rank] = jbase + cj;
+#pragma unroll
+        for (int e = 0; e < kSlots; ++e) rank += keys[e] > ck ? 1 : 0;
+        if (rank < k_eff) out_sel[rank] = jbase + static_cast<int>(~static_cast<uint32_t>(ck));
       }
       if (half == 0)
         for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;

@@ -22,6 +22,19 @@ __device__ __forceinline__ void wave_lds_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Instruction-scheduling pattern for the region that ends here: kMfma times
+// (one MFMA, then up to kValu vector ALU instructions).  An MFMA runs for many
+// cycles after issue, and the same wave can issue independent VALU work
+// meanwhile; the compiler otherwise tends to cluster the MFMAs.
+template <int kMfma, int kValu>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  if constexpr (kMfma > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    interleave_mfma_valu<kMfma - 1, kValu>();
+  }
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
