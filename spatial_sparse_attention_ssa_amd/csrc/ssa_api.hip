@@ -242,7 +242,10 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
     stages[1] = Stage{"generic_fwd", ssa::launch_generic};
     return 2;
   }
-  int n = 1;
+  // the window kernel is the first writer of the float32 branch accumulator
+  // (every token lies in exactly one window); the compressed kernels add to it
+  stages[1] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
+  int n = 2;
   if (use_gqa_path(attn)) {
     stages[n++] = Stage{"gqa_cmp_kernel", ssa::launch_gqa_cmp};
     stages[n++] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
@@ -253,7 +256,6 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
   }
   // geometric routing replaces the score-ranked lists
   if (attn->routing == SSA_ROUTE_GEOMETRIC) stages[n++] = Stage{"geo_topk_kernel", ssa::launch_geo_topk};
-  stages[n++] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
   stages[n++] = Stage{"sel_combine_kernel", ssa::launch_sel_combine};
   return n;
 }

@@ -480,7 +480,8 @@ cmp_mfma_kernel(FwdParams p) {
     pv(blk[1], va_prev, pb);
   }
 
-  // ---------------- o_cmp (times its gate) into the branch accumulator
+  // ---------------- o_cmp (times its gate) added to the branch accumulator (the
+  // window kernel, which runs first, wrote it)
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     QBlock<KMAX>& B = blk[x];
@@ -495,10 +496,12 @@ cmp_mfma_kernel(FwdParams p) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int d = 8 * rb + 4 * half;
-        *reinterpret_cast<float4*>(dst + d) =
-            make_float4(B.o0[4 * rb] * f, B.o0[4 * rb + 1] * f, B.o0[4 * rb + 2] * f, B.o0[4 * rb + 3] * f);
-        *reinterpret_cast<float4*>(dst + 32 + d) =
-            make_float4(B.o1[4 * rb] * f, B.o1[4 * rb + 1] * f, B.o1[4 * rb + 2] * f, B.o1[4 * rb + 3] * f);
+        float4 a = *reinterpret_cast<float4*>(dst + d);
+        float4 b = *reinterpret_cast<float4*>(dst + 32 + d);
+        a.x += B.o0[4 * rb] * f; a.y += B.o0[4 * rb + 1] * f; a.z += B.o0[4 * rb + 2] * f; a.w += B.o0[4 * rb + 3] * f;
+        b.x += B.o1[4 * rb] * f; b.y += B.o1[4 * rb + 1] * f; b.z += B.o1[4 * rb + 2] * f; b.w += B.o1[4 * rb + 3] * f;
+        *reinterpret_cast<float4*>(dst + d) = a;
+        *reinterpret_cast<float4*>(dst + 32 + d) = b;
       }
       if (p.lse && half == 0) {
         // p_j = 2^(s_j scale log2e + k0), so the denominator of the logits is

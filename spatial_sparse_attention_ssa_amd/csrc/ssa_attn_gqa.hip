@@ -262,8 +262,10 @@ gqa_cmp_kernel(FwdParams p) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int d = 32 * vb + 8 * rb + 4 * half;
-        *reinterpret_cast<float4*>(dst + d) = make_float4(o[x][vb][4 * rb] * f, o[x][vb][4 * rb + 1] * f,
-                                                          o[x][vb][4 * rb + 2] * f, o[x][vb][4 * rb + 3] * f);
+        float4 a = *reinterpret_cast<float4*>(dst + d);
+        a.x += o[x][vb][4 * rb] * f; a.y += o[x][vb][4 * rb + 1] * f;
+        a.z += o[x][vb][4 * rb + 2] * f; a.w += o[x][vb][4 * rb + 3] * f;
+        *reinterpret_cast<float4*>(dst + d) = a;
       }
   }
 }

@@ -3,8 +3,8 @@
 //
 // Direct3D-S2 page, "Method": all tokens of the top-k selected blocks take
 // part in a second attention; the three branch outputs are summed with the
-// predicted gates.  The compressed and window branches have already added
-// G0 * o_cmp + G2 * o_win to the float32 accumulator; this kernel adds
+// predicted gates.  The window and compressed branches have already written
+// G2 * o_win + G0 * o_cmp to the float32 accumulator; this kernel adds
 // G1 * o_sel, rounds once to bfloat16 and writes the output row.
 //
 // D / 16 lanes serve one (token, head) pair, each owning 16 dims; a wave

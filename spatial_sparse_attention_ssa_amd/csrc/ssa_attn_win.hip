@@ -2,8 +2,9 @@
 // h / (h_q / h_kv)).
 //
 // Direct3D-S2 page, "Method": every query attends to all tokens of its own
-// m_win^3 window (the windows do not overlap).  Adds G2 * o_win to the float32
-// branch accumulator.
+// m_win^3 window (the windows do not overlap).  Writes G2 * o_win to the
+// float32 branch accumulator: every token lies in exactly one window, so this
+// kernel runs first and the other branches add to what it wrote.
 //
 // Work split: one workgroup per (window, head) item (persistent grid, items
 // head-major).  Keys and values come from the head-major sorted copies made by
@@ -166,10 +167,8 @@ win_mfma_kernel(FwdParams p) {
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) {
             const int d = 32 * vb + 8 * rb + 4 * half;
-            float4 a = *reinterpret_cast<float4*>(dst + d);
-            a.x += o[vb][4 * rb] * f; a.y += o[vb][4 * rb + 1] * f;
-            a.z += o[vb][4 * rb + 2] * f; a.w += o[vb][4 * rb + 3] * f;
-            *reinterpret_cast<float4*>(dst + d) = a;
+            *reinterpret_cast<float4*>(dst + d) = make_float4(o[vb][4 * rb] * f, o[vb][4 * rb + 1] * f,
+                                                              o[vb][4 * rb + 2] * f, o[vb][4 * rb + 3] * f);
           }
         if (p.lse && half == 0)
           p.lse[2 * static_cast<int64_t>(p.n) * p.h_q + row] = (m * c2 + __log2f(l_win)) * kLn2;
