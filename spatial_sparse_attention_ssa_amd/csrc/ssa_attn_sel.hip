@@ -14,9 +14,11 @@
 // block is a contiguous run of rows.  First the pair's lanes turn its block
 // list into a list of row positions in LDS (each lane expands every fourth
 // block; one prefix over the four lanes places them), then the lanes stream
-// the rows four at a time (16 loads in flight per lane) with an online
-// softmax.  Rows past the LDS list's capacity, which only very large
-// selections reach, are walked block by block afterwards.
+// the listed rows with an online softmax: every row's position is known up
+// front, so a row's loads wait on no block offset.  (Streaming several rows
+// per step measured slower: the extra registers cost occupancy.)  Rows past
+// the LDS list's capacity, which only very large selections reach, are walked
+// block by block afterwards.
 #include <float.h>
 
 #include "ssa_internal.h"
