@@ -450,24 +450,33 @@ sel_dkv_kernel(BwdParams p) {
 }
 
 // dq of the selected branch, added to the other branches' share, written in
-// the input dtype.  LP lanes per (token, head) row, rows head-major.
-template <typename T, int D>
-__global__ void __launch_bounds__(256)
+// the input dtype.  LP lanes per (token, head) row, rows head-major.  As in the
+// forward's selection kernel, the row's lanes first load its selected blocks'
+// row ranges (all loads in flight at once) and list the first kList row
+// positions in LDS, so the loads of a row wait on no block offset; rows past
+// the list are walked block by block afterwards.  The rows are visited in
+// rank order, block by block, exactly as a plain loop over the list would.
+template <typename T, int D, int KMAX>
+__global__ void __launch_bounds__(256, 4)
 sel_dq_kernel(BwdParams p) {
   constexpr int LP = D / kDL;
   constexpr int NR = 256 / LP;
+  constexpr int kList = 64;
+  __shared__ int2 ranges[NR * KMAX];
+  __shared__ int32_t rows_l[NR * kList];
   const FwdParams& f = p.f;
   const int sub = threadIdx.x % LP;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * NR + threadIdx.x / LP;
+  const int pl = threadIdx.x / LP;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * NR + pl;
   const int64_t nrow = static_cast<int64_t>(f.n) * f.h_q;
-  if (row >= nrow) return;
-  const int h = static_cast<int>(row / f.n);
-  const int t = static_cast<int>(row % f.n);
+  const bool active = row < nrow;
+  const int h = active ? static_cast<int>(row / f.n) : 0;
+  const int t = active ? static_cast<int>(row % f.n) : 0;
   const int g = h / (f.h_q / f.h_kv);
   const int nb = f.counts[SSA_COUNT_NB];
   const int64_t qrow = static_cast<int64_t>(t) * f.h_q + h;
   const float c2 = f.scale * kLog2e;
-  const float l2 = p.lse[nrow + qrow] * kLog2e;
+  const float l2 = active ? p.lse[nrow + qrow] * kLog2e : 0.f;
   float q[kDL], d[kDL], aa[kDL], ab[kDL];
   load16(static_cast<const T*>(f.q) + qrow * D + kDL * sub, q);
   load16(static_cast<const T*>(p.dout) + qrow * D + kDL * sub, d);
@@ -477,25 +486,57 @@ sel_dq_kernel(BwdParams p) {
   const T* KS = static_cast<const T*>(f.k_s) + static_cast<int64_t>(g) * f.n * D + kDL * sub;
   const T* VS = static_cast<const T*>(f.v_s) + static_cast<int64_t>(g) * f.n * D + kDL * sub;
   const int32_t* sel = f.topk_idx + (static_cast<int64_t>(t) * f.h_kv + g) * f.topk;
-  for (int r = 0; r < f.topk; ++r) {
-    const int j = sel[r];
-    if (j < 0 || j >= nb) break;
-    for (int i = f.blk_off[j]; i < f.blk_off[j + 1]; ++i) {
-      float kr[kDL], vr[kDL];
-      load16(KS + static_cast<int64_t>(i) * D, kr);
-      load16(VS + static_cast<int64_t>(i) * D, vr);
-      const float s = row_sum<LP>(dot16(q, kr));
-      const float dp = row_sum<LP>(dot16(d, vr));
-      const float pr = exp2f(fmaf(s, c2, -l2));
-      const float pd = pr * dp;
-      dl += pd;
+
+  // the selected blocks' row ranges: lane sub loads ranks sub, sub + LP, ...;
+  // the list ends at the first block id outside [0, nb)
+  int2* const rng = ranges + pl * KMAX;
 #pragma unroll
-      for (int e = 0; e < kDL; ++e) {
-        aa[e] = fmaf(pd, kr[e], aa[e]);
-        ab[e] = fmaf(pr, kr[e], ab[e]);
-      }
+  for (int i = 0; i < KMAX / LP; ++i) {
+    const int r = sub + LP * i;
+    const int id = (active && r < f.topk) ? sel[r] : -1;
+    const bool ok = id >= 0 && id < nb;
+    rng[r] = ok ? make_int2(f.blk_off[id], f.blk_off[id + 1]) : make_int2(-1, -1);
+  }
+  wave_lds_sync();
+  int total = 0, k_eff = 0;
+  for (; k_eff < KMAX; ++k_eff) {
+    const int2 r = rng[k_eff];
+    if (r.x < 0) break;
+    for (int i = r.x + sub; i < r.y; i += LP) {
+      const int idx = total + (i - r.x);
+      if (idx < kList) rows_l[pl * kList + idx] = i;
+    }
+    total += r.y - r.x;
+  }
+  wave_lds_sync();
+
+  auto visit = [&](int64_t i) {
+    float kr[kDL], vr[kDL];
+    load16(KS + i * D, kr);
+    load16(VS + i * D, vr);
+    const float s = row_sum<LP>(dot16(q, kr));
+    const float dp = row_sum<LP>(dot16(d, vr));
+    const float pr = exp2f(fmaf(s, c2, -l2));
+    const float pd = pr * dp;
+    dl += pd;
+#pragma unroll
+    for (int e = 0; e < kDL; ++e) {
+      aa[e] = fmaf(pd, kr[e], aa[e]);
+      ab[e] = fmaf(pr, kr[e], ab[e]);
+    }
+  };
+  const int listed = min(total, kList);
+  for (int i = 0; i < listed; ++i) visit(rows_l[pl * kList + i]);
+  if (total > kList) {
+    int seen = 0;
+    for (int r = 0; r < k_eff; ++r) {
+      const int2 rr = rng[r];
+      for (int i = rr.x; i < rr.y; ++i, ++seen)
+        if (seen >= kList) visit(i);
     }
   }
+
+  if (!active) return;
   const float gs = Elt<T>::load(static_cast<const T*>(f.gates) + qrow * 3 + 1) * f.scale;
   float cur[kDL];
   load16(p.dq_acc + qrow * D + kDL * sub, cur);
@@ -611,10 +652,22 @@ hipError_t launch_bwd_sel_dkv(const BwdParams& p, ssa_dtype dtype, hipStream_t s
   return hipGetLastError();
 }
 
+template <int KMAX>
+void launch_sel_dq_k(const BwdParams& p, ssa_dtype dtype, int grid, hipStream_t stream) {
+  if (dtype == SSA_BF16) {
+    if (p.f.d == 32) sel_dq_kernel<uint16_t, 32, KMAX><<<grid, 256, 0, stream>>>(p);
+    else sel_dq_kernel<uint16_t, 64, KMAX><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (p.f.d == 32) sel_dq_kernel<float, 32, KMAX><<<grid, 256, 0, stream>>>(p);
+    else sel_dq_kernel<float, 64, KMAX><<<grid, 256, 0, stream>>>(p);
+  }
+}
+
 hipError_t launch_bwd_sel_dq(const BwdParams& p, ssa_dtype dtype, hipStream_t stream) {
   const int nr = 256 / (p.f.d / kDL);
   const int grid = rows_grid(static_cast<int64_t>(p.f.n) * p.f.h_q, nr);
-  SSA_BWD_LAUNCH(sel_dq_kernel, grid);
+  if (p.f.topk <= 16) launch_sel_dq_k<16>(p, dtype, grid, stream);
+  else launch_sel_dq_k<32>(p, dtype, grid, stream);
   return hipGetLastError();
 }
 
