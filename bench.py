@@ -20,6 +20,7 @@ Prints one JSON line (rank 0, N = 1 only).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -182,6 +183,49 @@ def algorithmic_flops(wl, blocks, topk, torch):
                 nb=int(h["counts"][0]), nw=int(h["counts"][1]))
 
 
+def build_bytes(n: int, nb: int, nw: int, batch: int) -> float:
+    """Algorithmic HBM bytes of the block build: coordinates read (12 B per
+    token), the permutation written (4 B per token), the segment offsets and
+    the sequence offsets."""
+    return 16.0 * n + 4.0 * (nb + nw + 2) + 8.0 * (batch + 1)
+
+
+def build_sweep(torch, ssa, dev, reps: int = 20):
+    """Block build time against the token count, 2^17 .. 2^24 tokens of
+    uniformly random voxels of a 1024^3 grid (one sequence; duplicates are
+    legal tokens), m_cmp = 4, m_win = 8: the build's HBM fraction shows only
+    at sizes far above one shape's 131072 tokens."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    points = []
+    for lg in range(17, 25):
+        n = 1 << lg
+        coords = torch.randint(0, 1024, (n, 3), generator=gen, device=dev, dtype=torch.int32)
+        cu = torch.tensor([0, n], dtype=torch.int32, device=dev)
+        b = ssa.build_blocks(coords, cu, 1024, 4, 8, sync=True)
+        nb, nw = int(b.struct.nb), int(b.struct.nw)
+        geo = ssa._binding.SsaGeometry(1024, 4, 8, 0)
+        ws_bytes = int(ssa._binding.lib().ssa_build_blocks_workspace(n, 1, ctypes.byref(geo)))
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            ssa.build_blocks(coords, cu, 1024, 4, 8, sync=False, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            ssa.build_blocks(coords, cu, 1024, 4, 8, sync=False, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        by = build_bytes(n, nb, nw, 1)
+        gbs = by / (us * 1e-6) / 1e9
+        points.append({"n_tokens": n, "nb": nb, "nw": nw, "us": us, "algorithmic_bytes": by, "GB/s": gbs,
+                       "hbm_frac": gbs / PEAK_HBM_GBS})
+        print(f"[build sweep] N=2^{lg}: {us:.1f} us, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del coords, b, ws
+    return points
+
+
 def cpu_baseline(wl, target_s: float, train: bool = False):
     """Time the oracle on a bounded sample of the same workload (test
     infrastructure, single thread): the full block build and pooling once,
@@ -235,6 +279,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only summarise two rocprofv3 --pmc runs into profiles/*_traffic.json")
     ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
+    ap.add_argument("--build-sweep", action="store_true",
+                    help="only time the block build at 2^17 .. 2^24 random voxel tokens (one JSON line)")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=sorted(WORKLOADS),
                     help="3: the 131072-token workload (default); 4: the grouped-head 262144-token "
                          "workload, for its kernel profile; 5: forward + backward on the varlen batch")
@@ -260,6 +306,14 @@ def main():
     from workloads import make_workload
 
     dev = torch.device("cuda:0")
+    if args.build_sweep:
+        pts = build_sweep(torch, ssa, dev)
+        print(json.dumps({"metric": "block build time and algorithmic HBM GB/s against the token count",
+                          "unit": "us", "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": "uniform random voxels of a 1024^3 grid, one sequence",
+                                     "m_cmp": 4, "m_win": 8},
+                          "points": pts}), flush=True)
+        return
     wl = make_workload(wid)
     bf = torch.bfloat16
     up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
@@ -365,6 +419,8 @@ def main():
         total_flops = 3.0 * work["total"]
     tflops = total_flops / (ms_step * 1e-3) / 1e12
     pool_gbs = pool_bytes(wl, work["nb"]) / (stage_ms["pool_kernel"] * 1e-3) / 1e9
+    bp_bytes = build_bytes(n, work["nb"], work["nw"], wl.batch) + pool_bytes(wl, work["nb"])
+    bp_gbs = bp_bytes / ((build_ms + stage_ms["pool_kernel"]) * 1e-3) / 1e9
 
     line = {
         "metric": WORKLOADS[wid]["metric"],
@@ -390,6 +446,8 @@ def main():
         "stage_ms": stage_ms,
         "pool_hbm": {"achieved": pool_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pool_gbs / PEAK_HBM_GBS,
                      "bytes": pool_bytes(wl, work["nb"])},
+        "build_pool_hbm": {"achieved": bp_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": bp_gbs / PEAK_HBM_GBS,
+                           "bytes": bp_bytes},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": stored_traffic(dom.split(":")[-1], wid)},

@@ -165,17 +165,27 @@ __global__ void __launch_bounds__(256) scan_chunk_apply(uint32_t* __restrict__ d
   }
 }
 
+// Stable scatter of one 4096-key tile: every key's rank among the tile's keys
+// of its digit (wave ballots, waves in order), the keys placed in LDS in
+// (digit, rank) order, then written out in that order so that consecutive
+// threads write consecutive addresses of a digit's output run.
 __global__ void __launch_bounds__(256)
 radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t n,
                 int shift, const uint32_t* __restrict__ tile_off, int ntiles) {
-  __shared__ uint32_t whist[4][256];
-  __shared__ uint32_t wbase[4][256];
+  __shared__ uint32_t whist[4][256];   // per wave: keys of each digit
+  __shared__ uint32_t wbase[4][256];   // per wave: tile-local start of its keys of each digit
+  __shared__ uint32_t lstart[256];     // tile-local start of each digit
+  __shared__ uint32_t gbase[256];      // output position of the tile's first key of each digit
+  __shared__ uint32_t scan[256];
+  __shared__ uint32_t skeys[kSortTile];
+  __shared__ int32_t svals[kSortTile];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 4 * 256; i += 256) (&whist[0][0])[i] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kSortTile + wave * (kSortTile / 4);
+  const int tile0 = blockIdx.x * kSortTile;
+  const int base = tile0 + wave * (kSortTile / 4);
   const uint64_t lt = lanemask_lt();
   uint32_t kk[kItems], rk[kItems], dg[kItems];
   int32_t vv[kItems];
@@ -202,13 +212,25 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     __builtin_amdgcn_wave_barrier();
     kk[r] = key;
     vv[r] = val;
-    rk[r] = before + static_cast<uint32_t>(__popcll(peers & lt));
+    rk[r] = valid ? before + static_cast<uint32_t>(__popcll(peers & lt)) : 0xFFFFFFFFu;
     dg[r] = d;
   }
   __syncthreads();
   {
+    // exclusive scan over the digits of the tile's digit totals
     const int d = threadIdx.x;
-    uint32_t run = tile_off[d * ntiles + blockIdx.x];
+    const uint32_t tot = whist[0][d] + whist[1][d] + whist[2][d] + whist[3][d];
+    scan[d] = tot;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const uint32_t v = d >= off ? scan[d - off] : 0u;
+      __syncthreads();
+      scan[d] += v;
+      __syncthreads();
+    }
+    uint32_t run = scan[d] - tot;
+    lstart[d] = run;
+    gbase[d] = tile_off[d * ntiles + blockIdx.x];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       wbase[w][d] = run;
@@ -218,12 +240,20 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const int p = base + r * kWave + lane;
-    if (p < n) {
-      const uint32_t dst = wbase[wave][dg[r]] + rk[r];
-      keys_out[dst] = kk[r];
-      vals_out[dst] = vv[r];
+    if (rk[r] != 0xFFFFFFFFu) {
+      const uint32_t pos = wbase[wave][dg[r]] + rk[r];
+      skeys[pos] = kk[r];
+      svals[pos] = vv[r];
     }
+  }
+  __syncthreads();
+  const int cnt = min(kSortTile, n - tile0);
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    const uint32_t key = skeys[i];
+    const uint32_t d = (key >> shift) & 255u;
+    const uint32_t dst = gbase[d] + (static_cast<uint32_t>(i) - lstart[d]);
+    keys_out[dst] = key;
+    vals_out[dst] = svals[i];
   }
 }
 
@@ -420,7 +450,7 @@ size_t build_workspace_bytes(int64_t n, int32_t /*batch*/) {
   size_t b = 0;
   b += 2 * align256(sizeof(uint32_t) * n);     // keys_a, keys_b
   b += align256(sizeof(int32_t) * n);          // vals_b
-  b += align256(sizeof(uint32_t) * 256 * ntiles);
+  b += align256(sort_pairs_hist_bytes(n));      // tile histograms and their scan's chunk sums
   b += 2 * align256(sizeof(int32_t) * 2 * ntiles);
   return b + 256;
 }
@@ -431,7 +461,7 @@ void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out) {
   out->keys_a = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * n);
   out->keys_b = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * n);
   out->vals_b = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * n);
-  out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * 256 * ntiles);
+  out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sort_pairs_hist_bytes(n));
   out->tile_cnt = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * 2 * ntiles);
   out->tile_base = reinterpret_cast<int32_t*>(p);
 }
@@ -447,12 +477,31 @@ size_t sort_pairs_hist_bytes(int64_t n) {
   return align256(sizeof(uint32_t) * m) + sizeof(uint32_t) * ((m + kScanChunk - 1) / kScanChunk);
 }
 
+namespace {
+
+// exclusive scan of the m = 256 * ntiles tile histograms in place: one
+// workgroup for small histograms, else chunk sums, their scan, and each chunk
+// rescanned with its offset (the sums live right after the histograms)
+void scan_tile_hist(uint32_t* tile_hist, int ntiles, hipStream_t stream) {
+  const int m = 256 * ntiles;
+  if (m <= 2 * kScanChunk) {   // measured: one workgroup wins only up to two chunks
+    scan_exclusive_u32<<<1, 1024, 0, stream>>>(tile_hist, m);
+    return;
+  }
+  uint32_t* sums = tile_hist + align256(sizeof(uint32_t) * 256 * static_cast<size_t>(ntiles)) / sizeof(uint32_t);
+  const int chunks = (m + kScanChunk - 1) / kScanChunk;
+  scan_chunk_sums<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
+  scan_exclusive_u32<<<1, 1024, 0, stream>>>(sums, chunks);
+  scan_chunk_apply<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
+}
+
+}  // namespace
+
 hipError_t launch_sort_pairs(uint32_t* keys, int32_t* vals, uint32_t* keys_tmp, int32_t* vals_tmp, int32_t n,
                              int key_bits, uint32_t* tile_hist, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int ntiles = (n + kSortTile - 1) / kSortTile;
   const int passes = (key_bits + kRadixBits - 1) / kRadixBits;
-  uint32_t* sums = tile_hist + align256(sizeof(uint32_t) * 256 * static_cast<size_t>(ntiles)) / sizeof(uint32_t);
   uint32_t* kin = keys;
   int32_t* vin = vals;
   uint32_t* kout = keys_tmp;
@@ -460,15 +509,7 @@ hipError_t launch_sort_pairs(uint32_t* keys, int32_t* vals, uint32_t* keys_tmp, 
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kRadixBits;
     radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, tile_hist, ntiles);
-    const int m = 256 * ntiles;
-    if (m <= 8 * kScanChunk) {
-      scan_exclusive_u32<<<1, 1024, 0, stream>>>(tile_hist, m);
-    } else {
-      const int chunks = (m + kScanChunk - 1) / kScanChunk;
-      scan_chunk_sums<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
-      scan_exclusive_u32<<<1, 1024, 0, stream>>>(sums, chunks);
-      scan_chunk_apply<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
-    }
+    scan_tile_hist(tile_hist, ntiles, stream);
     radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, tile_hist, ntiles);
     uint32_t* tk = kin; kin = kout; kout = tk;
     int32_t* tv = vin; vin = vout; vout = tv;
@@ -497,7 +538,7 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kRadixBits;
     radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, ws.tile_hist, ntiles);
-    scan_exclusive_u32<<<1, 1024, 0, stream>>>(ws.tile_hist, 256 * ntiles);
+    scan_tile_hist(ws.tile_hist, ntiles, stream);
     radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, ws.tile_hist, ntiles);
     uint32_t* tk = kin; kin = kout; kout = tk;
     int32_t* tv = vin; vin = vout; vout = tv;
@@ -510,7 +551,8 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
   seg_write<<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
                                         out.counts, out.blk_off, out.win_off, out.win_blk_off,
                                         out.seq_blk_off, out.seq_win_off);
-  const int sgrid = min((n + 255) / 256, 64);
+  // one workgroup per 4096 tokens, at least 64 and at most 1024 (two atomics each)
+  const int sgrid = max(64, min((n + 4095) / 4096, 1024));
   seg_stats<<<sgrid, 256, 0, stream>>>(out.blk_off, out.win_off, out.counts);
   return hipGetLastError();
 }
