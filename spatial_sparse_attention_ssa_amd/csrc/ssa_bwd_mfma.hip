@@ -68,6 +68,31 @@ __device__ __forceinline__ int mfma_pos(int r) {
   return (r & 16) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One MFMA A operand (dims x 16 rows, in the k order of mfma_pos) of a
+// wave-private 32-row tile stored row-major in LDS (row stride kRowP
+// elements), read with gfx950's transposing LDS load: within each 16-lane
+// group, output lane 4a + b receives element b of the 4-element chunks that
+// source lanes a, a + 4, a + 8 and a + 12 address.  So source lane
+// (g, a, i) = (lane / 16, lane % 4, lane % 16 / 4) addresses row
+// 16 ks + 4 (g / 2) + i (plus 8 for the operand's upper four k slots) at dims
+// 32 x + 16 (g % 2) + 4 a, and lane l receives dim 32 x + l % 32 of rows
+// 16 ks + 4 (l / 32) + {0..3} and 16 ks + 8 + 4 (l / 32) + {0..3}: the rows
+// that k slots 8 (l / 32) + {0..7} hold.
+template <int kRowP>
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int lane, int x, int ks) {
+  const int g = lane >> 4;
+  const int row = 16 * ks + 4 * (g >> 1) + ((lane & 15) >> 2);
+  const int dim = 32 * x + 16 * (g & 1) + 4 * (lane & 3);
+  const uint16_t* p0 = tile + row * kRowP + dim;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * kRowP));
+  const s16x4 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 b;
 #pragma unroll
@@ -723,10 +748,11 @@ __global__ void __launch_bounds__(256, 2)
 kv_grad_mfma_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int VB = D / 32;
-  constexpr int kTT = D * kTRow;
+  constexpr int kRowP = D + 8;                 // padded row of a gathered row tile (bf16)
+  constexpr int kRT = kKeyTile * kRowP;
   constexpr int kRed = kKeyTile * D;            // one partial tile (floats)
-  __shared__ __align__(16) uint16_t qt_lds[4 * kTT];   // per wave: Q^T of its row tile
-  __shared__ __align__(16) uint16_t dt_lds[4 * kTT];   // per wave: dO^T
+  __shared__ __align__(16) uint16_t qr_lds[4 * kRT];   // per wave: its 32 gathered Q rows, row-major
+  __shared__ __align__(16) uint16_t dr_lds[4 * kRT];   // per wave: dO rows
   __shared__ float4 st_lds[4 * kKeyTile];              // per wave: log2 lse, Delta, gate per row
   __shared__ float red_k[kRed];
   __shared__ float red_v[kRed];
@@ -744,8 +770,8 @@ kv_grad_mfma_kernel(BwdParams p) {
   const uint16_t* Q = static_cast<const uint16_t*>(f.q);
   const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
   const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
-  uint16_t* qt = qt_lds + wv * kTT;
-  uint16_t* dt = dt_lds + wv * kTT;
+  uint16_t* qr = qr_lds + wv * kRT;
+  uint16_t* dr = dr_lds + wv * kRT;
   float4* st = st_lds + wv * kKeyTile;
   const int n_units = MODE == kSelected ? f.counts[SSA_COUNT_NB] : f.counts[SSA_COUNT_NW];
   const int64_t n_items = static_cast<int64_t>(n_units) * f.h_kv;
@@ -818,18 +844,13 @@ kv_grad_mfma_kernel(BwdParams p) {
       };
       if (wv < n_rt) load(wv);
       for (int rt = wv; rt < n_rt; rt += 4) {
-        // the transposed copies and the row statistics, wave-private
-        const int pos = mfma_pos(lane & 31);
+        // the rows (row-major, 16-byte stores) and the row statistics,
+        // wave-private; the transposed operands are read back below
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int d0 = 16 * ks + 8 * half + 2 * e;
-            qt[d0 * kTRow + pos] = static_cast<uint16_t>(nq[ks][e] & 0xFFFFu);
-            qt[(d0 + 1) * kTRow + pos] = static_cast<uint16_t>(nq[ks][e] >> 16);
-            dt[d0 * kTRow + pos] = static_cast<uint16_t>(nd[ks][e] & 0xFFFFu);
-            dt[(d0 + 1) * kTRow + pos] = static_cast<uint16_t>(nd[ks][e] >> 16);
-          }
+        for (int ks = 0; ks < KS; ++ks) {
+          *reinterpret_cast<u32x4*>(qr + (lane & 31) * kRowP + 16 * ks + 8 * half) = nq[ks];
+          *reinterpret_cast<u32x4*>(dr + (lane & 31) * kRowP + 16 * ks + 8 * half) = nd[ks];
+        }
         if (half == 0) st[lane] = ns;
         wave_lds_sync();
         f32x16 s = {}, dp = {};
@@ -839,8 +860,6 @@ kv_grad_mfma_kernel(BwdParams p) {
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, nd[ks]), vb[ks], dp, 0, 0, 0);
         }
         if (rt + 4 < n_rt) load(rt + 4);   // in flight during the rest of this tile
-        const uint16_t* qtl = qt + (lane & 31) * kTRow + 8 * half;
-        const uint16_t* dtl = dt + (lane & 31) * kTRow + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           float pg[8], ds[8];
@@ -856,8 +875,8 @@ kv_grad_mfma_kernel(BwdParams p) {
           const bf16x8 sb = pack8(ds);
 #pragma unroll
           for (int x = 0; x < VB; ++x) {
-            dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dtl + x * 32 * kTRow + 16 * ks), pb, dv[x], 0, 0, 0);
-            dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qtl + x * 32 * kTRow + 16 * ks), sb, dk[x], 0, 0, 0);
+            dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand<kRowP>(dr, lane, x, ks), pb, dv[x], 0, 0, 0);
+            dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand<kRowP>(qr, lane, x, ks), sb, dk[x], 0, 0, 0);
           }
         }
         wave_lds_sync();  // the wave-private area is rewritten by the next row tile
