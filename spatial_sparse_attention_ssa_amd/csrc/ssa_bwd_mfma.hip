@@ -35,9 +35,10 @@
 //   window), the rows being the window's own (query, head) pairs.  The key
 //   tile is up to 32 tokens of the block or window (sorted copies, in
 //   registers); each wave streams its own share of the rows (A operands
-//   straight from memory, the transposed copies through a wave-private LDS
-//   area), and the four partial tiles are summed in LDS, in wave order, at
-//   the end.
+//   straight from memory; the rows also go row-major into a wave-private LDS
+//   area, from which the transposed operands come back through gfx950's
+//   transposing LDS load), and the four partial tiles are summed in LDS, in
+//   wave order, at the end.
 #include <float.h>
 
 #include <algorithm>
