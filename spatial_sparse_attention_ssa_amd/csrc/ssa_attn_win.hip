@@ -9,11 +9,11 @@
 // Work split: one workgroup per (window, head) item (persistent grid, items
 // head-major).  Keys and values come from the head-major sorted copies made by
 // the pooling kernel, so a window is one contiguous run of rows.  The
-// workgroup stages the window's key rows (row-major) and value rows
-// (transposed, in the MFMA operand order) in LDS, in chunks of up to kChunk
-// tokens; each of its 4 waves computes 32 queries with
-// v_mfma_f32_32x32x16_bf16 (S^T = K Q^T over 32-key tiles), an online softmax
-// (running max, rescaled sum and O^T), and O^T += V^T P^T.
+// workgroup stages the window's key and value rows (row-major, 16-byte
+// stores) in LDS, in chunks of up to kChunk tokens; each of its 4 waves
+// computes 32 queries with v_mfma_f32_32x32x16_bf16 (S^T = K Q^T over 32-key
+// tiles), an online softmax (running max, rescaled sum and O^T), and
+// O^T += V^T P^T with the V^T operands read through the transposing LDS load.
 #include <float.h>
 
 #include "ssa_internal.h"
@@ -27,15 +27,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 256;            // window tokens staged in LDS at a time
-constexpr int kVRow = kChunk + 8;      // padded transposed value row (bf16)
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ int mfma_key_pos(int jj) {
-  const int lo = jj & 15;
-  return (jj & ~15) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
 }
 
 template <int D>
@@ -47,7 +41,7 @@ win_mfma_kernel(FwdParams p) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int kKRow = kD + 8;          // padded key row (bf16)
   __shared__ __align__(16) uint16_t k_lds[kChunk * kKRow];
-  __shared__ __align__(16) uint16_t v_lds[kD * kVRow];
+  __shared__ __align__(16) uint16_t v_lds[kChunk * kKRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,7 +85,7 @@ win_mfma_kernel(FwdParams p) {
         const int nk = min(kChunk, n_w - kc);
         const int nk32 = (nk + 31) & ~31;
         __syncthreads();  // previous chunk fully consumed
-        // stage keys (row-major) and values (transposed) of this chunk
+        // stage the keys and values of this chunk (row-major)
         for (int e = tid; e < nk32 * CPR; e += 256) {
           const int row = e / CPR, c = e % CPR;
           u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
@@ -101,13 +95,7 @@ win_mfma_kernel(FwdParams p) {
             vr = *reinterpret_cast<const u32x4*>(VS + off);
           }
           *reinterpret_cast<u32x4*>(k_lds + row * kKRow + 8 * c) = kr;
-          const int kp = mfma_key_pos(row);
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const int d = 8 * c + 2 * e2;
-            v_lds[d * kVRow + kp] = static_cast<uint16_t>(vr[e2] & 0xFFFFu);
-            v_lds[(d + 1) * kVRow + kp] = static_cast<uint16_t>(vr[e2] >> 16);
-          }
+          *reinterpret_cast<u32x4*>(v_lds + row * kKRow + 8 * c) = vr;
         }
         __syncthreads();
         for (int kt = 0; kt < nk32; kt += kKeyTile) {
@@ -149,10 +137,10 @@ win_mfma_kernel(FwdParams p) {
             for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const uint16_t* vl = v_lds + (lane & 31) * kVRow + kt + 16 * ks + 8 * half;
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
-              o[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vl + vb * 32 * kVRow), pb[ks], o[vb], 0, 0, 0);
+              o[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand<kKRow>(v_lds + kt * kKRow, lane, vb, ks),
+                                                              pb[ks], o[vb], 0, 0, 0);
           }
         }
       }

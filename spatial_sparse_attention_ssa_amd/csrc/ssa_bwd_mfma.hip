@@ -69,31 +69,6 @@ __device__ __forceinline__ int mfma_pos(int r) {
   return (r & 16) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// One MFMA A operand (dims x 16 rows, in the k order of mfma_pos) of a
-// wave-private 32-row tile stored row-major in LDS (row stride kRowP
-// elements), read with gfx950's transposing LDS load: within each 16-lane
-// group, output lane 4a + b receives element b of the 4-element chunks that
-// source lanes a, a + 4, a + 8 and a + 12 address.  So source lane
-// (g, a, i) = (lane / 16, lane % 4, lane % 16 / 4) addresses row
-// 16 ks + 4 (g / 2) + i (plus 8 for the operand's upper four k slots) at dims
-// 32 x + 16 (g % 2) + 4 a, and lane l receives dim 32 x + l % 32 of rows
-// 16 ks + 4 (l / 32) + {0..3} and 16 ks + 8 + 4 (l / 32) + {0..3}: the rows
-// that k slots 8 (l / 32) + {0..7} hold.
-template <int kRowP>
-__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int lane, int x, int ks) {
-  const int g = lane >> 4;
-  const int row = 16 * ks + 4 * (g >> 1) + ((lane & 15) >> 2);
-  const int dim = 32 * x + 16 * (g & 1) + 4 * (lane & 3);
-  const uint16_t* p0 = tile + row * kRowP + dim;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * kRowP));
-  const s16x4 v[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 b;
 #pragma unroll

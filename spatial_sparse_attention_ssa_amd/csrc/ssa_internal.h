@@ -35,6 +35,34 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+typedef short tr_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr_s16x4 lds_tr_s16x4;
+typedef __bf16 tr_bf16x8 __attribute__((ext_vector_type(8)));
+
+// One v_mfma_f32_32x32x16_bf16 A operand (32 dims x 16 rows; lane half h
+// holds rows {0-3, 8-11} + 4 h of the 16, the k order in which a 32x32
+// accumulator feeds the next MFMA as its B operand) of a tile of rows stored
+// row-major in LDS (row stride kRowP elements), read with gfx950's
+// transposing LDS load (ds_read_b64_tr_b16): within each 16-lane
+// group, output lane 4a + b receives element b of the 4-element chunks that
+// source lanes a, a + 4, a + 8 and a + 12 address.  So source lane
+// (g, a, i) = (lane / 16, lane % 4, lane % 16 / 4) addresses row
+// 16 ks + 4 (g / 2) + i (plus 8 for the operand's upper four k slots) at dims
+// 32 x + 16 (g % 2) + 4 a, and lane l receives dim 32 x + l % 32 of rows
+// 16 ks + 4 (l / 32) + {0..3} and 16 ks + 8 + 4 (l / 32) + {0..3}: the rows
+// that k slots 8 (l / 32) + {0..7} hold.
+template <int kRowP>
+__device__ __forceinline__ tr_bf16x8 lds_tr_operand(const uint16_t* tile, int lane, int x, int ks) {
+  const int g = lane >> 4;
+  const int row = 16 * ks + 4 * (g >> 1) + ((lane & 15) >> 2);
+  const int dim = 32 * x + 16 * (g & 1) + 4 * (lane & 3);
+  const uint16_t* p0 = tile + row * kRowP + dim;
+  const tr_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_s16x4*)(p0));
+  const tr_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_s16x4*)(p0 + 8 * kRowP));
+  const tr_s16x4 v[2] = {lo, hi};
+  return __builtin_bit_cast(tr_bf16x8, v);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
