@@ -574,8 +574,9 @@ dkv_split_sum_kernel(BwdParams p) {
 
 // dq of the window branch on MFMA: one workgroup per (window, query head)
 // item (persistent grid, items head-major).  The window's key and value rows
-// (row-major) and its keys transposed in MFMA operand order are staged in LDS
-// kWinChunk tokens at a time; each wave owns 32 of the window's queries and
+// are staged row-major in LDS kWinChunk tokens at a time (the K^T operands
+// come back through the transposing LDS load); each wave owns 32 of the
+// window's queries and
 // accumulates A = K^T (P * dP)^T and B = K^T P^T as in the compressed
 // branch's dq kernel.  Adds to dq_acc; writes Delta and the gate gradient.
 constexpr int kWinChunk = 128;
@@ -587,10 +588,8 @@ win_dq_mfma_kernel(BwdParams p) {
   constexpr int VB = D / 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int kKRow = D + 8;               // padded key / value row (bf16)
-  constexpr int kCRow = kWinChunk + 8;       // padded transposed row
   __shared__ __align__(16) uint16_t k_lds[kWinChunk * kKRow];
   __shared__ __align__(16) uint16_t v_lds[kWinChunk * kKRow];
-  __shared__ __align__(16) uint16_t t_lds[D * kCRow];
 
   const FwdParams& f = p.f;
   const int tid = threadIdx.x;
@@ -649,13 +648,6 @@ win_dq_mfma_kernel(BwdParams p) {
           }
           *reinterpret_cast<u32x4*>(k_lds + row * kKRow + 8 * c) = kr;
           *reinterpret_cast<u32x4*>(v_lds + row * kKRow + 8 * c) = vr;
-          const int kp = (row & ~31) | mfma_pos(row & 31);
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const int d = 8 * c + 2 * e2;
-            t_lds[d * kCRow + kp] = static_cast<uint16_t>(kr[e2] & 0xFFFFu);
-            t_lds[(d + 1) * kCRow + kp] = static_cast<uint16_t>(kr[e2] >> 16);
-          }
         }
         __syncthreads();
         for (int kt = 0; kt < nk32; kt += kKeyTile) {
@@ -676,14 +668,13 @@ win_dq_mfma_kernel(BwdParams p) {
             pd[r] = x * dp[r];
             dl += pd[r];
           }
-          const uint16_t* tl = t_lds + (lane & 31) * kCRow + kt + 8 * half;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const bf16x8 pdb = pack8(pd + 8 * ks);
             const bf16x8 pb = pack8(pr + 8 * ks);
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) {
-              const bf16x8 a = lds_b128(tl + vb * 32 * kCRow + 16 * ks);
+              const bf16x8 a = lds_tr_operand<kKRow>(k_lds + kt * kKRow, lane, vb, ks);
               aa[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pdb, aa[vb], 0, 0, 0);
               ab[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ab[vb], 0, 0, 0);
             }
