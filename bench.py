@@ -183,6 +183,53 @@ def algorithmic_flops(wl, blocks, topk, torch):
                 nb=int(h["counts"][0]), nw=int(h["counts"][1]))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+N_SIMD = 256 * 4            # MI355X: 256 compute units of 4 SIMDs
+N_XCC = 8
+
+
+def summarize_mfma(pmc_csv: str, wid: int):
+    """Counter-based MFMA utilisation per attention kernel from one rocprofv3
+    --pmc run of MFMA_COUNTERS: executed bf16 MFMA flops (512 per MOPS unit),
+    the MFMA pipe's busy share of all SIMD cycles (cycles per XCC from
+    GRBM_GUI_ACTIVE), and the clock those cycles imply; prints a markdown
+    table and the time-weighted utilisation."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    per = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    with open(pmc_csv) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            name = re.sub(r"[<(].*", "", name).split("::")[-1]
+            per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    print("| kernel | launches | avg us | executed MFMA TFLOP | executed TFLOP/s | % of 2.5 PF | "
+          "MFMA busy % of SIMD cycles | implied clock GHz |")
+    print("|---|---|---|---|---|---|---|---|")
+    tw_busy, tw_t = 0.0, 0.0
+    for name, c in per.items():
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])
+        if not mops or max(mops) == 0:
+            continue
+        avg = lambda k: sum(c[k]) / len(c[k])
+        t = sum(dur[name]) / len(dur[name])
+        flops = 512.0 * avg("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        cycles = avg("GRBM_GUI_ACTIVE") / N_XCC
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * N_SIMD)
+        tw_busy += busy * t
+        tw_t += t
+        print(f"| {name} | {len(c['GRBM_GUI_ACTIVE'])} | {t * 1e6:.1f} | {flops / 1e12:.3f} | "
+              f"{flops / t / 1e12:.0f} | {100 * flops / t / 1e12 / PEAK_BF16_TFLOPS:.1f} | {100 * busy:.1f} | "
+              f"{cycles / t / 1e9:.2f} |")
+    if tw_t:
+        print(f"\ntime-weighted MFMA busy share over these kernels: {100 * tw_busy / tw_t:.1f} %")
+
+
 def build_bytes(n: int, nb: int, nw: int, batch: int) -> float:
     """Algorithmic HBM bytes of the block build: coordinates read (12 B per
     token), the permutation written (4 B per token), the segment offsets and
@@ -279,6 +326,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only summarise two rocprofv3 --pmc runs into profiles/*_traffic.json")
     ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="only summarise a rocprofv3 --pmc run of the MFMA counters into a markdown table")
     ap.add_argument("--build-sweep", action="store_true",
                     help="only time the block build at 2^17 .. 2^24 random voxel tokens (one JSON line)")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=sorted(WORKLOADS),
@@ -293,6 +342,9 @@ def main():
                 for c in ("FETCH_SIZE", "WRITE_SIZE")}
         cmds = {"fetch": cmds["fetch_size"], "write": cmds["write_size"]}
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel_stats, cmds, wid)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, wid)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
