@@ -5,6 +5,7 @@ blocks and non-overlapping m_win^3 windows.  Covers every named workload's
 geometry plus adversarial inputs (one block, one token per block, duplicates,
 empty sequences, no tokens, coordinates out of range).
 """
+import types
 import zlib
 
 import numpy as np
@@ -111,3 +112,21 @@ def test_out_of_range_coordinates_are_rejected_when_synced():
     gb = P.gpu_build(wl, sync=False)
     torch.cuda.synchronize()
     assert gb.counts.cpu().tolist()[2] == 2
+
+
+@pytest.mark.parametrize("lg", [20, 22])
+def test_large_random_build_bit_exact(lg):
+    """2^20 and 2^22 uniformly random voxels of a 1024^3 grid (duplicates
+    included) in three sequences: the multi-workgroup histogram scan and the
+    LDS-staged scatter at the sizes where they take over, nearly one token
+    per block."""
+    n = 1 << lg
+    rng = np.random.default_rng(lg)
+    coords = rng.integers(0, 1024, size=(n, 3))
+    cu = np.array([0, n // 3, n // 3 + 17, n], dtype=np.int32)
+    # the build needs only the geometry (no tensors at this size)
+    wl = types.SimpleNamespace(coords=coords.astype(np.int32), cu_seqlens=cu, grid_res=1024, m_cmp=4, m_win=8,
+                               win_shift=0)
+    print(f"large random build: N={n}", flush=True)
+    gb = P.gpu_build(wl)
+    P.check_build(gb, _oracle_blocks(wl))
