@@ -29,11 +29,10 @@
 //   summed afterwards in split order.
 //
 // kv_grad_mfma_kernel: the same block-major product for the token keys of
-//   the other two branches.  Selected branch: one workgroup per (group,
-//   block), the rows being every (query, head) whose top-k list holds the
-//   block (the inverted lists); window branch: one workgroup per (group,
-//   window), the rows being the window's own (query, head) pairs.  The key
-//   tile is up to 32 tokens of the block or window (sorted copies, in
+//   the selected branch (the window branch's token keys come from
+//   win_dkv_mfma_kernel): one workgroup per (group, block), the rows being
+//   every (query, head) whose top-k list holds the block (the inverted
+//   lists).  The key tile is up to 32 tokens of the block (sorted copies, in
 //   registers); each wave streams its own share of the rows (A operands
 //   straight from memory; the rows also go row-major into a wave-private LDS
 //   area, from which the transposed operands come back through gfx950's
@@ -706,11 +705,11 @@ win_dq_mfma_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------ token keys of the selected / window branch
+// ------------------------------------------------------------ token keys of the selected branch
 
-enum KvMode { kSelected = 1, kWindow = 2 };   // the branch index of each
+constexpr int kSelBranch = 1;   // the selected branch's slot in lse / delta / gates
 
-template <int D, int MODE>
+template <int D>
 __global__ void __launch_bounds__(256, 2)
 kv_grad_mfma_kernel(BwdParams p) {
   constexpr int KS = D / 16;
@@ -732,38 +731,30 @@ kv_grad_mfma_kernel(BwdParams p) {
   const int G = f.h_q / f.h_kv;
   const float c2 = f.scale * kLog2e;
   const int64_t nrow = static_cast<int64_t>(f.n) * f.h_q;
-  const float* lse = p.lse + MODE * nrow;
-  const float* dlt = p.delta + MODE * nrow;
+  const float* lse = p.lse + kSelBranch * nrow;
+  const float* dlt = p.delta + kSelBranch * nrow;
   const uint16_t* Q = static_cast<const uint16_t*>(f.q);
   const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
   const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
   uint16_t* qr = qr_lds + wv * kRT;
   uint16_t* dr = dr_lds + wv * kRT;
   float4* st = st_lds + wv * kKeyTile;
-  const int n_units = MODE == kSelected ? f.counts[SSA_COUNT_NB] : f.counts[SSA_COUNT_NW];
+  const int n_units = f.counts[SSA_COUNT_NB];
   const int64_t n_items = static_cast<int64_t>(n_units) * f.h_kv;
 
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int g = static_cast<int>(item / n_units);
     const int u = static_cast<int>(item % n_units);
-    int a, bnd, e0, R;
-    if (MODE == kSelected) {
-      const int64_t slot = static_cast<int64_t>(g) * f.nb_cap + u;
-      e0 = p.sel_off[slot];
-      R = (p.sel_off[slot + 1] - e0) * G;
-      a = f.blk_off[u];
-      bnd = f.blk_off[u + 1];
-    } else {
-      a = f.win_off[u];
-      bnd = f.win_off[u + 1];
-      e0 = a;
-      R = (bnd - a) * G;
-    }
+    const int64_t slot = static_cast<int64_t>(g) * f.nb_cap + u;
+    const int e0 = p.sel_off[slot];
+    const int R = (p.sel_off[slot + 1] - e0) * G;
+    const int a = f.blk_off[u];
+    const int bnd = f.blk_off[u + 1];
     if (R == 0) continue;
     const int n_rt = (R + kKeyTile - 1) / kKeyTile;
     // (query, head) of row rr of this item
     auto row_of = [&](int rr) -> int64_t {
-      const int t = MODE == kSelected ? p.sel_list[e0 + rr / G] : f.perm[e0 + rr / G];
+      const int t = p.sel_list[e0 + rr / G];
       return static_cast<int64_t>(t) * f.h_q + g * G + rr % G;
     };
     for (int k0 = a; k0 < bnd; k0 += kKeyTile) {
@@ -806,7 +797,7 @@ kv_grad_mfma_kernel(BwdParams p) {
             nq[ks] = *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * ks + 8 * half);
             nd[ks] = *reinterpret_cast<const u32x4*>(dO + qrow * D + 16 * ks + 8 * half);
           }
-          ns = make_float4(lse[qrow] * kLog2e, dlt[qrow], bf16_bits_to_f32(gates[qrow * 3 + MODE]), 0.f);
+          ns = make_float4(lse[qrow] * kLog2e, dlt[qrow], bf16_bits_to_f32(gates[qrow * 3 + kSelBranch]), 0.f);
         }
       };
       if (wv < n_rt) load(wv);
@@ -864,7 +855,7 @@ kv_grad_mfma_kernel(BwdParams p) {
         }
       }
       __syncthreads();
-      // add to the token rows (the window branch writes them first)
+      // add to the token rows (the window branch wrote them first)
       const int n_tok = min(kKeyTile, bnd - k0);
       for (int e = tid; e < n_tok * (D / 4); e += 256) {
         const int tok = e / (D / 4), d = 4 * (e % (D / 4));
@@ -873,12 +864,10 @@ kv_grad_mfma_kernel(BwdParams p) {
                                 f.scale * red_k[tok * D + d + 2], f.scale * red_k[tok * D + d + 3]);
         float4 rv = make_float4(red_v[tok * D + d], red_v[tok * D + d + 1], red_v[tok * D + d + 2],
                                 red_v[tok * D + d + 3]);
-        if (MODE == kSelected) {
-          const float4 ck = *reinterpret_cast<const float4*>(p.dk_acc + o);
-          const float4 cv = *reinterpret_cast<const float4*>(p.dv_acc + o);
-          rk.x += ck.x; rk.y += ck.y; rk.z += ck.z; rk.w += ck.w;
-          rv.x += cv.x; rv.y += cv.y; rv.z += cv.z; rv.w += cv.w;
-        }
+        const float4 ck = *reinterpret_cast<const float4*>(p.dk_acc + o);
+        const float4 cv = *reinterpret_cast<const float4*>(p.dv_acc + o);
+        rk.x += ck.x; rk.y += ck.y; rk.z += ck.z; rk.w += ck.w;
+        rv.x += cv.x; rv.y += cv.y; rv.z += cv.z; rv.w += cv.w;
         *reinterpret_cast<float4*>(p.dk_acc + o) = rk;
         *reinterpret_cast<float4*>(p.dv_acc + o) = rv;
       }
@@ -890,8 +879,8 @@ kv_grad_mfma_kernel(BwdParams p) {
 }  // namespace
 
 hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  if (p.f.d == 32) kv_grad_mfma_kernel<32, kSelected><<<8192, 256, 0, stream>>>(p);
-  else kv_grad_mfma_kernel<64, kSelected><<<8192, 256, 0, stream>>>(p);
+  if (p.f.d == 32) kv_grad_mfma_kernel<32><<<8192, 256, 0, stream>>>(p);
+  else kv_grad_mfma_kernel<64><<<8192, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
