@@ -23,12 +23,12 @@
 //    (token, head) pairs, 2 tokens x 16 heads, and the columns 32 blocks.  A
 //    lane then holds one block and 8 heads of each token, so the group sum is
 //    8 in-lane adds and one add across the lane halves.  Each lane keeps,
-//    per token, its 8 best (score, block) pairs in float32 (an insertion
+//    per token, its kLane = 6 best (score, block) pairs in float32 (an insertion
 //    network: one v_med3 for the scores and two selects for the ids per
 //    slot), and the 32 lanes' lists are merged by repeated wave maxima (equal
 //    scores: lower block first).  A workgroup owns 16 sorted tokens of one
 //    sequence and one group (4 waves x 2 row blocks).  A (token, group) pair
-//    for which one lane's 8 kept pairs all reach the top k, while that lane
+//    for which one lane's 6 kept pairs all reach the top k, while that lane
 //    saw more blocks than it kept, is queued for gqa_fixup_kernel, which
 //    ranks all blocks of the sequence exactly.
 #include <float.h>
@@ -48,7 +48,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kGroup = 16;            // query heads per key/value head on this path
 constexpr int kTopkTile = 16;         // sorted tokens per workgroup of the top-k kernel
-constexpr int kLane = 8;              // (score, block) pairs kept per lane and token
+// (score, block) pairs kept per lane and token.  A lane sees every 32nd block,
+// so it rarely holds more than 5 of a query's top 16: measured on the
+// 262144-token grouped workload, 8 pairs cost 18.8 ms with no fallback, 6
+// pairs 17.0 ms plus 0.16 ms of fallback, 4 pairs 15.7 ms plus 5.4 ms.
+constexpr int kLane = 6;
 constexpr float kRescale = 8.0f;      // log2 headroom before the running shift moves
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
