@@ -180,10 +180,13 @@ def test_varlen_workload5_sampled():
     _sampled_compare(5, 256, branches=False)
 
 
-@pytest.mark.parametrize("h_q,h_kv,head_dim", [(4, 2, 64), (16, 1, 32), (32, 2, 64)])
-def test_zero_queries_pick_first_blocks(h_q, h_kv, head_dim):
+@pytest.mark.parametrize("h_q,h_kv,head_dim,topk", [(4, 2, 64, 16), (16, 1, 32, 16), (32, 2, 64, 16),
+                                                   (4, 4, 64, 16), (4, 4, 64, 32)])
+def test_zero_queries_pick_first_blocks(h_q, h_kv, head_dim, topk):
     # every score ties, so the lowest block ids of the sequence are chosen
-    wl = make_custom([1200, 500], grid_res=64, n_prims=3, topk=16, h_q=h_q, h_kv=h_kv,
+    # (on the one-head-per-group kernel every query overflows its candidate
+    # list and goes to the exact fallback)
+    wl = make_custom([1200, 500], grid_res=64, n_prims=3, topk=topk, h_q=h_q, h_kv=h_kv,
                      head_dim=head_dim, dtype="bf16", seed=31)
     wl.q[:] = 0
     ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
@@ -193,7 +196,7 @@ def test_zero_queries_pick_first_blocks(h_q, h_kv, head_dim):
     for b in range(wl.batch):
         j0, j1 = ob.seq_blk_off[b], ob.seq_blk_off[b + 1]
         toks = ob.perm[ob.blk_off[j0]:ob.blk_off[j1]]
-        expect = np.arange(j0, min(j0 + 16, j1))
+        expect = np.arange(j0, min(j0 + topk, j1))
         assert (sel[toks][:, :, :len(expect)] == expect).all()
 
 
