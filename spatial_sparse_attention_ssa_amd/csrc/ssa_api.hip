@@ -406,8 +406,8 @@ namespace {
 
 struct BwdLayout {
   size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_keys, sel_vals, sel_keys_tmp,
-      sel_vals_tmp, sel_hist, sel_off, kbar_t, qtile_pre, btile_pre, dkbar_part, dvbar_part, q_rows, do_rows,
-      q_rt, do_rt, st_rows, total;
+      sel_vals_tmp, sel_hist, sel_off, qtile_pre, btile_pre, dkbar_part, dvbar_part, q_rows, do_rows,
+      st_rows, total;
 };
 
 // the sorted (query, head) rows of one group, rounded up to whole 32-row tiles
@@ -460,14 +460,11 @@ BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
   L.sel_hist = off; off += align256(ssa::sort_pairs_hist_bytes(static_cast<int64_t>(m)));
   L.sel_off = off; off += align256(sizeof(int32_t) * (a->h_kv * cap + 1));
   if (use_mfma_backward(a)) {
-    L.kbar_t = off; off += pooled;
     L.qtile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     L.btile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     const size_t rows = static_cast<size_t>(a->h_kv) * static_cast<size_t>(rows_capacity(b, a));
     L.q_rows = off; off += align256(eb * rows * D);
     L.do_rows = off; off += align256(eb * rows * D);
-    L.q_rt = off; off += align256(eb * rows * D);
-    L.do_rt = off; off += align256(eb * rows * D);
     L.st_rows = off; off += align256(4 * sizeof(float) * 2 * rows);
     const size_t splits = static_cast<size_t>(dkv_row_splits(b, a));
     if (splits > 1) {
@@ -587,7 +584,6 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
   bp.sel_sorted_keys = in_tmp ? bp.sel_keys_tmp : bp.sel_keys;
   bp.sel_off = reinterpret_cast<int32_t*>(w + lay.sel_off);
   if (use_mfma_backward(attn)) {
-    bp.kbar_t = w + lay.kbar_t;
     bp.qtile_pre = reinterpret_cast<int32_t*>(w + lay.qtile_pre);
     bp.btile_pre = reinterpret_cast<int32_t*>(w + lay.btile_pre);
     bp.max_qtiles = static_cast<int32_t>(blocks->n_tokens / 128 + blocks->batch + 1);
@@ -596,8 +592,6 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
     bp.rows_cap = static_cast<int32_t>(rows_capacity(blocks, attn));
     bp.q_rows = w + lay.q_rows;
     bp.do_rows = w + lay.do_rows;
-    bp.q_rt = w + lay.q_rt;
-    bp.do_rt = w + lay.do_rt;
     bp.st_rows = reinterpret_cast<float4*>(w + lay.st_rows);
     if (bp.row_splits > 1) {
       bp.dkbar_part = reinterpret_cast<float*>(w + lay.dkbar_part);

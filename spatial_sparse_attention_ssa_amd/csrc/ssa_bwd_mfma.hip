@@ -54,18 +54,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQT = 128;  // sorted queries per workgroup of the dq kernel (4 waves x 32)
 constexpr int kBT = 4;    // 32-block tiles per workgroup of the dkv kernel (one per wave)
-constexpr int kTRow = kKeyTile + 8;  // padded row (bf16) of a transposed 32-wide tile
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// Position of row r of a 32-row tile in the k order of the MFMA operand that
-// the 32x32 accumulator feeds: lane half 0 holds rows {0-3, 8-11} of each
-// 16-row half, lane half 1 rows {4-7, 12-15}.  Its own inverse.
-__device__ __forceinline__ int mfma_pos(int r) {
-  const int lo = r & 15;
-  return (r & 16) | (lo & 3) | ((lo & 4) << 1) | ((lo & 8) >> 1);
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
@@ -120,10 +111,8 @@ cmp_dq_mfma_kernel(BwdParams p) {
   constexpr int kKRow = D + 8;        // padded key / value row (bf16)
   constexpr int kRowCh = kKeyTile * D / 8;   // 16-byte chunks of a 32-row tile
   constexpr int kKT = kKeyTile * kKRow;
-  constexpr int kTT = D * kTRow;
   __shared__ __align__(16) uint16_t k_lds[2 * kKT];
   __shared__ __align__(16) uint16_t v_lds[2 * kKT];
-  __shared__ __align__(16) uint16_t t_lds[2 * kTT];
 
   const FwdParams& f = p.f;
   const int tid = threadIdx.x;
@@ -160,32 +149,27 @@ cmp_dq_mfma_kernel(BwdParams p) {
   const int kt0 = j0 / kKeyTile;
   const int n_kt = (j1 + kKeyTile - 1) / kKeyTile - kt0;
 
-  // staging: thread tid moves chunk tid of the key rows, of the value rows
-  // and of the transposed key tile (D = 32: threads below 128 only)
+  // staging: thread tid moves chunk tid of the key rows and of the value rows
+  // (D = 32: threads below 128 only); the key rows serve both as they are
+  // (S = K Q^T) and through the transposing LDS load (dq^T += K^T dS^T)
   const uint16_t* KB = static_cast<const uint16_t*>(f.kbar) + static_cast<int64_t>(g) * f.nb_cap * D;
   const uint16_t* VBR = static_cast<const uint16_t*>(f.vbar) + static_cast<int64_t>(g) * f.nb_cap * D;
-  const uint16_t* KT = static_cast<const uint16_t*>(p.kbar_t) + static_cast<int64_t>(g) * f.nb_cap * D;
   const bool stager = tid < kRowCh;
   const int r_row = tid / (D / 8), r_c = tid % (D / 8);   // key / value rows: row, 8-dim chunk
-  const int t_dim = tid >> 2, t_c = tid & 3;              // transposed tile: dim, 8-position chunk
   const int64_t src_r = static_cast<int64_t>(r_row) * D + 8 * r_c;
-  const int64_t src_t = static_cast<int64_t>(t_dim) * kKeyTile + 8 * t_c;
   const int dst_r = r_row * kKRow + 8 * r_c;
-  const int dst_t = t_dim * kTRow + 8 * t_c;
-  u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u}, rt = {0u, 0u, 0u, 0u};
+  u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
   auto load = [&](int kt) {
     if (stager) {
       const int64_t base = static_cast<int64_t>(kt) * kKeyTile * D;
       rk = *reinterpret_cast<const u32x4*>(KB + base + src_r);
       rv = *reinterpret_cast<const u32x4*>(VBR + base + src_r);
-      rt = *reinterpret_cast<const u32x4*>(KT + base + src_t);
     }
   };
   auto store = [&](int slot) {
     if (stager) {
       *reinterpret_cast<u32x4*>(k_lds + slot * kKT + dst_r) = rk;
       *reinterpret_cast<u32x4*>(v_lds + slot * kKT + dst_r) = rv;
-      *reinterpret_cast<u32x4*>(t_lds + slot * kTT + dst_t) = rt;
     }
   };
 
@@ -223,14 +207,13 @@ cmp_dq_mfma_kernel(BwdParams p) {
       pd[r] = x * dp[r];
       dl += pd[r];
     }
-    const uint16_t* tl = t_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 pdb = pack8(pd + 8 * ks);
       const bf16x8 pb = pack8(pr + 8 * ks);
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
-        const bf16x8 a = lds_b128(tl + vb * 32 * kTRow + 16 * ks);
+        const bf16x8 a = lds_tr_operand<kKRow>(k_lds + slot * kKT, lane, vb, ks);
         aa[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pdb, aa[vb], 0, 0, 0);
         ab[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ab[vb], 0, 0, 0);
       }
@@ -262,16 +245,13 @@ cmp_dq_mfma_kernel(BwdParams p) {
 
 // Row R = i * G + hh of group g is query head g * G + hh of the token at
 // sorted position i.  rows_prep_kernel writes, per group, the rows of Q and
-// dO in that order (row-major), the same rows as 32-row tiles transposed in
-// MFMA operand order ([D][32], row r at position mfma_pos(r)), and per row
-// (log2 lse, Delta, gate) of the compressed and the window branch.  The
-// block- and window-major gradient kernels then stage whole 16-byte chunks.
+// dO in that order (row-major) and per row (log2 lse, Delta, gate) of the
+// compressed and the window branch.  The block- and window-major gradient
+// kernels then stage whole 16-byte chunks.
 template <int D>
 __global__ void __launch_bounds__(256)
 rows_prep_kernel(BwdParams p) {
   constexpr int CPR = D / 8;
-  __shared__ uint16_t tq[kKeyTile][D + 2];
-  __shared__ uint16_t td[kKeyTile][D + 2];
   const FwdParams& f = p.f;
   const int tid = threadIdx.x;
   const int G = f.h_q / f.h_kv;
@@ -296,13 +276,6 @@ rows_prep_kernel(BwdParams p) {
       }
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.q_rows) + (rbase + row) * D + 8 * c) = uq;
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.do_rows) + (rbase + row) * D + 8 * c) = ud;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tq[row][8 * c + 2 * e] = static_cast<uint16_t>(uq[e] & 0xFFFFu);
-        tq[row][8 * c + 2 * e + 1] = static_cast<uint16_t>(uq[e] >> 16);
-        td[row][8 * c + 2 * e] = static_cast<uint16_t>(ud[e] & 0xFFFFu);
-        td[row][8 * c + 2 * e + 1] = static_cast<uint16_t>(ud[e] >> 16);
-      }
     }
     if (tid < kKeyTile) {
       const int64_t R = static_cast<int64_t>(T) * kKeyTile + tid;
@@ -316,21 +289,6 @@ rows_prep_kernel(BwdParams p) {
       p.st_rows[rbase + tid] = s0;
       p.st_rows[static_cast<int64_t>(f.h_kv) * p.rows_cap + rbase + tid] = s2;
     }
-    __syncthreads();
-    if (tid < D * 4) {
-      const int dd = tid >> 2, c = tid & 3;
-      u32x4 uq, ud;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = mfma_pos(8 * c + 2 * e), r1 = mfma_pos(8 * c + 2 * e + 1);
-        uq[e] = static_cast<uint32_t>(tq[r0][dd]) | (static_cast<uint32_t>(tq[r1][dd]) << 16);
-        ud[e] = static_cast<uint32_t>(td[r0][dd]) | (static_cast<uint32_t>(td[r1][dd]) << 16);
-      }
-      const int64_t o = ((static_cast<int64_t>(g) * ntile + T) * D + dd) * kKeyTile + 8 * c;
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.q_rt) + o) = uq;
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.do_rt) + o) = ud;
-    }
-    __syncthreads();
   }
 }
 
@@ -339,22 +297,21 @@ rows_prep_kernel(BwdParams p) {
 // One workgroup, four waves, each wave one 32-key tile (its key and value
 // rows in registers as MFMA B operands).  The rows [r_lo, r_hi) of group g
 // (sorted row space, tiles aligned to 32; rows outside the range get P = 0)
-// stream through a two-slot LDS ring: row-major (A operands of S = Q K^T and
-// dP = dO V^T) and transposed (A operands of dV^T += dO^T (gate P)^T and
-// dK^T += Q^T (gate P (dP - Delta))^T).  Tiles [t_beg, t_end) of the range
+// stream through a two-slot LDS ring, row-major: read as they are for the A
+// operands of S = Q K^T and dP = dO V^T, and with the transposing LDS load
+// for those of dV^T += dO^T (gate P)^T and dK^T += Q^T (gate P (dP - Delta))^T.
+// Tiles [t_beg, t_end) of the range
 // are this workgroup's share.  Writes scale * dK and dV rows of the valid
 // keys to dk_row / dv_row (null: nothing to write).
 template <int D>
 __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wave_on, const uint16_t* k_row,
                                               const uint16_t* v_row, int64_t r_lo, int64_t r_hi, int t_beg,
                                               int t_end, const float4* st, float* dk_row, float* dv_row,
-                                              uint16_t* q_lds, uint16_t* d_lds, uint16_t* qt_lds,
-                                              uint16_t* dt_lds, float4* st_lds) {
+                                              uint16_t* q_lds, uint16_t* d_lds, float4* st_lds) {
   constexpr int KS = D / 16;
   constexpr int VB = D / 32;
   constexpr int kRRow = D + 8;
   constexpr int kRT = kKeyTile * kRRow;
-  constexpr int kTT = D * kTRow;
   constexpr int CPR = D / 8;
   const FwdParams& f = p.f;
   const int tid = threadIdx.x;
@@ -372,25 +329,18 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
     kb[ks] = __builtin_bit_cast(bf16x8, a);
     vb[ks] = __builtin_bit_cast(bf16x8, c);
   }
-  const int ntile = p.rows_cap / kKeyTile;
   const uint16_t* QR = static_cast<const uint16_t*>(p.q_rows) + static_cast<int64_t>(g) * p.rows_cap * D;
   const uint16_t* DR = static_cast<const uint16_t*>(p.do_rows) + static_cast<int64_t>(g) * p.rows_cap * D;
-  const uint16_t* QT = static_cast<const uint16_t*>(p.q_rt) + static_cast<int64_t>(g) * ntile * D * kKeyTile;
-  const uint16_t* DT = static_cast<const uint16_t*>(p.do_rt) + static_cast<int64_t>(g) * ntile * D * kKeyTile;
-  // staging: thread tid moves chunk tid of each of the four tiles
+  // staging: thread tid moves chunk tid of each of the two tiles
   const bool stager = tid < kKeyTile * CPR;
-  const int r_row = tid / CPR, r_c = tid % CPR;    // row-major: row, 8-dim chunk
-  const int t_dim = tid >> 2, t_c = tid & 3;       // transposed: dim, 8-position chunk
-  u32x4 rq = {0u, 0u, 0u, 0u}, rd = rq, tq = rq, td = rq;
+  const int r_row = tid / CPR, r_c = tid % CPR;    // row, 8-dim chunk
+  u32x4 rq = {0u, 0u, 0u, 0u}, rd = rq;
   float4 rs = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
   auto load = [&](int T) {
     if (stager) {
       const int64_t ro = (static_cast<int64_t>(T) * kKeyTile + r_row) * D + 8 * r_c;
-      const int64_t to = (static_cast<int64_t>(T) * D + t_dim) * kKeyTile + 8 * t_c;
       rq = *reinterpret_cast<const u32x4*>(QR + ro);
       rd = *reinterpret_cast<const u32x4*>(DR + ro);
-      tq = *reinterpret_cast<const u32x4*>(QT + to);
-      td = *reinterpret_cast<const u32x4*>(DT + to);
     }
     if (tid < kKeyTile) {
       const int64_t R = static_cast<int64_t>(T) * kKeyTile + tid;
@@ -401,8 +351,6 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
     if (stager) {
       *reinterpret_cast<u32x4*>(q_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rq;
       *reinterpret_cast<u32x4*>(d_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rd;
-      *reinterpret_cast<u32x4*>(qt_lds + slot * kTT + t_dim * kTRow + 8 * t_c) = tq;
-      *reinterpret_cast<u32x4*>(dt_lds + slot * kTT + t_dim * kTRow + 8 * t_c) = td;
     }
     if (tid < kKeyTile) st_lds[slot * kKeyTile + tid] = rs;
   };
@@ -433,8 +381,6 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ql + 16 * ks), kb[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dl + 16 * ks), vb[ks], dp, 0, 0, 0);
     }
-    const uint16_t* qt = qt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
-    const uint16_t* dt = dt_lds + slot * kTT + (lane & 31) * kTRow + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile, for this key
@@ -451,8 +397,10 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
       const bf16x8 sb = pack8(ds);
 #pragma unroll
       for (int x = 0; x < VB; ++x) {
-        dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dt + x * 32 * kTRow + 16 * ks), pb, dv[x], 0, 0, 0);
-        dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qt + x * 32 * kTRow + 16 * ks), sb, dk[x], 0, 0, 0);
+        dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand<kRRow>(d_lds + slot * kRT, lane, x, ks), pb,
+                                                        dv[x], 0, 0, 0);
+        dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand<kRRow>(q_lds + slot * kRT, lane, x, ks), sb,
+                                                        dk[x], 0, 0, 0);
       }
     }
   }
@@ -473,8 +421,6 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
 #define SSA_ROWS_LDS(D)                                                   \
   __shared__ __align__(16) uint16_t q_lds[2 * kKeyTile * ((D) + 8)];    \
   __shared__ __align__(16) uint16_t d_lds[2 * kKeyTile * ((D) + 8)];    \
-  __shared__ __align__(16) uint16_t qt_lds[2 * (D) * kTRow];            \
-  __shared__ __align__(16) uint16_t dt_lds[2 * (D) * kTRow];            \
   __shared__ float4 st_lds[2 * kKeyTile]
 
 // Pooled-row gradients: a workgroup owns 128 blocks (a 32-block tile per
@@ -510,7 +456,7 @@ cmp_dkv_mfma_kernel(BwdParams p) {
   rows_dkv_body<D>(p, g, wave_on, wave_on ? static_cast<const uint16_t*>(f.kbar) + krow : nullptr,
                    static_cast<const uint16_t*>(f.vbar) + krow, r_lo, r_hi, t_beg, t_end,
                    p.st_rows + static_cast<int64_t>(g) * p.rows_cap, jok ? ok + krow : nullptr,
-                   ov + krow, q_lds, d_lds, qt_lds, dt_lds, st_lds);
+                   ov + krow, q_lds, d_lds, st_lds);
 }
 
 // Window tokens' key / value gradients (first writer of dk_acc / dv_acc): a
@@ -545,7 +491,7 @@ win_dkv_mfma_kernel(BwdParams p) {
     rows_dkv_body<D>(p, g, wave_on, iok ? static_cast<const uint16_t*>(f.k_s) + krow : nullptr,
                      static_cast<const uint16_t*>(f.v_s) + krow, r_lo, r_hi, T0, T1,
                      p.st_rows + (static_cast<int64_t>(f.h_kv) + g) * p.rows_cap,
-                     iok ? p.dk_acc + krow : nullptr, p.dv_acc + krow, q_lds, d_lds, qt_lds, dt_lds, st_lds);
+                     iok ? p.dk_acc + krow : nullptr, p.dv_acc + krow, q_lds, d_lds, st_lds);
     __syncthreads();  // the ring is reused by the next item
   }
 }
@@ -905,8 +851,6 @@ hipError_t launch_bwd_win_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 }
 
 hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  hipError_t e = launch_tile_transpose(p.f.kbar, p.kbar_t, p.f.counts, p.f.h_kv, p.f.nb_cap, p.f.d, stream);
-  if (e != hipSuccess) return e;
   bwd_tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
   const dim3 grid(p.max_qtiles, p.f.h_q);
   if (p.f.d == 32) cmp_dq_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);

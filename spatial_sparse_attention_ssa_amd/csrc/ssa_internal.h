@@ -221,7 +221,6 @@ struct BwdParams {
   int32_t* sel_list;    // the sorted tokens (one of the two value buffers)
   const uint32_t* sel_sorted_keys;   // the sorted keys (one of the two key buffers)
   // MFMA kernels of the compressed branch (bf16)
-  void* kbar_t;         // [h_kv][nb_cap / 32][D][32] pooled keys, each 32-block tile transposed
   int32_t* qtile_pre;   // [batch + 1] prefix of 128-query tiles per sequence
   int32_t* btile_pre;   // [batch + 1] prefix of 128-block chunks per sequence
   int32_t max_qtiles;   // grid bounds of the two
@@ -231,8 +230,6 @@ struct BwdParams {
   int32_t rows_cap;     // n * G rounded up to 32
   void* q_rows;         // [h_kv][rows_cap][D] Q rows (bf16)
   void* do_rows;        // [h_kv][rows_cap][D] dO rows
-  void* q_rt;           // [h_kv][rows_cap / 32][D][32] the same, 32-row tiles transposed
-  void* do_rt;
   float4* st_rows;      // [2][h_kv][rows_cap] (log2 lse, Delta, gate) of the compressed / window branch
   int32_t row_splits;   // the pooled-row gradients are summed over this many row ranges
   float* dkbar_part;    // [row_splits][h_kv][nb_cap][D] partial sums (row_splits > 1)
@@ -248,11 +245,6 @@ hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype dtype, hipStream_t strea
 hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_geo_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
-
-// [h_kv][nb_cap][D] -> [h_kv][nb_cap / 32][D][32] per 32-block tile, rows in
-// the order of the MFMA operands (ssa_pool.hip)
-hipError_t launch_tile_transpose(const void* src, void* dst, const int32_t* counts, int hkv, int nb_cap, int d,
-                                 hipStream_t stream);
 
 // backward stages (ssa_bwd.hip, ssa_bwd_mfma.hip)
 hipError_t launch_bwd_pool(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);

@@ -207,19 +207,6 @@ vt_transpose_kernel(const uint16_t* __restrict__ vbar, uint16_t* __restrict__ vb
 
 }  // namespace
 
-hipError_t launch_tile_transpose(const void* src, void* dst, const int32_t* counts, int hkv, int nb_cap, int d,
-                                 hipStream_t stream) {
-  const int tiles = hkv * (nb_cap / kKeyTile);
-  const int grid_t = tiles < 4096 ? tiles : 4096;
-  if (d == 32)
-    vt_transpose_kernel<32><<<grid_t, 256, 0, stream>>>(static_cast<const uint16_t*>(src),
-                                                         static_cast<uint16_t*>(dst), counts, hkv, nb_cap);
-  else
-    vt_transpose_kernel<64><<<grid_t, 256, 0, stream>>>(static_cast<const uint16_t*>(src),
-                                                         static_cast<uint16_t*>(dst), counts, hkv, nb_cap);
-  return hipGetLastError();
-}
-
 hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) {
   const int grid = p.nb_cap < 8192 ? p.nb_cap : 8192;
   if (dtype == SSA_BF16) {
