@@ -26,14 +26,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kChunk = 256;            // window tokens staged in LDS at a time
+// window tokens staged in LDS at a time: 128 (about the mean window size)
+// keeps the LDS of four workgroups per compute unit within its 160 KB, twice
+// the occupancy of 256-token chunks; larger windows take several chunks
+constexpr int kChunk = 128;
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 4)
 win_mfma_kernel(FwdParams p) {
   constexpr int kD = D;
   constexpr int KSTEPS = D / 16;         // MFMA k steps over the dims
@@ -60,9 +63,9 @@ win_mfma_kernel(FwdParams p) {
     const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(kvh) * p.n * kD;
     const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(kvh) * p.n * kD;
 
-    // query groups of 32 (round robin over the waves); every key chunk is
-    // staged once per group round, so windows up to kChunk tokens and 128
-    // queries are staged exactly once
+    // 128 queries per group round (32 per wave); every key chunk is staged
+    // once per group round, so windows of up to 128 tokens are staged exactly
+    // once
     for (int qg0 = 0; qg0 < n_w; qg0 += 128) {
       const int qi = wa + qg0 + wv * 32 + (lane & 31);
       const bool q_valid = qi < wb;
@@ -170,8 +173,8 @@ win_mfma_kernel(FwdParams p) {
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   // persistent grid over (window, head) items; the window count is read on
   // the device, so the grid does not depend on it
-  if (p.d == 32) win_mfma_kernel<32><<<2048, 256, 0, stream>>>(p);
-  else win_mfma_kernel<64><<<2048, 256, 0, stream>>>(p);
+  if (p.d == 32) win_mfma_kernel<32><<<4096, 256, 0, stream>>>(p);
+  else win_mfma_kernel<64><<<4096, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

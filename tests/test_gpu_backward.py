@@ -97,6 +97,14 @@ def test_shifted_windows_backward_full():
     _full_compare(wl, seed=6)
 
 
+def test_large_windows_backward_full():
+    # 2900 of the 4096 voxels of a 16^3 grid: eight windows of about 360 tokens
+    from tests.test_gpu_forward import dense_cube
+    wl = make_custom(None, coords=dense_cube(2900, 16, 11), grid_res=16, m_cmp=4, m_win=8, topk=8, h_q=4, h_kv=4,
+                     head_dim=64, dtype="bf16", seed=13)
+    _full_compare(wl, seed=8)
+
+
 def test_geometric_routing_backward_full():
     wl = make_custom([700, 300], grid_res=64, n_prims=3, topk=8, h_q=4, h_kv=4, head_dim=64,
                      dtype="bf16", seed=31, routing="geometric")

@@ -230,6 +230,23 @@ def test_gqa_top_blocks_in_one_lane(head_dim):
     assert np.isin(sel[:, 0, :], fav).mean() > 0.99
 
 
+def dense_cube(n, side, seed):
+    """n distinct voxels drawn uniformly from a side^3 grid"""
+    rng = np.random.default_rng(seed)
+    lin = rng.choice(side ** 3, size=n, replace=False)
+    return np.stack(np.unravel_index(lin, (side,) * 3), -1)
+
+
+@pytest.mark.parametrize("h_q,h_kv,head_dim", [(4, 4, 64), (16, 1, 32)])
+def test_large_windows_full(h_q, h_kv, head_dim):
+    # 2900 of the 4096 voxels of a 16^3 grid: eight windows of about 360
+    # tokens, each staged by the window kernel in several chunks
+    wl = make_custom(None, coords=dense_cube(2900, 16, 11), grid_res=16, m_cmp=4, m_win=8, topk=8, h_q=h_q,
+                     h_kv=h_kv, head_dim=head_dim, dtype="bf16", seed=13)
+    assert np.diff(P.oracle_blocks(wl).win_off).min() > 256
+    _full_compare(wl)
+
+
 def test_dense_reduction():
     # one window over the grid, voxel blocks, top-k covering every block:
     # every branch is dense attention and out = (G0 + G1 + G2) * dense
