@@ -230,6 +230,49 @@ def summarize_mfma(pmc_csv: str, wid: int):
         print(f"\ntime-weighted MFMA busy share over these kernels: {100 * tw_busy / tw_t:.1f} %")
 
 
+MEMPATH_COUNTERS = ("TA_TA_BUSY", "TA_DATA_STALLED_BY_TC_CYCLES", "TCP_TCC_READ_REQ", "TCP_TOTAL_CACHE_ACCESSES",
+                    "TCP_PENDING_STALL_CYCLES", "TCP_TCC_READ_REQ_LATENCY", "TCC_HIT", "TCC_MISS", "GRBM_GUI_ACTIVE",
+                    "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_VMEM_RD")
+N_CU = 256
+
+
+def summarize_mempath(pmc_csv: str):
+    """Memory-path counters per SSA kernel from one rocprofv3 --pmc run of
+    MEMPATH_COUNTERS: the texture addresser's busy share and its share stalled
+    by the cache (both over cycles x 256 compute units), the L2 hit rate, the
+    mean L1-to-L2 read latency in cycles, the L1's pending-request stall share,
+    and vector-memory read instructions per launch; prints a markdown table."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    per = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    with open(pmc_csv) as fh:
+        for r in csv.DictReader(fh):
+            m = re.search(r"ssa::\(anonymous namespace\)::(\w+)", r["Kernel_Name"])
+            if not m:
+                continue
+            per[m.group(1)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur[m.group(1)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    print("| kernel | launches | avg us | TA busy % | TA stalled by cache % | L2 hit % | L2 read latency (cycles) | "
+          "L1 pending-stall % | VMEM read insts |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, c in per.items():
+        avg = lambda k: sum(c[k]) / len(c[k])
+        t = sum(dur[name]) / len(dur[name])
+        if t < 50e-6:
+            continue
+        cu_cycles = avg("GRBM_GUI_ACTIVE") / N_XCC * N_CU
+        hits, miss = avg("TCC_HIT"), avg("TCC_MISS")
+        req = avg("TCP_TCC_READ_REQ")
+        lat = avg("TCP_TCC_READ_REQ_LATENCY") / req if req else 0.0
+        print(f"| {name} | {len(c['GRBM_GUI_ACTIVE'])} | {t * 1e6:.1f} | {100 * avg('TA_TA_BUSY') / cu_cycles:.0f} | "
+              f"{100 * avg('TA_DATA_STALLED_BY_TC_CYCLES') / cu_cycles:.0f} | {100 * hits / max(hits + miss, 1):.0f} | "
+              f"{lat:.0f} | {100 * avg('TCP_PENDING_STALL_CYCLES') / cu_cycles:.0f} | {avg('SQ_INSTS_VMEM_RD'):.3g} |")
+
+
 def build_bytes(n: int, nb: int, nw: int, batch: int) -> float:
     """Algorithmic HBM bytes of the block build: coordinates read (12 B per
     token), the permutation written (4 B per token), the segment offsets and
@@ -326,6 +369,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only summarise two rocprofv3 --pmc runs into profiles/*_traffic.json")
     ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
+    ap.add_argument("--summarize-mempath", metavar="PMC_CSV",
+                    help="print the memory-path counter table of one rocprofv3 --pmc run of MEMPATH_COUNTERS")
     ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
                     help="only summarise a rocprofv3 --pmc run of the MFMA counters into a markdown table")
     ap.add_argument("--build-sweep", action="store_true",
@@ -342,6 +387,9 @@ def main():
                 for c in ("FETCH_SIZE", "WRITE_SIZE")}
         cmds = {"fetch": cmds["fetch_size"], "write": cmds["write_size"]}
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel_stats, cmds, wid)
+        return
+    if args.summarize_mempath:
+        summarize_mempath(args.summarize_mempath)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, wid)
