@@ -406,7 +406,7 @@ namespace {
 
 struct BwdLayout {
   size_t kbar, vbar, k_s, v_s, delta, dq_acc, dk_acc, dv_acc, dkbar, dvbar, sel_keys, sel_vals, sel_keys_tmp,
-      sel_vals_tmp, sel_hist, sel_off, qtile_pre, btile_pre, dkbar_part, dvbar_part, q_rows, do_rows,
+      sel_vals_tmp, sel_hist, sel_off, qtile_pre, btile_pre, seq_order, dkbar_part, dvbar_part, q_rows, do_rows,
       st_rows, total;
 };
 
@@ -462,6 +462,7 @@ BwdLayout backward_layout(const ssa_blocks* b, const ssa_attn* a) {
   if (use_mfma_backward(a)) {
     L.qtile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     L.btile_pre = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    L.seq_order = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
     const size_t rows = static_cast<size_t>(a->h_kv) * static_cast<size_t>(rows_capacity(b, a));
     L.q_rows = off; off += align256(eb * rows * D);
     L.do_rows = off; off += align256(eb * rows * D);
@@ -586,6 +587,7 @@ ssa_status backward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const v
   if (use_mfma_backward(attn)) {
     bp.qtile_pre = reinterpret_cast<int32_t*>(w + lay.qtile_pre);
     bp.btile_pre = reinterpret_cast<int32_t*>(w + lay.btile_pre);
+    bp.seq_order = reinterpret_cast<int32_t*>(w + lay.seq_order);
     bp.max_qtiles = static_cast<int32_t>(blocks->n_tokens / 128 + blocks->batch + 1);
     bp.max_btiles = max_block_chunks(blocks);
     bp.row_splits = dkv_row_splits(blocks, attn);

@@ -83,22 +83,52 @@ __device__ __forceinline__ int find_seq(const int32_t* pre, int batch, int tile)
   return lo;
 }
 
-__global__ void bwd_tile_prefix_kernel(BwdParams p) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// Up to this many sequences are put in cost order (more, and the tail of
+// the grid is short anyway).
+constexpr int kOrderMax = 1024;
+
+// Tile prefixes of the two compressed-branch gradient kernels.  The
+// query-tile prefix follows the sequence order; the block-chunk prefix
+// follows seq_order, the sequences by decreasing token count, since a
+// pooled-row workgroup costs in proportion to its sequence's rows: with the
+// chunk index slowest in that kernel's grid, the costliest workgroups start
+// first and the short ones fill the end (longest-first list scheduling).
+__global__ void __launch_bounds__(256) bwd_tile_prefix_kernel(BwdParams p) {
+  __shared__ int len[kOrderMax];
+  __shared__ int ord[kOrderMax];
+  const int batch = p.f.batch;
+  const bool order = batch <= kOrderMax;
+  if (order) {
+    for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+      int s0, s1, j0, j1;
+      seq_bounds(p.f, b, &s0, &s1, &j0, &j1);
+      len[b] = s1 - s0;
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+      int rank = 0;
+      for (int c = 0; c < batch; ++c) rank += (len[c] > len[b] || (len[c] == len[b] && c < b)) ? 1 : 0;
+      ord[rank] = b;
+    }
+    __syncthreads();
+  }
+  for (int r = threadIdx.x; r < batch; r += blockDim.x) p.seq_order[r] = order ? ord[r] : r;
+  if (threadIdx.x != 0) return;
   int rq = 0, rb = 0;
-  for (int b = 0; b < p.f.batch; ++b) {
-    p.qtile_pre[b] = rq;
-    p.btile_pre[b] = rb;
+  for (int r = 0; r < batch; ++r) {
+    p.qtile_pre[r] = rq;
+    p.btile_pre[r] = rb;
     int s0, s1, j0, j1;
-    seq_bounds(p.f, b, &s0, &s1, &j0, &j1);
+    seq_bounds(p.f, r, &s0, &s1, &j0, &j1);
     rq += (s1 - s0 + kQT - 1) / kQT;
+    seq_bounds(p.f, order ? ord[r] : r, &s0, &s1, &j0, &j1);
     if (j1 > j0) {
       const int tiles = (j1 + kKeyTile - 1) / kKeyTile - j0 / kKeyTile;
       rb += (tiles + kBT - 1) / kBT;
     }
   }
-  p.qtile_pre[p.f.batch] = rq;
-  p.btile_pre[p.f.batch] = rb;
+  p.qtile_pre[batch] = rq;
+  p.btile_pre[batch] = rb;
 }
 
 // ------------------------------------------------------------ dq (query-major)
@@ -427,7 +457,9 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
   __shared__ float4 st_lds[2 * kKeyTile]
 
 // Pooled-row gradients: a workgroup owns 128 blocks (a 32-block tile per
-// wave) of one sequence and group, over split z of the sequence's rows.
+// wave) of one sequence and group, over split z of the sequence's rows.  The
+// 1D grid runs (chunk, split, group) with the group fastest and the chunk,
+// in cost order, slowest.
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 cmp_dkv_mfma_kernel(BwdParams p) {
@@ -435,14 +467,15 @@ cmp_dkv_mfma_kernel(BwdParams p) {
   const FwdParams& f = p.f;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int g = blockIdx.y;
+  const int g = static_cast<int>(blockIdx.x % f.h_kv);
+  const int z = static_cast<int>((blockIdx.x / f.h_kv) % p.row_splits);
   const int G = f.h_q / f.h_kv;
-  const int tile = blockIdx.x;
+  const int tile = static_cast<int>(blockIdx.x / (f.h_kv * p.row_splits));
   if (tile >= p.btile_pre[f.batch]) return;
-  const int b = find_seq(p.btile_pre, f.batch, tile);
+  const int r = find_seq(p.btile_pre, f.batch, tile);
   int s0, s1, j0, j1;
-  seq_bounds(f, b, &s0, &s1, &j0, &j1);
-  const int kt = j0 / kKeyTile + (tile - p.btile_pre[b]) * kBT + wv;
+  seq_bounds(f, p.seq_order[r], &s0, &s1, &j0, &j1);
+  const int kt = j0 / kKeyTile + (tile - p.btile_pre[r]) * kBT + wv;
   const bool wave_on = kt < (j1 + kKeyTile - 1) / kKeyTile;
   const int j = kt * kKeyTile + (lane & 31);
   const bool jok = wave_on && j >= j0 && j < j1;
@@ -451,9 +484,9 @@ cmp_dkv_mfma_kernel(BwdParams p) {
   const int T0 = static_cast<int>(r_lo / kKeyTile);
   const int n_all = static_cast<int>((r_hi + kKeyTile - 1) / kKeyTile) - T0;
   const int per = (n_all + p.row_splits - 1) / p.row_splits;
-  const int t_beg = T0 + min(n_all, static_cast<int>(blockIdx.z) * per);
-  const int t_end = T0 + min(n_all, static_cast<int>(blockIdx.z + 1) * per);
-  const int64_t part = p.row_splits > 1 ? static_cast<int64_t>(blockIdx.z) * f.h_kv * f.nb_cap * D : 0;
+  const int t_beg = T0 + min(n_all, z * per);
+  const int t_end = T0 + min(n_all, (z + 1) * per);
+  const int64_t part = p.row_splits > 1 ? static_cast<int64_t>(z) * f.h_kv * f.nb_cap * D : 0;
   float* ok = (p.row_splits > 1 ? p.dkbar_part : p.dkbar) + part;
   float* ov = (p.row_splits > 1 ? p.dvbar_part : p.dvbar) + part;
   rows_dkv_body<D>(p, g, wave_on, wave_on ? static_cast<const uint16_t*>(f.kbar) + krow : nullptr,
@@ -854,7 +887,7 @@ hipError_t launch_bwd_win_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 }
 
 hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  bwd_tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
+  bwd_tile_prefix_kernel<<<1, 256, 0, stream>>>(p);
   const dim3 grid(p.max_qtiles, p.f.h_q);
   if (p.f.d == 32) cmp_dq_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
   else cmp_dq_mfma_kernel<64><<<grid, 256, 0, stream>>>(p);
@@ -862,7 +895,7 @@ hipError_t launch_bwd_cmp_dq_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 }
 
 hipError_t launch_bwd_cmp_dkv_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  const dim3 grid(p.max_btiles, p.f.h_kv, p.row_splits);
+  const int grid = p.max_btiles * p.f.h_kv * p.row_splits;
   if (p.f.d == 32) cmp_dkv_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
   else cmp_dkv_mfma_kernel<64><<<grid, 256, 0, stream>>>(p);
   if (p.row_splits > 1) {

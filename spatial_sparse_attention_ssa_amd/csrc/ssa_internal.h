@@ -222,7 +222,8 @@ struct BwdParams {
   const uint32_t* sel_sorted_keys;   // the sorted keys (one of the two key buffers)
   // MFMA kernels of the compressed branch (bf16)
   int32_t* qtile_pre;   // [batch + 1] prefix of 128-query tiles per sequence
-  int32_t* btile_pre;   // [batch + 1] prefix of 128-block chunks per sequence
+  int32_t* btile_pre;   // [batch + 1] prefix of 128-block chunks per sequence, in seq_order
+  int32_t* seq_order;   // [batch] sequences by decreasing token count (ties: lower index first)
   int32_t max_qtiles;   // grid bounds of the two
   int32_t max_btiles;
   // (query, head) rows of each group in sorted order: row R = i * G + hh is
