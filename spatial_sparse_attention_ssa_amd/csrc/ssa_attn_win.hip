@@ -10,7 +10,7 @@
 // head-major).  Keys and values come from the head-major sorted copies made by
 // the pooling kernel, so a window is one contiguous run of rows.  The
 // workgroup stages the window's key and value rows (row-major, 16-byte
-// stores) in LDS, in chunks of up to kChunk tokens; each of its 4 waves
+// stores) in LDS, in chunks of up to 128 tokens; each of its 4 waves
 // computes 32 queries with v_mfma_f32_32x32x16_bf16 (S^T = K Q^T over 32-key
 // tiles), an online softmax (running max, rescaled sum and O^T), and
 // O^T += V^T P^T with the V^T operands read through the transposing LDS load.

@@ -11,8 +11,9 @@
 //
 // cmp_dq_mfma_kernel (query-major): a workgroup owns 128 sorted queries of
 //   one sequence and one query head, a wave 32 of them.  Pooled key / value
-//   rows and the transposed key tile stream through a two-slot LDS ring, 32
-//   blocks per tile.  Per tile: S^T = Kbar Q^T and dP^T = Vbar dO^T, then
+//   rows stream through a two-slot LDS ring, 32 blocks per tile (the key
+//   rows are read as they are and, for Kbar^T, with gfx950's transposing LDS
+//   load).  Per tile: S^T = Kbar Q^T and dP^T = Vbar dO^T, then
 //   P and P * dP in registers, and dq^T accumulates as A - Delta B with
 //   A = Kbar^T (P * dP)^T and B = Kbar^T P^T, so Delta (summed on the fly)
 //   comes from the same float32 P as the rest.  Writes dq_acc (first writer),
@@ -21,10 +22,11 @@
 // cmp_dkv_mfma_kernel (block-major): a workgroup owns 128 blocks of one
 //   sequence and one key/value group, a wave one 32-block tile whose pooled
 //   rows stay in registers as MFMA operands.  The sequence's (query, head)
-//   rows stream through LDS 32 at a time, row-major (for S = Q Kbar^T and
-//   dP = dO Vbar^T) and transposed in MFMA operand order (for
-//   dVbar^T += dO^T (G0 P)^T and dKbar^T += Q^T (G0 P (dP - Delta))^T).
-//   When there are few block tiles (grouped heads: few key/value groups, many
+//   rows stream through LDS 32 at a time, row-major, read as they are for
+//   S = Q Kbar^T and dP = dO Vbar^T and with the transposing LDS load for
+//   dVbar^T += dO^T (G0 P)^T and dKbar^T += Q^T (G0 P (dP - Delta))^T.
+//   Its 1D grid starts the chunks of the longest sequences first.  When
+//   there are few block tiles (grouped heads: few key/value groups, many
 //   rows), the rows are split over several workgroups whose partial tiles are
 //   summed afterwards in split order.
 //
