@@ -7,7 +7,11 @@ Tolerances (the stated parity bar for this path):
     group) pairs, and every mismatch has a score gap ln S(b_k) - ln S(a)
     below 1e-3, where b_k is the oracle's k-th block and a the lowest-scored
     block only the GPU chose;
-  * output: max |dO| <= 2e-2 and mean |dO| <= 2e-3 against the float64 oracle;
+  * output: max |dO| <= 2e-2 and mean |dO| <= 2e-3 against the float64 oracle
+    (whose output is rounded to the output dtype, as the library's is); for a
+    bfloat16 output of magnitude >= 4, whose unit in the last place is >= 2^-5
+    and so above 2e-2, one unit in the last place of the reference is allowed
+    instead (the two roundings may land on neighbouring values);
   * each branch alone (one-hot gates): ||do_x||_2 / ||o_x||_2 <= 1e-2.
 """
 from __future__ import annotations
@@ -63,9 +67,18 @@ def check_build(gblocks, ob):
         assert h["counts"][4] == int(np.diff(ob.win_off).max())
 
 
-def check_outputs(got, ref, what="out"):
+def bf16_ulp(x):
+    """Unit in the last place of bfloat16 values of magnitude |x| (8
+    significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_outputs(got, ref, what="out", dtype="bf16"):
     err = np.abs(got - ref)
-    assert err.max() <= MAX_ABS, f"{what}: max |err| {err.max():.3e}"
+    tol = np.maximum(MAX_ABS, bf16_ulp(ref)) if dtype == "bf16" else MAX_ABS
+    bad = err > tol
+    assert not bad.any(), f"{what}: |err| {err[bad].max():.3e} above the bar at {int(bad.sum())} entries"
     assert err.mean() <= MEAN_ABS, f"{what}: mean |err| {err.mean():.3e}"
     return err.max(), err.mean()
 

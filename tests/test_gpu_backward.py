@@ -105,6 +105,28 @@ def test_large_windows_backward_full():
     _full_compare(wl, seed=8)
 
 
+def many_sequences(lengths, seed):
+    """A varlen batch of the given sequence lengths, each sequence a set of
+    distinct random voxels of a 64^3 grid."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lengths, dtype=np.int64)
+    lin = rng.choice(64 ** 3, size=int(lens.sum()), replace=False)
+    coords = np.stack(np.unravel_index(lin, (64,) * 3), -1)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return make_custom(None, coords=coords, cu_seqlens=cu, grid_res=64, m_cmp=4, m_win=8, topk=4, h_q=4, h_kv=4,
+                       head_dim=64, dtype="bf16", seed=seed)
+
+
+@pytest.mark.parametrize("n_seq", [40, 1100])
+def test_many_sequences_backward_full(n_seq):
+    # 40 sequences with repeated lengths (ties in the longest-first chunk
+    # order of the pooled-row gradients), and 1100, past the 1024 sequences
+    # that are put in cost order
+    rng = np.random.default_rng(n_seq)
+    lengths = rng.choice([7, 7, 13, 30, 30, 64], size=n_seq) if n_seq < 1024 else rng.choice([1, 2, 3, 5], size=n_seq)
+    _full_compare(many_sequences(lengths, seed=41), seed=9)
+
+
 def test_geometric_routing_backward_full():
     wl = make_custom([700, 300], grid_res=64, n_prims=3, topk=8, h_q=4, h_kv=4, head_dim=64,
                      dtype="bf16", seed=31, routing="geometric")

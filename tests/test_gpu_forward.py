@@ -28,7 +28,7 @@ def _full_compare(wl, branches=True):
     rows = [(t, h) for t in range(N) for h in range(H)]
     ref = oracle.forward_rows(wl, ob, rows, with_branches=branches, with_scores=True)
     got = P.host(res["out"]).reshape(N * H, -1)
-    mx, mean = P.check_outputs(got, ref["out"])
+    mx, mean = P.check_outputs(got, ref["out"], dtype=wl.dtype)
     G = H // Hkv
     gsel = res["topk"].cpu().numpy()[[t for t, _ in rows], [h // G for _, h in rows]]
     agree, gap = P.check_topk(gsel, ref["topk"], ref["scores"], ref["first_block"])
@@ -110,7 +110,7 @@ def test_geometric_routing_full(case):
     G = H // wl.h_kv
     gsel = res["topk"].cpu().numpy()[[t for t, _ in rows], [h // G for _, h in rows]]
     assert np.array_equal(gsel, ref["topk"])
-    P.check_outputs(P.host(res["out"]).reshape(N * H, -1), ref["out"])
+    P.check_outputs(P.host(res["out"]).reshape(N * H, -1), ref["out"], dtype=wl.dtype)
     o = P.host(P.gpu_forward(wl, gb, gates=P.one_hot_gates(wl, 1), routing="geometric")).reshape(N * H, -1)
     P.check_branch(o, ref["o_sel"], "o_sel")
 
@@ -127,7 +127,7 @@ def test_geometric_routing_headline_sampled():
     assert np.array_equal(gsel, ref["topk"])
     tt = torch.tensor([t for t, _ in rows], device=P.DEV)
     hh = torch.tensor([h for _, h in rows], device=P.DEV)
-    P.check_outputs(P.host(res["out"][tt, hh]), ref["out"])
+    P.check_outputs(P.host(res["out"][tt, hh]), ref["out"], dtype=wl.dtype)
 
 
 def test_tiny_fp32_workload_full():
@@ -146,7 +146,7 @@ def _sampled_check(wl, rows, branches=True, min_agree=0.99, tag=""):
     tt = torch.tensor([t for t, _ in rows], device=P.DEV)
     hh = torch.tensor([h for _, h in rows], device=P.DEV)
     got = P.host(res["out"][tt, hh])
-    mx, mean = P.check_outputs(got, ref["out"])
+    mx, mean = P.check_outputs(got, ref["out"], dtype=wl.dtype)
     G = wl.h_q // wl.h_kv
     gsel = res["topk"][tt, hh // G].cpu().numpy()
     agree, gap = P.check_topk(gsel, ref["topk"], ref["scores"], ref["first_block"], min_agree=min_agree)
@@ -245,6 +245,14 @@ def test_large_windows_full(h_q, h_kv, head_dim):
                      h_kv=h_kv, head_dim=head_dim, dtype="bf16", seed=13)
     assert np.diff(P.oracle_blocks(wl).win_off).min() > 256
     _full_compare(wl)
+
+
+def test_many_sequences_full():
+    # 1100 sequences of 1 to 5 tokens (every per-sequence tile prefix and
+    # search over a long batch)
+    from tests.test_gpu_backward import many_sequences
+    lengths = np.random.default_rng(1100).choice([1, 2, 3, 5], size=1100)
+    _full_compare(many_sequences(lengths, seed=41))
 
 
 def test_dense_reduction():
