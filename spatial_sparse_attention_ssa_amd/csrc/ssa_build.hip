@@ -18,6 +18,8 @@
 namespace ssa {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kItems = kSortTile / 256;  // keys per thread per tile (16)
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -76,92 +78,108 @@ keys_kernel(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, 
   vals[t] = t;
 }
 
+// Digit counts of one 4096-key tile, written tile-major (one contiguous
+// 1 KB row per tile: tile_hist[tile * 256 + digit]).  Full tiles are read as
+// 16-byte vectors, four per thread, all in flight at once; each wave counts
+// into its own LDS histogram.
 __global__ void __launch_bounds__(256)
 radix_upsweep(const uint32_t* __restrict__ keys, int32_t n, int shift,
-              uint32_t* __restrict__ tile_hist, int ntiles) {
-  __shared__ uint32_t hist[256];
-  hist[threadIdx.x] = 0;
+              uint32_t* __restrict__ tile_hist) {
+  __shared__ uint32_t hist[4][256];
+  for (int i = threadIdx.x; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
   __syncthreads();
+  uint32_t* const h = hist[threadIdx.x >> 6];
   const int base = blockIdx.x * kSortTile;
-  for (int i = threadIdx.x; i < kSortTile; i += 256) {
-    const int p = base + i;
-    if (p < n) atomicAdd(&hist[(keys[p] >> shift) & 255u], 1u);
+  if (base + kSortTile <= n) {
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(keys + base);
+    u32x4 v[kItems / 4];
+#pragma unroll
+    for (int j = 0; j < kItems / 4; ++j) v[j] = k4[threadIdx.x + 256 * j];
+#pragma unroll
+    for (int j = 0; j < kItems / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&h[(v[j][e] >> shift) & 255u], 1u);
+  } else {
+    for (int i = threadIdx.x; i < kSortTile; i += 256) {
+      const int p = base + i;
+      if (p < n) atomicAdd(&h[(keys[p] >> shift) & 255u], 1u);
+    }
   }
   __syncthreads();
-  tile_hist[threadIdx.x * ntiles + blockIdx.x] = hist[threadIdx.x];
+  const int d = threadIdx.x;
+  tile_hist[static_cast<size_t>(blockIdx.x) * 256 + d] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
 }
 
-// In-place exclusive scan of `m` uint32 values by one 1024-thread workgroup.
-__global__ void __launch_bounds__(1024) scan_exclusive_u32(uint32_t* __restrict__ data, int m) {
-  __shared__ uint32_t part[1024];
-  const int tid = threadIdx.x;
-  const int per = (m + 1023) / 1024;
-  const int beg = min(tid * per, m), end = min(beg + per, m);
+// Scan of the tile-major digit counts in (digit, tile) order, the order of
+// the stable scatter's output: offset(t, d) = (all tiles' keys of digits
+// below d) + (digit d's keys in tiles before t).  Thread d owns column d;
+// every step reads or writes one contiguous 1 KB row.  Up to kColSmall
+// tiles one workgroup does it all; above, tiles are taken `per` at a time
+// (at least 8, and at most 256 chunks).
+constexpr int kColSmall = 32;
+constexpr int kColChunksMax = 256;
+
+__host__ __device__ constexpr int hist_chunk_tiles(int64_t ntiles) {
+  return static_cast<int>(ntiles > 8 * kColChunksMax ? (ntiles + kColChunksMax - 1) / kColChunksMax : 8);
+}
+
+// column totals of each chunk of `per` tiles
+__global__ void __launch_bounds__(256) hist_col_sums(const uint32_t* __restrict__ hist, int ntiles, int per,
+                                                     uint32_t* __restrict__ csum) {
+  const int d = threadIdx.x;
+  const int t0 = blockIdx.x * per, t1 = min(t0 + per, ntiles);
   uint32_t s = 0;
-  for (int i = beg; i < end; ++i) s += data[i];
-  part[tid] = s;
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) s += hist[static_cast<size_t>(t) * 256 + d];
+  csum[static_cast<size_t>(blockIdx.x) * 256 + d] = s;
+}
+
+// One workgroup of 1024 threads, in place over `rows` rows of 256 counts
+// (tiles, or chunk totals): each row becomes its exclusive (digit, row)-order
+// offsets.  Thread (q, d) walks column d over the q-th quarter of the rows.
+__global__ void __launch_bounds__(1024) hist_col_scan(uint32_t* __restrict__ rowsv, int rows) {
+  __shared__ uint32_t part[4][256];
+  __shared__ uint32_t scan[256];
+  const int d = threadIdx.x & 255, q = threadIdx.x >> 8;
+  const int quarter = (rows + 3) / 4;
+  const int r0 = min(q * quarter, rows), r1 = min(r0 + quarter, rows);
+  uint32_t s = 0;
+#pragma unroll 8
+  for (int r = r0; r < r1; ++r) s += rowsv[static_cast<size_t>(r) * 256 + d];
+  part[q][d] = s;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+  const uint32_t tot = part[0][d] + part[1][d] + part[2][d] + part[3][d];
+  if (q == 0) scan[d] = tot;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t x = (q == 0 && d >= off) ? scan[d - off] : 0u;
     __syncthreads();
-    part[tid] += v;
+    if (q == 0) scan[d] += x;
     __syncthreads();
   }
-  uint32_t run = tid ? part[tid - 1] : 0u;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t v = data[i];
-    data[i] = run;
+  uint32_t run = scan[d] - tot;   // keys of the digits below d
+  for (int k = 0; k < q; ++k) run += part[k][d];
+#pragma unroll 8
+  for (int r = r0; r < r1; ++r) {
+    const size_t i = static_cast<size_t>(r) * 256 + d;
+    const uint32_t v = rowsv[i];
+    rowsv[i] = run;
     run += v;
   }
 }
 
-// Exclusive scan of many values: per-chunk sums, one scan of the sums, then
-// each chunk rescanned with its offset (chunks of kScanChunk values, 16 per
-// thread, contiguous).
-constexpr int kScanChunk = 4096;
-
-__global__ void __launch_bounds__(256) scan_chunk_sums(const uint32_t* __restrict__ data, int m,
-                                                       uint32_t* __restrict__ sums) {
-  __shared__ uint32_t part[256];
-  const int base = blockIdx.x * kScanChunk + threadIdx.x * 16;
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (base + i < m) s += data[base + i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) sums[blockIdx.x] = part[0];
-}
-
-__global__ void __launch_bounds__(256) scan_chunk_apply(uint32_t* __restrict__ data, int m,
-                                                        const uint32_t* __restrict__ sums) {
-  __shared__ uint32_t part[256];
-  const int tid = threadIdx.x;
-  const int base = blockIdx.x * kScanChunk + tid * 16;
-  uint32_t v[16];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = base + i < m ? data[base + i] : 0u;
-    s += v[i];
-  }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t x = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += x;
-    __syncthreads();
-  }
-  uint32_t run = sums[blockIdx.x] + part[tid] - s;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (base + i < m) data[base + i] = run;
-    run += v[i];
+// each chunk's tiles rewritten with their offsets, from the chunk's scanned total
+__global__ void __launch_bounds__(256) hist_col_apply(uint32_t* __restrict__ hist, int ntiles, int per,
+                                                      const uint32_t* __restrict__ csum) {
+  const int d = threadIdx.x;
+  const int t0 = blockIdx.x * per, t1 = min(t0 + per, ntiles);
+  uint32_t run = csum[static_cast<size_t>(blockIdx.x) * 256 + d];
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    const size_t i = static_cast<size_t>(t) * 256 + d;
+    const uint32_t v = hist[i];
+    hist[i] = run;
+    run += v;
   }
 }
 
@@ -172,7 +190,7 @@ __global__ void __launch_bounds__(256) scan_chunk_apply(uint32_t* __restrict__ d
 __global__ void __launch_bounds__(256)
 radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t n,
-                int shift, const uint32_t* __restrict__ tile_off, int ntiles) {
+                int shift, const uint32_t* __restrict__ tile_off) {
   __shared__ uint32_t whist[4][256];   // per wave: keys of each digit
   __shared__ uint32_t wbase[4][256];   // per wave: tile-local start of its keys of each digit
   __shared__ uint32_t lstart[256];     // tile-local start of each digit
@@ -230,7 +248,7 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     }
     uint32_t run = scan[d] - tot;
     lstart[d] = run;
-    gbase[d] = tile_off[d * ntiles + blockIdx.x];
+    gbase[d] = tile_off[static_cast<size_t>(blockIdx.x) * 256 + d];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       wbase[w][d] = run;
@@ -472,27 +490,29 @@ bool sort_pairs_lands_in_tmp(int key_bits) {
 
 size_t sort_pairs_hist_bytes(int64_t n) {
   const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
-  const int64_t m = 256 * (ntiles > 0 ? ntiles : 1);
-  // tile histograms, then the chunk sums of their scan
-  return align256(sizeof(uint32_t) * m) + sizeof(uint32_t) * ((m + kScanChunk - 1) / kScanChunk);
+  const int64_t rows = ntiles > 0 ? ntiles : 1;
+  // tile histograms, then the column totals of their chunks
+  const int64_t per = hist_chunk_tiles(rows);
+  return align256(sizeof(uint32_t) * 256 * rows) + sizeof(uint32_t) * 256 * ((rows + per - 1) / per);
 }
 
 namespace {
 
-// exclusive scan of the m = 256 * ntiles tile histograms in place: one
-// workgroup for small histograms, else chunk sums, their scan, and each chunk
-// rescanned with its offset (the sums live right after the histograms)
+// the tile histograms' (digit, tile)-order offsets, in place: one workgroup
+// up to kColSmall tiles, else column totals per chunk of tiles, their scan,
+// and each chunk rewritten from its total (the totals live right after the
+// histograms)
 void scan_tile_hist(uint32_t* tile_hist, int ntiles, hipStream_t stream) {
-  const int m = 256 * ntiles;
-  if (m <= 2 * kScanChunk) {   // measured: one workgroup wins only up to two chunks
-    scan_exclusive_u32<<<1, 1024, 0, stream>>>(tile_hist, m);
+  if (ntiles <= kColSmall) {
+    hist_col_scan<<<1, 1024, 0, stream>>>(tile_hist, ntiles);
     return;
   }
-  uint32_t* sums = tile_hist + align256(sizeof(uint32_t) * 256 * static_cast<size_t>(ntiles)) / sizeof(uint32_t);
-  const int chunks = (m + kScanChunk - 1) / kScanChunk;
-  scan_chunk_sums<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
-  scan_exclusive_u32<<<1, 1024, 0, stream>>>(sums, chunks);
-  scan_chunk_apply<<<chunks, 256, 0, stream>>>(tile_hist, m, sums);
+  uint32_t* csum = tile_hist + align256(sizeof(uint32_t) * 256 * static_cast<size_t>(ntiles)) / sizeof(uint32_t);
+  const int per = hist_chunk_tiles(ntiles);
+  const int chunks = (ntiles + per - 1) / per;
+  hist_col_sums<<<chunks, 256, 0, stream>>>(tile_hist, ntiles, per, csum);
+  hist_col_scan<<<1, 1024, 0, stream>>>(csum, chunks);
+  hist_col_apply<<<chunks, 256, 0, stream>>>(tile_hist, ntiles, per, csum);
 }
 
 }  // namespace
@@ -508,9 +528,9 @@ hipError_t launch_sort_pairs(uint32_t* keys, int32_t* vals, uint32_t* keys_tmp, 
   int32_t* vout = vals_tmp;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kRadixBits;
-    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, tile_hist, ntiles);
+    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, tile_hist);
     scan_tile_hist(tile_hist, ntiles, stream);
-    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, tile_hist, ntiles);
+    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, tile_hist);
     uint32_t* tk = kin; kin = kout; kout = tk;
     int32_t* tv = vin; vin = vout; vout = tv;
   }
@@ -537,9 +557,9 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
                                                     out.counts);
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kRadixBits;
-    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, ws.tile_hist, ntiles);
+    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, ws.tile_hist);
     scan_tile_hist(ws.tile_hist, ntiles, stream);
-    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, ws.tile_hist, ntiles);
+    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, ws.tile_hist);
     uint32_t* tk = kin; kin = kout; kout = tk;
     int32_t* tv = vin; vin = vout; vout = tv;
   }
