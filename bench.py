@@ -236,12 +236,14 @@ MEMPATH_COUNTERS = ("TA_TA_BUSY", "TA_DATA_STALLED_BY_TC_CYCLES", "TCP_TCC_READ_
 N_CU = 256
 
 
-def summarize_mempath(pmc_csv: str):
+def summarize_mempath(pmc_csv: str, grid: int = 0):
     """Memory-path counters per SSA kernel from one rocprofv3 --pmc run of
     MEMPATH_COUNTERS: the texture addresser's busy share and its share stalled
     by the cache (both over cycles x 256 compute units), the L2 hit rate, the
     mean L1-to-L2 read latency in cycles, the L1's pending-request stall share,
-    and vector-memory read instructions per launch; prints a markdown table."""
+    and vector-memory read instructions per launch; prints a markdown table.
+    With `grid`, only the launches of that many threads are counted (one
+    size of a sweep)."""
     import csv
     import re
     from collections import defaultdict
@@ -251,7 +253,7 @@ def summarize_mempath(pmc_csv: str):
     with open(pmc_csv) as fh:
         for r in csv.DictReader(fh):
             m = re.search(r"ssa::\(anonymous namespace\)::(\w+)", r["Kernel_Name"])
-            if not m:
+            if not m or (grid and int(r["Grid_Size"]) != grid):
                 continue
             per[m.group(1)][r["Counter_Name"]].append(float(r["Counter_Value"]))
             if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
@@ -262,7 +264,7 @@ def summarize_mempath(pmc_csv: str):
     for name, c in per.items():
         avg = lambda k: sum(c[k]) / len(c[k])
         t = sum(dur[name]) / len(dur[name])
-        if t < 50e-6:
+        if not grid and t < 50e-6:
             continue
         cu_cycles = avg("GRBM_GUI_ACTIVE") / N_XCC * N_CU
         hits, miss = avg("TCC_HIT"), avg("TCC_MISS")
@@ -371,6 +373,8 @@ def main():
     ap.add_argument("--kernel-stats", help="rocprofv3 --stats kernel_stats.csv for the summary")
     ap.add_argument("--summarize-mempath", metavar="PMC_CSV",
                     help="print the memory-path counter table of one rocprofv3 --pmc run of MEMPATH_COUNTERS")
+    ap.add_argument("--mempath-grid", type=int, default=0,
+                    help="with --summarize-mempath: only launches of this many threads")
     ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
                     help="only summarise a rocprofv3 --pmc run of the MFMA counters into a markdown table")
     ap.add_argument("--build-sweep", action="store_true",
@@ -389,7 +393,7 @@ def main():
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel_stats, cmds, wid)
         return
     if args.summarize_mempath:
-        summarize_mempath(args.summarize_mempath)
+        summarize_mempath(args.summarize_mempath, args.mempath_grid)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, wid)
