@@ -366,6 +366,7 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
   const uint64_t lt = lanemask_lt();
   int rb = 0, rw = 0;
   int rank_b[kItems], rank_w[kItems];
+  static_assert(2 * kItems <= 32, "two boundary flags per row are packed into 32 bits");
   uint32_t flags = 0;
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
