@@ -84,6 +84,7 @@ def _full_compare(wl, seed, one_hot=False):
     dict(seqs=[400], h_q=2, h_kv=2, head_dim=32, topk=4, dtype="f32"),
     dict(seqs=[350, 90], h_q=32, h_kv=2, head_dim=64, topk=16, dtype="bf16"),
     dict(seqs=[900, 0, 300], h_q=4, h_kv=4, head_dim=64, topk=24, dtype="bf16"),
+    dict(seqs=[800, 450], h_q=4, h_kv=4, head_dim=32, topk=20, dtype="bf16"),
 ])
 def test_small_backward_full(case):
     wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],

@@ -63,6 +63,8 @@ def _check_pooled(got, ref, dtype):
     # kernel's 32-entry list variant)
     dict(seqs=[2000, 0, 1100], h_q=4, h_kv=4, head_dim=64, topk=32, dtype="bf16"),
     dict(seqs=[1600], h_q=2, h_kv=2, head_dim=64, topk=20, dtype="bf16"),
+    # one query head per key/value head at head_dim 32 (the generic kernel), k above 16
+    dict(seqs=[800, 450], h_q=4, h_kv=4, head_dim=32, topk=20, dtype="bf16"),
     # grouped heads, 16 query heads per key/value head (the MFMA group path)
     dict(seqs=[900, 0, 701], h_q=16, h_kv=1, head_dim=32, topk=8, dtype="bf16"),
     dict(seqs=[1203], h_q=32, h_kv=2, head_dim=64, topk=16, dtype="bf16"),
