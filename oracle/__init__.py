@@ -33,7 +33,8 @@ from .ssa_oracle import (  # noqa: F401
     forward,
     forward_rows,
     backward,
+    backward_rows,
+    pooled_to_tokens,
     softmax_attention_grad,
-    token_window_and_seq,
     round_to,
 )

@@ -168,18 +168,6 @@ def build_blocks(coords, cu_seqlens, grid_res: int, m_cmp: int, m_win: int, shif
                   seq_win_off=seq_win_off, n_invalid=int((~valid).sum()), r3=r3)
 
 
-def token_window_and_seq(blocks: Blocks):
-    """For every sorted position: its window id and sequence id."""
-    n = len(blocks.perm)
-    win_of_pos = np.zeros(n, dtype=np.int64)
-    for w in range(blocks.nw):
-        win_of_pos[blocks.win_off[w]:blocks.win_off[w + 1]] = w
-    seq_of_win = np.zeros(blocks.nw, dtype=np.int64)
-    for b in range(len(blocks.seq_win_off) - 1):
-        seq_of_win[blocks.seq_win_off[b]:blocks.seq_win_off[b + 1]] = b
-    return win_of_pos, seq_of_win[win_of_pos] if n else win_of_pos
-
-
 # ----------------------------------------------------------------------------
 # Compression: mean pooling of keys/values per block
 # ----------------------------------------------------------------------------
@@ -225,11 +213,15 @@ def geometric_topk(coords, blocks: Blocks, t: int, j0: int, j1: int, k: int):
     integer squared distances; ties go to the lower block id.
     """
     c = np.asarray(coords[t], dtype=np.int64)
-    d = np.empty(j1 - j0, dtype=np.int64)
-    for j in range(j0, j1):
-        toks = blocks.perm[blocks.blk_off[j]:blocks.blk_off[j + 1]]
-        diff = np.asarray(coords[toks], dtype=np.int64) - c
-        d[j - j0] = int((diff * diff).sum(axis=1).min())
+    first, last = int(blocks.blk_off[j0]), int(blocks.blk_off[j1])
+    if j1 <= j0:
+        return np.zeros(0, dtype=np.int64)
+    toks = blocks.perm[first:last]
+    diff = np.asarray(coords[toks], dtype=np.int64) - c
+    d_tok = (diff * diff).sum(axis=1)                     # squared distance of every voxel
+    # the block's distance is the smallest over its voxels (blocks are
+    # contiguous runs of the sorted order)
+    d = np.minimum.reduceat(d_tok, np.asarray(blocks.blk_off[j0:j1], dtype=np.int64) - first)
     order = np.lexsort((np.arange(j1 - j0), d))
     return order[:min(k, j1 - j0)]
 
@@ -369,47 +361,39 @@ def softmax_attention_grad(q, k, v, do, scale: float):
     return scale * (ds @ k), scale * np.outer(ds, q), np.outer(p, do), o
 
 
-def backward(wl, dout, blocks: Blocks | None = None, rows=None):
-    """Gradients of L = sum(dout * O), O the SSA output before its rounding.
+def backward_rows(wl, dout, blocks: Blocks, rows, kbar=None, vbar=None):
+    """Backward contributions of the given (input token index, query head) rows.
 
     O[t, h] = G0 o_cmp + G1 o_sel + G2 o_win (Direct3D-S2 page, "Method"), so
     branch x sees the output gradient G_x * dout[t, h] and the gate gets
-    dout[t, h] . o_x.  The compressed branch's key / value gradients land on
-    the pooled rows and are then shared by each block's tokens, divided by the
-    token count (the pooling is a mean).  The top-k choice is held fixed.
-
-    Without ``rows``: float64 dq [N, H, D], dk / dv [N, Hkv, D], dgates
-    [N, H, 3] and dkbar / dvbar [nb, Hkv, D].  With ``rows`` (a list of
-    (token, head)): only dq [len(rows), D] and dgates [len(rows), 3] of those
-    rows, which depend on nothing else.
+    dout[t, h] . o_x.  Every row's own dq [len(rows), D] and dgates
+    [len(rows), 3] depend on that row alone.  The key / value gradients are
+    sums over rows: each row adds its selected- and window-branch terms to the
+    token gradients dk, dv [N, Hkv, D] and its compressed-branch terms to the
+    pooled-row gradients dkbar, dvbar [nb, Hkv, D].  The sum over all rows,
+    passed to ``pooled_to_tokens``, is the gradient.  The top-k choice is held
+    fixed.
     """
-    if blocks is None:
-        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win,
-                              getattr(wl, "win_shift", 0))
     H, Hkv, D, K = wl.h_q, wl.h_kv, wl.head_dim, wl.topk
     G = H // Hkv
     N = wl.n_tokens
     scale = 1.0 / math.sqrt(D)
-    kbar = pool_blocks(wl.k, blocks, wl.dtype)
-    vbar = pool_blocks(wl.v, blocks, wl.dtype)
+    if kbar is None:
+        kbar = pool_blocks(wl.k, blocks, wl.dtype)
+    if vbar is None:
+        vbar = pool_blocks(wl.v, blocks, wl.dtype)
     pos_of_tok = np.empty(len(blocks.perm), dtype=np.int64)
     pos_of_tok[blocks.perm] = np.arange(len(blocks.perm))
 
     def f64(a):
         return np.asarray(a, dtype=np.float64)
 
-    full = rows is None
-    if full:
-        rows = [(t, h) for t in range(N) for h in range(H)]
-        dq = np.zeros((N, H, D))
-        dgates = np.zeros((N, H, 3))
-        dk = np.zeros((N, Hkv, D))
-        dv = np.zeros((N, Hkv, D))
-        dkbar = np.zeros((blocks.nb, Hkv, D))
-        dvbar = np.zeros((blocks.nb, Hkv, D))
-    else:
-        dq = np.zeros((len(rows), D))
-        dgates = np.zeros((len(rows), 3))
+    dq = np.zeros((len(rows), D))
+    dgates = np.zeros((len(rows), 3))
+    dk = np.zeros((N, Hkv, D))
+    dv = np.zeros((N, Hkv, D))
+    dkbar = np.zeros((blocks.nb, Hkv, D))
+    dvbar = np.zeros((blocks.nb, Hkv, D))
     for n_row, (t, h) in enumerate(rows):
         i = int(pos_of_tok[t])
         b, w = _token_rows(blocks, i)
@@ -432,23 +416,48 @@ def backward(wl, dout, blocks: Blocks | None = None, rows=None):
         # (b) selected tokens and (c) window tokens (each a set of distinct tokens)
         dq_s, dks, dvs, o_s = softmax_attention_grad(q, f64(wl.k[sel, g]), f64(wl.v[sel, g]), gt[1] * do, scale)
         dq_w, dkw, dvw, o_w = softmax_attention_grad(q, f64(wl.k[win, g]), f64(wl.v[win, g]), gt[2] * do, scale)
-        if full:
-            dkbar[j0:j1, g] += dkb
-            dvbar[j0:j1, g] += dvb
-            dk[sel, g] += dks
-            dv[sel, g] += dvs
-            dk[win, g] += dkw
-            dv[win, g] += dvw
-            dq[t, h] = dq_c + dq_s + dq_w
-            dgates[t, h] = (do @ o_c, do @ o_s, do @ o_w)
-        else:
-            dq[n_row] = dq_c + dq_s + dq_w
-            dgates[n_row] = (do @ o_c, do @ o_s, do @ o_w)
-    if not full:
-        return dict(dq=dq, dgates=dgates)
-    # the pooling is a mean: each token of block j gets 1 / n_j of its gradient
+        dkbar[j0:j1, g] += dkb
+        dvbar[j0:j1, g] += dvb
+        dk[sel, g] += dks
+        dv[sel, g] += dvs
+        dk[win, g] += dkw
+        dv[win, g] += dvw
+        dq[n_row] = dq_c + dq_s + dq_w
+        dgates[n_row] = (do @ o_c, do @ o_s, do @ o_w)
+    return dict(dq=dq, dgates=dgates, dk=dk, dv=dv, dkbar=dkbar, dvbar=dvbar)
+
+
+def pooled_to_tokens(blocks: Blocks, dk, dv, dkbar, dvbar):
+    """Token gradients from the summed row contributions: the pooling is a
+    mean, so each token of block j gets 1 / n_j of the pooled row's gradient
+    (added to dk, dv in place, which are returned)."""
     for j in range(blocks.nb):
         toks = blocks.perm[blocks.blk_off[j]:blocks.blk_off[j + 1]]
         dk[toks] += dkbar[j] / len(toks)
         dv[toks] += dvbar[j] / len(toks)
-    return dict(dq=dq, dk=dk, dv=dv, dgates=dgates, dkbar=dkbar, dvbar=dvbar)
+    return dk, dv
+
+
+def backward(wl, dout, blocks: Blocks | None = None, rows=None):
+    """Gradients of L = sum(dout * O), O the SSA output before its rounding.
+
+    The compressed branch's key / value gradients land on the pooled rows and
+    are then shared by each block's tokens, divided by the token count (the
+    pooling is a mean).  The top-k choice is held fixed.
+
+    Without ``rows``: float64 dq [N, H, D], dk / dv [N, Hkv, D], dgates
+    [N, H, 3] and dkbar / dvbar [nb, Hkv, D].  With ``rows`` (a list of
+    (token, head)): only dq [len(rows), D] and dgates [len(rows), 3] of those
+    rows, which depend on nothing else.
+    """
+    if blocks is None:
+        blocks = build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win,
+                              getattr(wl, "win_shift", 0))
+    if rows is not None:
+        part = backward_rows(wl, dout, blocks, rows)
+        return dict(dq=part["dq"], dgates=part["dgates"])
+    N, H, D = wl.n_tokens, wl.h_q, wl.head_dim
+    part = backward_rows(wl, dout, blocks, [(t, h) for t in range(N) for h in range(H)])
+    dk, dv = pooled_to_tokens(blocks, part["dk"], part["dv"], part["dkbar"], part["dvbar"])
+    return dict(dq=part["dq"].reshape(N, H, D), dk=dk, dv=dv, dgates=part["dgates"].reshape(N, H, 3),
+                dkbar=part["dkbar"], dvbar=part["dvbar"])
