@@ -318,44 +318,73 @@ def build_sweep(torch, ssa, dev, reps: int = 20):
     return points
 
 
-def cpu_baseline(wl, target_s: float, train: bool = False):
-    """Time the oracle on a bounded sample of the same workload (test
-    infrastructure, single thread): the full block build and pooling once,
-    then sampled (token, head) rows (forward, and with ``train`` also their
-    backward), extrapolated to all rows."""
+def host_description() -> dict:
+    """CPU model, numpy version and BLAS build of this host (for the baseline)."""
+    import numpy as np
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or blas
+    except Exception:
+        pass
+    return {"cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+CPU_ROW_STRIDE = 16   # the oracle runs every 16th token (all heads) of the workload
+
+
+def cpu_baseline(wl, train: bool = False):
+    """Time the float64 oracle (test infrastructure) on the host's cores: the
+    block build and pooling once in this process, then every head of every
+    CPU_ROW_STRIDE-th token (input order) over one worker process per core,
+    one BLAS thread each (with ``train`` also those rows' backward).  The
+    step time is stated as build + pooling + CPU_ROW_STRIDE x the sampled
+    rows' time, since the rows are independent and equally distributed."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
+    from oracle import parallel
+    workers = parallel.default_workers()
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         ob = oracle.build_blocks(wl.coords, wl.cu_seqlens, wl.grid_res, wl.m_cmp, wl.m_win)
         kbar = oracle.pool_blocks(wl.k, ob, wl.dtype)
         vbar = oracle.pool_blocks(wl.v, ob, wl.dtype)
         t_fixed = time.perf_counter() - t0
-        dout = np.broadcast_to(np.ones((1, 1, wl.head_dim), np.float32), wl.q.shape)
-        rng = np.random.default_rng(7)
-        rows_done, t_rows = 0, 0.0
-        budget = max(target_s - t_fixed, 2.0)
-        while t_rows < budget:
-            rows = list(zip(rng.integers(0, wl.n_tokens, 16).tolist(), rng.integers(0, wl.h_q, 16).tolist()))
-            t1 = time.perf_counter()
-            oracle.forward_rows(wl, ob, rows, kbar=kbar, vbar=vbar)
-            if train:
-                oracle.backward(wl, dout, blocks=ob, rows=rows)
-            t_rows += time.perf_counter() - t1
-            rows_done += len(rows)
-    per_row = t_rows / rows_done
-    t_step = t_fixed + per_row * wl.n_tokens * wl.h_q
+    toks = range(0, wl.n_tokens, CPU_ROW_STRIDE)
+    rows = [(t, h) for t in toks for h in range(wl.h_q)]
+    tf = {}
+    parallel.forward_rows(wl, ob, rows, kbar=kbar, vbar=vbar, workers=workers, timing=tf)
+    t_rows = tf["rows_s"]
+    if train:
+        dout = np.ones(wl.q.shape, np.float32)
+        tb = {}
+        parallel.backward_rows(wl, dout, ob, rows, workers=workers, timing=tb)
+        t_rows += tb["rows_s"]
+    t_step = t_fixed + CPU_ROW_STRIDE * t_rows
     what = "forward + backward" if train else "forward"
     return {
         "value": wl.n_tokens / t_step,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle, one thread: full block build + pooling ({t_fixed:.1f} s), "
-                   f"then the {what} of {rows_done} random (token, head) rows ({t_rows:.1f} s); per-step time "
-                   f"extrapolated to all {wl.n_tokens * wl.h_q} rows = {t_step:.0f} s"),
+        "sample": (f"float64 numpy oracle over {workers} worker processes (one BLAS thread each): block build + "
+                   f"pooling of all {wl.n_tokens} tokens once ({t_fixed:.1f} s, one process), then the {what} of "
+                   f"all {wl.h_q} heads of every {CPU_ROW_STRIDE}th token, {len(rows)} (token, head) rows, timed "
+                   f"in full ({t_rows:.1f} s); step time = build + pooling + {CPU_ROW_STRIDE} x rows = "
+                   f"{t_step:.0f} s"),
+        "host": host_description(),
     }
 
 
@@ -364,7 +393,6 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -557,7 +585,7 @@ def main():
                      "traffic": stored_traffic(dom.split(":")[-1], wid)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, train=train)
+        line["cpu_baseline"] = cpu_baseline(wl, train=train)
     print(json.dumps(line), flush=True)
 
 

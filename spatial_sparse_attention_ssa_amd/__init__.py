@@ -173,6 +173,8 @@ def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, q)
     kc = vc = tk = None
     if return_pooled:
         if blocks.nb < 0:
@@ -202,6 +204,24 @@ def forward(blocks: Blocks, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
     if return_topk:
         res["topk"] = tk[:n]
     return res
+
+
+def _check_out(out, q):
+    """A caller's output buffer must be exactly what the kernels write: a
+    contiguous GPU tensor shaped and typed like q, 16-byte aligned, on q's
+    device (the kernels write N * Hq * D elements 16 bytes at a time)."""
+    if not isinstance(out, torch.Tensor):
+        raise ValueError("out must be a tensor")
+    if out.dtype != q.dtype:
+        raise ValueError(f"out dtype {out.dtype} differs from q dtype {q.dtype}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out shape {tuple(out.shape)} differs from q shape {tuple(q.shape)}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if out.data_ptr() % 16:
+        raise ValueError("out must be 16-byte aligned")
+    if not out.is_cuda or out.device != q.device:
+        raise ValueError("out must be a GPU tensor on q's device")
 
 
 def _check_inputs(blocks, q, k, v, gates):

@@ -7,14 +7,22 @@ Tolerances (the stated parity bar for this path):
     group) pairs, and every mismatch has a score gap ln S(b_k) - ln S(a)
     below 1e-3, where b_k is the oracle's k-th block and a the lowest-scored
     block only the GPU chose;
-  * output: max |dO| <= 2e-2 and mean |dO| <= 2e-3 against the float64 oracle
-    (whose output is rounded to the output dtype, as the library's is); for a
-    bfloat16 output of magnitude >= 4, whose unit in the last place is >= 2^-5
-    and so above 2e-2, one unit in the last place of the reference is allowed
-    instead (the two roundings may land on neighbouring values);
+  * output: max |dO| <= 2e-2 and mean |dO| <= 2e-3 against the float64
+    oracle's unrounded output.  The library rounds its float32 result once to
+    the output dtype, which alone moves a bfloat16 value by up to half a unit
+    in its last place: 2^-6 for 4 <= |O| < 8, 2^-5 from 8 up.  So the bar per
+    entry is max(2e-2, ulp/2 + 4e-3), the 4e-3 covering the float32
+    accumulation; it is 2e-2 everywhere below |O| = 8;
   * each branch alone (one-hot gates): ||do_x||_2 / ||o_x||_2 <= 1e-2.
+
+With SSA_PARITY_LOG set to a file path, every check appends one JSON line
+with what it measured (agreement, worst gap, errors), so the figures of a run
+are kept.
 """
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import torch
@@ -24,6 +32,7 @@ import spatial_sparse_attention_ssa_amd as ssa
 
 DEV = torch.device("cuda:0")
 MAX_ABS, MEAN_ABS, BRANCH_REL = 2e-2, 2e-3, 1e-2
+ACC_ABS = 4e-3
 TOPK_AGREE, TOPK_GAP = 0.999, 1e-3
 
 
@@ -74,19 +83,33 @@ def bf16_ulp(x):
     return 2.0 ** (e - 7)
 
 
-def check_outputs(got, ref, what="out", dtype="bf16"):
-    err = np.abs(got - ref)
-    tol = np.maximum(MAX_ABS, bf16_ulp(ref)) if dtype == "bf16" else MAX_ABS
+def check_outputs(got, ref_exact, what="out", dtype="bf16"):
+    """got: the library's output (rounded to its dtype); ref_exact: the
+    oracle's unrounded float64 output."""
+    err = np.abs(got - ref_exact)
+    if dtype == "bf16":
+        tol = np.maximum(MAX_ABS, 0.5 * bf16_ulp(np.maximum(np.abs(got), np.abs(ref_exact))) + ACC_ABS)
+    else:
+        tol = MAX_ABS
     bad = err > tol
     assert not bad.any(), f"{what}: |err| {err[bad].max():.3e} above the bar at {int(bad.sum())} entries"
     assert err.mean() <= MEAN_ABS, f"{what}: mean |err| {err.mean():.3e}"
-    return err.max(), err.mean()
+    return float(err.max()), float(err.mean())
 
 
 def check_branch(got, ref, what):
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     assert rel <= BRANCH_REL, f"{what}: relative L2 error {rel:.3e}"
-    return rel
+    return float(rel)
+
+
+def record(kind, **fields):
+    """Append one JSON line of measured parity figures to $SSA_PARITY_LOG."""
+    path = os.environ.get("SSA_PARITY_LOG")
+    if not path:
+        return
+    with open(path, "a") as fh:
+        fh.write(json.dumps(dict(kind=kind, **fields)) + "\n")
 
 
 def topk_agreement(gpu_sel, ref_sel, scores, firsts):
@@ -110,7 +133,7 @@ def topk_agreement(gpu_sel, ref_sel, scores, firsts):
         gap = np.log(max(s[o[-1] - j0], 1e-300)) - np.log(max(s[a - j0], 1e-300))
         worst_gap = max(worst_gap, gap)
     agree = 1.0 - mismatches / max(n_rows, 1)
-    return agree, worst_gap
+    return agree, float(worst_gap)
 
 
 def check_topk(gpu_sel, ref_sel, scores, firsts, min_agree=TOPK_AGREE):

@@ -2,12 +2,16 @@
 
 The forward runs in its training form (it also saves each branch's
 log-sum-exp), then the backward gives dq, dk, dv and dgates for a seeded
-output gradient.  Small workloads are compared element by element
-against oracle.backward; the varlen workload is compared on sampled (token,
-head) rows for dq and dgates, and its key / value gradients through two
-closed forms that hold at any size (Direct3D-S2 page, "Method": the softmax
-of every branch is unchanged when all keys of a sequence move together, and
-every branch output moves with a common shift of the values).
+output gradient.  Small workloads and the whole 16384-token workload are
+compared element by element against oracle.backward.  On the varlen workload
+every gradient of its shortest sequence is compared element by element (the
+oracle runs that sequence alone: sequences never interact), and dq / dgates
+on sampled rows of all sequences; the grouped-head workload is compared on
+sampled rows for dq and dgates.  On both, the key / value gradients are also
+checked through two closed forms that hold at any size (Direct3D-S2 page,
+"Method": the softmax of every branch is unchanged when all keys of a
+sequence move together, and every branch output moves with a common shift of
+the values).
 
 Bar: relative L2 error of each gradient tensor <= 1e-2 for bfloat16 (1e-4
 for float32 storage), and max |error| <= 5 % of the tensor's largest
@@ -22,6 +26,7 @@ import torch
 
 import oracle
 import spatial_sparse_attention_ssa_amd as ssa
+from oracle import parallel as oracle_pool
 from tests import _parity as P
 from workloads import make_custom, make_workload
 
@@ -172,7 +177,46 @@ def _sequence_sums(wl, grads, dout):
     return worst
 
 
-@pytest.mark.parametrize("cfg,n_rows", [(5, 48), (4, 24)])
+def _selection_agreement(saved_topk, ref_topk, G, rows=None):
+    """share of (token, group) selections equal as sets; ref_topk is
+    [N, Hkv, k] (or [len(rows), k] with rows)"""
+    sel = np.sort(saved_topk.cpu().numpy(), axis=-1)
+    if rows is None:
+        return float((sel == np.sort(ref_topk, axis=-1)).all(-1).mean())
+    got = sel[[t for t, _ in rows], [h // G for _, h in rows]]
+    return float((got == np.sort(ref_topk, axis=-1)).all(-1).mean())
+
+
+def test_workload2_backward_full():
+    # every gradient entry of the 16384-token workload (multi-tile MFMA paths,
+    # real inverted top-k lists), the oracle over worker processes
+    wl = make_workload(2)
+    ob = P.oracle_blocks(wl)
+    gb = P.gpu_build(wl)
+    dout = _dout(wl, 2)
+    saved, grads = _gpu_grads(wl, gb, dout)
+    torch.cuda.synchronize()
+    fwd = oracle_pool.forward_rows(wl, ob, [(t, g) for t in range(wl.n_tokens) for g in range(wl.h_kv)])
+    agree = _selection_agreement(saved["topk"], fwd["topk"].reshape(wl.n_tokens, wl.h_kv, -1), 1)
+    assert agree >= P.TOPK_AGREE, f"selection agrees on only {agree:.5f} of (token, group) pairs"
+    ref = oracle_pool.backward_full(wl, dout, ob)
+    rels = {nm: _compare(nm, P.host(grads[nm]), ref[nm], wl.dtype) for nm in ("dq", "dk", "dv", "dgates")}
+    P.record("backward_full", tag="workload 2", n_tokens=wl.n_tokens, selection_agree=agree, rel_l2=rels)
+    print("workload 2:", agree, {k2: f"{v2:.2e}" for k2, v2 in rels.items()})
+
+
+def _subsequence(wl, b, dout):
+    """Sequence b of a varlen workload as a workload of its own (and its slice
+    of the output gradient)."""
+    s, e = int(wl.cu_seqlens[b]), int(wl.cu_seqlens[b + 1])
+    sub = copy.copy(wl)
+    sub.coords = wl.coords[s:e]
+    sub.cu_seqlens = np.array([0, e - s], dtype=np.int32)
+    sub.q, sub.k, sub.v, sub.gates = wl.q[s:e], wl.k[s:e], wl.v[s:e], wl.gates[s:e]
+    return sub, dout[s:e], slice(s, e)
+
+
+@pytest.mark.parametrize("cfg,n_rows", [(5, 2000), (4, 1000)])
 def test_large_workload_backward(cfg, n_rows):
     wl = make_workload(cfg)
     print(f"workload {cfg}: N={wl.n_tokens}", flush=True)
@@ -182,18 +226,36 @@ def test_large_workload_backward(cfg, n_rows):
     saved, grads = _gpu_grads(wl, gb, dout)
     torch.cuda.synchronize()
     rows = P.sample_rows(wl, n_rows, seed=cfg)
-    ref = oracle.backward(wl, dout, blocks=ob, rows=rows)
-    fwd = oracle.forward_rows(wl, ob, rows)
     G = wl.h_q // wl.h_kv
-    sel = saved["topk"].cpu().numpy()
-    same = [bool(set(sel[t, h // G]) == set(fwd["topk"][r])) for r, (t, h) in enumerate(rows)]
-    assert np.mean(same) >= 0.97, f"selection agrees on only {np.mean(same):.3f} of the rows"
-    rr = [r for r in range(len(rows)) if same[r]]
+    fwd = oracle_pool.forward_rows(wl, ob, rows)
+    same = np.sort(saved["topk"].cpu().numpy(), axis=-1)[[t for t, _ in rows], [h // G for _, h in rows]] \
+        == np.sort(fwd["topk"], axis=-1)
+    same = same.all(-1)
+    agree = float(same.mean())
+    assert agree >= P.TOPK_AGREE, f"selection agrees on only {agree:.5f} of the rows"
+    ref = oracle_pool.backward_rows(wl, dout, ob, rows)
+    rr = np.flatnonzero(same)
     tt = [rows[r][0] for r in rr]
     hh = [rows[r][1] for r in rr]
-    for nm in ("dq", "dgates"):
-        got = P.host(grads[nm])[tt, hh]
-        _compare(nm, got, ref[nm][rr], wl.dtype)
+    rels = {nm: _compare(nm, P.host(grads[nm])[tt, hh], ref[nm][rr], wl.dtype) for nm in ("dq", "dgates")}
     worst = _sequence_sums(wl, grads, dout)
-    print(f"workload {cfg}: sequence-sum residual {worst:.2e}")
+    print(f"workload {cfg}: selection agree {agree:.5f}, sequence-sum residual {worst:.2e}")
     assert worst <= 2e-2, f"sequence sums of dk / dv off by {worst:.3e}"
+    if cfg == 5:
+        # every gradient of the shortest sequence, element by element
+        b = int(np.argmin(np.diff(wl.cu_seqlens)))
+        sub, sub_dout, sl = _subsequence(wl, b, dout)
+        sob = P.oracle_blocks(sub)
+        sfwd = oracle_pool.forward_rows(sub, sob, [(t, g) for t in range(sub.n_tokens) for g in range(sub.h_kv)])
+        # the batch numbers blocks globally, the sequence alone from 0
+        j0 = int(ob.seq_blk_off[b])
+        sel_b = saved["topk"][sl]
+        sel_b = torch.where(sel_b >= 0, sel_b - j0, sel_b)
+        sagree = _selection_agreement(sel_b, sfwd["topk"].reshape(sub.n_tokens, sub.h_kv, -1), 1)
+        assert sagree >= P.TOPK_AGREE, f"sequence {b}: selection agrees on only {sagree:.5f}"
+        sref = oracle_pool.backward_full(sub, sub_dout, sob)
+        for nm in ("dq", "dk", "dv", "dgates"):
+            rels[f"seq{b}_{nm}"] = _compare(f"sequence {b} {nm}", P.host(grads[nm][sl]), sref[nm], wl.dtype)
+        print(f"workload 5, sequence {b} ({sub.n_tokens} tokens): selection agree {sagree:.5f}")
+    P.record("backward_sampled", tag=f"workload {cfg}", rows=len(rows), selection_agree=agree,
+             sequence_sum_residual=worst, rel_l2=rels)

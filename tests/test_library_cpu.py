@@ -188,3 +188,22 @@ def test_forward_train_needs_its_outputs():
                                None) == B.SSA_ERR_INVALID_ARGUMENT
     assert L.ssa_forward_train(ctypes.byref(st), ctypes.byref(a), p, p, p, p, p, p, None, p, 1 << 40,
                                None) == B.SSA_ERR_INVALID_ARGUMENT
+
+
+def test_forward_rejects_bad_out_buffers():
+    # the kernels write N * Hq * D elements of q's dtype, 16 bytes at a time:
+    # anything else passed as `out` is refused before the library is called
+    import torch
+
+    import spatial_sparse_attention_ssa_amd as ssa
+    q = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    bad = {
+        "dtype": torch.zeros(10, 4, 64, dtype=torch.float32),
+        "shape": torch.zeros(9, 4, 64, dtype=torch.bfloat16),
+        "contiguous": torch.zeros(10, 64, 4, dtype=torch.bfloat16).transpose(1, 2),
+        "aligned": torch.zeros(10 * 4 * 64 + 1, dtype=torch.bfloat16)[1:].view(10, 4, 64),
+        "GPU": torch.zeros(10, 4, 64, dtype=torch.bfloat16),   # a host tensor
+    }
+    for what, out in bad.items():
+        with pytest.raises(ValueError, match=what):
+            ssa._check_out(out, q)

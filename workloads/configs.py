@@ -78,7 +78,7 @@ def _varlen_counts() -> list[int]:
     return [int(round(math.exp(x))) for x in rng.uniform(lo, hi, size=8)]
 
 
-@functools.lru_cache(maxsize=4)
+@functools.lru_cache(maxsize=8)
 def _geometry(cfg_id: int):
     cfg = CONFIGS[cfg_id]
     R = cfg["grid_res"]

@@ -12,10 +12,18 @@ import numpy as np
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to nearest-even bfloat16; returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    """Round finite float32 values to nearest-even bfloat16; returns uint16 bit
+    patterns.  (Adding 0x7FFF plus the kept part's lowest bit to the 32-bit
+    pattern carries into the kept 16 bits exactly when the dropped half is
+    above one half, or equal to it with an odd kept part; for finite values
+    the sum stays below 2^32.)"""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
