@@ -114,8 +114,16 @@ bool use_mfma_path(const ssa_attn* a) {
 }
 
 struct FwdLayout {
-  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, blk_cell, total;
+  size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, blk_cell, knorm2, probe_slot,
+      probe_seq, probe_maxn2, probe, total;
 };
+
+// probe sets of the one-head-per-group compressed kernel: one per sequence
+// with more than kProbeBlocks blocks, so at most nb_cap / (kProbeBlocks + 1)
+int32_t max_probe_slots(const ssa_blocks* b) {
+  const int64_t by_blocks = nb_capacity(b) / (ssa::kProbeBlocks + 1);
+  return static_cast<int32_t>(by_blocks < b->batch ? by_blocks : b->batch);
+}
 
 FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
   const size_t cap = static_cast<size_t>(nb_capacity(b));
@@ -137,6 +145,14 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
     if (use_gqa_path(a)) {
       L.norm = off; off += align256(sizeof(float) * n * a->h_q);
       L.tile_pre2 = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+    } else {
+      const size_t slots = static_cast<size_t>(max_probe_slots(b));
+      L.knorm2 = off; off += align256(sizeof(float) * a->h_kv * cap);
+      L.probe_slot = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+      L.probe_seq = off; off += align256(sizeof(int32_t) * (slots + 1));
+      L.probe_maxn2 = off; off += align256(sizeof(float) * a->h_kv * (slots + 1));
+      L.probe = off; off += align256(static_cast<size_t>(elt_bytes(a->dtype)) * a->h_kv * slots * ssa::kProbeBlocks *
+                                     a->head_dim);
     }
     if (a->routing == SSA_ROUTE_GEOMETRIC) {
       L.blk_cell = off; off += align256(4 * sizeof(int32_t) * cap);
@@ -251,6 +267,7 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
     stages[n++] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
     stages[n++] = Stage{"gqa_fixup_kernel", ssa::launch_gqa_fixup};
   } else {
+    stages[n++] = Stage{"probe_kernel", ssa::launch_cmp_probe};
     stages[n++] = Stage{"cmp_mfma_kernel", ssa::launch_cmp_mfma};
     stages[n++] = Stage{"topk_fixup_kernel", ssa::launch_topk_fixup};
   }
@@ -330,6 +347,13 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
       p.norm = reinterpret_cast<float*>(w + lay.norm);
       p.tile_pre2 = reinterpret_cast<int32_t*>(w + lay.tile_pre2);
       p.max_tiles2 = static_cast<int32_t>(blocks->n_tokens / 16 + blocks->batch + 1);
+    } else {
+      p.knorm2 = reinterpret_cast<float*>(w + lay.knorm2);
+      p.probe_slot = reinterpret_cast<int32_t*>(w + lay.probe_slot);
+      p.probe_seq = reinterpret_cast<int32_t*>(w + lay.probe_seq);
+      p.probe_maxn2 = reinterpret_cast<float*>(w + lay.probe_maxn2);
+      p.probe = w + lay.probe;
+      p.max_probe_slots = max_probe_slots(blocks);
     }
     if (attn->routing == SSA_ROUTE_GEOMETRIC) {
       p.coords = blocks->coords;

@@ -89,18 +89,129 @@ __device__ __forceinline__ void seq_token_range(const FwdParams& p, int b, int* 
   *s1 = p.win_off[p.seq_win_off[b + 1]];
 }
 
-// tile_pre[b] = number of query tiles of sequences before b
+// tile_pre[b] = number of query tiles of sequences before b; with probes,
+// also the probe slot of every sequence with more than kProbeBlocks blocks
 __global__ void tile_prefix_kernel(FwdParams p) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int run = 0;
+  int run = 0, slots = 0;
   for (int b = 0; b < p.batch; ++b) {
     p.tile_pre[b] = run;
     int s0, s1;
     seq_token_range(p, b, &s0, &s1);
     run += (s1 - s0 + kQueryTile - 1) / kQueryTile;
+    if (p.probe_slot) {
+      int slot = -1;
+      if (p.seq_blk_off[b + 1] - p.seq_blk_off[b] > kProbeBlocks && slots < p.max_probe_slots) {
+        slot = slots++;
+        p.probe_seq[slot] = b;
+      }
+      p.probe_slot[b] = slot;
+    }
   }
   p.tile_pre[p.batch] = run;
+  if (p.probe_slot) p.probe_slot[p.batch] = slots;
   p.fix[0] = 0;
+}
+
+// Probe set of one (sequence, head): the kProbeBlocks pooled keys of largest
+// squared norm, copied in block order, and the largest squared norm.  Any
+// set of the sequence's blocks gives a valid lower bound on its k-th largest
+// logit (the compressed kernel's first pass); blocks of large key norm give
+// a tight one, since a logit is at most |q| |Kbar_j|.  The selection is a
+// 1024-bin histogram of the norms' top bits: every block of a bin above the
+// threshold bin, then the lowest-numbered blocks of the threshold bin until
+// kProbeBlocks are chosen.
+__global__ void __launch_bounds__(256)
+probe_select_kernel(FwdParams p) {
+  constexpr int kBins = 1024;
+  __shared__ int hist[kBins];
+  __shared__ int wcnt[2][4];
+  __shared__ float wmax[4];
+  __shared__ int sh_bin, sh_need;
+  const int s = blockIdx.x, g = blockIdx.y;
+  if (s >= p.probe_slot[p.batch]) return;   // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = p.probe_seq[s];
+  const int j0 = p.seq_blk_off[b], nbs = p.seq_blk_off[b + 1] - j0;   // nbs > kProbeBlocks
+  const float* n2 = p.knorm2 + static_cast<int64_t>(g) * p.nb_cap + j0;
+  for (int i = tid; i < kBins; i += 256) hist[i] = 0;
+  __syncthreads();
+  float mx = 0.f;
+  for (int j = tid; j < nbs; j += 256) {
+    const float v = n2[j];   // >= 0: the bits order like the values
+    mx = fmaxf(mx, v);
+    atomicAdd(&hist[__float_as_uint(v) >> 21], 1);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) wmax[wv] = mx;
+  __syncthreads();
+  if (wv == 0) {
+    // lane l counts bins 1023 - 16 l - (0..15); an inclusive scan over the
+    // lanes runs from the top bin down, and the lane where it reaches
+    // kProbeBlocks finds the threshold bin in its range
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c += hist[kBins - 1 - 16 * lane - i];
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const int excl = incl - c;
+    if (excl < kProbeBlocks && incl >= kProbeBlocks) {
+      int cum = excl;
+      for (int i = 0; i < 16; ++i) {
+        const int bin = kBins - 1 - 16 * lane - i;
+        if (cum + hist[bin] >= kProbeBlocks) {
+          sh_bin = bin;
+          sh_need = kProbeBlocks - cum;
+          break;
+        }
+        cum += hist[bin];
+      }
+    }
+    if (lane == 0)
+      p.probe_maxn2[g * p.max_probe_slots + s] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  }
+  __syncthreads();
+  const int tbin = sh_bin, need = sh_need;
+  const uint16_t* src = static_cast<const uint16_t*>(p.kbar) + (static_cast<int64_t>(g) * p.nb_cap + j0) * 64;
+  uint16_t* dst = static_cast<uint16_t*>(p.probe) +
+                  static_cast<int64_t>(g * p.max_probe_slots + s) * kProbeBlocks * 64;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int base_gt = 0, base_eq = 0;   // chosen blocks above / in the threshold bin before this chunk
+  for (int c0 = 0; c0 < nbs; c0 += 256) {
+    const int j = c0 + tid;
+    const int bin = j < nbs ? static_cast<int>(__float_as_uint(n2[j]) >> 21) : -1;
+    const bool gt = bin > tbin, eq = bin == tbin;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    if (lane == 0) {
+      wcnt[0][wv] = __popcll(bg);
+      wcnt[1][wv] = __popcll(be);
+    }
+    __syncthreads();
+    int pgt = base_gt + __popcll(bg & below), peq = base_eq + __popcll(be & below);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) {
+        pgt += wcnt[0][w];
+        peq += wcnt[1][w];
+      }
+      base_gt += wcnt[0][w];
+      base_eq += wcnt[1][w];
+    }
+    __syncthreads();   // wcnt is rewritten by the next chunk
+    if (gt || (eq && peq < need)) {
+      // position among the chosen blocks, in block order
+      const int pos = pgt + min(peq, need);
+      const u32x4* from = reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(j) * 64);
+      u32x4* to = reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(pos) * 64);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) to[c] = from[c];
+    }
+  }
 }
 
 template <int KMAX>
@@ -272,6 +383,34 @@ cmp_mfma_kernel(FwdParams p) {
   };
 
   // ---------------- pass 1: sorted lists of the KMAX largest group maxima
+  // A sequence with a probe set (its kProbeBlocks keys of largest norm) runs
+  // pass 1 over those 16 tiles instead of all of its tiles, when every query
+  // of the workgroup has |q| max_j |Kbar_j| scale log2 e <= 60: every logit s
+  // then satisfies |s| c2 <= 60, so x = (s - tau') c2 stays within +-120 and
+  // 2^x neither overflows nor flushes the row to zero (the shift by tau' is
+  // always safe; the pass never needs the row maximum).
+  const float c2 = p.scale * kLog2e;
+  const int pslot = p.probe_slot ? p.probe_slot[b] : -1;
+  bool probe_ok = true;
+  if (pslot >= 0) {
+    const float maxn2 = p.probe_maxn2[h * p.max_probe_slots + pslot];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      float qn2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float qv = static_cast<float>(blk[x].qb[ks][e]);
+          qn2 = fmaf(qv, qv, qn2);
+        }
+      qn2 += __shfl_xor(qn2, 32);
+      // 1 % covers the float32 rounding of the products' sum
+      probe_ok = probe_ok && sqrtf(qn2 * maxn2) * 1.01f * c2 <= 60.f;
+    }
+  }
+  const bool use_probe = pslot >= 0 && __syncthreads_and(probe_ok ? 1 : 0);
+  const int n1 = use_probe ? kProbeBlocks / kKeyTile : n_kt;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -281,7 +420,7 @@ cmp_mfma_kernel(FwdParams p) {
   // give a looser bound; each lane keeps at least ~48 groups:
   //   glog 32: two tiles (16 logits each), glog 16: one tile,
   //   glog 8: half a tile, glog 4: a quarter tile.
-  const int glog = n_kt >= 96 ? 32 : n_kt >= 48 ? 16 : n_kt >= 24 ? 8 : 4;
+  const int glog = n1 >= 96 ? 32 : n1 >= 48 ? 16 : n1 >= 24 ? 8 : 4;
   auto list_insert = [&](QBlock<KMAX>& B, float m) {
 #pragma unroll
     for (int i = KMAX - 1; i >= 1; --i) B.L[i] = __builtin_amdgcn_fmed3f(B.L[i - 1], m, B.L[i]);
@@ -318,15 +457,24 @@ cmp_mfma_kernel(FwdParams p) {
   };
   {
     blk[0].g = blk[1].g = -FLT_MAX;
+    // pass 1 reads the probe tiles (every row a real key) or the sequence's
+    // own tiles
+    const uint16_t* kg1 = kg;
+    if (use_probe)
+      kg1 = static_cast<const uint16_t*>(p.probe) +
+            (static_cast<int64_t>(h * p.max_probe_slots + pslot) * kProbeBlocks + k_row) * kD + 8 * k_chunk;
+    auto load_k1 = [&](int rel) {
+      return *reinterpret_cast<const u32x4*>(kg1 + static_cast<int64_t>(rel) * kKeyTile * kD);
+    };
     u32x4 kr = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(k_lds + ks_dst) = load_k(0);
-    if (n_kt > 1) kr = load_k(1);
+    *reinterpret_cast<u32x4*>(k_lds + ks_dst) = load_k1(0);
+    if (n1 > 1) kr = load_k1(1);
     // step rel: S of block A for tile rel next to block B's update for tile
     // rel - 1, then S of block B next to block A's update
     auto step = [&](int rel, auto mask_a, auto has_b, auto mask_b) {
       __syncthreads();  // key tile rel stored; everyone is done with tile rel - 1
-      if (rel + 1 < n_kt) *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTileElems + ks_dst) = kr;
-      if (rel + 2 < n_kt) kr = load_k(rel + 2);
+      if (rel + 1 < n1) *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTileElems + ks_dst) = kr;
+      if (rel + 2 < n1) kr = load_k1(rel + 2);
       bf16x8 a[4];
       read_k(rel, a);
       const f32x16 sa = qk(a, blk[0].qb);
@@ -335,17 +483,22 @@ cmp_mfma_kernel(FwdParams p) {
       blk[0].s = sa;
       group_update(blk[0], rel, mask_a);
     };
-    run_tiles(step);
-    group_update(blk[1], n_kt - 1, kT{});
+    if (use_probe) {
+      step(0, kF{}, kF{}, kF{});
+      for (int rel = 1; rel < n1; ++rel) step(rel, kF{}, kT{}, kF{});
+      group_update(blk[1], n1 - 1, kF{});
+    } else {
+      run_tiles(step);
+      group_update(blk[1], n_kt - 1, kT{});
+    }
     // an open two-tile group (odd tile count)
-    if (glog == 32 && (n_kt & 1)) {
+    if (glog == 32 && (n1 & 1)) {
       list_insert(blk[0], blk[0].g);
       list_insert(blk[1], blk[1].g);
     }
   }
 
   // ---------------- per-query constants for pass 2
-  const float c2 = p.scale * kLog2e;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     QBlock<KMAX>& B = blk[x];
@@ -370,7 +523,9 @@ cmp_mfma_kernel(FwdParams p) {
       B.f_and = 0xFFFFu;
       if (tau > -FLT_MAX) {
         const float tp = tau - (fabsf(tau) + fabsf(row_max)) * (1.0f / 4096.0f);
-        if ((row_max - tp) * c2 <= 64.f) {
+        // with the probe, row_max is only the probe's maximum, but every
+        // exponent is bounded (see pass 1)
+        if (use_probe || (row_max - tp) * c2 <= 64.f) {
           B.k0 = -tp * c2;
         } else {
           B.k0 = -row_max * c2;
@@ -728,8 +883,16 @@ void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream) {
   tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
 }
 
-hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+// the query-tile prefix, the probe slots and the probe sets (the compressed
+// kernel reads all three)
+hipError_t launch_cmp_probe(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   tile_prefix_kernel_launch(p, stream);
+  if (p.probe_slot && p.max_probe_slots > 0)
+    probe_select_kernel<<<dim3(p.max_probe_slots, p.h_kv), 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   const dim3 grid(p.max_tiles, p.h_q);
   if (p.topk <= 16) cmp_mfma_kernel<16><<<grid, 256, 0, stream>>>(p);
   else cmp_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);

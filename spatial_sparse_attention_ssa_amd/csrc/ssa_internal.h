@@ -175,6 +175,15 @@ struct FwdParams {
   int32_t* fix;       // [1 + n * h_kv] overflow counter, then (token * h_kv + group) entries
   float* acc;         // [n][h_q][D] partial sum of the gated branches (input token order)
   int32_t max_tiles;  // upper bound of query tiles
+  // probe set of the one-head-per-group compressed kernel (bf16, D = 64): for
+  // every sequence with more than kProbeBlocks blocks, per head, the
+  // kProbeBlocks pooled keys of largest norm (null = no probes)
+  float* knorm2;         // [h_kv][nb_cap] squared norm of each pooled key row (written by pooling)
+  int32_t* probe_slot;   // [batch + 1] probe slot of each sequence or -1; [batch] = slots used
+  int32_t* probe_seq;    // [max_probe_slots] sequence of each slot
+  float* probe_maxn2;    // [h_kv][max_probe_slots] largest squared key norm of the slot's sequence
+  void* probe;           // [h_kv][max_probe_slots][kProbeBlocks][D] the probe keys, in block order
+  int32_t max_probe_slots;
   // grouped-head path: log2 softmax normaliser per (token, query head), and
   // the prefix of 16-token tiles per sequence
   float* norm;        // [n][h_q]
@@ -239,6 +248,7 @@ struct BwdParams {
 
 constexpr int kKeyTile = 32;     // pooled blocks per MFMA key tile
 constexpr int kQueryTile = 256;  // queries per workgroup of the compressed MFMA kernel (4 waves x 64)
+constexpr int kProbeBlocks = 512;  // pooled keys per probe set (16 key tiles)
 
 hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream);
@@ -263,6 +273,7 @@ hipError_t launch_bwd_win_dq_mfma(const BwdParams& p, ssa_dtype dtype, hipStream
 hipError_t launch_bwd_kv_sel_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_bwd_rows_prep(const BwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_cmp_probe(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);

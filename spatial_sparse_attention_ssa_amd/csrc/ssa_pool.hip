@@ -9,13 +9,17 @@
 //
 // pool_kernel: one workgroup per block (grid-stride over the device-side
 // block count).  On the MFMA path it also writes the key and value rows in
-// sorted order, head-major, for the window and selection kernels.  A token row (h_kv * D elements, contiguous in HBM) is split
+// sorted order, head-major, for the window and selection kernels, and the
+// squared norm of every pooled key row (of its bfloat16 values), from which
+// the compressed kernel's probe set is chosen.  A token row (h_kv * D elements, contiguous in HBM) is split
 // into 16-byte chunks, one per thread; rows with fewer than 256 chunks run
 // several token slots side by side, summed afterwards in slot order through
 // LDS (deterministic).  Each thread keeps four row loads in flight.
 //
 // vt_transpose_kernel: rewrites the pooled values of every 32-block tile as
 // [D][32 blocks], blocks in the order the MFMA kernels' P^T operand uses.
+#include <type_traits>
+
 #include "ssa_internal.h"
 
 namespace ssa {
@@ -61,7 +65,7 @@ __global__ void __launch_bounds__(256)
 pool_kernel(const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ perm,
             const int32_t* __restrict__ blk_off, const int32_t* __restrict__ counts, int n, int hkv, int d,
             int nb_cap, T* __restrict__ kbar, T* __restrict__ vbar, T* __restrict__ k_cmp,
-            T* __restrict__ v_cmp, T* __restrict__ k_s, T* __restrict__ v_s) {
+            T* __restrict__ v_cmp, T* __restrict__ k_s, T* __restrict__ v_s, float* __restrict__ knorm2) {
   constexpr int EC = Chunk<T>::kN;                      // elements per 16-byte chunk
   __shared__ float red[256 * EC];
   const int e_per_tok = hkv * d;
@@ -137,6 +141,22 @@ pool_kernel(const T* __restrict__ k, const T* __restrict__ v, const int32_t* __r
           *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(g) * nb_cap + j) * d + dd) = packed;
           T* pub = which ? v_cmp : k_cmp;
           if (pub) *reinterpret_cast<u32x4*>(pub + static_cast<int64_t>(j) * e_per_tok + e0) = packed;
+          if constexpr (std::is_same<T, uint16_t>::value) {
+            if (knorm2 && which == 0) {
+              // squared norm of the rounded key row: the d / 8 threads of one
+              // head are consecutive lanes (d / 8 divides tpt)
+              float n2 = 0.f;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(packed[e] << 16), hi = __uint_as_float(packed[e] & 0xFFFF0000u);
+                n2 = fmaf(lo, lo, fmaf(hi, hi, n2));
+              }
+              n2 += __shfl_xor(n2, 1);
+              n2 += __shfl_xor(n2, 2);
+              if (d == 64) n2 += __shfl_xor(n2, 4);
+              if (dd == 0) knorm2[static_cast<int64_t>(g) * nb_cap + j] = n2;
+            }
+          }
         }
         if (slots > 1) __syncthreads();
       }
@@ -214,7 +234,8 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
         static_cast<const uint16_t*>(p.k), static_cast<const uint16_t*>(p.v), p.perm, p.blk_off,
         p.counts, p.n, p.h_kv, p.d, p.nb_cap, static_cast<uint16_t*>(p.kbar),
         static_cast<uint16_t*>(p.vbar), static_cast<uint16_t*>(p.k_cmp),
-        static_cast<uint16_t*>(p.v_cmp), static_cast<uint16_t*>(p.k_s), static_cast<uint16_t*>(p.v_s));
+        static_cast<uint16_t*>(p.v_cmp), static_cast<uint16_t*>(p.k_s), static_cast<uint16_t*>(p.v_s),
+        p.knorm2);
     if (p.vbar_t) {
       const int tiles = p.h_kv * (p.nb_cap / kKeyTile);
       const int grid_t = tiles < 4096 ? tiles : 4096;
@@ -230,7 +251,7 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
         static_cast<const float*>(p.k), static_cast<const float*>(p.v), p.perm, p.blk_off,
         p.counts, p.n, p.h_kv, p.d, p.nb_cap, static_cast<float*>(p.kbar), static_cast<float*>(p.vbar),
         static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp), static_cast<float*>(p.k_s),
-        static_cast<float*>(p.v_s));
+        static_cast<float*>(p.v_s), nullptr);
   }
   return hipGetLastError();
 }

@@ -250,6 +250,38 @@ def test_gqa_top_blocks_in_one_lane(head_dim):
     assert np.isin(sel[:, 0, :], fav).mean() > 0.99
 
 
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_probe_bound_paths_full(q_scale):
+    # a sequence with more than 512 blocks takes the compressed kernel's
+    # first pass over its 512 largest-norm pooled keys; queries scaled by 4
+    # break the magnitude guard (|q| max |Kbar| scale log2 e <= 60), so the
+    # same sequence takes the pass over all of its key tiles
+    wl = make_custom([14000, 700], grid_res=128, n_prims=4, topk=16, h_q=4, h_kv=4, head_dim=64, dtype="bf16",
+                     seed=51)
+    assert np.diff(P.oracle_blocks(wl).seq_blk_off).max() > 512
+    if q_scale != 1.0:
+        wl.q = bf16_bits_to_f32(bf16_bits_from_f32(wl.q * np.float32(q_scale)))
+    _full_compare(wl, tag=f"probe paths, q x {q_scale:g}")
+
+
+def test_constant_keys_pick_first_blocks():
+    # every pooled key equal: all norms fall in one histogram bin (the probe
+    # takes the sequence's first 512 blocks) and all logits tie, so each
+    # query selects the sequence's lowest block ids
+    wl = make_custom([14000, 300], grid_res=128, n_prims=4, topk=16, h_q=4, h_kv=4, head_dim=64, dtype="bf16",
+                     seed=52)
+    wl.k[:] = wl.k[0:1, 0:1, :]
+    ob = P.oracle_blocks(wl)
+    assert np.diff(ob.seq_blk_off).max() > 512
+    gb = P.gpu_build(wl)
+    sel = P.gpu_forward(wl, gb, return_topk=True)["topk"].cpu().numpy()
+    for b in range(wl.batch):
+        j0, j1 = ob.seq_blk_off[b], ob.seq_blk_off[b + 1]
+        toks = ob.perm[ob.blk_off[j0]:ob.blk_off[j1]]
+        expect = np.arange(j0, min(j0 + wl.topk, j1))
+        assert (sel[toks][:, :, :len(expect)] == expect).all()
+
+
 def dense_cube(n, side, seed):
     """n distinct voxels drawn uniformly from a side^3 grid"""
     rng = np.random.default_rng(seed)
