@@ -176,6 +176,28 @@ ssa_status ssa_forward(const ssa_blocks *blocks, const ssa_attn *attn, const voi
                        void *k_cmp, void *v_cmp, int32_t *topk_idx, void *workspace,
                        size_t ws_bytes, void *hip_stream);
 
+/* Largest workspace ssa_forward_noalloc can serve (64 MiB). */
+#define SSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* ssa_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The scratch is a
+ * file-scope device array of SSA_NOALLOC_SCRATCH_BYTES inside the library;
+ * every GPU it runs on holds its own copy until the process ends.  Arguments,
+ * outputs and results are those of ssa_forward (q, k, v, gates, out and the
+ * optional k_cmp, v_cmp, topk_idx stay caller-owned).  The device current on
+ * the calling thread must be the one hip_stream and the pointers belong to.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on the same GPU (other streams, other threads) race and must be ordered by
+ * the caller.  Each kernel reads only scratch bytes written earlier in the
+ * same call, so what a previous call left there does not matter.
+ * Errors: as ssa_forward; WORKSPACE when ssa_forward_workspace() for these
+ * blocks and this layout exceeds SSA_NOALLOC_SCRATCH_BYTES (nothing is
+ * launched); DEVICE when the array's address cannot be obtained. */
+ssa_status ssa_forward_noalloc(const ssa_blocks *blocks, const ssa_attn *attn, const void *q,
+                               const void *k, const void *v, const void *gates, void *out,
+                               void *k_cmp, void *v_cmp, int32_t *topk_idx, void *hip_stream);
+
 /* Stages of ssa_forward, in launch order (indices into stage_ms below). */
 enum {
   SSA_STAGE_POOL = 0,        /* mean pooling of keys / values                      */

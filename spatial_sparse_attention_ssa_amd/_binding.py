@@ -33,6 +33,7 @@ SSA_COUNT_MAX_WIN = 4
 SSA_COUNT_KEY_BITS = 5
 SSA_COUNTS = 8
 SSA_STAGES = 12
+SSA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/ssa.h declares
 EXPORTED = (
@@ -41,6 +42,7 @@ EXPORTED = (
     "ssa_forward_workspace",
     "ssa_forward",
     "ssa_forward_timed",
+    "ssa_forward_noalloc",
     "ssa_stage_name",
     "ssa_forward_train",
     "ssa_backward_workspace",
@@ -124,6 +126,9 @@ def lib() -> ctypes.CDLL:
                                     vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float),
                                     ctypes.POINTER(i32)]
     L.ssa_forward_timed.restype = ctypes.c_int
+    L.ssa_forward_noalloc.argtypes = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn), vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp]
+    L.ssa_forward_noalloc.restype = ctypes.c_int
     L.ssa_stage_name.argtypes = [ctypes.POINTER(SsaAttn), i32]
     L.ssa_stage_name.restype = ctypes.c_char_p
     L.ssa_forward_train.argtypes = [ctypes.POINTER(SsaBlocks), ctypes.POINTER(SsaAttn), vp, vp, vp, vp, vp,

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "ssa_internal.h"
@@ -413,6 +414,71 @@ ssa_status ssa_forward_train(const ssa_blocks* blocks, const ssa_attn* attn, con
   if (!topk_idx || !lse) return fail(SSA_ERR_INVALID_ARGUMENT, "topk_idx and lse must be non-null");
   return forward_impl(blocks, attn, q, k, v, gates, out, nullptr, nullptr, topk_idx, workspace, ws_bytes,
                       hip_stream, nullptr, nullptr, lse);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free forward
+
+namespace {
+
+// The workspace of ssa_forward_noalloc.  In host code this name is only a
+// stand-in for the symbol: the device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever handed to a kernel.
+__device__ __align__(256) unsigned char scratch[SSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of this device's copy of `scratch` (null on failure, with
+// the error recorded)
+void* scratch_address() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(SSA_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(SSA_ERR_DEVICE, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(SSA_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+ssa_status ssa_forward_noalloc(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                               const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
+                               int32_t* topk_idx, void* hip_stream) {
+  if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
+  ssa_status st = check_attn(attn);
+  if (st != SSA_OK) return st;
+  if (blocks->n_tokens < 0) return fail(SSA_ERR_INVALID_ARGUMENT, "n_tokens %lld < 0",
+                                        static_cast<long long>(blocks->n_tokens));
+  // forward_layout aligns the workspace start to 256 bytes itself; the array
+  // is 256-aligned, so the whole array is usable
+  const size_t need = forward_ws_bytes(blocks, attn);
+  if (need > SSA_NOALLOC_SCRATCH_BYTES)
+    return fail(SSA_ERR_WORKSPACE, "forward needs %zu bytes of scratch, above the %zu of the allocation-free entry",
+                need, static_cast<size_t>(SSA_NOALLOC_SCRATCH_BYTES));
+  void* ws = scratch_address();
+  if (!ws) return SSA_ERR_DEVICE;
+  return forward_impl(blocks, attn, q, k, v, gates, out, k_cmp, v_cmp, topk_idx, ws, SSA_NOALLOC_SCRATCH_BYTES,
+                      hip_stream, nullptr, nullptr);
 }
 
 const char* ssa_stage_name(const ssa_attn* attn, int32_t stage) {

@@ -207,3 +207,16 @@ def test_forward_rejects_bad_out_buffers():
     for what, out in bad.items():
         with pytest.raises(ValueError, match=what):
             ssa._check_out(out, q)
+
+
+def test_noalloc_forward_rejects_inputs_beyond_its_scratch():
+    # 60000 tokens x 16 heads x 64 dims: the float32 branch accumulator alone
+    # is 245 MB, beyond the 64 MiB array; rejected before anything runs
+    L = _lib()
+    st = _fake_blocks(n=60000)
+    a = B.SsaAttn(h_q=16, h_kv=16, head_dim=64, topk=16, scale=0.0, dtype=B.SSA_BF16, routing=0)
+    assert L.ssa_forward_workspace(ctypes.byref(st), ctypes.byref(a)) > B.SSA_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x100000)
+    assert L.ssa_forward_noalloc(ctypes.byref(st), ctypes.byref(a), fake, fake, fake, fake, fake, None, None, None,
+                                 None) == B.SSA_ERR_WORKSPACE
+    assert b"64" in L.ssa_last_error() or b"scratch" in L.ssa_last_error()
