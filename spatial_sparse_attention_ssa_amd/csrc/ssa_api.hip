@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <mutex>
 #include <string>
@@ -75,13 +76,23 @@ ssa::KeyLayout key_layout(const ssa_geometry* geo, int32_t batch) {
   return kl;
 }
 
+// The dtype field as the integer a C caller stored: any value may arrive
+// through the C ABI, and loading one outside the enumerators through the C++
+// enum type would be undefined.
+int raw_dtype(const ssa_attn* a) {
+  static_assert(sizeof(ssa_dtype) == sizeof(int), "ssa_dtype is stored as an int");
+  int v;
+  memcpy(&v, &a->dtype, sizeof(v));
+  return v;
+}
+
 ssa_status check_attn(const ssa_attn* a) {
   if (!a) return fail(SSA_ERR_INVALID_ARGUMENT, "attn is null");
   if (a->h_q < 1 || a->h_kv < 1 || a->h_q % a->h_kv)
     return fail(SSA_ERR_INVALID_ARGUMENT, "need h_q, h_kv >= 1 and h_q %% h_kv == 0 (got %d, %d)",
                 a->h_q, a->h_kv);
-  if (a->dtype != SSA_F32 && a->dtype != SSA_BF16)
-    return fail(SSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(a->dtype));
+  if (raw_dtype(a) != SSA_F32 && raw_dtype(a) != SSA_BF16)
+    return fail(SSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", raw_dtype(a));
   if (a->head_dim < 1) return fail(SSA_ERR_INVALID_ARGUMENT, "head_dim %d < 1", a->head_dim);
   if (a->topk < 1) return fail(SSA_ERR_INVALID_ARGUMENT, "topk %d < 1", a->topk);
   if (a->head_dim != 32 && a->head_dim != 64)
@@ -278,10 +289,9 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
   return n;
 }
 
-ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
-                        const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
-                        int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream,
-                        float* stage_ms, int32_t* n_stages, float* lse = nullptr) {
+// every argument check of the forward except the workspace's
+ssa_status check_forward_args(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                              const void* v, const void* gates, const void* out) {
   if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
   ssa_status st = check_attn(attn);
   if (st != SSA_OK) return st;
@@ -299,6 +309,15 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
     if (blocks->n_tokens > 0 && !blocks->coords)
       return fail(SSA_ERR_INVALID_ARGUMENT, "geometric routing needs the blocks' coordinates");
   }
+  return SSA_OK;
+}
+
+ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
+                        const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
+                        int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream,
+                        float* stage_ms, int32_t* n_stages, float* lse = nullptr) {
+  ssa_status st = check_forward_args(blocks, attn, q, k, v, gates, out);
+  if (st != SSA_OK) return st;
   const size_t need = forward_ws_bytes(blocks, attn);
   if (!workspace || ws_bytes < need)
     return fail(SSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? ws_bytes : 0, need);
@@ -464,11 +483,8 @@ extern "C" {
 ssa_status ssa_forward_noalloc(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
                                const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
                                int32_t* topk_idx, void* hip_stream) {
-  if (!blocks) return fail(SSA_ERR_INVALID_ARGUMENT, "blocks is null");
-  ssa_status st = check_attn(attn);
+  ssa_status st = check_forward_args(blocks, attn, q, k, v, gates, out);
   if (st != SSA_OK) return st;
-  if (blocks->n_tokens < 0) return fail(SSA_ERR_INVALID_ARGUMENT, "n_tokens %lld < 0",
-                                        static_cast<long long>(blocks->n_tokens));
   // forward_layout aligns the workspace start to 256 bytes itself; the array
   // is 256-aligned, so the whole array is usable
   const size_t need = forward_ws_bytes(blocks, attn);
