@@ -207,12 +207,19 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
   const uint64_t lt = lanemask_lt();
   uint32_t kk[kItems], rk[kItems], dg[kItems];
   int32_t vv[kItems];
+  // every load of the thread in flight before the ranking (which waits on
+  // LDS and ballots between keys)
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int p = base + r * kWave + lane;
+    kk[r] = p < n ? keys_in[p] : 0u;
+    vv[r] = p < n ? vals_in[p] : 0;
+  }
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const int p = base + r * kWave + lane;
     const bool valid = p < n;
-    const uint32_t key = valid ? keys_in[p] : 0u;
-    const int32_t val = valid ? vals_in[p] : 0;
+    const uint32_t key = kk[r];
     const uint32_t d = (key >> shift) & 255u;
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -228,8 +235,6 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     __builtin_amdgcn_wave_barrier();
     if (leader) whist[wave][d] = before + cnt;
     __builtin_amdgcn_wave_barrier();
-    kk[r] = key;
-    vv[r] = val;
     rk[r] = valid ? before + static_cast<uint32_t>(__popcll(peers & lt)) : 0xFFFFFFFFu;
     dg[r] = d;
   }
@@ -280,17 +285,23 @@ seg_count(const uint32_t* __restrict__ keys, int32_t n, int win_shift, int32_t* 
   __shared__ int32_t red[2][256];
   const int base = blockIdx.x * kSortTile;
   int cb = 0, cw = 0;
-  for (int i = threadIdx.x; i < kSortTile; i += 256) {
-    const int p = base + i;
+  uint32_t kc[kItems], kprev[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {   // all loads in flight first
+    const int p = base + r * 256 + threadIdx.x;
+    kc[r] = p < n ? keys[p] : 0u;
+    kprev[r] = (p < n && p > 0) ? keys[p - 1] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int p = base + r * 256 + threadIdx.x;
     if (p < n) {
-      const uint32_t k = keys[p];
       if (p == 0) {
         cb += 1;
         cw += 1;
       } else {
-        const uint32_t kp = keys[p - 1];
-        cb += (k != kp);
-        cw += ((k >> win_shift) != (kp >> win_shift));
+        cb += (kc[r] != kprev[r]);
+        cw += ((kc[r] >> win_shift) != (kprev[r] >> win_shift));
       }
     }
   }
@@ -368,6 +379,13 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
   int rank_b[kItems], rank_w[kItems];
   static_assert(2 * kItems <= 32, "two boundary flags per row are packed into 32 bits");
   uint32_t flags = 0;
+  uint32_t kc[kItems], kprev[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {   // all loads in flight before the ballots
+    const int p = base + r * kWave + lane;
+    kc[r] = p < n ? keys[p] : 0u;
+    kprev[r] = (p < n && p > 0) ? keys[p - 1] : 0u;
+  }
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const int p = base + r * kWave + lane;
@@ -377,9 +395,8 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
       if (p == 0) {
         isb = isw = true;
       } else {
-        const uint32_t k = keys[p], kp = keys[p - 1];
-        isb = k != kp;
-        isw = (k >> win_shift) != (kp >> win_shift);
+        isb = kc[r] != kprev[r];
+        isw = (kc[r] >> win_shift) != (kprev[r] >> win_shift);
       }
     }
     const uint64_t mb = __ballot(isb), mw = __ballot(isw);
@@ -413,16 +430,15 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
       const int wid = pw + rank_w[r];
       win_off[wid] = p;
       win_blk_off[wid] = bid;
-      const uint32_t k = keys[p];
-      const int s = seq_of(k, seq_shift);
-      const int sp = p ? seq_of(keys[p - 1], seq_shift) : -1;
+      const int s = seq_of(kc[r], seq_shift);
+      const int sp = p ? seq_of(kprev[r], seq_shift) : -1;
       for (int b = sp + 1; b <= s; ++b) {
         seq_blk_off[b] = bid;
         seq_win_off[b] = wid;
       }
     }
     if (p == n - 1) {
-      const int s = seq_of(keys[p], seq_shift);
+      const int s = seq_of(kc[r], seq_shift);
       for (int b = s + 1; b <= batch; ++b) {
         seq_blk_off[b] = nb_tot;
         seq_win_off[b] = nw_tot;
