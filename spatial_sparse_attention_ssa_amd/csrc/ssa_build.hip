@@ -48,24 +48,23 @@ __global__ void empty_offsets_kernel(int32_t batch, int32_t* blk_off, int32_t* w
   }
 }
 
-__global__ void __launch_bounds__(256)
-keys_kernel(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, int32_t n,
-            int32_t batch, KeyLayout kl, uint32_t* __restrict__ keys, int32_t* __restrict__ vals,
-            int32_t* __restrict__ counts) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n) return;
+// Block key of token t (input order) from its coordinates c; an out-of-grid
+// coordinate is clamped (keeping later stages in bounds) and counted as
+// invalid.
+__device__ __forceinline__ uint32_t block_key(int c0, int c1, int c2, const int32_t* __restrict__ cu, int32_t t,
+                                              int32_t batch, const KeyLayout& kl, int32_t* __restrict__ counts) {
   // sequence b: the largest b < batch with cu[b] <= t (empty sequences skipped)
   int lo = 0, hi = batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (cu[mid] <= t) lo = mid; else hi = mid - 1;
   }
-  int c[3] = {coords[3 * t], coords[3 * t + 1], coords[3 * t + 2]};
+  int c[3] = {c0, c1, c2};
   bool bad = false;
   for (int a = 0; a < 3; ++a) {
     if (c[a] < 0 || c[a] >= kl.grid_res) {
       bad = true;
-      c[a] = c[a] < 0 ? 0 : kl.grid_res - 1;  // clamp: keeps later stages in bounds
+      c[a] = c[a] < 0 ? 0 : kl.grid_res - 1;
     }
   }
   if (bad) atomicAdd(&counts[SSA_COUNT_INVALID], 1);
@@ -74,8 +73,62 @@ keys_kernel(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, 
   for (int a = 0; a < 3; ++a) c[a] += kl.shift;   // shifted windows: cells of c + shift
   for (int a = 0; a < 3; ++a) key = (key << kl.l_rw) | static_cast<uint32_t>(c[a] >> kl.l_win);
   for (int a = 0; a < 3; ++a) key = (key << kl.l_r) | (static_cast<uint32_t>(c[a] >> kl.l_cmp) & rmask);
-  keys[t] = static_cast<uint32_t>(key);
-  vals[t] = t;
+  return static_cast<uint32_t>(key);
+}
+
+// First radix pass, upsweep: every key of a 4096-token tile computed from its
+// coordinates, written out, and counted into the tile's digit histogram.  A
+// full tile gives each thread four runs of four consecutive tokens: their 12
+// coordinates are three 16-byte loads, their keys one 16-byte store, and all
+// loads are in flight before any key is formed.  The permutation starts as
+// the identity, which the first scatter generates itself.
+__global__ void __launch_bounds__(256)
+radix_upsweep_keys(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, int32_t n, int32_t batch,
+                   KeyLayout kl, uint32_t* __restrict__ keys, int32_t* __restrict__ counts,
+                   uint32_t* __restrict__ tile_hist) {
+  __shared__ uint32_t hist[4][256];
+  for (int i = threadIdx.x; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  uint32_t* const h = hist[threadIdx.x >> 6];
+  const int base = blockIdx.x * kSortTile;
+  if (base + kSortTile <= n) {
+    u32x4 cv[4][3];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int t0 = base + 4 * (g * 256 + threadIdx.x);
+      const u32x4* src = reinterpret_cast<const u32x4*>(coords + 3 * static_cast<int64_t>(t0));
+#pragma unroll
+      for (int w = 0; w < 3; ++w) cv[g][w] = src[w];
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int t0 = base + 4 * (g * 256 + threadIdx.x);
+      int c[12];
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[4 * w + e] = static_cast<int>(cv[g][w][e]);
+      u32x4 kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[e] = block_key(c[3 * e], c[3 * e + 1], c[3 * e + 2], cu, t0 + e, batch, kl, counts);
+        atomicAdd(&h[kv[e] & 255u], 1u);
+      }
+      *reinterpret_cast<u32x4*>(keys + t0) = kv;
+    }
+  } else {
+    for (int i = threadIdx.x; i < kSortTile; i += 256) {
+      const int t = base + i;
+      if (t < n) {
+        const uint32_t key = block_key(coords[3 * t], coords[3 * t + 1], coords[3 * t + 2], cu, t, batch, kl, counts);
+        keys[t] = key;
+        atomicAdd(&h[key & 255u], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  const int d = threadIdx.x;
+  tile_hist[static_cast<size_t>(blockIdx.x) * 256 + d] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
 }
 
 // Digit counts of one 4096-key tile, written tile-major (one contiguous
@@ -213,7 +266,8 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
   for (int r = 0; r < kItems; ++r) {
     const int p = base + r * kWave + lane;
     kk[r] = p < n ? keys_in[p] : 0u;
-    vv[r] = p < n ? vals_in[p] : 0;
+    // the first pass starts from the identity permutation
+    vv[r] = vals_in ? (p < n ? vals_in[p] : 0) : p;
   }
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
@@ -457,9 +511,23 @@ seg_stats(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ win_o
   const int nb = counts[SSA_COUNT_NB], nw = counts[SSA_COUNT_NW];
   const int m = nb > nw ? nb : nw;
   int mb = 0, mw = 0;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < m; i += gridDim.x * blockDim.x) {
-    if (i < nb) mb = max(mb, blk_off[i + 1] - blk_off[i]);
-    if (i < nw) mw = max(mw, win_off[i + 1] - win_off[i]);
+  const int stride = gridDim.x * blockDim.x;
+  // four segments per thread and step, their loads in flight together
+  for (int i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < m; i0 += 4 * stride) {
+    int b0[4], b1[4], w0[4], w1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * stride;
+      b0[u] = i < nb ? blk_off[i] : 0;
+      b1[u] = i < nb ? blk_off[i + 1] : 0;
+      w0[u] = i < nw ? win_off[i] : 0;
+      w1[u] = i < nw ? win_off[i + 1] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mb = max(mb, b1[u] - b0[u]);
+      mw = max(mw, w1[u] - w0[u]);
+    }
   }
   for (int off = 32; off > 0; off >>= 1) {
     mb = max(mb, __shfl_xor(mb, off));
@@ -570,13 +638,16 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
   int32_t* vin = (passes % 2 == 0) ? out.perm : ws.vals_b;
   uint32_t* kout = (passes % 2 == 0) ? ws.keys_b : ws.keys_a;
   int32_t* vout = (passes % 2 == 0) ? ws.vals_b : out.perm;
-  keys_kernel<<<(n + 255) / 256, 256, 0, stream>>>(coords, cu_seqlens, n, batch, kl, kin, vin,
-                                                    out.counts);
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kRadixBits;
-    radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, ws.tile_hist);
+    if (pass == 0)
+      radix_upsweep_keys<<<ntiles, 256, 0, stream>>>(coords, cu_seqlens, n, batch, kl, kin, out.counts,
+                                                     ws.tile_hist);
+    else
+      radix_upsweep<<<ntiles, 256, 0, stream>>>(kin, n, shift, ws.tile_hist);
     scan_tile_hist(ws.tile_hist, ntiles, stream);
-    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, vin, kout, vout, n, shift, ws.tile_hist);
+    radix_downsweep<<<ntiles, 256, 0, stream>>>(kin, pass == 0 ? nullptr : vin, kout, vout, n, shift,
+                                                ws.tile_hist);
     uint32_t* tk = kin; kin = kout; kout = tk;
     int32_t* tv = vin; vin = vout; vout = tv;
   }
