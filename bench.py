@@ -55,6 +55,7 @@ CSRC = os.path.join(ROOT, "spatial_sparse_attention_ssa_amd", "csrc")
 KERNEL_SOURCES = {
     "cmp_mfma_kernel": "ssa_attn_cmp.hip",
     "topk_fixup_kernel": "ssa_attn_cmp.hip",
+    "probe_select_kernel": "ssa_attn_cmp.hip",
     "win_mfma_kernel": "ssa_attn_win.hip",
     "sel_combine_kernel": "ssa_attn_sel.hip",
     "pool_kernel": "ssa_pool.hip",
