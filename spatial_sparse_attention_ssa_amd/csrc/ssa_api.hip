@@ -127,7 +127,7 @@ bool use_mfma_path(const ssa_attn* a) {
 
 struct FwdLayout {
   size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, blk_cell, knorm2, probe_slot,
-      probe_seq, probe_maxn2, probe, total;
+      probe_seq, probe_maxn2, probe, seq_kmax2, total;
 };
 
 // probe sets of the one-head-per-group compressed kernel: one per sequence
@@ -157,6 +157,8 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
     if (use_gqa_path(a)) {
       L.norm = off; off += align256(sizeof(float) * n * a->h_q);
       L.tile_pre2 = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+      L.knorm2 = off; off += align256(sizeof(float) * a->h_kv * cap);
+      L.seq_kmax2 = off; off += align256(sizeof(float) * a->h_kv * static_cast<size_t>(b->batch));
     } else {
       const size_t slots = static_cast<size_t>(max_probe_slots(b));
       L.knorm2 = off; off += align256(sizeof(float) * a->h_kv * cap);
@@ -367,6 +369,8 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
       p.norm = reinterpret_cast<float*>(w + lay.norm);
       p.tile_pre2 = reinterpret_cast<int32_t*>(w + lay.tile_pre2);
       p.max_tiles2 = static_cast<int32_t>(blocks->n_tokens / 16 + blocks->batch + 1);
+      p.knorm2 = reinterpret_cast<float*>(w + lay.knorm2);
+      p.seq_kmax2 = reinterpret_cast<float*>(w + lay.seq_kmax2);
     } else {
       p.knorm2 = reinterpret_cast<float*>(w + lay.knorm2);
       p.probe_slot = reinterpret_cast<int32_t*>(w + lay.probe_slot);

@@ -54,6 +54,17 @@ constexpr int kTopkTile = 16;         // sorted tokens per workgroup of the top-
 // pairs 17.0 ms plus 0.16 ms of fallback, 4 pairs 15.7 ms plus 5.4 ms.
 constexpr int kLane = 6;
 constexpr float kRescale = 8.0f;      // log2 headroom before the running shift moves
+// bf16 P by truncation (the fixed-shift loop): the mean relative loss of
+// truncating a float32 with a log-uniform mantissa to 8 significant bits is
+// 2^-8 * (1/ln 2) * (1/2); p is scaled up by the inverse factor and the row
+// sum divided by it again, so P V and the row sum agree on average
+constexpr float kTruncLog2 = 0.0040711f;   // log2(1 / (1 - 2^-8 * 0.5 / ln 2))
+constexpr float kTruncInv = 0.99718215f;   // 1 - 2^-8 * 0.5 / ln 2
+// largest |q| max_j |Kbar_j| * scale * log2 e for which the fixed shift keeps
+// every exponent within [-120, 0]
+constexpr float kFixedBound = 60.f;
+template <bool B>
+using kBool = std::integral_constant<bool, B>;
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -86,10 +97,36 @@ __global__ void gqa_tile_prefix_kernel(FwdParams p) {
   p.tile_pre2[p.batch] = run;
 }
 
+// seq_kmax2[g][b] = largest squared norm of sequence b's pooled keys of
+// group g; one workgroup per (sequence, group)
+__global__ void __launch_bounds__(256)
+gqa_seq_kmax_kernel(FwdParams p) {
+  __shared__ float wmax[4];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int j0 = p.seq_blk_off[b], j1 = p.seq_blk_off[b + 1];
+  const float* n2 = p.knorm2 + static_cast<int64_t>(g) * p.nb_cap;
+  float m = 0.f;
+  for (int j = j0 + static_cast<int>(threadIdx.x); j < j1; j += 256) m = fmaxf(m, n2[j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    p.seq_kmax2[static_cast<int64_t>(g) * p.batch + b] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
 // ------------------------------------------------------------ o_cmp + normalisers
 
 // D = 32 runs four workgroups per compute unit (128 registers, a 12-byte
 // spill; 5 % faster than two); D = 64 keeps two, since four would spill 224 bytes.
+//
+// A logit of query q is at most |q| max_j |Kbar_j| (Cauchy-Schwarz).  When
+// that bound B_q, times scale * log2 e, is at most kFixedBound for every query
+// of the workgroup, the softmax is shifted by B_q once: every exponent then
+// lies in [-2 B_q, 0] c2 >= -120, so 2^x neither overflows nor flushes the row
+// to zero, and no running maximum or rescaling is needed (P is truncated to
+// bf16 with the mean-loss correction).  Otherwise the streaming softmax with a
+// running shift runs.
 template <int D>
 __global__ void __launch_bounds__(256, D == 32 ? 4 : 2)
 gqa_cmp_kernel(FwdParams p) {
@@ -160,18 +197,41 @@ gqa_cmp_kernel(FwdParams p) {
     if (stager) *reinterpret_cast<u32x4*>(v_lds + slot * kVTile + vs_dst) = u;
   };
 
-  // streaming-softmax state per block: shift m (logit units), row-sum
-  // partials, O^T row blocks
-  float m[2], l[2];
+  // fixed shift per query (see above): k0 = -B_q c2 (+ the truncation
+  // offset); the workgroup takes it only if every query's bound fits
+  const float kmax2 = p.seq_kmax2[static_cast<int64_t>(g) * p.batch + b];
+  float k0[2];
+  bool fits = true;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    float qn2 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 u = __builtin_bit_cast(u32x4, qb[x][ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
+        qn2 = fmaf(lo, lo, fmaf(hi, hi, qn2));
+      }
+    }
+    qn2 += __shfl_xor(qn2, 32);
+    const float bound = sqrtf(qn2 * kmax2) * c2;
+    fits = fits && bound <= kFixedBound;
+    k0[x] = -bound + kTruncLog2;
+  }
+  const bool fixed = __syncthreads_and(fits ? 1 : 0) != 0;
+
+  // softmax state per block: running shift m (logit units; streaming loop
+  // only), row-sum partials, O^T row blocks
+  float m[2], l[2][2];
   f32x16 o[2][VB];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     m[x] = -FLT_MAX;
-    l[x] = 0.f;
+    l[x][0] = l[x][1] = 0.f;
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) o[x][vb] = f32x16{};
   }
-  f32x16 s_b;   // block B's logits of the previous tile
 
   auto qk = [&](int slot, const bf16x8 (&q)[KS]) {
     const uint16_t* kl = k_lds + slot * kKTile + (lane & 31) * kKRow + 8 * half;
@@ -182,7 +242,7 @@ gqa_cmp_kernel(FwdParams p) {
   };
   // probabilities of block x for tile rel (keys outside [j0, j1) masked),
   // P^T as two bf16 operands, then O^T += Vbar^T P^T
-  auto attend = [&](int x, int rel, int slot, f32x16& s) {
+  auto attend = [&](int x, int rel, int slot, f32x16& s, auto fixed_shift) {
     const int kt = kt0 + rel;
     if (kt * kKeyTile < j0 || kt * kKeyTile + kKeyTile > j1) {
 #pragma unroll
@@ -191,31 +251,52 @@ gqa_cmp_kernel(FwdParams p) {
         if (j < j0 || j >= j1) s[r] = -FLT_MAX;
       }
     }
-    float tm = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) tm = fmaxf(tm, fmaxf(s[r], s[r + 1]));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
-    if ((tm - m[x]) * c2 > kRescale) {
-      const float corr = m[x] == -FLT_MAX ? 0.f : __builtin_amdgcn_exp2f((m[x] - tm) * c2);
-      l[x] *= corr;
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[x][vb][r] *= corr;
-      m[x] = tm;
-    }
-    const float mc = m[x] * c2;
-    float pr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
-      l[x] += pr[r];
-    }
     bf16x8 pb[2];
+    if constexpr (decltype(fixed_shift)::value) {
+      float pr[16];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, k0[x]));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+      for (int r = 0; r < 16; r += 2) {
+        l[x][0] += pr[r];
+        l[x][1] += pr[r + 1];
+      }
+      // truncation: v_perm_b32 takes the high halves of two float32 values
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          u[e] = __builtin_amdgcn_perm(__float_as_uint(pr[8 * ks + 2 * e + 1]), __float_as_uint(pr[8 * ks + 2 * e]),
+                                       0x07060302u);
+        pb[ks] = __builtin_bit_cast(bf16x8, u);
+      }
+    } else {
+      float tm = fmaxf(s[0], s[1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) tm = fmaxf(tm, fmaxf(s[r], s[r + 1]));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      if ((tm - m[x]) * c2 > kRescale) {
+        const float corr = m[x] == -FLT_MAX ? 0.f : __builtin_amdgcn_exp2f((m[x] - tm) * c2);
+        l[x][0] *= corr;
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[x][vb][r] *= corr;
+        m[x] = tm;
+      }
+      const float mc = m[x] * c2;
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
+        l[x][0] += pr[r];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+    }
     const uint16_t* vl = v_lds + slot * kVTile + (lane & 31) * kVRow + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -226,42 +307,48 @@ gqa_cmp_kernel(FwdParams p) {
 
   // ring: slot (rel & 1) holds key and value tile rel; register sets hold
   // tile rel + 1 until it is stored at the start of step rel + 1
-  u32x4 kr = load_k(0), vr = load_v(0);
-  store_k(0, kr);
-  store_v(0, vr);
-  if (n_kt > 1) {
-    kr = load_k(1);
-    vr = load_v(1);
-  }
-  for (int rel = 0; rel < n_kt; ++rel) {
-    __syncthreads();  // tiles rel stored; everyone is done with tiles rel - 1
-    if (rel + 1 < n_kt) {
-      store_k((rel + 1) & 1, kr);
-      store_v((rel + 1) & 1, vr);
+  auto run = [&](auto fixed_shift) {
+    u32x4 kr = load_k(0), vr = load_v(0);
+    store_k(0, kr);
+    store_v(0, vr);
+    if (n_kt > 1) {
+      kr = load_k(1);
+      vr = load_v(1);
     }
-    if (rel + 2 < n_kt) {
-      kr = load_k(rel + 2);
-      vr = load_v(rel + 2);
+    for (int rel = 0; rel < n_kt; ++rel) {
+      __syncthreads();  // tiles rel stored; everyone is done with tiles rel - 1
+      if (rel + 1 < n_kt) {
+        store_k((rel + 1) & 1, kr);
+        store_v((rel + 1) & 1, vr);
+      }
+      if (rel + 2 < n_kt) {
+        kr = load_k(rel + 2);
+        vr = load_v(rel + 2);
+      }
+      f32x16 s_a = qk(rel & 1, qb[0]);
+      f32x16 s_b = qk(rel & 1, qb[1]);
+      attend(0, rel, rel & 1, s_a, fixed_shift);
+      attend(1, rel, rel & 1, s_b, fixed_shift);
     }
-    f32x16 s_a = qk(rel & 1, qb[0]);
-    s_b = qk(rel & 1, qb[1]);
-    attend(0, rel, rel & 1, s_a);
-    attend(1, rel, rel & 1, s_b);
-  }
+  };
+  if (fixed) run(kBool<true>{});
+  else run(kBool<false>{});
 
   // o_cmp times its gate into the accumulator; the head's log2 normaliser
+  // c = log2 sum_j 2^(s_j c2), so that block j's probability is 2^(s_j c2 - c)
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const float lq = l[x] + __shfl_xor(l[x], 32);
+    const float lsum = l[x][0] + l[x][1];
+    const float lq = lsum + __shfl_xor(lsum, 32);
     if (!valid[x]) continue;
     const int64_t row = static_cast<int64_t>(t[x]) * p.h_q + h;
-    const float c = m[x] * c2 + __log2f(lq);
+    const float c = fixed ? __log2f(lq) - k0[x] : m[x] * c2 + __log2f(lq);
     if (half == 0) {
       p.norm[row] = c;
       if (p.lse) p.lse[row] = c * kLn2;
     }
     const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + row * 3;
-    const float f = bf16_bits_to_f32(gt[0]) / lq;
+    const float f = bf16_bits_to_f32(gt[0]) / (fixed ? lq * kTruncInv : lq);
     float* dst = p.acc + row * D;
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb)
@@ -561,6 +648,7 @@ gqa_fixup_kernel(FwdParams p) {
 
 hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   tile_prefix_kernel_launch(p, stream);
+  gqa_seq_kmax_kernel<<<dim3(p.batch, p.h_kv), 256, 0, stream>>>(p);
   const dim3 grid(p.max_tiles, p.h_q);
   if (p.d == 32) gqa_cmp_kernel<32><<<grid, 256, 0, stream>>>(p);
   else gqa_cmp_kernel<64><<<grid, 256, 0, stream>>>(p);

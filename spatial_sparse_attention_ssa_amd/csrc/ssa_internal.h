@@ -189,6 +189,7 @@ struct FwdParams {
   float* norm;        // [n][h_q]
   int32_t* tile_pre2; // [batch + 1]
   int32_t max_tiles2;
+  float* seq_kmax2;   // [h_kv][batch] largest squared pooled-key norm of each sequence (knorm2 above)
   // optional public outputs
   void* k_cmp;       // [nb][h_kv][D] or null
   void* v_cmp;

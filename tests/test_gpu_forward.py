@@ -264,6 +264,33 @@ def test_probe_bound_paths_full(q_scale):
     _full_compare(wl, tag=f"probe paths, q x {q_scale:g}")
 
 
+@pytest.mark.parametrize("h_q,h_kv,head_dim,topk", [(32, 2, 64, 16), (16, 1, 32, 8)])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_gqa_shift_paths_full(h_q, h_kv, head_dim, topk, q_scale):
+    # the grouped compressed kernel shifts each query's softmax by the bound
+    # |q| max_j |Kbar_j| scale log2 e when that is at most 60 for every query
+    # of the workgroup, and otherwise keeps a running maximum; queries scaled
+    # by 8 put the bound above 60 for most queries
+    wl = make_custom([3000, 900], grid_res=64, n_prims=3, topk=topk, h_q=h_q, h_kv=h_kv, head_dim=head_dim,
+                     dtype="bf16", seed=61)
+    if q_scale != 1.0:
+        wl.q = bf16_bits_to_f32(bf16_bits_from_f32(wl.q * np.float32(q_scale)))
+    ob = P.oracle_blocks(wl)
+    kbar = oracle.pool_blocks(wl.k, ob, wl.dtype)
+    kmax = np.zeros((wl.batch, wl.h_kv))
+    for b in range(wl.batch):
+        j0, j1 = ob.seq_blk_off[b], ob.seq_blk_off[b + 1]
+        kmax[b] = np.linalg.norm(kbar[j0:j1].astype(np.float64), axis=-1).max(0)
+    seq = np.searchsorted(wl.cu_seqlens, np.arange(wl.n_tokens), side="right") - 1
+    bound = (np.linalg.norm(wl.q.astype(np.float64), axis=-1) *
+             kmax[seq][:, np.arange(wl.h_q) // (wl.h_q // wl.h_kv)]) / np.sqrt(wl.head_dim) * np.log2(np.e)
+    if q_scale == 1.0:
+        assert bound.max() < 30
+    else:
+        assert (bound > 60).mean() > 0.5
+    _full_compare(wl, tag=f"grouped shift paths D={head_dim}, q x {q_scale:g}")
+
+
 def test_constant_keys_pick_first_blocks():
     # every pooled key equal: all norms fall in one histogram bin (the probe
     # takes the sequence's first 512 blocks) and all logits tie, so each
