@@ -61,7 +61,6 @@ KERNEL_SOURCES = {
     "pool_kernel": "ssa_pool.hip",
     "gqa_cmp_kernel": "ssa_attn_gqa.hip",
     "gqa_topk_kernel": "ssa_attn_gqa.hip",
-    "gqa_fixup_kernel": "ssa_attn_gqa.hip",
     "cmp_dq_mfma_kernel": "ssa_bwd_mfma.hip",
     "cmp_dkv_mfma_kernel": "ssa_bwd_mfma.hip",
     "kv_grad_mfma_kernel": "ssa_bwd_mfma.hip",

@@ -127,7 +127,7 @@ bool use_mfma_path(const ssa_attn* a) {
 
 struct FwdLayout {
   size_t kbar, vbar, vbar_t, k_s, v_s, topk, tile_pre, fix, acc, norm, tile_pre2, blk_cell, knorm2, probe_slot,
-      probe_seq, probe_maxn2, probe, seq_kmax2, total;
+      probe_seq, probe_maxn2, probe, probe_ids, seq_kmax2, total;
 };
 
 // probe sets of the one-head-per-group compressed kernel: one per sequence
@@ -159,6 +159,11 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
       L.tile_pre2 = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
       L.knorm2 = off; off += align256(sizeof(float) * a->h_kv * cap);
       L.seq_kmax2 = off; off += align256(sizeof(float) * a->h_kv * static_cast<size_t>(b->batch));
+      const size_t slots = static_cast<size_t>(max_probe_slots(b));
+      L.probe_slot = off; off += align256(sizeof(int32_t) * (static_cast<size_t>(b->batch) + 1));
+      L.probe_seq = off; off += align256(sizeof(int32_t) * (slots + 1));
+      L.probe_maxn2 = off; off += align256(sizeof(float) * a->h_kv * (slots + 1));
+      L.probe_ids = off; off += align256(sizeof(int32_t) * a->h_kv * slots * ssa::kProbeBlocks);
     } else {
       const size_t slots = static_cast<size_t>(max_probe_slots(b));
       L.knorm2 = off; off += align256(sizeof(float) * a->h_kv * cap);
@@ -279,7 +284,6 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
   if (use_gqa_path(attn)) {
     stages[n++] = Stage{"gqa_cmp_kernel", ssa::launch_gqa_cmp};
     stages[n++] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
-    stages[n++] = Stage{"gqa_fixup_kernel", ssa::launch_gqa_fixup};
   } else {
     stages[n++] = Stage{"probe_kernel", ssa::launch_cmp_probe};
     stages[n++] = Stage{"cmp_mfma_kernel", ssa::launch_cmp_mfma};
@@ -371,6 +375,11 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
       p.max_tiles2 = static_cast<int32_t>(blocks->n_tokens / 16 + blocks->batch + 1);
       p.knorm2 = reinterpret_cast<float*>(w + lay.knorm2);
       p.seq_kmax2 = reinterpret_cast<float*>(w + lay.seq_kmax2);
+      p.probe_slot = reinterpret_cast<int32_t*>(w + lay.probe_slot);
+      p.probe_seq = reinterpret_cast<int32_t*>(w + lay.probe_seq);
+      p.probe_maxn2 = reinterpret_cast<float*>(w + lay.probe_maxn2);
+      p.probe_ids = reinterpret_cast<int32_t*>(w + lay.probe_ids);
+      p.max_probe_slots = max_probe_slots(blocks);
     } else {
       p.knorm2 = reinterpret_cast<float*>(w + lay.knorm2);
       p.probe_slot = reinterpret_cast<int32_t*>(w + lay.probe_slot);

@@ -114,7 +114,8 @@ __global__ void tile_prefix_kernel(FwdParams p) {
 }
 
 // Probe set of one (sequence, head): the kProbeBlocks pooled keys of largest
-// squared norm, copied in block order, and the largest squared norm.  Any
+// squared norm, copied in block order (when p.probe is set), their block ids
+// (when p.probe_ids is set), and the largest squared norm.  Any
 // set of the sequence's blocks gives a valid lower bound on its k-th largest
 // logit (the compressed kernel's first pass); blocks of large key norm give
 // a tight one, since a logit is at most |q| |Kbar_j|.  The selection is a
@@ -178,8 +179,9 @@ probe_select_kernel(FwdParams p) {
   __syncthreads();
   const int tbin = sh_bin, need = sh_need;
   const uint16_t* src = static_cast<const uint16_t*>(p.kbar) + (static_cast<int64_t>(g) * p.nb_cap + j0) * 64;
-  uint16_t* dst = static_cast<uint16_t*>(p.probe) +
-                  static_cast<int64_t>(g * p.max_probe_slots + s) * kProbeBlocks * 64;
+  const int64_t set = static_cast<int64_t>(g) * p.max_probe_slots + s;
+  uint16_t* dst = p.probe ? static_cast<uint16_t*>(p.probe) + set * kProbeBlocks * 64 : nullptr;
+  int32_t* ids = p.probe_ids ? p.probe_ids + set * kProbeBlocks : nullptr;
   const uint64_t below = (uint64_t(1) << lane) - 1;
   int base_gt = 0, base_eq = 0;   // chosen blocks above / in the threshold bin before this chunk
   for (int c0 = 0; c0 < nbs; c0 += 256) {
@@ -206,10 +208,13 @@ probe_select_kernel(FwdParams p) {
     if (gt || (eq && peq < need)) {
       // position among the chosen blocks, in block order
       const int pos = pgt + min(peq, need);
-      const u32x4* from = reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(j) * 64);
-      u32x4* to = reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(pos) * 64);
+      if (ids) ids[pos] = j0 + j;
+      if (dst) {
+        const u32x4* from = reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(j) * 64);
+        u32x4* to = reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(pos) * 64);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) to[c] = from[c];
+        for (int c = 0; c < 8; ++c) to[c] = from[c];
+      }
     }
   }
 }
@@ -885,10 +890,14 @@ void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream) {
 
 // the query-tile prefix, the probe slots and the probe sets (the compressed
 // kernel reads all three)
-hipError_t launch_cmp_probe(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  tile_prefix_kernel_launch(p, stream);
+void probe_select_launch(const FwdParams& p, hipStream_t stream) {
   if (p.probe_slot && p.max_probe_slots > 0)
     probe_select_kernel<<<dim3(p.max_probe_slots, p.h_kv), 256, 0, stream>>>(p);
+}
+
+hipError_t launch_cmp_probe(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  tile_prefix_kernel_launch(p, stream);
+  probe_select_launch(p, stream);
   return hipGetLastError();
 }
 

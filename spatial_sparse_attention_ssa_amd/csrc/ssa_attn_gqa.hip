@@ -7,31 +7,30 @@
 // heads of a key/value group.  Here the score of block j for a query token t
 // and group g is the sum over the group's heads of the softmax probability of
 // j, so the heads' softmax normalisers are needed before any block can be
-// ranked.  Three kernels:
+// ranked.  Two kernels:
 //
-//  gqa_cmp_kernel: o_cmp of every (token, query head) with a streaming
-//    softmax (S^T = Kbar Q^T, one running shift per query head, rescaled only
-//    when a tile maximum exceeds it by 8 in log2 units, so the probabilities
-//    stay below 256), adds G0 * o_cmp to the float32 branch accumulator and
-//    stores the head's log2 normaliser c = shift * scale * log2 e + log2(sum),
-//    so that the probability of block j is 2^(s_j * scale * log2 e - c).
-//    Work split as in the one-head-per-group kernel: 256 sorted queries of one
-//    sequence and one query head per workgroup, 4 waves x two 32-query
-//    blocks, pooled keys / values streamed through a two-slot LDS ring.
+//  gqa_cmp_kernel: o_cmp of every (token, query head) (S^T = Kbar Q^T; the
+//    softmax shift is the bound |q| max|Kbar| when it is small enough, else a
+//    running shift per query head, rescaled only when a tile maximum exceeds
+//    it by 8 in log2 units), adds G0 * o_cmp to the float32 branch
+//    accumulator and stores the head's log2 normaliser c, so that the
+//    probability of block j is 2^(s_j * scale * log2 e - c).  Work split as
+//    in the one-head-per-group kernel: 256 sorted queries of one sequence and
+//    one query head per workgroup, 4 waves x two 32-query blocks, pooled keys
+//    / values streamed through a two-slot LDS ring.
 //
 //  gqa_topk_kernel: S = Q Kbar^T with the rows of the MFMA tile being
 //    (token, head) pairs, 2 tokens x 16 heads, and the columns 32 blocks.  A
-//    lane then holds one block and 8 heads of each token, so the group sum is
-//    8 in-lane adds and one add across the lane halves.  Each lane keeps,
-//    per token, its kLane = 6 best (score, block) pairs in float32 (an insertion
-//    network: one v_med3 for the scores and two selects for the ids per
-//    slot), and the 32 lanes' lists are merged by repeated wave maxima (equal
-//    scores: lower block first).  A workgroup owns 16 sorted tokens of one
-//    sequence and one group (4 waves x 2 row blocks).  A (token, group) pair
-//    for which one lane's 6 kept pairs all reach the top k, while that lane
-//    saw more blocks than it kept, is queued for gqa_fixup_kernel, which
-//    ranks all blocks of the sequence exactly.
+//    lane then holds one block and 8 heads of each token.  A workgroup owns
+//    16 sorted tokens of one sequence and one group (4 waves x 2 row blocks).
+//    A warm-up over the sequence's probe set gives each token a lower bound
+//    on its k-th score; in the main pass a (token, block) pair is scored
+//    exactly only when the bound 16 * max_h p_h reaches the admission score,
+//    which most pairs do not, so most pairs cost an FMA and a max per head
+//    instead of an exponential.  Exact: the top k of the blocks seen so far
+//    are always among the admitted candidates (see the kernel).
 #include <float.h>
+#include <math.h>
 #include <limits.h>
 
 #include <type_traits>
@@ -48,11 +47,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kGroup = 16;            // query heads per key/value head on this path
 constexpr int kTopkTile = 16;         // sorted tokens per workgroup of the top-k kernel
-// (score, block) pairs kept per lane and token.  A lane sees every 32nd block,
-// so it rarely holds more than 5 of a query's top 16: measured on the
-// 262144-token grouped workload, 8 pairs cost 18.8 ms with no fallback, 6
-// pairs 17.0 ms plus 0.16 ms of fallback, 4 pairs 15.7 ms plus 5.4 ms.
-constexpr int kLane = 6;
 constexpr float kRescale = 8.0f;      // log2 headroom before the running shift moves
 // bf16 P by truncation (the fixed-shift loop): the mean relative loss of
 // truncating a float32 with a log-uniform mantissa to 8 significant bits is
@@ -68,6 +62,18 @@ using kBool = std::integral_constant<bool, B>;
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// lane l and lane l ^ 32 exchange v (v_permlane32_swap, no LDS); the two
+// results are v of both lanes, so a max or a sum over them is the same on
+// both lanes of a pair
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void seq_token_range(const FwdParams& p, int b, int* s0, int* s1) {
@@ -365,19 +371,27 @@ gqa_cmp_kernel(FwdParams p) {
 
 // ------------------------------------------------------------ group top-k
 
+// Per wave: a ring of (token, block) pairs that passed the bound, scored in
+// batches of up to 64, and per token a list of admitted candidates.
+constexpr int kQCap = 128;     // queue entries per wave (at most 63 + 64 are pending)
+constexpr int kLCap = 96;      // candidate keys per token
+constexpr int kCompact = 32;   // a list longer than this is cut to its top k (k <= 32)
+
+// D = 32: three workgroups per compute unit (LDS: 46 KB each; at most 168
+// registers); D = 64 keeps two, since three would spill
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, D == 32 ? 3 : 2)
 gqa_topk_kernel(FwdParams p) {
   constexpr int KS = D / 16;
-  constexpr int kKRow = D + 8;
-  constexpr int kKTile = kKeyTile * kKRow;
-  constexpr int kChunks = kKeyTile * D / 8;
-  __shared__ __align__(16) uint16_t k_lds[2 * kKTile];
+  __shared__ __align__(16) float qy[4][kQCap][16];   // a pair's 16 exponents y_h (lane half h wrote 8 h ... 8 h + 7)
+  __shared__ int qm[4][kQCap];                       // block << 2 | token of the wave
+  __shared__ uint64_t lst[4][4][kLCap];              // candidate keys per wave and token
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int half = lane >> 5;
+  const int l32 = lane & 31;
   const int g = blockIdx.y;
   const int tile = blockIdx.x;
   if (tile >= p.tile_pre2[p.batch]) return;
@@ -389,11 +403,14 @@ gqa_topk_kernel(FwdParams p) {
   const int j0 = p.seq_blk_off[b], j1 = p.seq_blk_off[b + 1];
   const int kt0 = j0 / kKeyTile, kt1 = (j1 + kKeyTile - 1) / kKeyTile;
   const int n_kt = kt1 - kt0;
+  const int nbs = j1 - j0;
+  const int k_eff = min(p.topk, nbs);
   const float c2 = p.scale * kLog2e;
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
 
-  // row blocks x = 0, 1 of this wave: tokens 4 wv + 2 x + {0, 1};
-  // A operand row (lane % 32) = (token (lane % 32) / 16, head lane % 16)
+  // row blocks x = 0, 1 of this wave: tokens 4 wv + 2 x + {0, 1} (the wave's
+  // tokens 2 x + 0 and 2 x + 1); A operand row (lane % 32) = (token
+  // (lane % 32) / 16, head lane % 16)
   bf16x8 qa[2][KS];
   float cn[2][16];       // log2 normalisers of this lane's 16 accumulator rows
   int tk[2][2];          // sorted positions of the row block's two tokens
@@ -401,7 +418,7 @@ gqa_topk_kernel(FwdParams p) {
   for (int x = 0; x < 2; ++x) {
     tk[x][0] = t_begin + 4 * wv + 2 * x;
     tk[x][1] = tk[x][0] + 1;
-    const int mine = tk[x][(lane & 31) >> 4];
+    const int mine = tk[x][l32 >> 4];
     const bool ok = mine < t_end;
     const int tt = ok ? p.perm[mine] : 0;
     const int hq = g * kGroup + (lane & 15);
@@ -423,224 +440,276 @@ gqa_topk_kernel(FwdParams p) {
   }
 
   const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(g) * p.nb_cap * D;
-  const bool stager = tid < kChunks;
-  const int k_row = tid / (D / 8), k_c = tid % (D / 8);
-  const uint16_t* kg = KB + (static_cast<int64_t>(kt0) * kKeyTile + k_row) * D + 8 * k_c;
-  auto load_k = [&](int rel) {
-    return stager ? *reinterpret_cast<const u32x4*>(kg + static_cast<int64_t>(rel) * kKeyTile * D) : u32x4{0u, 0u, 0u, 0u};
-  };
-  const int ks_dst = k_row * kKRow + 8 * k_c;
-
-  // per lane and row block: the lane's kLane best (score, block) pairs for
-  // token `half` of the row block (both halves hold the same sums), score
-  // descending, equal scores by block ascending; an empty slot holds -1
-  // (every score is >= 0)
-  float Lv[2][kLane];
-  int Lj[2][kLane];
+  // Each lane loads its own MFMA operand of every key tile (16 bytes per k
+  // step of row row_of(rel, lane % 32)), two tiles ahead; the four waves read
+  // the same tiles at about the same time, mostly from L1, and need no
+  // barrier, so a wave that stops to score a batch does not hold up the
+  // others.
+  auto stream_tiles = [&](int n_t, auto row_of, auto body) {
+    auto load = [&](int rel, bf16x8 (&kb)[KS]) {
+      const uint16_t* src = KB + static_cast<int64_t>(row_of(rel, l32)) * D + 8 * half;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+      for (int ks = 0; ks < KS; ++ks) kb[ks] = lds_b128(src + 16 * ks);
+    };
+    bf16x8 cur[KS], nxt[KS];
+    load(0, cur);
+    load(n_t > 1 ? 1 : 0, nxt);
+    for (int rel = 0; rel < n_t; ++rel) {
+      bf16x8 kb[KS];
 #pragma unroll
-    for (int i = 0; i < kLane; ++i) {
-      Lv[x][i] = -1.f;
-      Lj[x][i] = INT_MAX;
+      for (int ks = 0; ks < KS; ++ks) {
+        kb[ks] = cur[ks];
+        cur[ks] = nxt[ks];
+      }
+      load(rel + 2 < n_t ? rel + 2 : n_t - 1, nxt);
+      body(rel, kb);
     }
-
-  u32x4 kr = load_k(0);
-  if (stager) *reinterpret_cast<u32x4*>(k_lds + ks_dst) = kr;
-  if (n_kt > 1) kr = load_k(1);
-  for (int rel = 0; rel < n_kt; ++rel) {
-    __syncthreads();
-    if (rel + 1 < n_kt && stager) *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTile + ks_dst) = kr;
-    if (rel + 2 < n_kt) kr = load_k(rel + 2);
-    const uint16_t* kl = k_lds + (rel & 1) * kKTile + (lane & 31) * kKRow + 8 * half;
-    bf16x8 kb[KS];
+  };
+  // S of row block x against a key tile, and the exponents
+  // y = s * scale * log2 e - c_h, so that the head's probability is 2^y
+  auto exponents = [&](int x, const bf16x8 (&kb)[KS], float (&y)[16]) {
+    f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = lds_b128(kl + 16 * ks);
-    const int j = (kt0 + rel) * kKeyTile + (lane & 31);     // this lane's block
-    const bool jok = j >= j0 && j < j1;
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[x][ks], kb[ks], s, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[r] = fmaf(s[r], c2, -cn[x][r]);
+  };
+  // a token's group score from its 16 exponents: each lane half sums its
+  // 8 heads in order, then the two halves are added
+  auto half_sum = [](const float* yv) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sum += __builtin_amdgcn_exp2f(yv[r]);
+    return sum;
+  };
+
+  // ---------------- warm-up: a lower bound tau0 on each token's k-th score
+  // The probe set (the sequence's kProbeBlocks pooled keys of largest norm,
+  // which hold most of the top k) or, for a sequence of at most that many
+  // blocks, the sequence itself, is scored exactly; each lane keeps the two
+  // best scores it saw per token, and the k-th largest of the 64 values of a
+  // token bounds its k-th score from below (they are scores of 64 distinct
+  // blocks).
+  const int pslot = p.probe_slot[b];
+  const int32_t* pids =
+      pslot >= 0 ? p.probe_ids + (static_cast<int64_t>(g) * p.max_probe_slots + pslot) * kProbeBlocks : nullptr;
+  float w1[2] = {-2.f, -2.f}, w2[2] = {-2.f, -2.f};
+  auto warm_body = [&](int rel, const bf16x8 (&kb)[KS]) {
+    bool jok;
+    if (pids) {
+      jok = true;
+    } else {
+      const int j = (kt0 + rel) * kKeyTile + l32;
+      jok = j >= j0 && j < j1;
+    }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      f32x16 s = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[x][ks], kb[ks], s, 0, 0, 0);
-      float sum0 = 0.f, sum1 = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) sum0 += __builtin_amdgcn_exp2f(fmaf(s[r], c2, -cn[x][r]));
-#pragma unroll
-      for (int r = 8; r < 16; ++r) sum1 += __builtin_amdgcn_exp2f(fmaf(s[r], c2, -cn[x][r]));
-      sum0 += __shfl_xor(sum0, 32);
-      sum1 += __shfl_xor(sum1, 32);
-      // a block outside the sequence scores -2 and changes no slot
+      float y[16];
+      exponents(x, kb, y);
+      const float sum0 = pair_add(half_sum(y)), sum1 = pair_add(half_sum(y + 8));
       const float sc = jok ? (half ? sum1 : sum0) : -2.f;
-      // slot i takes slot i - 1 when sc beats it, else sc when sc beats slot i;
-      // blocks of a lane arrive in increasing id, so an equal score stays behind
+      w2[x] = __builtin_amdgcn_fmed3f(w1[x], sc, w2[x]);
+      w1[x] = fmaxf(w1[x], sc);
+    }
+  };
+  if (pids) {
+    stream_tiles(kProbeBlocks / kKeyTile, [&](int rel, int r) { return pids[rel * kKeyTile + r]; }, warm_body);
+  } else {
+    stream_tiles(n_kt, [&](int rel, int r) { return (kt0 + rel) * kKeyTile + r; }, warm_body);
+  }
+
+  // per wave token t = 2 x + h: admission key, bound threshold, list length
+  uint64_t min_key[4];
+  float theta[4];
+  int cnt[4] = {0, 0, 0, 0};
+  {
+    float* wv_scr = &qy[wv][0][0];   // 256 floats: [x][h][l32][2]
 #pragma unroll
-      for (int i = kLane - 1; i >= 1; --i) {
-        const bool up = sc > Lv[x][i - 1];
-        const bool here = sc > Lv[x][i];
-        Lj[x][i] = up ? Lj[x][i - 1] : (here ? j : Lj[x][i]);
-        Lv[x][i] = __builtin_amdgcn_fmed3f(Lv[x][i - 1], sc, Lv[x][i]);
+    for (int x = 0; x < 2; ++x) {
+      wv_scr[((2 * x + half) * 32 + l32) * 2] = w1[x];
+      wv_scr[((2 * x + half) * 32 + l32) * 2 + 1] = w2[x];
+    }
+    wave_lds_sync();
+    float tau[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      // the k-th largest of the token's 64 values (or -1: fewer than k valid)
+      const float* v = wv_scr + (2 * x + half) * 64;
+      const float a = w1[x], c = w2[x];
+      int gt_a = 0, ge_a = 0, gt_c = 0, ge_c = 0;
+      for (int i = 0; i < 64; ++i) {
+        const float vi = v[i];
+        gt_a += vi > a ? 1 : 0;
+        ge_a += vi >= a ? 1 : 0;
+        gt_c += vi > c ? 1 : 0;
+        ge_c += vi >= c ? 1 : 0;
       }
-      const bool top = sc > Lv[x][0];
-      Lj[x][0] = top ? j : Lj[x][0];
-      Lv[x][0] = top ? sc : Lv[x][0];
+      float t = -FLT_MAX;
+      if (gt_a < k_eff && ge_a >= k_eff) t = a;
+      if (gt_c < k_eff && ge_c >= k_eff) t = c;
+      // every lane of the half that holds the k-th value holds the same one
+      t = fmaxf(t, __shfl_xor(t, 1));
+      t = fmaxf(t, __shfl_xor(t, 2));
+      t = fmaxf(t, __shfl_xor(t, 4));
+      t = fmaxf(t, __shfl_xor(t, 8));
+      t = fmaxf(t, __shfl_xor(t, 16));
+      tau[x] = t;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int x = t >> 1, h = t & 1;
+      const float tau0 = __shfl(tau[x], 32 * h);
+      if (tk[x][h] >= t_end) {
+        min_key[t] = ~0ull;      // no token: admit nothing
+        theta[t] = INFINITY;
+      } else if (tau0 >= 0.f) {
+        // scores are >= 0, so their float bits order like their values
+        min_key[t] = static_cast<uint64_t>(__float_as_uint(tau0)) << 32;
+        theta[t] = tau0 > 0.f ? __log2f(tau0) - 4.001f : -INFINITY;
+      } else {
+        min_key[t] = 0ull;       // fewer than k scored blocks: admit all
+        theta[t] = -INFINITY;
+      }
     }
   }
 
-  // merge the 32 lanes of each half by repeated maxima of the list heads
-  // (equal scores: lower block first).  A lane holding more than kLane of the
-  // sequence's blocks has dropped some; if all its kept pairs are taken, a
-  // dropped one may belong to the top k, and the (token, group) pair is handed
-  // to the exact fallback kernel.
-  const int nbs = j1 - j0;
-  const int k_eff = min(p.topk, nbs);
-  const int l32 = lane & 31;
-  const int n_mine = n_kt - (l32 < j0 - kt0 * kKeyTile ? 1 : 0) - (l32 >= j1 - (kt1 - 1) * kKeyTile ? 1 : 0);
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pos = tk[x][half];
-    const bool ok = pos < t_end;
-    int32_t* out_sel = ok ? p.topk_idx + (static_cast<int64_t>(p.perm[pos]) * p.h_kv + g) * p.topk : nullptr;
-    int used = 0;
-    for (int r = 0; r < k_eff; ++r) {
-      float bv = Lv[x][0];
-      int bj = Lj[x][0];
-#pragma unroll
-      for (int off = 16; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov > bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
-      }
-      if (bv >= 0.f && bj == Lj[x][0]) {
-#pragma unroll
-        for (int i = 0; i < kLane - 1; ++i) {
-          Lv[x][i] = Lv[x][i + 1];
-          Lj[x][i] = Lj[x][i + 1];
-        }
-        Lv[x][kLane - 1] = -1.f;
-        Lj[x][kLane - 1] = INT_MAX;
-        ++used;
-      }
-      if (ok && l32 == 0) out_sel[r] = bv >= 0.f ? bj : -1;
+  // ---------------- main pass over the sequence's tiles
+  // A pair (token, block) whose largest exponent m = max_h y_h satisfies
+  // 16 * 2^m < (the admission score) cannot be admitted, since its score is
+  // a sum of 16 terms 2^y_h; theta holds log2 of that score minus 4 (and a
+  // margin for rounding).  Pairs that pass are queued with their 16
+  // exponents; a batch computes their scores exactly, and a pair whose key
+  // (score, then lower block first) reaches min_key joins its token's list.
+  // A list longer than kCompact is cut to its top k by rank counting, and
+  // min_key becomes one above the k-th key: the top k of the blocks seen so
+  // far are always in the list, and no list exceeds kCompact + 64 entries.
+  int qh = 0, qn = 0;   // queue head and pending entries (wave-uniform, qn < 64 between row blocks)
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  auto list_rank = [&](int t, int n, uint64_t& k1, uint64_t& k2, int& r1, int& r2) {
+    const uint64_t* L = lst[wv][t];
+    k1 = lane < n ? L[lane] : 0ull;
+    k2 = lane + 64 < n ? L[lane + 64] : 0ull;
+    r1 = 0;
+    r2 = 0;
+    for (int i = 0; i < n; ++i) {
+      const uint64_t ki = L[i];
+      r1 += ki > k1 ? 1 : 0;
+      r2 += ki > k2 ? 1 : 0;
     }
-    const uint64_t spill = __ballot(n_mine > kLane && used == kLane);
-    const bool overflow = ((half ? spill >> 32 : spill) & 0xFFFFFFFFull) != 0;
-    if (ok && l32 == 0) {
-      for (int r = k_eff; r < p.topk; ++r) out_sel[r] = -1;
-      if (overflow) {
-        const int slot = atomicAdd(&p.fix[0], 1);
-        p.fix[1 + slot] = pos * p.h_kv + g;
+  };
+  auto compact = [&](int t) {
+    const int n = cnt[t];
+    uint64_t k1, k2;
+    int r1, r2;
+    list_rank(t, n, k1, k2, r1, r2);
+    wave_lds_sync();
+    uint64_t* L = lst[wv][t];
+    if (lane < n && r1 < k_eff) L[r1] = k1;
+    if (lane + 64 < n && r2 < k_eff) L[r2] = k2;
+    wave_lds_sync();
+    cnt[t] = k_eff;   // n > kCompact >= k_eff
+    min_key[t] = L[k_eff - 1] + 1;
+    const float smin = __uint_as_float(static_cast<uint32_t>(min_key[t] >> 32));
+    theta[t] = smin > 0.f ? __log2f(smin) - 4.001f : -INFINITY;
+  };
+  auto process = [&]() {
+    const int nbat = min(qn, 64);
+    const bool act = lane < nbat;
+    const int e = (qh + lane) & (kQCap - 1);
+    uint64_t key = 0ull;
+    int tok = -1;
+    if (act) {
+      float yv[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 u = *reinterpret_cast<const float4*>(&qy[wv][e][4 * c]);
+        yv[4 * c] = u.x;
+        yv[4 * c + 1] = u.y;
+        yv[4 * c + 2] = u.z;
+        yv[4 * c + 3] = u.w;
+      }
+      // the same two half sums, added as the warm-up adds them
+      const float sc = half_sum(yv) + half_sum(yv + 8);
+      const int m = qm[wv][e];
+      tok = m & 3;
+      key = (static_cast<uint64_t>(__float_as_uint(sc)) << 32) | static_cast<uint32_t>(~(m >> 2));
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bool adm = tok == t && key >= min_key[t];
+      const uint64_t bt = __ballot(adm);
+      if (adm) lst[wv][t][cnt[t] + __popcll(bt & lt_mask)] = key;
+      cnt[t] += __popcll(bt);
+    }
+    qh = (qh + nbat) & (kQCap - 1);
+    qn -= nbat;
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (cnt[t] > kCompact) compact(t);
+  };
+  auto main_body = [&](int rel, const bf16x8 (&kb)[KS]) {
+    const int j = (kt0 + rel) * kKeyTile + l32;
+    const bool jok = j >= j0 && j < j1;
+    const uint32_t below = (1u << l32) - 1u;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      float y[16];
+      exponents(x, kb, y);
+      float m0 = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+      m0 = fmaxf(m0, fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      float m1 = fmaxf(fmaxf(y[8], y[9]), fmaxf(y[10], y[11]));
+      m1 = fmaxf(m1, fmaxf(fmaxf(y[12], y[13]), fmaxf(y[14], y[15])));
+      m0 = pair_max(m0);
+      m1 = pair_max(m1);
+      const bool p0 = jok && m0 >= theta[2 * x];
+      const bool p1 = jok && m1 >= theta[2 * x + 1];
+      // both lane halves hold the same decisions; the low 32 bits suffice
+      const uint32_t b0 = static_cast<uint32_t>(__ballot(p0));
+      const uint32_t b1 = static_cast<uint32_t>(__ballot(p1));
+      const int n0 = __popc(b0), n1 = __popc(b1);
+      if (p0) {
+        const int e = (qh + qn + __popc(b0 & below)) & (kQCap - 1);
+        float4* dst = reinterpret_cast<float4*>(&qy[wv][e][8 * half]);
+        dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+        dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+        if (half == 0) qm[wv][e] = (j << 2) | (2 * x);
+      }
+      if (p1) {
+        const int e = (qh + qn + n0 + __popc(b1 & below)) & (kQCap - 1);
+        float4* dst = reinterpret_cast<float4*>(&qy[wv][e][8 * half]);
+        dst[0] = make_float4(y[8], y[9], y[10], y[11]);
+        dst[1] = make_float4(y[12], y[13], y[14], y[15]);
+        if (half == 0) qm[wv][e] = (j << 2) | (2 * x + 1);
+      }
+      qn += n0 + n1;
+      if (qn >= 64) {
+        wave_lds_sync();
+        process();
       }
     }
-  }
-}
+  };
+  stream_tiles(n_kt, [&](int rel, int r) { return (kt0 + rel) * kKeyTile + r; }, main_body);
+  wave_lds_sync();
+  while (qn > 0) process();
 
-// ------------------------------------------------------------ exact fallback
-
-// One workgroup per (token, group) pair whose lane lists overflowed: every
-// thread scores blocks j0 + tid, j0 + tid + 256, ... exactly as above (the
-// group's 16 query rows and normalisers staged in LDS) and keeps its KMAX best
-// pairs; each wave pops its KMAX best and wave 0 ranks the 4 x KMAX survivors.
-template <int D, int KMAX>
-__global__ void __launch_bounds__(256)
-gqa_fixup_kernel(FwdParams p) {
-  __shared__ float qs[kGroup * D];
-  __shared__ float cs[kGroup];
-  __shared__ float wv_val[4 * KMAX];
-  __shared__ int wv_idx[4 * KMAX];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int n_fix = p.fix[0];
-  const float c2 = p.scale * kLog2e;
-  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  for (int item = blockIdx.x; item < n_fix; item += gridDim.x) {
-    const int entry = p.fix[1 + item];
-    const int i = entry / p.h_kv, g = entry % p.h_kv;
-    const int t = p.perm[i];
-    int lo = 0, hi = p.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.win_off[p.seq_win_off[mid]] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int j0 = p.seq_blk_off[lo], j1 = p.seq_blk_off[lo + 1];
-    for (int e = tid; e < kGroup * D; e += 256)
-      qs[e] = bf16_bits_to_f32(Q[(static_cast<int64_t>(t) * p.h_q + g * kGroup) * D + e]);
-    if (tid < kGroup) cs[tid] = p.norm[static_cast<int64_t>(t) * p.h_q + g * kGroup + tid];
-    __syncthreads();
-    const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(g) * p.nb_cap * D;
-    float lv[KMAX];
-    int li[KMAX];
+  // ---------------- each token's top k: rank its list (score descending,
+  // equal scores by block ascending)
 #pragma unroll
-    for (int e = 0; e < KMAX; ++e) { lv[e] = -1.f; li[e] = INT_MAX; }
-    for (int j = j0 + tid; j < j1; j += 256) {
-      float kf[D];
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(KB + static_cast<int64_t>(j) * D + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
-          kf[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-        }
-      }
-      float sc = 0.f;
-      for (int hh = 0; hh < kGroup; ++hh) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < D; ++e) d = fmaf(qs[hh * D + e], kf[e], d);
-        sc += __builtin_amdgcn_exp2f(fmaf(d, c2, -cs[hh]));
-      }
-      // blocks arrive in increasing id, so an equal score stays behind
-      if (sc > lv[KMAX - 1]) {
-        bool placed = false;
-#pragma unroll
-        for (int e = KMAX - 1; e >= 1; --e) {
-          if (!placed) {
-            if (sc > lv[e - 1]) { lv[e] = lv[e - 1]; li[e] = li[e - 1]; }
-            else { lv[e] = sc; li[e] = j; placed = true; }
-          }
-        }
-        if (!placed) { lv[0] = sc; li[0] = j; }
-      }
-    }
-    for (int r = 0; r < KMAX; ++r) {
-      float bv = lv[0];
-      int bi = li[0];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bv >= 0.f && li[0] == bi) {
-#pragma unroll
-        for (int e = 0; e < KMAX - 1; ++e) { lv[e] = lv[e + 1]; li[e] = li[e + 1]; }
-        lv[KMAX - 1] = -1.f;
-        li[KMAX - 1] = INT_MAX;
-      }
-      if (lane == 0) { wv_val[wv * KMAX + r] = bv; wv_idx[wv * KMAX + r] = bi; }
-    }
-    __syncthreads();
-    // wave 0 ranks the survivors (an empty slot holds -1 and the largest id,
-    // so it ranks after every real block)
-    const int k_eff = min(p.topk, j1 - j0);
-    int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
-    if (wv == 0) {
-      for (int e = lane; e < 4 * KMAX; e += 64) {
-        const float cv = wv_val[e];
-        const int ci = wv_idx[e];
-        int rank = 0;
-        for (int o = 0; o < 4 * KMAX; ++o) {
-          const float ov = wv_val[o];
-          const int oi = wv_idx[o];
-          rank += (ov > cv) || (ov == cv && oi < ci);
-        }
-        if (rank < k_eff) out_sel[rank] = ci;
-      }
-      for (int r = k_eff + lane; r < p.topk; r += 64) out_sel[r] = -1;
-    }
-    __syncthreads();  // LDS is reused by the next pair
+  for (int t = 0; t < 4; ++t) {
+    const int x = t >> 1, h = t & 1;
+    const int pos = tk[x][h];
+    if (pos >= t_end) continue;   // uniform
+    int32_t* out_sel = p.topk_idx + (static_cast<int64_t>(p.perm[pos]) * p.h_kv + g) * p.topk;
+    const int n = cnt[t];
+    uint64_t k1, k2;
+    int r1, r2;
+    list_rank(t, n, k1, k2, r1, r2);
+    if (lane < n && r1 < k_eff) out_sel[r1] = static_cast<int32_t>(~static_cast<uint32_t>(k1));
+    if (lane + 64 < n && r2 < k_eff) out_sel[r2] = static_cast<int32_t>(~static_cast<uint32_t>(k2));
+    for (int r = min(n, k_eff) + lane; r < p.topk; r += 64) out_sel[r] = -1;
   }
 }
 
@@ -657,21 +726,10 @@ hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t s
 
 hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   gqa_tile_prefix_kernel<<<1, 64, 0, stream>>>(p);
+  probe_select_launch(p, stream);
   const dim3 grid(p.max_tiles2, p.h_kv);
   if (p.d == 32) gqa_topk_kernel<32><<<grid, 256, 0, stream>>>(p);
   else gqa_topk_kernel<64><<<grid, 256, 0, stream>>>(p);
-  return hipGetLastError();
-}
-
-hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  // the number of pairs is read on the device, so the grid does not depend on it
-  if (p.d == 32) {
-    if (p.topk <= 16) gqa_fixup_kernel<32, 16><<<2048, 256, 0, stream>>>(p);
-    else gqa_fixup_kernel<32, 32><<<2048, 256, 0, stream>>>(p);
-  } else {
-    if (p.topk <= 16) gqa_fixup_kernel<64, 16><<<2048, 256, 0, stream>>>(p);
-    else gqa_fixup_kernel<64, 32><<<2048, 256, 0, stream>>>(p);
-  }
   return hipGetLastError();
 }
 

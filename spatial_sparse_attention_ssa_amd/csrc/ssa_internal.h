@@ -182,7 +182,8 @@ struct FwdParams {
   int32_t* probe_slot;   // [batch + 1] probe slot of each sequence or -1; [batch] = slots used
   int32_t* probe_seq;    // [max_probe_slots] sequence of each slot
   float* probe_maxn2;    // [h_kv][max_probe_slots] largest squared key norm of the slot's sequence
-  void* probe;           // [h_kv][max_probe_slots][kProbeBlocks][D] the probe keys, in block order
+  void* probe;           // [h_kv][max_probe_slots][kProbeBlocks][D] the probe keys, in block order (or null)
+  int32_t* probe_ids;    // [h_kv][max_probe_slots][kProbeBlocks] their block ids (or null)
   int32_t max_probe_slots;
   // grouped-head path: log2 softmax normaliser per (token, query head), and
   // the prefix of 16-token tiles per sequence
@@ -253,9 +254,10 @@ constexpr int kProbeBlocks = 512;  // pooled keys per probe set (16 key tiles)
 
 hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 void tile_prefix_kernel_launch(const FwdParams& p, hipStream_t stream);
+// probe sets (needs the pooled-key norms and the probe slots of tile_prefix_kernel)
+void probe_select_launch(const FwdParams& p, hipStream_t stream);
 hipError_t launch_gqa_cmp(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_gqa_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
-hipError_t launch_gqa_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_geo_topk(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 
 // backward stages (ssa_bwd.hip, ssa_bwd_mfma.hip)

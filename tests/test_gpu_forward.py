@@ -225,8 +225,8 @@ def test_gqa_top_blocks_in_one_lane(head_dim):
     # Scattered voxels give about one token per block (over a thousand blocks
     # in one sequence).  Keys of the blocks whose id is 5 mod 32 are pushed
     # along one direction that every query shares, so the top k all come from
-    # the same column of 32-block key tiles: the grouped top-k kernel keeps
-    # only 8 blocks per column and token, and the exact fallback must decide.
+    # the same column of 32-block key tiles (the same lane of the grouped
+    # top-k kernel's MFMA tiles) and stand far above every other block.
     rng = np.random.default_rng(7)
     lin = rng.choice(64 ** 3, size=1500, replace=False)
     coords = np.stack(np.unravel_index(lin, (64,) * 3), -1)
@@ -307,6 +307,38 @@ def test_constant_keys_pick_first_blocks():
         toks = ob.perm[ob.blk_off[j0]:ob.blk_off[j1]]
         expect = np.arange(j0, min(j0 + wl.topk, j1))
         assert (sel[toks][:, :, :len(expect)] == expect).all()
+
+
+@pytest.mark.parametrize("head_dim", [32, 64])
+def test_gqa_constant_keys_pick_first_blocks(head_dim):
+    # grouped heads with every pooled key equal: all of a token's block scores
+    # tie, so the grouped top-k kernel admits every block and cuts its lists
+    # to the top k again and again (ties: lower block first); the long
+    # sequence takes the probe-set warm-up, the short one its own tiles
+    wl = make_custom([14000, 300], grid_res=128, n_prims=4, topk=16, h_q=16, h_kv=1, head_dim=head_dim,
+                     dtype="bf16", seed=53)
+    wl.k[:] = wl.k[0:1, 0:1, :]
+    ob = P.oracle_blocks(wl)
+    nbs = np.diff(ob.seq_blk_off)
+    assert nbs[0] > 512 >= nbs[1]
+    gb = P.gpu_build(wl)
+    sel = P.gpu_forward(wl, gb, return_topk=True)["topk"].cpu().numpy()
+    for b in range(wl.batch):
+        j0, j1 = ob.seq_blk_off[b], ob.seq_blk_off[b + 1]
+        toks = ob.perm[ob.blk_off[j0]:ob.blk_off[j1]]
+        expect = np.arange(j0, min(j0 + wl.topk, j1))
+        assert (sel[toks][:, :, :len(expect)] == expect).all()
+
+
+def test_gqa_probe_warmup_full():
+    # grouped heads on a sequence of more than 512 blocks (its lower bound on
+    # each token's k-th score comes from the probe set) beside a short one
+    # (bounded from its own blocks); compared in full with the oracle
+    wl = make_custom([14000, 700], grid_res=128, n_prims=4, topk=16, h_q=16, h_kv=1, head_dim=32, dtype="bf16",
+                     seed=54)
+    nbs = np.diff(P.oracle_blocks(wl).seq_blk_off)
+    assert nbs[0] > 512 >= nbs[1]
+    _full_compare(wl, tag="grouped probe warm-up")
 
 
 def dense_cube(n, side, seed):
