@@ -383,7 +383,7 @@ template <int D>
 __global__ void __launch_bounds__(256, D == 32 ? 3 : 2)
 gqa_topk_kernel(FwdParams p) {
   constexpr int KS = D / 16;
-  __shared__ __align__(16) float qy[4][kQCap][16];   // a pair's 16 exponents y_h (lane half h wrote 8 h ... 8 h + 7)
+  __shared__ __align__(16) float qy[4][kQCap][16];   // a pair's 16 values z_h (lane half h wrote 8 h ... 8 h + 7)
   __shared__ int qm[4][kQCap];                       // block << 2 | token of the wave
   __shared__ uint64_t lst[4][4][kLCap];              // candidate keys per wave and token
 
@@ -412,7 +412,10 @@ gqa_topk_kernel(FwdParams p) {
   // tokens 2 x + 0 and 2 x + 1); A operand row (lane % 32) = (token
   // (lane % 32) / 16, head lane % 16)
   bf16x8 qa[2][KS];
-  float cn[2][16];       // log2 normalisers of this lane's 16 accumulator rows
+  // -c_h / c2 for this lane's 16 accumulator rows (c_h: the head's log2
+  // normaliser): the MFMA accumulators start there, so they hold
+  // z = s - c_h / c2 and the head's probability of the block is 2^(z c2)
+  float cz[2][16];
   int tk[2][2];          // sorted positions of the row block's two tokens
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
@@ -433,9 +436,9 @@ gqa_topk_kernel(FwdParams p) {
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * half + (r & 3);
       const int pos = tk[x][row >> 4];
-      cn[x][r] = FLT_MAX;  // no probability for a missing token
+      cz[x][r] = -INFINITY;  // no probability for a missing token
       if (pos < t_end)
-        cn[x][r] = p.norm[static_cast<int64_t>(p.perm[pos]) * p.h_q + g * kGroup + (row & 15)];
+        cz[x][r] = -p.norm[static_cast<int64_t>(p.perm[pos]) * p.h_q + g * kGroup + (row & 15)] / c2;
     }
   }
 
@@ -465,21 +468,21 @@ gqa_topk_kernel(FwdParams p) {
       body(rel, kb);
     }
   };
-  // S of row block x against a key tile, and the exponents
-  // y = s * scale * log2 e - c_h, so that the head's probability is 2^y
-  auto exponents = [&](int x, const bf16x8 (&kb)[KS], float (&y)[16]) {
-    f32x16 s = {};
+  // z of row block x against a key tile
+  auto shifted = [&](int x, const bf16x8 (&kb)[KS]) {
+    f32x16 z;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[x][ks], kb[ks], s, 0, 0, 0);
+    for (int r = 0; r < 16; ++r) z[r] = cz[x][r];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) y[r] = fmaf(s[r], c2, -cn[x][r]);
+    for (int ks = 0; ks < KS; ++ks) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[x][ks], kb[ks], z, 0, 0, 0);
+    return z;
   };
-  // a token's group score from its 16 exponents: each lane half sums its
-  // 8 heads in order, then the two halves are added
-  auto half_sum = [](const float* yv) {
+  // a token's group score: each lane half sums the probabilities 2^(z c2)
+  // of its 8 heads in order, then the two halves are added
+  auto half_sum = [c2](const float* zv) {
     float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) sum += __builtin_amdgcn_exp2f(yv[r]);
+    for (int r = 0; r < 8; ++r) sum += __builtin_amdgcn_exp2f(zv[r] * c2);
     return sum;
   };
 
@@ -504,8 +507,10 @@ gqa_topk_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
+      const f32x16 z = shifted(x, kb);
       float y[16];
-      exponents(x, kb, y);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) y[r] = z[r];
       const float sum0 = pair_add(half_sum(y)), sum1 = pair_add(half_sum(y + 8));
       const float sc = jok ? (half ? sum1 : sum0) : -2.f;
       w2[x] = __builtin_amdgcn_fmed3f(w1[x], sc, w2[x]);
@@ -566,7 +571,7 @@ gqa_topk_kernel(FwdParams p) {
       } else if (tau0 >= 0.f) {
         // scores are >= 0, so their float bits order like their values
         min_key[t] = static_cast<uint64_t>(__float_as_uint(tau0)) << 32;
-        theta[t] = tau0 > 0.f ? __log2f(tau0) - 4.001f : -INFINITY;
+        theta[t] = tau0 > 0.f ? (__log2f(tau0) - 4.001f) / c2 : -INFINITY;
       } else {
         min_key[t] = 0ull;       // fewer than k scored blocks: admit all
         theta[t] = -INFINITY;
@@ -575,11 +580,12 @@ gqa_topk_kernel(FwdParams p) {
   }
 
   // ---------------- main pass over the sequence's tiles
-  // A pair (token, block) whose largest exponent m = max_h y_h satisfies
-  // 16 * 2^m < (the admission score) cannot be admitted, since its score is
-  // a sum of 16 terms 2^y_h; theta holds log2 of that score minus 4 (and a
-  // margin for rounding).  Pairs that pass are queued with their 16
-  // exponents; a batch computes their scores exactly, and a pair whose key
+  // A pair (token, block) whose largest z over the heads, m, satisfies
+  // 16 * 2^(m c2) < (the admission score) cannot be admitted, since its score
+  // is a sum of 16 terms 2^(z_h c2); theta holds log2 of that score minus 4
+  // (and a margin for rounding), divided by c2.  Pairs that pass are queued
+  // with their 16 values z; a batch computes their scores exactly (in the
+  // warm-up's arithmetic), and a pair whose key
   // (score, then lower block first) reaches min_key joins its token's list.
   // A list longer than kCompact is cut to its top k by rank counting, and
   // min_key becomes one above the k-th key: the top k of the blocks seen so
@@ -611,7 +617,7 @@ gqa_topk_kernel(FwdParams p) {
     cnt[t] = k_eff;   // n > kCompact >= k_eff
     min_key[t] = L[k_eff - 1] + 1;
     const float smin = __uint_as_float(static_cast<uint32_t>(min_key[t] >> 32));
-    theta[t] = smin > 0.f ? __log2f(smin) - 4.001f : -INFINITY;
+    theta[t] = smin > 0.f ? (__log2f(smin) - 4.001f) / c2 : -INFINITY;
   };
   auto process = [&]() {
     const int nbat = min(qn, 64);
@@ -656,8 +662,7 @@ gqa_topk_kernel(FwdParams p) {
     const uint32_t below = (1u << l32) - 1u;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      float y[16];
-      exponents(x, kb, y);
+      const f32x16 y = shifted(x, kb);
       float m0 = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
       m0 = fmaxf(m0, fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
       float m1 = fmaxf(fmaxf(y[8], y[9]), fmaxf(y[10], y[11]));
