@@ -65,12 +65,8 @@ __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
 }
 
 // lane l and lane l ^ 32 exchange v (v_permlane32_swap, no LDS); the two
-// results are v of both lanes, so a max or a sum over them is the same on
-// both lanes of a pair
-__device__ __forceinline__ float pair_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// results are v of both lanes, so their sum is the same on both lanes of a
+// pair
 __device__ __forceinline__ float pair_add(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -454,19 +450,20 @@ gqa_topk_kernel(FwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kb[ks] = lds_b128(src + 16 * ks);
     };
-    bf16x8 cur[KS], nxt[KS];
-    load(0, cur);
-    load(n_t > 1 ? 1 : 0, nxt);
-    for (int rel = 0; rel < n_t; ++rel) {
-      bf16x8 kb[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kb[ks] = cur[ks];
-        cur[ks] = nxt[ks];
-      }
-      load(rel + 2 < n_t ? rel + 2 : n_t - 1, nxt);
-      body(rel, kb);
+    // two register sets used in turn (the loop is unrolled by two, so no
+    // register is copied while its load is in flight): each set is reloaded
+    // right after its step and has two steps to arrive
+    bf16x8 ba[KS], bb[KS];
+    load(0, ba);
+    load(min(1, n_t - 1), bb);
+    int rel = 0;
+    for (; rel + 1 < n_t; rel += 2) {
+      body(rel, ba);
+      load(min(rel + 2, n_t - 1), ba);
+      body(rel + 1, bb);
+      load(min(rel + 3, n_t - 1), bb);
     }
+    if (rel < n_t) body(rel, ba);
   };
   // z of row block x against a key tile
   auto shifted = [&](int x, const bf16x8 (&kb)[KS]) {
@@ -667,13 +664,13 @@ gqa_topk_kernel(FwdParams p) {
       m0 = fmaxf(m0, fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
       float m1 = fmaxf(fmaxf(y[8], y[9]), fmaxf(y[10], y[11]));
       m1 = fmaxf(m1, fmaxf(fmaxf(y[12], y[13]), fmaxf(y[14], y[15])));
-      m0 = pair_max(m0);
-      m1 = pair_max(m1);
-      const bool p0 = jok && m0 >= theta[2 * x];
-      const bool p1 = jok && m1 >= theta[2 * x + 1];
-      // both lane halves hold the same decisions; the low 32 bits suffice
-      const uint32_t b0 = static_cast<uint32_t>(__ballot(p0));
-      const uint32_t b1 = static_cast<uint32_t>(__ballot(p1));
+      // the pair in lanes l and l + 32 passes when either half's maximum
+      // does: the two halves of the ballot, or-ed
+      const uint64_t v0 = __ballot(jok && m0 >= theta[2 * x]);
+      const uint64_t v1 = __ballot(jok && m1 >= theta[2 * x + 1]);
+      const uint32_t b0 = static_cast<uint32_t>(v0) | static_cast<uint32_t>(v0 >> 32);
+      const uint32_t b1 = static_cast<uint32_t>(v1) | static_cast<uint32_t>(v1 >> 32);
+      const bool p0 = (b0 >> l32) & 1u, p1 = (b1 >> l32) & 1u;
       const int n0 = __popc(b0), n1 = __popc(b1);
       if (p0) {
         const int e = (qh + qn + __popc(b0 & below)) & (kQCap - 1);
