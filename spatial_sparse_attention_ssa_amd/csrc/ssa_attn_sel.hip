@@ -1,5 +1,6 @@
 // Selected-block attention and the gated sum (bf16, D = 32 or 64; query head
 // h reads key/value head g = h / (h_q / h_kv) and the selection of group g).
+// Groups of 16 query heads take the MFMA kernel at the end of this file.
 //
 // Direct3D-S2 page, "Method": all tokens of the top-k selected blocks take
 // part in a second attention; the three branch outputs are summed with the
@@ -20,6 +21,7 @@
 // the LDS list's capacity, which only very large selections reach, are walked
 // block by block afterwards.
 #include <float.h>
+#include <math.h>
 
 #include "ssa_internal.h"
 
@@ -234,9 +236,189 @@ sel_combine_kernel(FwdParams p) {
   *reinterpret_cast<u32x4*>(out + 8) = w1;
 }
 
+// ---------------------------------------------------------------------------
+// Grouped heads (16 query heads per key/value head): the heads of a group
+// share one selection, so one wave serves one (token, group) item and runs
+// the branch on MFMA, 16 selected rows at a time:
+//   S^T = K Q^T        (v_mfma_f32_16x16x32_bf16: rows x heads, k = dims)
+//   O^T += V^T P^T     (v_mfma_f32_16x16x16_bf16: dims x heads, k = rows)
+// A 16x16 accumulator puts rows 4 (l / 16) + v of column l % 16 in lane l,
+// which is also how the second product takes its k = rows operand, so P^T
+// feeds it from the lane's own registers, and every lane's softmax state and
+// output belong to one head (l % 16).  The rows' values are staged
+// transposed in LDS for the V^T operand; each key and value row is loaded
+// once per group instead of once per head.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroupHeads = 16;
+constexpr int kVtRow = 16 + 4;   // LDS row of the transposed value chunk (bf16), padded against bank conflicts
+
+template <int KMAX, int D>
+__global__ void __launch_bounds__(256)
+sel_group_kernel(FwdParams p) {
+  constexpr int KQ = D / 32;   // 16x16x32 steps over the dims
+  constexpr int NB = D / 16;   // 16-dim blocks of O^T
+  __shared__ int off_s[4][KMAX + 1];
+  __shared__ int start_s[4][KMAX];
+  __shared__ __align__(16) uint16_t vt_s[4][D * kVtRow];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t n_items = static_cast<int64_t>(p.n) * p.h_kv;
+  // items group-major in sorted token order: neighbouring waves select
+  // neighbouring blocks of the same group
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+  if (item >= n_items) return;   // uniform over the wave; no barrier follows
+  const int g = static_cast<int>(item / p.n);
+  const int t = p.perm[static_cast<int>(item % p.n)];
+  const int hq = g * kGroupHeads + col;
+  const int nb = p.counts[SSA_COUNT_NB];
+  const float c2 = p.scale * kLog2e;
+
+  // selected blocks: lane i < KMAX takes entry i; the list ends at the first
+  // id outside [0, nb)
+  const int32_t* sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
+  int id = lane < KMAX && lane < p.topk ? sel[lane] : -1;
+  const uint64_t bad = __ballot(!(id >= 0 && id < nb));   // lanes >= KMAX always count as ends
+  const int k_eff = static_cast<int>(__builtin_ctzll(bad));
+  int a = 0, size = 0;
+  if (lane < k_eff) {
+    a = p.blk_off[id];
+    size = p.blk_off[id + 1] - a;
+  }
+  int incl = size;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  const int total = __shfl(incl, 63);
+  if (lane < k_eff) {
+    off_s[wv][lane + 1] = incl;
+    start_s[wv][lane] = a;
+  }
+  if (lane == 0) off_s[wv][0] = 0;
+  wave_lds_sync();
+
+  // Q^T operands: head col, dims 8 grp .. 8 grp + 7 of each 32-dim step
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (static_cast<int64_t>(t) * p.h_q + hq) * D;
+  bf16x8 qb[KQ];
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) qb[kq] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * kq + 8 * grp));
+
+  const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(g) * p.n * D;
+  const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(g) * p.n * D;
+  uint16_t* vt = vt_s[wv];
+  float m = -FLT_MAX, l = 0.f;
+  f32x4 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < total; c0 += 16) {
+    // row of list position c0 + col (this lane's K row and V row)
+    const int pos = c0 + col;
+    const bool ok = pos < total;
+    u32x4 kr[KQ], vr[KQ];
+    if (ok) {
+      int lo = 0, hi = k_eff - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off_s[wv][mid] <= pos) lo = mid; else hi = mid - 1;
+      }
+      const int64_t row = start_s[wv][lo] + (pos - off_s[wv][lo]);
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        kr[kq] = *reinterpret_cast<const u32x4*>(KS + row * D + 32 * kq + 8 * grp);
+        vr[kq] = *reinterpret_cast<const u32x4*>(VS + row * D + 32 * kq + 8 * grp);
+      }
+    } else {
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) kr[kq] = vr[kq] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // V^T chunk: element (dim, row col)
+    wave_lds_sync();   // the previous chunk's V^T reads are done
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 32 * kq + 8 * grp + 2 * e;
+        vt[d * kVtRow + col] = static_cast<uint16_t>(vr[kq][e] & 0xFFFFu);
+        vt[(d + 1) * kVtRow + col] = static_cast<uint16_t>(vr[kq][e] >> 16);
+      }
+    // S^T: rows 4 grp + v, head col
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kq]), qb[kq], s, 0, 0, 0);
+    float x[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[v] = c0 + 4 * grp + v < total ? s[v] * c2 : -INFINITY;
+    // the head's chunk maximum over the four lane groups
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float corr = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    // P rounded to bf16; the row sum adds the rounded values, so the weights
+    // of O and of the sum are the same numbers
+    bf16x4 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const __bf16 pv = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[v] - m));
+      pb[v] = pv;
+      ps += static_cast<float>(pv);
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * corr + ps;
+    wave_lds_sync();   // V^T stored
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bf16x4 va = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(vt + (16 * b + col) * kVtRow + 4 * grp));
+      o[b] *= corr;
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[b], 0, 0, 0);
+    }
+  }
+
+  // out = acc + G1 * o_sel / l for dims 16 b + 4 grp + v of head col
+  const int64_t orow = (static_cast<int64_t>(t) * p.h_q + hq) * D;
+  if (p.lse && grp == 0)
+    p.lse[static_cast<int64_t>(p.n) * p.h_q + static_cast<int64_t>(t) * p.h_q + hq] =
+        l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + hq) * 3;
+  const float f = l > 0.f ? bf16_bits_to_f32(gt[1]) / l : 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int d = 16 * b + 4 * grp;
+    const float4 av = *reinterpret_cast<const float4*>(p.acc + orow + d);
+    uint2 w;
+    w.x = static_cast<uint32_t>(f32_to_bf16_bits(fmaf(o[b][0], f, av.x))) |
+          (static_cast<uint32_t>(f32_to_bf16_bits(fmaf(o[b][1], f, av.y))) << 16);
+    w.y = static_cast<uint32_t>(f32_to_bf16_bits(fmaf(o[b][2], f, av.z))) |
+          (static_cast<uint32_t>(f32_to_bf16_bits(fmaf(o[b][3], f, av.w))) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + d) = w;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sel_combine(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  if (p.h_q == kGroupHeads * p.h_kv) {
+    const int grid = static_cast<int>((static_cast<int64_t>(p.n) * p.h_kv + 3) / 4);
+    if (p.d == 32) {
+      if (p.topk <= 16) sel_group_kernel<16, 32><<<grid, 256, 0, stream>>>(p);
+      else sel_group_kernel<32, 32><<<grid, 256, 0, stream>>>(p);
+    } else {
+      if (p.topk <= 16) sel_group_kernel<16, 64><<<grid, 256, 0, stream>>>(p);
+      else sel_group_kernel<32, 64><<<grid, 256, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+  }
   const int64_t pairs = static_cast<int64_t>(p.n) * p.h_q;
   const int np = 256 / (p.d / kDL);
   const int grid = static_cast<int>((pairs + np - 1) / np);
