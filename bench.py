@@ -58,9 +58,11 @@ KERNEL_SOURCES = {
     "probe_select_kernel": "ssa_attn_cmp.hip",
     "win_mfma_kernel": "ssa_attn_win.hip",
     "sel_combine_kernel": "ssa_attn_sel.hip",
+    "sel_group_kernel": "ssa_attn_sel.hip",
     "pool_kernel": "ssa_pool.hip",
     "gqa_cmp_kernel": "ssa_attn_gqa.hip",
     "gqa_topk_kernel": "ssa_attn_gqa.hip",
+    "gqa_seq_kmax_kernel": "ssa_attn_gqa.hip",
     "cmp_dq_mfma_kernel": "ssa_bwd_mfma.hip",
     "cmp_dkv_mfma_kernel": "ssa_bwd_mfma.hip",
     "kv_grad_mfma_kernel": "ssa_bwd_mfma.hip",
