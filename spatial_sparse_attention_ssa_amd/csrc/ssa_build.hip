@@ -27,9 +27,13 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
-__global__ void init_counts_kernel(int32_t* counts, int32_t key_bits) {
+// counts, and the one-sweep sort's digit totals and tile counters
+__global__ void init_counts_kernel(int32_t* counts, int32_t key_bits, uint32_t* glob_hist, int32_t* tile_ctr) {
   const int i = threadIdx.x;
   if (i < SSA_COUNTS) counts[i] = (i == SSA_COUNT_KEY_BITS) ? key_bits : 0;
+  if (glob_hist)
+    for (int j = i; j < kMaxPasses * 256; j += blockDim.x) glob_hist[j] = 0u;
+  if (tile_ctr && i < kMaxPasses) tile_ctr[i] = 0;
 }
 
 // Offsets for an empty token set: every offset array holds zeros.
@@ -129,6 +133,73 @@ radix_upsweep_keys(const int32_t* __restrict__ coords, const int32_t* __restrict
   __syncthreads();
   const int d = threadIdx.x;
   tile_hist[static_cast<size_t>(blockIdx.x) * 256 + d] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+}
+
+// Keys and digit counts for the one-sweep sort: every key of a tile of
+// 256 x ITEMS tokens computed from its coordinates and written out, its
+// digits of every pass counted (one LDS histogram per wave and pass) and
+// added to the passes' totals over all keys, and the tile's look-back words
+// of every pass cleared.  A full tile gives each thread ITEMS / 4 runs of four
+// consecutive tokens: their 12 coordinates are three 16-byte loads, their
+// keys one 16-byte store, and all loads are in flight before any key is
+// formed.  The
+// permutation starts as the identity, which the first scatter generates.
+template <int ITEMS>
+__global__ void __launch_bounds__(256)
+build_hist_kernel(const int32_t* __restrict__ coords, const int32_t* __restrict__ cu, int32_t n, int32_t batch,
+                  KeyLayout kl, int passes, uint32_t* __restrict__ keys, int32_t* __restrict__ counts,
+                  uint32_t* __restrict__ glob_hist, uint64_t* __restrict__ tile_state, int ntiles) {
+  __shared__ uint32_t hist[kMaxPasses][4][256];
+  for (int i = threadIdx.x; i < kMaxPasses * 4 * 256; i += 256) (&hist[0][0][0])[i] = 0;
+  __syncthreads();
+  const int wv = threadIdx.x >> 6;
+  auto count = [&](uint32_t key) {
+    for (int ps = 0; ps < passes; ++ps) atomicAdd(&hist[ps][wv][(key >> (kRadixBits * ps)) & 255u], 1u);
+  };
+  constexpr int TILE = 256 * ITEMS, G = ITEMS / 4;
+  const int base = blockIdx.x * TILE;
+  if (base + TILE <= n) {
+    u32x4 cv[G][3];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t0 = base + 4 * (g * 256 + threadIdx.x);
+      const u32x4* src = reinterpret_cast<const u32x4*>(coords + 3 * static_cast<int64_t>(t0));
+#pragma unroll
+      for (int w = 0; w < 3; ++w) cv[g][w] = src[w];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t0 = base + 4 * (g * 256 + threadIdx.x);
+      int c[12];
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[4 * w + e] = static_cast<int>(cv[g][w][e]);
+      u32x4 kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[e] = block_key(c[3 * e], c[3 * e + 1], c[3 * e + 2], cu, t0 + e, batch, kl, counts);
+        count(kv[e]);
+      }
+      *reinterpret_cast<u32x4*>(keys + t0) = kv;
+    }
+  } else {
+    for (int i = threadIdx.x; i < TILE; i += 256) {
+      const int t = base + i;
+      if (t < n) {
+        const uint32_t key = block_key(coords[3 * t], coords[3 * t + 1], coords[3 * t + 2], cu, t, batch, kl, counts);
+        keys[t] = key;
+        count(key);
+      }
+    }
+  }
+  __syncthreads();
+  const int d = threadIdx.x;
+  for (int ps = 0; ps < passes; ++ps) {
+    const uint32_t c = hist[ps][0][d] + hist[ps][1][d] + hist[ps][2][d] + hist[ps][3][d];
+    if (c) atomicAdd(&glob_hist[ps * 256 + d], c);
+    tile_state[(static_cast<size_t>(ps) * ntiles + blockIdx.x) * 256 + d] = 0ull;
+  }
 }
 
 // Digit counts of one 4096-key tile, written tile-major (one contiguous
@@ -334,20 +405,180 @@ radix_downsweep(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
   }
 }
 
+// One pass of the one-sweep sort (decoupled look-back, as in Merrill & Garland,
+// "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016, applied
+// to the radix scatter): a workgroup takes the next tile index from a
+// counter, ranks its 4096 keys as the scatter above does, publishes its
+// per-digit key counts (flag 1), then walks back over the tiles before it,
+// adding their counts until it meets an inclusive prefix (flag 2), and
+// publishes its own inclusive prefix.  A tile waits only on tiles that
+// started before it, so the walk always ends; the spin is bounded anyway
+// (kSpinMax polls), so a fault in the protocol cannot keep the kernel from
+// exiting.  Look-back word: (flag << 32) | count.
+constexpr int kSpinMax = 1 << 20;
+constexpr int kLook = 16;   // look-back words read per round
+template <int ITEMS>
+__global__ void __launch_bounds__(256)
+onesweep_kernel(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+                uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t n, int shift,
+                const uint32_t* __restrict__ glob_hist, int32_t* __restrict__ tile_ctr,
+                uint64_t* __restrict__ tile_state) {
+  __shared__ uint32_t whist[4][256];   // per wave: keys of each digit
+  __shared__ uint32_t wbase[4][256];   // per wave: tile-local start of its keys of each digit
+  __shared__ uint32_t lstart[256];     // tile-local start of each digit
+  __shared__ uint32_t gbase[256];      // output position of the tile's first key of each digit
+  __shared__ uint32_t scan[256];
+  constexpr int TILE = 256 * ITEMS;
+  __shared__ uint32_t ehist[4][256];   // per wave: keys of each digit, counted before the ranking
+  __shared__ uint32_t skeys[TILE];
+  __shared__ int32_t svals[TILE];
+  __shared__ int s_tile;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int d0 = threadIdx.x;
+  for (int i = threadIdx.x; i < 4 * 256; i += 256) {
+    (&whist[0][0])[i] = 0;
+    (&ehist[0][0])[i] = 0;
+  }
+  if (threadIdx.x == 0) s_tile = atomicAdd(tile_ctr, 1);
+  __syncthreads();
+  const int tile = s_tile;
+  const int tile0 = tile * TILE;
+  const int base = tile0 + wave * (TILE / 4);
+  const uint64_t lt = lanemask_lt();
+  uint32_t kk[ITEMS], rk[ITEMS], dg[ITEMS];
+  int32_t vv[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int p = base + r * kWave + lane;
+    kk[r] = p < n ? keys_in[p] : 0u;
+    vv[r] = vals_in ? (p < n ? vals_in[p] : 0) : p;
+  }
+  const uint32_t gcount = glob_hist[d0];
+  // the tile's digit counts first, published before the (much longer)
+  // ranking, so that later tiles' look-backs find them early
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r)
+    if (base + r * kWave + lane < n) atomicAdd(&ehist[wave][(kk[r] >> shift) & 255u], 1u);
+  __syncthreads();
+  const uint32_t tot = ehist[0][d0] + ehist[1][d0] + ehist[2][d0] + ehist[3][d0];
+  uint64_t* const st = tile_state + static_cast<size_t>(tile) * 256 + d0;
+  __hip_atomic_store(st, (uint64_t(1) << 32) | tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int p = base + r * kWave + lane;
+    const bool valid = p < n;
+    const uint32_t key = kk[r];
+    const uint32_t d = (key >> shift) & 255u;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kRadixBits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint32_t before = whist[wave][d];
+    const uint32_t cnt = static_cast<uint32_t>(__popcll(peers));
+    const bool leader = valid && ((peers & lt) == 0);
+    __builtin_amdgcn_wave_barrier();
+    if (leader) whist[wave][d] = before + cnt;
+    __builtin_amdgcn_wave_barrier();
+    rk[r] = valid ? before + static_cast<uint32_t>(__popcll(peers & lt)) : 0xFFFFFFFFu;
+    dg[r] = d;
+  }
+  __syncthreads();
+  {
+    const int d = d0;
+    // exclusive prefix of digit d over the tiles before this one: kLook
+    // earlier tiles' words per round, loaded together, consumed in order up
+    // to the first inclusive prefix (done) or the first tile not yet
+    // published (the next round starts there)
+    uint32_t prefix = 0;
+    int j = tile - 1, stall = 0;
+    while (j >= 0) {
+      uint64_t w[kLook];
+#pragma unroll
+      for (int k = 0; k < kLook; ++k)
+        w[k] = j - k >= 0 ? __hip_atomic_load(tile_state + static_cast<size_t>(j - k) * 256 + d, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                          : (uint64_t(2) << 32);   // before tile 0: an inclusive prefix of 0
+      int used = 0;
+      bool done = false;
+#pragma unroll
+      for (int k = 0; k < kLook; ++k) {
+        const uint32_t f = static_cast<uint32_t>(w[k] >> 32);
+        if (!done && used == k && f != 0) {
+          prefix += static_cast<uint32_t>(w[k]);
+          used = k + 1;
+          done = f == 2;
+        }
+      }
+      if (done) break;
+      j -= used;
+      if (used == 0) {
+        if (++stall > kSpinMax) break;   // gave up: the output is wrong but stays in bounds
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __hip_atomic_store(st, (uint64_t(2) << 32) | (prefix + tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // exclusive scans over the digits: of the tile's totals, and of all keys' totals
+    scan[d] = tot;
+    lstart[d] = gcount;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const uint32_t v = d >= off ? scan[d - off] : 0u;
+      const uint32_t g = d >= off ? lstart[d - off] : 0u;
+      __syncthreads();
+      scan[d] += v;
+      lstart[d] += g;
+      __syncthreads();
+    }
+    const uint32_t gstart = lstart[d] - gcount;   // keys of all digits below d
+    __syncthreads();
+    uint32_t run = scan[d] - tot;
+    lstart[d] = run;
+    gbase[d] = gstart + prefix;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wbase[w][d] = run;
+      run += whist[w][d];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    if (rk[r] != 0xFFFFFFFFu) {
+      const uint32_t pos = wbase[wave][dg[r]] + rk[r];
+      skeys[pos] = kk[r];
+      svals[pos] = vv[r];
+    }
+  }
+  __syncthreads();
+  const int cnt = min(TILE, n - tile0);
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    const uint32_t key = skeys[i];
+    const uint32_t d = (key >> shift) & 255u;
+    const uint32_t dst = gbase[d] + (static_cast<uint32_t>(i) - lstart[d]);
+    keys_out[dst] = key;
+    vals_out[dst] = svals[i];
+  }
+}
+
+template <int ITEMS>
 __global__ void __launch_bounds__(256)
 seg_count(const uint32_t* __restrict__ keys, int32_t n, int win_shift, int32_t* __restrict__ tile_cnt) {
   __shared__ int32_t red[2][256];
-  const int base = blockIdx.x * kSortTile;
+  const int base = blockIdx.x * 256 * ITEMS;
   int cb = 0, cw = 0;
-  uint32_t kc[kItems], kprev[kItems];
+  uint32_t kc[ITEMS], kprev[ITEMS];
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {   // all loads in flight first
+  for (int r = 0; r < ITEMS; ++r) {   // all loads in flight first
     const int p = base + r * 256 + threadIdx.x;
     kc[r] = p < n ? keys[p] : 0u;
     kprev[r] = (p < n && p > 0) ? keys[p - 1] : 0u;
   }
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
+  for (int r = 0; r < ITEMS; ++r) {
     const int p = base + r * 256 + threadIdx.x;
     if (p < n) {
       if (p == 0) {
@@ -418,6 +649,7 @@ __device__ __forceinline__ int seq_of(uint32_t key, int seq_shift) {
   return seq_shift < 0 ? 0 : static_cast<int>(key >> seq_shift);
 }
 
+template <int ITEMS>
 __global__ void __launch_bounds__(256)
 seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_shift,
           int seq_shift, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ counts,
@@ -427,21 +659,21 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
   __shared__ int32_t wcnt[2][4];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int base = blockIdx.x * kSortTile + wave * (kSortTile / 4);
+  const int base = blockIdx.x * 256 * ITEMS + wave * (64 * ITEMS);
   const uint64_t lt = lanemask_lt();
   int rb = 0, rw = 0;
-  int rank_b[kItems], rank_w[kItems];
-  static_assert(2 * kItems <= 32, "two boundary flags per row are packed into 32 bits");
+  int rank_b[ITEMS], rank_w[ITEMS];
+  static_assert(2 * ITEMS <= 32, "two boundary flags per row are packed into 32 bits");
   uint32_t flags = 0;
-  uint32_t kc[kItems], kprev[kItems];
+  uint32_t kc[ITEMS], kprev[ITEMS];
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {   // all loads in flight before the ballots
+  for (int r = 0; r < ITEMS; ++r) {   // all loads in flight before the ballots
     const int p = base + r * kWave + lane;
     kc[r] = p < n ? keys[p] : 0u;
     kprev[r] = (p < n && p > 0) ? keys[p - 1] : 0u;
   }
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
+  for (int r = 0; r < ITEMS; ++r) {
     const int p = base + r * kWave + lane;
     const bool valid = p < n;
     bool isb = false, isw = false;
@@ -474,7 +706,7 @@ seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_s
   const int nb_tot = counts[SSA_COUNT_NB];
   const int nw_tot = counts[SSA_COUNT_NW];
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
+  for (int r = 0; r < ITEMS; ++r) {
     const int p = base + r * kWave + lane;
     if (p >= n) continue;
     const bool isb = (flags >> (2 * r)) & 1u, isw = (flags >> (2 * r + 1)) & 1u;
@@ -548,23 +780,53 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
 
+// Up to 2^18 tokens the build sorts with the one-sweep kernels on 1024-key
+// tiles (nine short launches; four times the workgroups of 4096-key tiles,
+// whose per-workgroup latency otherwise sets a small build's time).  Above,
+// the three-kernel reduce-then-scan passes on 4096-key tiles are faster:
+// measured on MI355X, one-sweep 61 / 76 / 106 / 578 us against 74 / 88 / 96 /
+// 466 us at 2^17 / 2^18 / 2^19 / 2^24 random voxel tokens.
+bool build_onesweep(int64_t n) { return n <= (int64_t(1) << 18); }
+int build_items(int64_t n) { return build_onesweep(n) ? 4 : kItems; }
+int64_t build_tiles(int64_t n) {
+  const int64_t tile = 256 * build_items(n);
+  return (n + tile - 1) / tile;
+}
+
 size_t build_workspace_bytes(int64_t n, int32_t /*batch*/) {
-  const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
+  const int64_t ntiles = build_tiles(n);
   size_t b = 0;
   b += 2 * align256(sizeof(uint32_t) * n);     // keys_a, keys_b
   b += align256(sizeof(int32_t) * n);          // vals_b
-  b += align256(sort_pairs_hist_bytes(n));      // tile histograms and their scan's chunk sums
+  if (build_onesweep(n)) {
+    b += align256(sizeof(uint32_t) * kMaxPasses * 256);                    // digit totals
+    b += align256(sizeof(int32_t) * kMaxPasses);                           // tile counters
+    b += align256(sizeof(uint64_t) * kMaxPasses * 256 * (ntiles > 0 ? ntiles : 1));   // look-back words
+  } else {
+    b += align256(sort_pairs_hist_bytes(n));   // tile histograms and their scan's chunk sums
+  }
   b += 2 * align256(sizeof(int32_t) * 2 * ntiles);
   return b + 256;
 }
 
 void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out) {
-  const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
+  const int64_t ntiles = build_tiles(n);
   char* p = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
   out->keys_a = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * n);
   out->keys_b = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * n);
   out->vals_b = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * n);
-  out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sort_pairs_hist_bytes(n));
+  out->glob_hist = nullptr;
+  out->tile_ctr = nullptr;
+  out->tile_state = nullptr;
+  out->tile_hist = nullptr;
+  if (build_onesweep(n)) {
+    out->glob_hist = reinterpret_cast<uint32_t*>(p); p += align256(sizeof(uint32_t) * kMaxPasses * 256);
+    out->tile_ctr = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * kMaxPasses);
+    out->tile_state = reinterpret_cast<uint64_t*>(p);
+    p += align256(sizeof(uint64_t) * kMaxPasses * 256 * (ntiles > 0 ? ntiles : 1));
+  } else {
+    out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sort_pairs_hist_bytes(n));
+  }
   out->tile_cnt = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * 2 * ntiles);
   out->tile_base = reinterpret_cast<int32_t*>(p);
 }
@@ -622,18 +884,35 @@ hipError_t launch_sort_pairs(uint32_t* keys, int32_t* vals, uint32_t* keys_tmp, 
   return hipGetLastError();
 }
 
-hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,
-                        const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
-                        hipStream_t stream) {
-  init_counts_kernel<<<1, 64, 0, stream>>>(out.counts, kl.key_bits);
-  if (n == 0) {
-    empty_offsets_kernel<<<(batch + 1 + 255) / 256, 256, 0, stream>>>(
-        batch, out.blk_off, out.win_off, out.win_blk_off, out.seq_blk_off, out.seq_win_off);
-    return hipGetLastError();
-  }
-  const int ntiles = (n + kSortTile - 1) / kSortTile;
+namespace {
+
+// the sorted keys land in ws.keys_a and the permutation in out.perm
+void build_sort_onesweep(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,
+                         const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws, hipStream_t stream) {
+  constexpr int ITEMS = 4;
+  const int ntiles = static_cast<int>(build_tiles(n));
   const int passes = (kl.key_bits + kRadixBits - 1) / kRadixBits;
   // ping-pong so that the last pass lands in (keys_a, perm)
+  uint32_t* kin = (passes % 2 == 0) ? ws.keys_a : ws.keys_b;
+  int32_t* vin = (passes % 2 == 0) ? out.perm : ws.vals_b;
+  uint32_t* kout = (passes % 2 == 0) ? ws.keys_b : ws.keys_a;
+  int32_t* vout = (passes % 2 == 0) ? ws.vals_b : out.perm;
+  build_hist_kernel<ITEMS><<<ntiles, 256, 0, stream>>>(coords, cu_seqlens, n, batch, kl, passes, kin, out.counts,
+                                                       ws.glob_hist, ws.tile_state, ntiles);
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = pass * kRadixBits;
+    onesweep_kernel<ITEMS><<<ntiles, 256, 0, stream>>>(kin, pass == 0 ? nullptr : vin, kout, vout, n, shift,
+                                                       ws.glob_hist + 256 * pass, ws.tile_ctr + pass,
+                                                       ws.tile_state + static_cast<size_t>(pass) * ntiles * 256);
+    uint32_t* tk = kin; kin = kout; kout = tk;
+    int32_t* tv = vin; vin = vout; vout = tv;
+  }
+}
+
+void build_sort_passes(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,
+                       const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws, hipStream_t stream) {
+  const int ntiles = static_cast<int>(build_tiles(n));
+  const int passes = (kl.key_bits + kRadixBits - 1) / kRadixBits;
   uint32_t* kin = (passes % 2 == 0) ? ws.keys_a : ws.keys_b;
   int32_t* vin = (passes % 2 == 0) ? out.perm : ws.vals_b;
   uint32_t* kout = (passes % 2 == 0) ? ws.keys_b : ws.keys_a;
@@ -651,17 +930,44 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
     uint32_t* tk = kin; kin = kout; kout = tk;
     int32_t* tv = vin; vin = vout; vout = tv;
   }
-  // sorted keys now in ws.keys_a, permutation in out.perm
+}
+
+// CSR offsets, counts and maxima from the sorted keys
+template <int ITEMS>
+void build_segments(int32_t n, int32_t batch, const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
+                    hipStream_t stream) {
+  const int ntiles = static_cast<int>(build_tiles(n));
   const int win_shift = 3 * kl.l_r;
   const int seq_shift = kl.seq_bits ? 3 * (kl.l_rw + kl.l_r) : -1;
-  seg_count<<<ntiles, 256, 0, stream>>>(ws.keys_a, n, win_shift, ws.tile_cnt);
+  seg_count<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, win_shift, ws.tile_cnt);
   seg_scan<<<1, 1024, 0, stream>>>(ws.tile_cnt, ntiles, ws.tile_base, out.counts);
-  seg_write<<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
-                                        out.counts, out.blk_off, out.win_off, out.win_blk_off,
-                                        out.seq_blk_off, out.seq_win_off);
+  seg_write<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
+                                               out.counts, out.blk_off, out.win_off, out.win_blk_off,
+                                               out.seq_blk_off, out.seq_win_off);
   // one workgroup per 4096 tokens, at least 64 and at most 1024 (two atomics each)
   const int sgrid = max(64, min((n + 4095) / 4096, 1024));
   seg_stats<<<sgrid, 256, 0, stream>>>(out.blk_off, out.win_off, out.counts);
+}
+
+}  // namespace
+
+hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_t n, int32_t batch,
+                        const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
+                        hipStream_t stream) {
+  init_counts_kernel<<<1, 256, 0, stream>>>(out.counts, kl.key_bits, n > 0 ? ws.glob_hist : nullptr,
+                                            n > 0 ? ws.tile_ctr : nullptr);
+  if (n == 0) {
+    empty_offsets_kernel<<<(batch + 1 + 255) / 256, 256, 0, stream>>>(
+        batch, out.blk_off, out.win_off, out.win_blk_off, out.seq_blk_off, out.seq_win_off);
+    return hipGetLastError();
+  }
+  if (build_onesweep(n)) {
+    build_sort_onesweep(coords, cu_seqlens, n, batch, kl, out, ws, stream);
+    build_segments<4>(n, batch, kl, out, ws, stream);
+  } else {
+    build_sort_passes(coords, cu_seqlens, n, batch, kl, out, ws, stream);
+    build_segments<kItems>(n, batch, kl, out, ws, stream);
+  }
   return hipGetLastError();
 }
 

@@ -110,17 +110,23 @@ struct KeyLayout {
   int shift;     // window origin at -shift per axis (a multiple of m_cmp), 0 = unshifted
 };
 
+constexpr int kSortTile = 4096;   // keys per workgroup tile (256 threads x 16)
+constexpr int kRadixBits = 8;
+constexpr int kMaxPasses = 4;     // 8-bit digits of a 32-bit key
+
 struct BuildWorkspace {
   uint32_t* keys_a;      // [N]
   uint32_t* keys_b;      // [N]
   int32_t* vals_b;       // [N]
-  uint32_t* tile_hist;   // [256 * ntiles]
+  // one-sweep sort (small builds; null otherwise)
+  uint32_t* glob_hist;   // [kMaxPasses][256] keys of each digit, per pass
+  int32_t* tile_ctr;     // [kMaxPasses] next tile of each pass
+  uint64_t* tile_state;  // [kMaxPasses][ntiles][256] look-back words
+  // reduce-then-scan passes (large builds; null otherwise)
+  uint32_t* tile_hist;   // [256 * ntiles] plus the scan's chunk sums
   int32_t* tile_cnt;     // [2 * ntiles]
   int32_t* tile_base;    // [2 * ntiles]
 };
-
-constexpr int kSortTile = 4096;   // keys per workgroup tile (256 threads x 16)
-constexpr int kRadixBits = 8;
 
 size_t build_workspace_bytes(int64_t n, int32_t batch);
 void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out);
