@@ -44,6 +44,8 @@
 
 #include <algorithm>
 
+#include <type_traits>
+
 #include "ssa_internal.h"
 
 namespace ssa {
@@ -218,7 +220,10 @@ cmp_dq_mfma_kernel(BwdParams p) {
   load(kt0);
   store(0);
   if (n_kt > 1) load(kt0 + 1);
-  for (int rel = 0; rel < n_kt; ++rel) {
+  // the first and the last tile are the only ones that can hold blocks
+  // outside [j0, j1): they run with the range check, the tiles between
+  // without it
+  auto step = [&](int rel, auto masked) {
     __syncthreads();  // tile rel stored; every wave is done with tile rel - 1
     if (rel + 1 < n_kt) store((rel + 1) & 1);
     if (rel + 2 < n_kt) load(kt0 + rel + 2);
@@ -236,8 +241,11 @@ cmp_dq_mfma_kernel(BwdParams p) {
     float pr[16], pd[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = jb + 8 * (r >> 2) + (r & 3);
-      const float x = (j >= j0 && j < j1) ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2)) : 0.f;
+      float x = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2));
+      if constexpr (decltype(masked)::value) {
+        const int j = jb + 8 * (r >> 2) + (r & 3);
+        if (j < j0 || j >= j1) x = 0.f;
+      }
       pr[r] = x;
       pd[r] = x * dp[r];
       dl += pd[r];
@@ -253,7 +261,10 @@ cmp_dq_mfma_kernel(BwdParams p) {
         ab[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ab[vb], 0, 0, 0);
       }
     }
-  }
+  };
+  step(0, std::true_type{});
+  for (int rel = 1; rel < n_kt - 1; ++rel) step(rel, std::false_type{});
+  if (n_kt > 1) step(n_kt - 1, std::true_type{});
   dl += __shfl_xor(dl, 32);
   if (!valid) return;
   const float gs = bf16_bits_to_f32(static_cast<const uint16_t*>(f.gates)[qrow * 3]) * f.scale;
@@ -644,11 +655,15 @@ win_dq_mfma_kernel(BwdParams p) {
           }
           float pr[16], pd[16];
 #pragma unroll
+          for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2));
+          if (kt + kKeyTile > nk) {   // a partial last tile (uniform branch)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kt + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) pr[r] = 0.f;
+          }
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kt + 8 * (r >> 2) + 4 * half + (r & 3);
-            const float x = key < nk ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2)) : 0.f;
-            pr[r] = x;
-            pd[r] = x * dp[r];
+            pd[r] = pr[r] * dp[r];
             dl += pd[r];
           }
 #pragma unroll
