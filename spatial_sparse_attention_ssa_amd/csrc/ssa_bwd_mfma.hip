@@ -393,12 +393,21 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
       rs = (R >= r_lo && R < r_hi) ? st[R] : make_float4(FLT_MAX, 0.f, 0.f, 0.f);
     }
   };
+  // per slot, three arrays over the tile's rows: -lse2 / c2 and -Delta (the
+  // starting values of the S and dP accumulators, so that they hold
+  // s - lse2 / c2 and dP - Delta) and the gate
+  float* const st_f = reinterpret_cast<float*>(st_lds);
   auto store = [&](int slot) {
     if (stager) {
       *reinterpret_cast<u32x4*>(q_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rq;
       *reinterpret_cast<u32x4*>(d_lds + slot * kRT + r_row * kRRow + 8 * r_c) = rd;
     }
-    if (tid < kKeyTile) st_lds[slot * kKeyTile + tid] = rs;
+    if (tid < kKeyTile) {
+      float* const sf = st_f + slot * 4 * kKeyTile;
+      sf[tid] = -rs.x / c2;
+      sf[kKeyTile + tid] = -rs.y;
+      sf[2 * kKeyTile + tid] = rs.z;
+    }
   };
 
   f32x16 dk[VB], dv[VB];
@@ -421,7 +430,20 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
     const int slot = rt & 1;
     const uint16_t* ql = q_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
     const uint16_t* dl = d_lds + slot * kRT + (lane & 31) * kRRow + 8 * half;
-    f32x16 s = {}, dp = {};
+    // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile, for this key:
+    // rows 8 q + 4 half .. + 3 of each quarter q are one 16-byte read
+    const float* sf = st_f + slot * 4 * kKeyTile + 4 * half;
+    f32x16 s, dp;
+    float gt[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a = *reinterpret_cast<const float4*>(sf + 8 * q);
+      const float4 b = *reinterpret_cast<const float4*>(sf + kKeyTile + 8 * q);
+      const float4 c = *reinterpret_cast<const float4*>(sf + 2 * kKeyTile + 8 * q);
+      s[4 * q] = a.x; s[4 * q + 1] = a.y; s[4 * q + 2] = a.z; s[4 * q + 3] = a.w;
+      dp[4 * q] = b.x; dp[4 * q + 1] = b.y; dp[4 * q + 2] = b.z; dp[4 * q + 3] = b.w;
+      gt[4 * q] = c.x; gt[4 * q + 1] = c.y; gt[4 * q + 2] = c.z; gt[4 * q + 3] = c.w;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ql + 16 * ks), kb[ks], s, 0, 0, 0);
@@ -429,15 +451,13 @@ __device__ __forceinline__ void rows_dkv_body(const BwdParams& p, int g, bool wa
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile, for this key
       float pg[8], ds[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 8 * ks + i;
-        const float4 sr = st_lds[slot * kKeyTile + 8 * (r >> 2) + 4 * half + (r & 3)];
-        const float x = sr.z * __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sr.x));
+        const float x = gt[r] * __builtin_amdgcn_exp2f(s[r] * c2);
         pg[i] = x;
-        ds[i] = x * (dp[r] - sr.y);
+        ds[i] = x * dp[r];
       }
       const bf16x8 pb = pack8(pg);
       const bf16x8 sb = pack8(ds);
