@@ -735,10 +735,11 @@ kv_grad_mfma_kernel(BwdParams p) {
   constexpr int VB = D / 32;
   constexpr int kRowP = D + 8;                 // padded row of a gathered row tile (bf16)
   constexpr int kRT = kKeyTile * kRowP;
-  constexpr int kRed = kKeyTile * D;            // one partial tile (floats)
+  constexpr int kTS = kKeyTile + 8;             // padded token row of a partial tile (floats)
+  constexpr int kRed = D * kTS;                 // one partial tile, [dim][token] (floats)
   __shared__ __align__(16) uint16_t qr_lds[4 * kRT];   // per wave: its 32 gathered Q rows, row-major
   __shared__ __align__(16) uint16_t dr_lds[4 * kRT];   // per wave: dO rows
-  __shared__ float4 st_lds[4 * kKeyTile];              // per wave: log2 lse, Delta, gate per row
+  __shared__ __align__(16) float st_lds[4 * 3 * kKeyTile];   // per wave: -lse2 / c2, -Delta, gate per row
   __shared__ float red_k[kRed];
   __shared__ float red_v[kRed];
 
@@ -757,7 +758,7 @@ kv_grad_mfma_kernel(BwdParams p) {
   const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
   uint16_t* qr = qr_lds + wv * kRT;
   uint16_t* dr = dr_lds + wv * kRT;
-  float4* st = st_lds + wv * kKeyTile;
+  float* st = st_lds + wv * 3 * kKeyTile;
   const int n_units = f.counts[SSA_COUNT_NB];
   const int64_t n_items = static_cast<int64_t>(n_units) * f.h_kv;
 
@@ -771,11 +772,6 @@ kv_grad_mfma_kernel(BwdParams p) {
     const int bnd = f.blk_off[u + 1];
     if (R == 0) continue;
     const int n_rt = (R + kKeyTile - 1) / kKeyTile;
-    // (query, head) of row rr of this item
-    auto row_of = [&](int rr) -> int64_t {
-      const int t = p.sel_list[e0 + rr / G];
-      return static_cast<int64_t>(t) * f.h_q + g * G + rr % G;
-    };
     for (int k0 = a; k0 < bnd; k0 += kKeyTile) {
       // B operands: the lane's key / value token of this tile
       const int i = k0 + (lane & 31);
@@ -800,53 +796,84 @@ kv_grad_mfma_kernel(BwdParams p) {
         dk[x] = f32x16{};
         dv[x] = f32x16{};
       }
-      // rows of tile rt: this lane loads row 32 rt + lane % 32 (its 16 dims
-      // per k step and lane half), prefetched one tile ahead
+      // rows of tile rt, prefetched one tile ahead: a row is CPR 16-byte
+      // chunks, and load j of a lane moves chunk lane % CPR of row
+      // j RPI + lane / CPR (so one load instruction covers RPI whole rows);
+      // the row state is loaded by lanes 0..31, one row each
+      constexpr int CPR = D / 8;
+      constexpr int RPI = 64 / CPR;
       u32x4 nq[KS], nd[KS];
-      float4 ns = make_float4(FLT_MAX, 0.f, 0.f, 0.f);
+      // the row state: -lse2 / c2 and -Delta (the starting values of the S
+      // and dP accumulators, so that they hold s - lse2 / c2 and dP - Delta)
+      // and the gate
+      float3 ns = make_float3(-FLT_MAX, 0.f, 0.f);
       auto load = [&](int rt) {
-        const int rr = rt * kKeyTile + (lane & 31);
+        const int r0 = rt * kKeyTile;
+        const int rr = r0 + (lane & 31);
+        int t = 0;
+        ns = make_float3(-FLT_MAX, 0.f, 0.f);   // a missing row has P = 0
+        if (half == 0 && rr < R) {
+          t = p.sel_list[e0 + rr / G];
+          const int64_t qrow = static_cast<int64_t>(t) * f.h_q + g * G + rr % G;
+          ns = make_float3(-(lse[qrow] * kLog2e) / c2, -dlt[qrow], bf16_bits_to_f32(gates[qrow * 3 + kSelBranch]));
+        }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) nq[ks] = nd[ks] = u32x4{0u, 0u, 0u, 0u};
-        ns = make_float4(FLT_MAX, 0.f, 0.f, 0.f);   // a missing row has P = 0
-        if (rr < R) {
-          const int64_t qrow = row_of(rr);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            nq[ks] = *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * ks + 8 * half);
-            nd[ks] = *reinterpret_cast<const u32x4*>(dO + qrow * D + 16 * ks + 8 * half);
+        for (int j = 0; j < KS; ++j) {
+          const int row = j * RPI + lane / CPR;
+          const int tj = __shfl(t, row);
+          nq[j] = nd[j] = u32x4{0u, 0u, 0u, 0u};
+          if (r0 + row < R) {
+            const int64_t qrow = static_cast<int64_t>(tj) * f.h_q + g * G + (r0 + row) % G;
+            nq[j] = *reinterpret_cast<const u32x4*>(Q + qrow * D + 8 * (lane % CPR));
+            nd[j] = *reinterpret_cast<const u32x4*>(dO + qrow * D + 8 * (lane % CPR));
           }
-          ns = make_float4(lse[qrow] * kLog2e, dlt[qrow], bf16_bits_to_f32(gates[qrow * 3 + kSelBranch]), 0.f);
         }
       };
       if (wv < n_rt) load(wv);
       for (int rt = wv; rt < n_rt; rt += 4) {
         // the rows (row-major, 16-byte stores) and the row statistics,
-        // wave-private; the transposed operands are read back below
+        // wave-private; the operands, plain and transposed, are read back
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          *reinterpret_cast<u32x4*>(qr + (lane & 31) * kRowP + 16 * ks + 8 * half) = nq[ks];
-          *reinterpret_cast<u32x4*>(dr + (lane & 31) * kRowP + 16 * ks + 8 * half) = nd[ks];
+        for (int j = 0; j < KS; ++j) {
+          const int row = j * RPI + lane / CPR;
+          *reinterpret_cast<u32x4*>(qr + row * kRowP + 8 * (lane % CPR)) = nq[j];
+          *reinterpret_cast<u32x4*>(dr + row * kRowP + 8 * (lane % CPR)) = nd[j];
         }
-        if (half == 0) st[lane] = ns;
+        if (half == 0) {
+          st[lane] = ns.x;
+          st[kKeyTile + lane] = ns.y;
+          st[2 * kKeyTile + lane] = ns.z;
+        }
         wave_lds_sync();
-        f32x16 s = {}, dp = {};
+        // entry r is row 8 (r / 4) + 4 half + r % 4 of the tile: rows
+        // 8 q + 4 half .. + 3 of each quarter q are one 16-byte read
+        f32x16 s, dp;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 a = *reinterpret_cast<const float4*>(st + 8 * q + 4 * half);
+          const float4 b = *reinterpret_cast<const float4*>(st + kKeyTile + 8 * q + 4 * half);
+          s[4 * q] = a.x; s[4 * q + 1] = a.y; s[4 * q + 2] = a.z; s[4 * q + 3] = a.w;
+          dp[4 * q] = b.x; dp[4 * q + 1] = b.y; dp[4 * q + 2] = b.z; dp[4 * q + 3] = b.w;
+        }
+        const uint16_t* ql = qr + (lane & 31) * kRowP + 8 * half;
+        const uint16_t* dl = dr + (lane & 31) * kRowP + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, nq[ks]), kb[ks], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, nd[ks]), vb[ks], dp, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ql + 16 * ks), kb[ks], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dl + 16 * ks), vb[ks], dp, 0, 0, 0);
         }
         if (rt + 4 < n_rt) load(rt + 4);   // in flight during the rest of this tile
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          float pg[8], ds[8];
+          float pg[8], ds[8], gt[8];
+          *reinterpret_cast<float4*>(gt) = *reinterpret_cast<const float4*>(st + 2 * kKeyTile + 16 * ks + 4 * half);
+          *reinterpret_cast<float4*>(gt + 4) = *reinterpret_cast<const float4*>(st + 2 * kKeyTile + 16 * ks + 8 + 4 * half);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int r = 8 * ks + i;
-            const float4 sr = st[8 * (r >> 2) + 4 * half + (r & 3)];
-            const float x = sr.z * __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sr.x));
+            const float x = gt[i] * __builtin_amdgcn_exp2f(s[r] * c2);
             pg[i] = x;
-            ds[i] = x * (dp[r] - sr.y);
+            ds[i] = x * dp[r];
           }
           const bf16x8 pb = pack8(pg);
           const bf16x8 sb = pack8(ds);
@@ -858,8 +885,10 @@ kv_grad_mfma_kernel(BwdParams p) {
         }
         wave_lds_sync();  // the wave-private area is rewritten by the next row tile
       }
-      // sum the four waves' partial tiles, [token][dim], in wave order
-      // (a fixed order keeps the result identical from run to run)
+      // sum the four waves' partial tiles, [dim][token], in wave order (a
+      // fixed order keeps the result identical from run to run); a lane
+      // half's 32 tokens are 32 consecutive banks and the two halves' rows
+      // (4 dims apart, 4 kTS = 32 mod 64 floats) the other 32
       for (int w = 0; w < 4; ++w) {
         __syncthreads();
         if (wv == w) {
@@ -867,7 +896,7 @@ kv_grad_mfma_kernel(BwdParams p) {
           for (int x = 0; x < VB; ++x)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int e = (lane & 31) * D + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+              const int e = (32 * x + 8 * (r >> 2) + 4 * half + (r & 3)) * kTS + (lane & 31);
               red_k[e] = w == 0 ? dk[x][r] : red_k[e] + dk[x][r];
               red_v[e] = w == 0 ? dv[x][r] : red_v[e] + dv[x][r];
             }
@@ -879,10 +908,10 @@ kv_grad_mfma_kernel(BwdParams p) {
       for (int e = tid; e < n_tok * (D / 4); e += 256) {
         const int tok = e / (D / 4), d = 4 * (e % (D / 4));
         const int64_t o = (static_cast<int64_t>(g) * f.n + k0 + tok) * D + d;
-        float4 rk = make_float4(f.scale * red_k[tok * D + d], f.scale * red_k[tok * D + d + 1],
-                                f.scale * red_k[tok * D + d + 2], f.scale * red_k[tok * D + d + 3]);
-        float4 rv = make_float4(red_v[tok * D + d], red_v[tok * D + d + 1], red_v[tok * D + d + 2],
-                                red_v[tok * D + d + 3]);
+        const float* pk = red_k + d * kTS + tok;
+        const float* pv = red_v + d * kTS + tok;
+        float4 rk = make_float4(f.scale * pk[0], f.scale * pk[kTS], f.scale * pk[2 * kTS], f.scale * pk[3 * kTS]);
+        float4 rv = make_float4(pv[0], pv[kTS], pv[2 * kTS], pv[3 * kTS]);
         const float4 ck = *reinterpret_cast<const float4*>(p.dk_acc + o);
         const float4 cv = *reinterpret_cast<const float4*>(p.dv_acc + o);
         rk.x += ck.x; rk.y += ck.y; rk.z += ck.z; rk.w += ck.w;
