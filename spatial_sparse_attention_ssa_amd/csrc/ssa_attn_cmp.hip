@@ -79,6 +79,11 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// maxima of logits that are never NaN: v_maximum3_f32 needs no
+// canonicalising of MFMA results first (fmaxf does)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -437,9 +442,8 @@ cmp_mfma_kernel(FwdParams p) {
     if (decltype(masked)::value) mask(rel, B.s);
     const f32x16& s = B.s;
     if (glog >= 16) {
-      float m = fmaxf(B.g, fmaxf(s[0], s[1]));
-#pragma unroll
-      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+      const float m = vmax3(vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax3(s[6], s[7], s[8])),
+                            vmax3(s[9], s[10], s[11]), vmax3(vmax3(s[12], s[13], s[14]), s[15], B.g));
       if (glog == 16 || (rel & 1)) {
         list_insert(B, m);
         B.g = -FLT_MAX;
@@ -449,15 +453,13 @@ cmp_mfma_kernel(FwdParams p) {
     } else if (glog == 8) {
 #pragma unroll
       for (int q8 = 0; q8 < 2; ++q8) {
-        float m = fmaxf(s[8 * q8], s[8 * q8 + 1]);
-#pragma unroll
-        for (int r = 2; r < 8; r += 2) m = fmaxf(m, fmaxf(s[8 * q8 + r], s[8 * q8 + r + 1]));
-        list_insert(B, m);
+        const int o = 8 * q8;
+        list_insert(B, vmax3(vmax3(s[o], s[o + 1], s[o + 2]), vmax3(s[o + 3], s[o + 4], s[o + 5]), vmax(s[o + 6], s[o + 7])));
       }
     } else {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        list_insert(B, fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3])));
+        list_insert(B, vmax3(vmax(s[4 * q4], s[4 * q4 + 1]), s[4 * q4 + 2], s[4 * q4 + 3]));
     }
   };
   {

@@ -60,6 +60,14 @@ constexpr float kFixedBound = 60.f;
 template <bool B>
 using kBool = std::integral_constant<bool, B>;
 
+// maximum of 8 values that are never NaN: v_maximum3_f32 needs no
+// canonicalising of MFMA results first (fmaxf does)
+__device__ __forceinline__ float max8(const float* v) {
+  const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
+  const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[3], v[4]), v[5]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), __builtin_elementwise_maximum(v[6], v[7]));
+}
+
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -657,13 +665,16 @@ gqa_topk_kernel(FwdParams p) {
     const int j = (kt0 + rel) * kKeyTile + l32;
     const bool jok = j >= j0 && j < j1;
     const uint32_t below = (1u << l32) - 1u;
+    // both row blocks' MFMAs first: block 1's run beside block 0's filter
+    f32x16 yx[2];
+    yx[0] = shifted(0, kb);
+    yx[1] = shifted(1, kb);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      const f32x16 y = shifted(x, kb);
-      float m0 = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-      m0 = fmaxf(m0, fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-      float m1 = fmaxf(fmaxf(y[8], y[9]), fmaxf(y[10], y[11]));
-      m1 = fmaxf(m1, fmaxf(fmaxf(y[12], y[13]), fmaxf(y[14], y[15])));
+      float y[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) y[r] = yx[x][r];
+      const float m0 = max8(y), m1 = max8(y + 8);
       // the pair in lanes l and l + 32 passes when either half's maximum
       // does: the two halves of the ballot, or-ed
       const uint64_t v0 = __ballot(jok && m0 >= theta[2 * x]);
