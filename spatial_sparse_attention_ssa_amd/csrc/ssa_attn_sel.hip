@@ -29,6 +29,7 @@ namespace ssa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDL = 16;      // dims per lane
@@ -50,6 +51,14 @@ __device__ __forceinline__ void load16(const uint16_t* p, float (&x)[kDL]) {
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
+// two packed bf16 values times two others, plus c (v_dot2_f32_bf16: the
+// products are exact, the sum is float32); the words go through scalars
+// because this compiler's __builtin_bit_cast of a vector element reads
+// element 0
+__device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), c, false);
+}
+
 // 16 bf16 values of a row, packed
 struct Row16 {
   u32x4 a, b;
@@ -57,14 +66,14 @@ struct Row16 {
     a = *reinterpret_cast<const u32x4*>(p);
     b = *reinterpret_cast<const u32x4*>(p + 8);
   }
-  __device__ __forceinline__ float dot(const float (&q)[kDL]) const {
+  // the row times 16 packed bf16 query values
+  __device__ __forceinline__ float dot(const Row16& q) const {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s0 = fmaf(q[2 * e], bf_lo(a[e]), s0);
-      s1 = fmaf(q[2 * e + 1], bf_hi(a[e]), s1);
-      s0 = fmaf(q[8 + 2 * e], bf_lo(b[e]), s0);
-      s1 = fmaf(q[8 + 2 * e + 1], bf_hi(b[e]), s1);
+      const uint32_t ae = a[e], be = b[e], qa = q.a[e], qb = q.b[e];
+      s0 = dot2(ae, qa, s0);
+      s1 = dot2(be, qb, s1);
     }
     return s0 + s1;
   }
@@ -94,7 +103,7 @@ struct SelState {
   __device__ __forceinline__ void add(const float (&s2)[U], const Row16 (&v)[U]) {
     float mx = m;
 #pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, s2[u]);
+    for (int u = 0; u < U; ++u) mx = __builtin_elementwise_maximum(mx, s2[u]);
     if (mx > m) {
       const float corr = __builtin_amdgcn_exp2f(m - mx);
       l *= corr;
@@ -111,11 +120,13 @@ struct SelState {
   }
 };
 
-// sum over the LP lanes of a pair
+// sum over the LP (2 or 4) lanes of a pair: DPP quad permutations (lane
+// xor 1, then xor 2), no LDS round trip
 template <int LP>
 __device__ __forceinline__ float pair_sum(float s) {
-#pragma unroll
-  for (int o = 1; o < LP; o <<= 1) s += __shfl_xor(s, o);
+  static_assert(LP == 2 || LP == 4, "pairs of 2 or 4 lanes");
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  if (LP == 4) s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
   return s;
 }
 
@@ -142,8 +153,8 @@ sel_combine_kernel(FwdParams p) {
 
   const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(g) * p.n * kD + kDL * sub;
   const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(g) * p.n * kD + kDL * sub;
-  float q[kDL];
-  load16(static_cast<const uint16_t*>(p.q) + (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub, q);
+  Row16 q;
+  q.load(static_cast<const uint16_t*>(p.q) + (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub);
   const int32_t* sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
 
   // ---------------- the selected blocks' row ranges, all loads in flight at once
