@@ -57,6 +57,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kD = 64;
@@ -720,30 +721,28 @@ cmp_mfma_kernel(FwdParams p) {
     // exact float32 logits of this lane's candidates into the high key words
     const int mine0 = qbase + (half ? kCap + 1 - cnt : 1);
     if (B.valid && !overflow && cnt > 0) {
-      float qf[kD];
+      // products of bf16 pairs are exact in float32 (v_dot2_f32_bf16); four
+      // partial sums keep the dependent chains short
+      u32x4 qw[kD / 8];
 #pragma unroll
-      for (int c = 0; c < kD / 8; ++c) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(B.q_row + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qf[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
-          qf[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-        }
-      }
+      for (int c = 0; c < kD / 8; ++c) qw[c] = *reinterpret_cast<const u32x4*>(B.q_row + 8 * c);
       for (int i = 0; i < cnt; ++i) {
         uint32_t* const slot = reinterpret_cast<uint32_t*>(cand_key + mine0 + i);
         const uint16_t* kr = kb0 + static_cast<int64_t>(~slot[0]) * kD;
-        float sc = 0.f;
+        float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kD / 8; ++c) {
           const u32x4 u = *reinterpret_cast<const u32x4*>(kr + 8 * c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sc = fmaf(qf[8 * c + 2 * e], __uint_as_float(u[e] << 16), sc);
-            sc = fmaf(qf[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), sc);
+            // (words through scalars: this compiler's __builtin_bit_cast of
+            // a vector element reads element 0)
+            const uint32_t ke = u[e], qe = qw[c][e];
+            sp[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ke), __builtin_bit_cast(bf16x2, qe),
+                                                    sp[e], false);
           }
         }
-        slot[1] = ordered_bits(sc);
+        slot[1] = ordered_bits((sp[0] + sp[1]) + (sp[2] + sp[3]));
       }
     }
     wave_lds_sync();

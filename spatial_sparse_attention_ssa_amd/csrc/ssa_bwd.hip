@@ -86,12 +86,53 @@ __device__ __forceinline__ float dot16(const float (&a)[kDL], const float (&b)[k
   return s0 + s1;
 }
 
-// sum over the LP lanes of a row
+// sum over the LP lanes of a row (the row's lanes share their control
+// flow): DPP quad permutations for LP 2 and 4, no LDS round trip
 template <int LP>
 __device__ __forceinline__ float row_sum(float s) {
+  if (LP == 2 || LP == 4) {
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    if (LP == 4) s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+    return s;
+  }
 #pragma unroll
   for (int o = 1; o < LP; o <<= 1) s += __shfl_xor(s, o);
   return s;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 16 packed bf16 values (two 16-byte words) times 16 others: v_dot2_f32_bf16
+// (exact products, float32 sums) on the raw words
+__device__ __forceinline__ float dot16_bf16(const uint4 (&a)[2], const uint4 (&b)[2]) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t x[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
+    const uint32_t y[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[e]), __builtin_bit_cast(bf16x2, y[e]), s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[e + 1]), __builtin_bit_cast(bf16x2, y[e + 1]), s1,
+                                           false);
+    }
+  }
+  return s0 + s1;
+}
+__device__ __forceinline__ void load_raw16(const uint16_t* p, uint4 (&w)[2]) {
+  w[0] = reinterpret_cast<const uint4*>(p)[0];
+  w[1] = reinterpret_cast<const uint4*>(p)[1];
+}
+__device__ __forceinline__ void widen16(const uint4 (&w)[2], float (&x)[kDL]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t u[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
+      x[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  }
 }
 
 __device__ __forceinline__ int seq_of_window(const int32_t* seq_win_off, int batch, int w) {
@@ -477,9 +518,17 @@ sel_dq_kernel(BwdParams p) {
   const int64_t qrow = static_cast<int64_t>(t) * f.h_q + h;
   const float c2 = f.scale * kLog2e;
   const float l2 = active ? p.lse[nrow + qrow] * kLog2e : 0.f;
+  // bf16 rows stay packed for the dot products (v_dot2); float rows widen
+  constexpr bool kBf16 = sizeof(T) == 2;
   float q[kDL], d[kDL], aa[kDL], ab[kDL];
-  load16(static_cast<const T*>(f.q) + qrow * D + kDL * sub, q);
-  load16(static_cast<const T*>(p.dout) + qrow * D + kDL * sub, d);
+  uint4 qw[2], dw[2];
+  if constexpr (kBf16) {
+    load_raw16(reinterpret_cast<const uint16_t*>(f.q) + qrow * D + kDL * sub, qw);
+    load_raw16(reinterpret_cast<const uint16_t*>(p.dout) + qrow * D + kDL * sub, dw);
+  } else {
+    load16(static_cast<const T*>(f.q) + qrow * D + kDL * sub, q);
+    load16(static_cast<const T*>(p.dout) + qrow * D + kDL * sub, d);
+  }
 #pragma unroll
   for (int e = 0; e < kDL; ++e) aa[e] = ab[e] = 0.f;
   float dl = 0.f;
@@ -511,11 +560,22 @@ sel_dq_kernel(BwdParams p) {
   wave_lds_sync();
 
   auto visit = [&](int64_t i) {
-    float kr[kDL], vr[kDL];
-    load16(KS + i * D, kr);
-    load16(VS + i * D, vr);
-    const float s = row_sum<LP>(dot16(q, kr));
-    const float dp = row_sum<LP>(dot16(d, vr));
+    float kr[kDL];
+    float s, dp;
+    if constexpr (kBf16) {
+      uint4 kw[2], vw[2];
+      load_raw16(reinterpret_cast<const uint16_t*>(KS) + i * D, kw);
+      load_raw16(reinterpret_cast<const uint16_t*>(VS) + i * D, vw);
+      s = row_sum<LP>(dot16_bf16(qw, kw));
+      dp = row_sum<LP>(dot16_bf16(dw, vw));
+      widen16(kw, kr);
+    } else {
+      float vr[kDL];
+      load16(KS + i * D, kr);
+      load16(VS + i * D, vr);
+      s = row_sum<LP>(dot16(q, kr));
+      dp = row_sum<LP>(dot16(d, vr));
+    }
     const float pr = exp2f(fmaf(s, c2, -l2));
     const float pd = pr * dp;
     dl += pd;
