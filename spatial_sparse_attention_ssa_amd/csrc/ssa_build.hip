@@ -27,13 +27,18 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
-// counts, and the one-sweep sort's digit totals and tile counters
-__global__ void init_counts_kernel(int32_t* counts, int32_t key_bits, uint32_t* glob_hist, int32_t* tile_ctr) {
+// counts, the one-sweep sort's digit totals and tile counters, and the
+// segment pass's tile counter and look-back words
+__global__ void init_counts_kernel(int32_t* counts, int32_t key_bits, uint32_t* glob_hist, int32_t* tile_ctr,
+                                   int32_t* seg_ctr, uint64_t* seg_state, int32_t seg_tiles) {
   const int i = threadIdx.x;
   if (i < SSA_COUNTS) counts[i] = (i == SSA_COUNT_KEY_BITS) ? key_bits : 0;
   if (glob_hist)
     for (int j = i; j < kMaxPasses * 256; j += blockDim.x) glob_hist[j] = 0u;
   if (tile_ctr && i < kMaxPasses) tile_ctr[i] = 0;
+  if (seg_ctr && i == 0) *seg_ctr = 0;
+  if (seg_state)
+    for (int j = i; j < seg_tiles; j += blockDim.x) seg_state[j] = 0ull;
 }
 
 // Offsets for an empty token set: every offset array holds zeros.
@@ -649,6 +654,159 @@ __device__ __forceinline__ int seq_of(uint32_t key, int seq_shift) {
   return seq_shift < 0 ? 0 : static_cast<int>(key >> seq_shift);
 }
 
+// Segment look-back word of a tile: flag (1 = the tile's own counts, 2 = the
+// counts of every tile up to and including it) in bits 62-63, block starts in
+// bits 31-61, window starts in bits 0-30.
+__device__ __forceinline__ uint64_t seg_word(uint64_t flag, uint32_t nb, uint32_t nw) {
+  return (flag << 62) | (static_cast<uint64_t>(nb) << 31) | nw;
+}
+
+// CSR offsets from the sorted keys in one pass.  Tiles are taken in order
+// from a counter; each counts its block and window starts (a key differs from
+// the one before it; a window start also in the window bits), publishes the
+// counts, finds the counts of all earlier tiles by a look-back over their
+// words (wave 0, 64 words per round, bounded spin), publishes its inclusive
+// counts and writes its starts: blk_off, win_off, win_blk_off and the
+// sequences' first block and window.  The tile holding the last token writes
+// the totals and the closing entries.
+template <int ITEMS>
+__global__ void __launch_bounds__(256)
+seg_onesweep(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_shift, int seq_shift,
+             int32_t* __restrict__ seg_ctr, uint64_t* __restrict__ seg_state, int32_t* __restrict__ counts,
+             int32_t* __restrict__ blk_off, int32_t* __restrict__ win_off, int32_t* __restrict__ win_blk_off,
+             int32_t* __restrict__ seq_blk_off, int32_t* __restrict__ seq_win_off) {
+  __shared__ int32_t wcnt[2][4];
+  __shared__ int32_t s_pre[2];
+  __shared__ int s_tile;
+  if (threadIdx.x == 0) s_tile = atomicAdd(seg_ctr, 1);
+  __syncthreads();
+  const int tile = s_tile;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int base = tile * 256 * ITEMS + wave * (64 * ITEMS);
+  const uint64_t lt = lanemask_lt();
+  int rb = 0, rw = 0;
+  int rank_b[ITEMS], rank_w[ITEMS];
+  static_assert(2 * ITEMS <= 32, "two boundary flags per row are packed into 32 bits");
+  uint32_t flags = 0;
+  uint32_t kc[ITEMS], kprev[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {   // all loads in flight before the ballots
+    const int p = base + r * kWave + lane;
+    kc[r] = p < n ? keys[p] : 0u;
+    kprev[r] = (p < n && p > 0) ? keys[p - 1] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int p = base + r * kWave + lane;
+    const bool valid = p < n;
+    bool isb = false, isw = false;
+    if (valid) {
+      if (p == 0) {
+        isb = isw = true;
+      } else {
+        isb = kc[r] != kprev[r];
+        isw = (kc[r] >> win_shift) != (kprev[r] >> win_shift);
+      }
+    }
+    const uint64_t mb = __ballot(isb), mw = __ballot(isw);
+    rank_b[r] = rb + static_cast<int>(__popcll(mb & lt));
+    rank_w[r] = rw + static_cast<int>(__popcll(mw & lt));
+    rb += static_cast<int>(__popcll(mb));
+    rw += static_cast<int>(__popcll(mw));
+    flags |= (isb ? 1u : 0u) << (2 * r);
+    flags |= (isw ? 1u : 0u) << (2 * r + 1);
+  }
+  if (lane == 0) {
+    wcnt[0][wave] = rb;
+    wcnt[1][wave] = rw;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // wave 0 looks back 64 tiles per round: lane k reads the word of tile
+    // j - k; the run of published words from lane 0 up to the first
+    // inclusive one (done) or up to the first unpublished one (the next
+    // round starts there) is summed
+    const uint32_t tb = wcnt[0][0] + wcnt[0][1] + wcnt[0][2] + wcnt[0][3];
+    const uint32_t tw = wcnt[1][0] + wcnt[1][1] + wcnt[1][2] + wcnt[1][3];
+    if (lane == 0)
+      __hip_atomic_store(seg_state + tile, seg_word(1, tb, tw), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t pb = 0, pw = 0;
+    int j = tile - 1, stall = 0;
+    while (j >= 0) {
+      const int idx = j - lane;
+      const uint64_t w = idx >= 0 ? __hip_atomic_load(seg_state + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : seg_word(2, 0, 0);   // before tile 0: inclusive counts of zero
+      const uint32_t f = static_cast<uint32_t>(w >> 62);
+      const uint64_t unpub = __ballot(f == 0), incl = __ballot(f == 2);
+      const int z = unpub ? __builtin_ctzll(unpub) : 64;
+      const int c = incl ? __builtin_ctzll(incl) : 64;
+      const bool done = c < z;
+      const int take = done ? c + 1 : z;   // lanes 0 .. take - 1
+      uint32_t ab = lane < take ? (static_cast<uint32_t>(w >> 31) & 0x7FFFFFFFu) : 0u;
+      uint32_t aw = lane < take ? (static_cast<uint32_t>(w) & 0x7FFFFFFFu) : 0u;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        ab += __shfl_xor(ab, o);
+        aw += __shfl_xor(aw, o);
+      }
+      pb += ab;
+      pw += aw;
+      if (done) break;
+      j -= take;
+      if (take == 0) {
+        if (++stall > kSpinMax) break;   // gave up: the offsets are wrong but stay in bounds
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (lane == 0) {
+      __hip_atomic_store(seg_state + tile, seg_word(2, pb + tb, pw + tw), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      s_pre[0] = static_cast<int32_t>(pb);
+      s_pre[1] = static_cast<int32_t>(pw);
+    }
+  }
+  __syncthreads();
+  int pb = s_pre[0], pw = s_pre[1];
+  const int nb_tot = pb + wcnt[0][0] + wcnt[0][1] + wcnt[0][2] + wcnt[0][3];   // used by the last tile only
+  const int nw_tot = pw + wcnt[1][0] + wcnt[1][1] + wcnt[1][2] + wcnt[1][3];
+  for (int w = 0; w < wave; ++w) {
+    pb += wcnt[0][w];
+    pw += wcnt[1][w];
+  }
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int p = base + r * kWave + lane;
+    if (p >= n) continue;
+    const bool isb = (flags >> (2 * r)) & 1u, isw = (flags >> (2 * r + 1)) & 1u;
+    const int bid = pb + rank_b[r];
+    if (isb) blk_off[bid] = p;
+    if (isw) {
+      const int wid = pw + rank_w[r];
+      win_off[wid] = p;
+      win_blk_off[wid] = bid;
+      const int s = seq_of(kc[r], seq_shift);
+      const int sp = p ? seq_of(kprev[r], seq_shift) : -1;
+      for (int b = sp + 1; b <= s; ++b) {
+        seq_blk_off[b] = bid;
+        seq_win_off[b] = wid;
+      }
+    }
+    if (p == n - 1) {
+      const int s = seq_of(kc[r], seq_shift);
+      for (int b = s + 1; b <= batch; ++b) {
+        seq_blk_off[b] = nb_tot;
+        seq_win_off[b] = nw_tot;
+      }
+      blk_off[nb_tot] = n;
+      win_off[nw_tot] = n;
+      win_blk_off[nw_tot] = nb_tot;
+      counts[SSA_COUNT_NB] = nb_tot;
+      counts[SSA_COUNT_NW] = nw_tot;
+    }
+  }
+}
+
 template <int ITEMS>
 __global__ void __launch_bounds__(256)
 seg_write(const uint32_t* __restrict__ keys, int32_t n, int32_t batch, int win_shift,
@@ -787,6 +945,11 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // measured on MI355X, one-sweep 61 / 76 / 106 / 578 us against 74 / 88 / 96 /
 // 466 us at 2^17 / 2^18 / 2^19 / 2^24 random voxel tokens.
 bool build_onesweep(int64_t n) { return n <= (int64_t(1) << 18); }
+// The segment pass is one look-back kernel up to 2^21 tokens; above, the
+// count / scan / write kernels, whose tiles wait on no other tile, are faster
+// (measured on MI355X: 57 / 98 / 188 / 497 us against 60 / 101 / 178 / 470 us
+// for the whole build at 2^17 / 2^20 / 2^22 / 2^24 random voxel tokens).
+bool seg_onesweep_path(int64_t n) { return n <= (int64_t(1) << 21); }
 int build_items(int64_t n) { return build_onesweep(n) ? 4 : kItems; }
 int64_t build_tiles(int64_t n) {
   const int64_t tile = 256 * build_items(n);
@@ -805,7 +968,12 @@ size_t build_workspace_bytes(int64_t n, int32_t /*batch*/) {
   } else {
     b += align256(sort_pairs_hist_bytes(n));   // tile histograms and their scan's chunk sums
   }
-  b += 2 * align256(sizeof(int32_t) * 2 * ntiles);
+  if (seg_onesweep_path(n)) {
+    b += align256(sizeof(uint64_t) * (ntiles > 0 ? ntiles : 1));   // segment look-back words
+    b += align256(sizeof(int32_t));                                  // segment tile counter
+  } else {
+    b += 2 * align256(sizeof(int32_t) * 2 * ntiles);                 // tile counts and bases
+  }
   return b + 256;
 }
 
@@ -827,8 +995,17 @@ void carve_build_workspace(void* ws, int64_t n, BuildWorkspace* out) {
   } else {
     out->tile_hist = reinterpret_cast<uint32_t*>(p); p += align256(sort_pairs_hist_bytes(n));
   }
-  out->tile_cnt = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * 2 * ntiles);
-  out->tile_base = reinterpret_cast<int32_t*>(p);
+  out->seg_state = nullptr;
+  out->seg_ctr = nullptr;
+  out->tile_cnt = nullptr;
+  out->tile_base = nullptr;
+  if (seg_onesweep_path(n)) {
+    out->seg_state = reinterpret_cast<uint64_t*>(p); p += align256(sizeof(uint64_t) * (ntiles > 0 ? ntiles : 1));
+    out->seg_ctr = reinterpret_cast<int32_t*>(p);
+  } else {
+    out->tile_cnt = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * 2 * ntiles);
+    out->tile_base = reinterpret_cast<int32_t*>(p);
+  }
 }
 
 bool sort_pairs_lands_in_tmp(int key_bits) {
@@ -939,11 +1116,17 @@ void build_segments(int32_t n, int32_t batch, const KeyLayout& kl, const ssa_blo
   const int ntiles = static_cast<int>(build_tiles(n));
   const int win_shift = 3 * kl.l_r;
   const int seq_shift = kl.seq_bits ? 3 * (kl.l_rw + kl.l_r) : -1;
-  seg_count<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, win_shift, ws.tile_cnt);
-  seg_scan<<<1, 1024, 0, stream>>>(ws.tile_cnt, ntiles, ws.tile_base, out.counts);
-  seg_write<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
-                                               out.counts, out.blk_off, out.win_off, out.win_blk_off,
-                                               out.seq_blk_off, out.seq_win_off);
+  if (seg_onesweep_path(n)) {
+    seg_onesweep<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.seg_ctr,
+                                                     ws.seg_state, out.counts, out.blk_off, out.win_off,
+                                                     out.win_blk_off, out.seq_blk_off, out.seq_win_off);
+  } else {
+    seg_count<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, win_shift, ws.tile_cnt);
+    seg_scan<<<1, 1024, 0, stream>>>(ws.tile_cnt, ntiles, ws.tile_base, out.counts);
+    seg_write<ITEMS><<<ntiles, 256, 0, stream>>>(ws.keys_a, n, batch, win_shift, seq_shift, ws.tile_base,
+                                                 out.counts, out.blk_off, out.win_off, out.win_blk_off,
+                                                 out.seq_blk_off, out.seq_win_off);
+  }
   // one workgroup per 4096 tokens, at least 64 and at most 1024 (two atomics each)
   const int sgrid = max(64, min((n + 4095) / 4096, 1024));
   seg_stats<<<sgrid, 256, 0, stream>>>(out.blk_off, out.win_off, out.counts);
@@ -955,7 +1138,9 @@ hipError_t launch_build(const int32_t* coords, const int32_t* cu_seqlens, int32_
                         const KeyLayout& kl, const ssa_blocks& out, const BuildWorkspace& ws,
                         hipStream_t stream) {
   init_counts_kernel<<<1, 256, 0, stream>>>(out.counts, kl.key_bits, n > 0 ? ws.glob_hist : nullptr,
-                                            n > 0 ? ws.tile_ctr : nullptr);
+                                            n > 0 ? ws.tile_ctr : nullptr, n > 0 ? ws.seg_ctr : nullptr,
+                                            n > 0 ? ws.seg_state : nullptr,
+                                            ws.seg_state ? static_cast<int32_t>(build_tiles(n)) : 0);
   if (n == 0) {
     empty_offsets_kernel<<<(batch + 1 + 255) / 256, 256, 0, stream>>>(
         batch, out.blk_off, out.win_off, out.win_blk_off, out.seq_blk_off, out.seq_win_off);

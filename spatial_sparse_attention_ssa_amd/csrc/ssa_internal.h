@@ -124,6 +124,10 @@ struct BuildWorkspace {
   uint64_t* tile_state;  // [kMaxPasses][ntiles][256] look-back words
   // reduce-then-scan passes (large builds; null otherwise)
   uint32_t* tile_hist;   // [256 * ntiles] plus the scan's chunk sums
+  // segment pass: one look-back kernel (smaller builds) or count / scan /
+  // write kernels (larger builds); the other path's pointers are null
+  uint64_t* seg_state;   // [ntiles] look-back words
+  int32_t* seg_ctr;      // next tile
   int32_t* tile_cnt;     // [2 * ntiles]
   int32_t* tile_base;    // [2 * ntiles]
 };
