@@ -72,6 +72,12 @@ __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// the larger of v in lane l and lane l ^ 32 (v_permlane32_swap, no LDS)
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // lane l and lane l ^ 32 exchange v (v_permlane32_swap, no LDS); the two
 // results are v of both lanes, so their sum is the same on both lanes of a
 // pair
@@ -458,20 +464,24 @@ gqa_topk_kernel(FwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kb[ks] = lds_b128(src + 16 * ks);
     };
-    // two register sets used in turn (the loop is unrolled by two, so no
+    // three register sets used in turn (the loop is unrolled by three, so no
     // register is copied while its load is in flight): each set is reloaded
-    // right after its step and has two steps to arrive
-    bf16x8 ba[KS], bb[KS];
+    // right after its step and has the next two steps to arrive
+    bf16x8 ba[KS], bb[KS], bc[KS];
     load(0, ba);
     load(min(1, n_t - 1), bb);
+    load(min(2, n_t - 1), bc);
     int rel = 0;
-    for (; rel + 1 < n_t; rel += 2) {
+    for (; rel + 2 < n_t; rel += 3) {
       body(rel, ba);
-      load(min(rel + 2, n_t - 1), ba);
+      load(min(rel + 3, n_t - 1), ba);
       body(rel + 1, bb);
-      load(min(rel + 3, n_t - 1), bb);
+      load(min(rel + 4, n_t - 1), bb);
+      body(rel + 2, bc);
+      load(min(rel + 5, n_t - 1), bc);
     }
     if (rel < n_t) body(rel, ba);
+    if (rel + 1 < n_t) body(rel + 1, bb);
   };
   // z of row block x against a key tile
   auto shifted = [&](int x, const bf16x8 (&kb)[KS]) {
@@ -674,14 +684,13 @@ gqa_topk_kernel(FwdParams p) {
       float y[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) y[r] = yx[x][r];
-      const float m0 = max8(y), m1 = max8(y + 8);
       // the pair in lanes l and l + 32 passes when either half's maximum
-      // does: the two halves of the ballot, or-ed
-      const uint64_t v0 = __ballot(jok && m0 >= theta[2 * x]);
-      const uint64_t v1 = __ballot(jok && m1 >= theta[2 * x + 1]);
-      const uint32_t b0 = static_cast<uint32_t>(v0) | static_cast<uint32_t>(v0 >> 32);
-      const uint32_t b1 = static_cast<uint32_t>(v1) | static_cast<uint32_t>(v1 >> 32);
-      const bool p0 = (b0 >> l32) & 1u, p1 = (b1 >> l32) & 1u;
+      // does: both lanes take the larger of the two (v_permlane32_swap), so
+      // they decide alike and the low half of the ballot has one bit per pair
+      const float m0 = pair_max(max8(y)), m1 = pair_max(max8(y + 8));
+      const bool p0 = (m0 >= theta[2 * x]) & jok, p1 = (m1 >= theta[2 * x + 1]) & jok;
+      const uint32_t b0 = static_cast<uint32_t>(__ballot(p0));
+      const uint32_t b1 = static_cast<uint32_t>(__ballot(p1));
       const int n0 = __popc(b0), n1 = __popc(b1);
       if (p0) {
         const int e = (qh + qn + __popc(b0 & below)) & (kQCap - 1);
