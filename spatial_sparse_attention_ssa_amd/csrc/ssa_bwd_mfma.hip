@@ -35,11 +35,12 @@
 //   win_dkv_mfma_kernel): one workgroup per (group, block), the rows being
 //   every (query, head) whose top-k list holds the block (the inverted
 //   lists).  The key tile is up to 32 tokens of the block (sorted copies, in
-//   registers); each wave streams its own share of the rows (A operands
-//   straight from memory; the rows also go row-major into a wave-private LDS
-//   area, from which the transposed operands come back through gfx950's
-//   transposing LDS load), and the four partial tiles are summed in LDS, in
-//   wave order, at the end.
+//   registers); each wave streams its own share of the rows, gathered as
+//   whole 16-byte chunks (8 lanes per 64-dim row) into a wave-private LDS
+//   area, row-major, from which the A operands are read as they are and the
+//   transposed operands through gfx950's transposing LDS load; the four
+//   partial tiles are summed in LDS ([dim][token]), in wave order, at the
+//   end.
 #include <float.h>
 
 #include <algorithm>
