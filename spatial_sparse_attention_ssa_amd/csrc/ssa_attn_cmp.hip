@@ -80,8 +80,8 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// maxima of logits that are never NaN: v_maximum3_f32 needs no
-// canonicalising of MFMA results first (fmaxf does)
+// maxima of logits (never NaN here) as explicit three-operand trees, which
+// become v_maximum3_f32
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 

@@ -60,8 +60,8 @@ constexpr float kFixedBound = 60.f;
 template <bool B>
 using kBool = std::integral_constant<bool, B>;
 
-// maximum of 8 values that are never NaN: v_maximum3_f32 needs no
-// canonicalising of MFMA results first (fmaxf does)
+// maximum of 8 values (never NaN here) as a three-operand tree, which
+// becomes v_maximum3_f32
 __device__ __forceinline__ float max8(const float* v) {
   const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
   const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[3], v[4]), v[5]);
