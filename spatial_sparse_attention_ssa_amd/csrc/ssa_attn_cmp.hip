@@ -80,6 +80,47 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// inverse of ordered_bits
+__device__ __forceinline__ float ordered_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// the larger 64-bit key of this lane and the lane that the DPP control CTRL
+// selects (the two 32-bit halves moved by two DPP moves)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_key(uint64_t k) {
+  const uint32_t hi = static_cast<uint32_t>(k >> 32), lo = static_cast<uint32_t>(k);
+  const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(hi), static_cast<int>(hi), CTRL, 0xF, 0xF, false));
+  const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(lo), static_cast<int>(lo), CTRL, 0xF, 0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(ohi) << 32) | olo;
+  return o > k ? o : k;
+}
+
+// the largest 64-bit key of the wave, on every lane: DPP butterflies within
+// 16-lane rows (lane ^ 1, lane ^ 2, then the mirrors of 8 and 16 lanes), a
+// lane shuffle across rows, and v_permlane32_swap across the halves
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max_key<0xB1>(k);    // quad_perm [1,0,3,2]
+  k = dpp_max_key<0x4E>(k);    // quad_perm [2,3,0,1]
+  k = dpp_max_key<0x141>(k);   // row_half_mirror
+  k = dpp_max_key<0x140>(k);   // row_mirror
+  {
+    const uint32_t hi = static_cast<uint32_t>(k >> 32), lo = static_cast<uint32_t>(k);
+    const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), 16))) << 32) |
+                       static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), 16));
+    k = o > k ? o : k;
+  }
+  {
+    const uint32_t hi = static_cast<uint32_t>(k >> 32), lo = static_cast<uint32_t>(k);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const uint64_t a = (static_cast<uint64_t>(rh[0]) << 32) | rl[0];
+    const uint64_t b = (static_cast<uint64_t>(rh[1]) << 32) | rl[1];
+    k = a > b ? a : b;
+  }
+  return k;
+}
+
 // maxima of logits (never NaN here) as explicit three-operand trees, which
 // become v_maximum3_f32
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -803,32 +844,32 @@ topk_fixup_kernel(FwdParams p) {
       if (p.win_off[p.seq_win_off[mid]] <= i) lo = mid; else hi = mid - 1;
     }
     const int j0 = p.seq_blk_off[lo], j1 = p.seq_blk_off[lo + 1];
-    float q[kD];
+    // the query row stays packed: v_dot2_f32_bf16 (exact products, float32
+    // sums, four partial sums) scores a block as the epilogue does
+    u32x4 qw[kD / 8];
 #pragma unroll
-    for (int c = 0; c < kD / 8; ++c) {
-      const u32x4 u = *reinterpret_cast<const u32x4*>(Q + (static_cast<int64_t>(t) * p.h_q + g) * kD + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
-        q[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-      }
-    }
+    for (int c = 0; c < kD / 8; ++c)
+      qw[c] = *reinterpret_cast<const u32x4*>(Q + (static_cast<int64_t>(t) * p.h_q + g) * kD + 8 * c);
     const uint16_t* KB = static_cast<const uint16_t*>(p.kbar) + static_cast<int64_t>(g) * p.nb_cap * kD;
     float lv[KMAX];
     int li[KMAX];
 #pragma unroll
     for (int e = 0; e < KMAX; ++e) { lv[e] = -FLT_MAX; li[e] = 0x7FFFFFFF; }
     for (int j = j0 + tid; j < j1; j += 256) {
-      float s = 0.f;
+      float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < kD / 8; ++c) {
         const u32x4 u = *reinterpret_cast<const u32x4*>(KB + static_cast<int64_t>(j) * kD + 8 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s = fmaf(q[8 * c + 2 * e], __uint_as_float(u[e] << 16), s);
-          s = fmaf(q[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), s);
+          // (words through scalars: this compiler's __builtin_bit_cast of a
+          // vector element reads element 0)
+          const uint32_t ke = u[e], qe = qw[c][e];
+          sp[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ke), __builtin_bit_cast(bf16x2, qe), sp[e],
+                                                  false);
         }
       }
+      const float s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
       // blocks arrive in increasing id, so a tie keeps the earlier (lower) id ahead
       if (s > lv[KMAX - 1]) {
         bool placed = false;
@@ -844,14 +885,11 @@ topk_fixup_kernel(FwdParams p) {
     }
     // each wave pops its KMAX best (value descending, block ascending)
     for (int r = 0; r < KMAX; ++r) {
-      float bv = lv[0];
-      int bi = li[0];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
+      // (value, then lower block first) as one 64-bit key
+      const uint64_t key = wave_max_key((static_cast<uint64_t>(ordered_bits(lv[0])) << 32) |
+                                        static_cast<uint32_t>(~li[0]));
+      const float bv = ordered_value(static_cast<uint32_t>(key >> 32));
+      const int bi = static_cast<int>(~static_cast<uint32_t>(key));
       if (li[0] == bi) {
 #pragma unroll
         for (int e = 0; e < KMAX - 1; ++e) { lv[e] = lv[e + 1]; li[e] = li[e + 1]; }
