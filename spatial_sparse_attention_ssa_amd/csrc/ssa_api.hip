@@ -183,6 +183,33 @@ FwdLayout forward_layout(const ssa_blocks* b, const ssa_attn* a) {
 
 size_t forward_ws_bytes(const ssa_blocks* b, const ssa_attn* a) { return forward_layout(b, a).total; }
 
+// A second stream and two events per host thread and device, on which the
+// probe-set selection runs beside the window kernel (it reads only what
+// the pooling kernel wrote, and only the compressed kernel reads what it
+// writes).  Created on first use (default priority, non-blocking) and kept
+// until the process ends; if creation fails the kernels run in order on the
+// caller's stream.
+struct SideStream {
+  bool tried = false, ok = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+
+SideStream* side_stream() {
+  thread_local SideStream side[kMaxSideDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& s = side[dev];
+  if (!s.tried) {
+    s.tried = true;
+    s.ok = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return s.ok ? &s : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,10 +345,13 @@ ssa_status check_forward_args(const ssa_blocks* blocks, const ssa_attn* attn, co
   return SSA_OK;
 }
 
+// side_by_side: run the probe-set selection on a second stream beside the
+// window kernel (the timed and allocation-free forwards run every kernel in
+// order on the caller's stream)
 ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const void* q, const void* k,
                         const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
                         int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream,
-                        float* stage_ms, int32_t* n_stages, float* lse = nullptr) {
+                        float* stage_ms, int32_t* n_stages, float* lse = nullptr, bool side_by_side = false) {
   ssa_status st = check_forward_args(blocks, attn, q, k, v, gates, out);
   if (st != SSA_OK) return st;
   const size_t need = forward_ws_bytes(blocks, attn);
@@ -404,9 +434,26 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
     for (int i = 0; i <= ns && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
     if (e == hipSuccess) e = hipEventRecord(ev[0], stream);
   }
-  for (int i = 0; i < ns && e == hipSuccess; ++i) {
-    e = stages[i].launch(p, attn->dtype, stream);
-    if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[i + 1], stream);
+  // the plan of the one-head-per-group MFMA path is pooling, window, probe,
+  // compressed, ...: the probe stage can run beside the window kernel
+  SideStream* side = nullptr;
+  if (side_by_side && !stage_ms && ns > 3 && stages[1].launch == ssa::launch_win_mfma &&
+      stages[2].launch == ssa::launch_cmp_probe)
+    side = side_stream();
+  if (side) {
+    e = stages[0].launch(p, attn->dtype, stream);
+    if (e == hipSuccess) e = hipEventRecord(side->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+    if (e == hipSuccess) e = stages[2].launch(p, attn->dtype, side->stream);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+    if (e == hipSuccess) e = stages[1].launch(p, attn->dtype, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
+    for (int i = 3; i < ns && e == hipSuccess; ++i) e = stages[i].launch(p, attn->dtype, stream);
+  } else {
+    for (int i = 0; i < ns && e == hipSuccess; ++i) {
+      e = stages[i].launch(p, attn->dtype, stream);
+      if (e == hipSuccess && stage_ms) e = hipEventRecord(ev[i + 1], stream);
+    }
   }
   if (stage_ms) {
     if (e == hipSuccess) e = hipEventSynchronize(ev[ns]);
@@ -427,7 +474,7 @@ ssa_status ssa_forward(const ssa_blocks* blocks, const ssa_attn* attn, const voi
                        const void* v, const void* gates, void* out, void* k_cmp, void* v_cmp,
                        int32_t* topk_idx, void* workspace, size_t ws_bytes, void* hip_stream) {
   return forward_impl(blocks, attn, q, k, v, gates, out, k_cmp, v_cmp, topk_idx, workspace, ws_bytes,
-                      hip_stream, nullptr, nullptr);
+                      hip_stream, nullptr, nullptr, nullptr, true);
 }
 
 ssa_status ssa_forward_timed(const ssa_blocks* blocks, const ssa_attn* attn, const void* q,
@@ -445,7 +492,7 @@ ssa_status ssa_forward_train(const ssa_blocks* blocks, const ssa_attn* attn, con
                              void* hip_stream) {
   if (!topk_idx || !lse) return fail(SSA_ERR_INVALID_ARGUMENT, "topk_idx and lse must be non-null");
   return forward_impl(blocks, attn, q, k, v, gates, out, nullptr, nullptr, topk_idx, workspace, ws_bytes,
-                      hip_stream, nullptr, nullptr, lse);
+                      hip_stream, nullptr, nullptr, lse, true);
 }
 
 }  // extern "C"
