@@ -304,10 +304,12 @@ int forward_plan(const ssa_attn* attn, Stage* stages) {
     stages[1] = Stage{"generic_fwd", ssa::launch_generic};
     return 2;
   }
-  // the window kernel is the first writer of the float32 branch accumulator
-  // (every token lies in exactly one window); the compressed kernels add to it
-  stages[1] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
-  int n = 2;
+  // the pooled values transposed for the compressed kernels; the window
+  // kernel is the first writer of the float32 branch accumulator (every
+  // token lies in exactly one window); the compressed kernels add to it
+  stages[1] = Stage{"vt_transpose_kernel", ssa::launch_vt_transpose};
+  stages[2] = Stage{"win_mfma_kernel", ssa::launch_win_mfma};
+  int n = 3;
   if (use_gqa_path(attn)) {
     stages[n++] = Stage{"gqa_cmp_kernel", ssa::launch_gqa_cmp};
     stages[n++] = Stage{"gqa_topk_kernel", ssa::launch_gqa_topk};
@@ -434,21 +436,25 @@ ssa_status forward_impl(const ssa_blocks* blocks, const ssa_attn* attn, const vo
     for (int i = 0; i <= ns && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
     if (e == hipSuccess) e = hipEventRecord(ev[0], stream);
   }
-  // the plan of the one-head-per-group MFMA path is pooling, window, probe,
-  // compressed, ...: the probe stage can run beside the window kernel
+  // the MFMA plans start with pooling, the transpose of the pooled values,
+  // the window kernel and (one head per group) the probe stage: the transpose
+  // and the probe stage run beside the window kernel, joined before the
+  // compressed kernels
   SideStream* side = nullptr;
-  if (side_by_side && !stage_ms && ns > 3 && stages[1].launch == ssa::launch_win_mfma &&
-      stages[2].launch == ssa::launch_cmp_probe)
+  if (side_by_side && !stage_ms && ns > 3 && stages[1].launch == ssa::launch_vt_transpose &&
+      stages[2].launch == ssa::launch_win_mfma)
     side = side_stream();
   if (side) {
+    const bool probe = stages[3].launch == ssa::launch_cmp_probe;
     e = stages[0].launch(p, attn->dtype, stream);
     if (e == hipSuccess) e = hipEventRecord(side->fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-    if (e == hipSuccess) e = stages[2].launch(p, attn->dtype, side->stream);
+    if (e == hipSuccess) e = stages[1].launch(p, attn->dtype, side->stream);
+    if (e == hipSuccess && probe) e = stages[3].launch(p, attn->dtype, side->stream);
     if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
-    if (e == hipSuccess) e = stages[1].launch(p, attn->dtype, stream);
+    if (e == hipSuccess) e = stages[2].launch(p, attn->dtype, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
-    for (int i = 3; i < ns && e == hipSuccess; ++i) e = stages[i].launch(p, attn->dtype, stream);
+    for (int i = probe ? 4 : 3; i < ns && e == hipSuccess; ++i) e = stages[i].launch(p, attn->dtype, stream);
   } else {
     for (int i = 0; i < ns && e == hipSuccess; ++i) {
       e = stages[i].launch(p, attn->dtype, stream);

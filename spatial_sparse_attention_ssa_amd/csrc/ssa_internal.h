@@ -290,6 +290,7 @@ hipError_t launch_cmp_probe(const FwdParams& p, ssa_dtype dtype, hipStream_t str
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_win_mfma(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
+hipError_t launch_vt_transpose(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_sel_combine(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 hipError_t launch_generic(const FwdParams& p, ssa_dtype dtype, hipStream_t stream);
 

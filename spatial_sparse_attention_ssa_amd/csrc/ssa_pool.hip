@@ -236,16 +236,6 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
         static_cast<uint16_t*>(p.vbar), static_cast<uint16_t*>(p.k_cmp),
         static_cast<uint16_t*>(p.v_cmp), static_cast<uint16_t*>(p.k_s), static_cast<uint16_t*>(p.v_s),
         p.knorm2);
-    if (p.vbar_t) {
-      const int tiles = p.h_kv * (p.nb_cap / kKeyTile);
-      const int grid_t = tiles < 4096 ? tiles : 4096;
-      if (p.d == 32)
-        vt_transpose_kernel<32><<<grid_t, 256, 0, stream>>>(
-            static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv, p.nb_cap);
-      else
-        vt_transpose_kernel<64><<<grid_t, 256, 0, stream>>>(
-            static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv, p.nb_cap);
-    }
   } else {
     pool_kernel<float><<<grid, 256, 0, stream>>>(
         static_cast<const float*>(p.k), static_cast<const float*>(p.v), p.perm, p.blk_off,
@@ -253,6 +243,21 @@ hipError_t launch_pool(const FwdParams& p, ssa_dtype dtype, hipStream_t stream) 
         static_cast<float*>(p.k_cmp), static_cast<float*>(p.v_cmp), static_cast<float*>(p.k_s),
         static_cast<float*>(p.v_s), nullptr);
   }
+  return hipGetLastError();
+}
+
+// the pooled values of every 32-block tile as [D][32 blocks] for the
+// compressed kernels (bf16 MFMA path only; the pooling kernel writes vbar first)
+hipError_t launch_vt_transpose(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
+  if (!p.vbar_t) return hipSuccess;
+  const int tiles = p.h_kv * (p.nb_cap / kKeyTile);
+  const int grid_t = tiles < 4096 ? tiles : 4096;
+  if (p.d == 32)
+    vt_transpose_kernel<32><<<grid_t, 256, 0, stream>>>(
+        static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv, p.nb_cap);
+  else
+    vt_transpose_kernel<64><<<grid_t, 256, 0, stream>>>(
+        static_cast<const uint16_t*>(p.vbar), static_cast<uint16_t*>(p.vbar_t), p.counts, p.h_kv, p.nb_cap);
   return hipGetLastError();
 }
 
