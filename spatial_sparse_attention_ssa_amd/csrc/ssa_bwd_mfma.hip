@@ -298,43 +298,65 @@ cmp_dq_mfma_kernel(BwdParams p) {
 template <int D>
 __global__ void __launch_bounds__(256)
 rows_prep_kernel(BwdParams p) {
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D / 8;   // 16-byte chunks of one (token, head) row
+  constexpr int U = 8;         // chunks per thread in flight
   const FwdParams& f = p.f;
   const int tid = threadIdx.x;
   const int G = f.h_q / f.h_kv;
-  const int64_t n_rows = static_cast<int64_t>(f.n) * G;
-  const int ntile = p.rows_cap / kKeyTile;
   const int64_t nrow = static_cast<int64_t>(f.n) * f.h_q;
+  const int cpt = f.h_q * CPR;                          // chunks of a token's whole row (every head)
+  const int n_pos = (p.rows_cap + G - 1) / G;           // sorted positions, the padding rows included
+  const int ntile = (n_pos + kKeyTile - 1) / kKeyTile;
   const uint16_t* Q = static_cast<const uint16_t*>(f.q);
   const uint16_t* dO = static_cast<const uint16_t*>(p.dout);
   const uint16_t* gates = static_cast<const uint16_t*>(f.gates);
-  for (int64_t item = blockIdx.x; item < static_cast<int64_t>(f.h_kv) * ntile; item += gridDim.x) {
-    const int g = static_cast<int>(item / ntile);
-    const int T = static_cast<int>(item % ntile);
-    const int64_t rbase = static_cast<int64_t>(g) * p.rows_cap + static_cast<int64_t>(T) * kKeyTile;
-    if (tid < kKeyTile * CPR) {
-      const int row = tid / CPR, c = tid % CPR;
-      const int64_t R = static_cast<int64_t>(T) * kKeyTile + row;
-      u32x4 uq = {0u, 0u, 0u, 0u}, ud = {0u, 0u, 0u, 0u};
-      if (R < n_rows) {
-        const int64_t qrow = static_cast<int64_t>(f.perm[R / G]) * f.h_q + g * G + R % G;
-        uq = *reinterpret_cast<const u32x4*>(Q + qrow * D + 8 * c);
-        ud = *reinterpret_cast<const u32x4*>(dO + qrow * D + 8 * c);
+  // a workgroup takes 32 sorted positions: it reads their tokens' whole rows
+  // (every head, contiguous in HBM) and writes each head's row to its
+  // group's sorted row space, row i G + head % G
+  for (int T = blockIdx.x; T < ntile; T += gridDim.x) {
+    const int i0 = T * kKeyTile;
+    const int n_ch = kKeyTile * cpt;
+    for (int e0 = tid; e0 < n_ch; e0 += 256 * U) {
+      u32x4 uq[U], ud[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * 256;
+        uq[u] = ud[u] = u32x4{0u, 0u, 0u, 0u};
+        const int i = i0 + e / cpt;
+        if (e < n_ch && i < f.n) {
+          const int64_t off = static_cast<int64_t>(f.perm[i]) * f.h_q * D + 8 * (e % cpt);
+          uq[u] = *reinterpret_cast<const u32x4*>(Q + off);
+          ud[u] = *reinterpret_cast<const u32x4*>(dO + off);
+        }
       }
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.q_rows) + (rbase + row) * D + 8 * c) = uq;
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.do_rows) + (rbase + row) * D + 8 * c) = ud;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * 256;
+        if (e >= n_ch) continue;
+        const int i = i0 + e / cpt;
+        const int cc = e % cpt, hh = cc / CPR, c = cc % CPR;
+        const int64_t R = static_cast<int64_t>(i) * G + hh % G;
+        if (R >= p.rows_cap) continue;
+        const int64_t dst = (static_cast<int64_t>(hh / G) * p.rows_cap + R) * D + 8 * c;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.q_rows) + dst) = uq[u];
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.do_rows) + dst) = ud[u];
+      }
     }
-    if (tid < kKeyTile) {
-      const int64_t R = static_cast<int64_t>(T) * kKeyTile + tid;
+    // per row (log2 lse, Delta, gate) of the compressed and the window branch
+    for (int e = tid; e < kKeyTile * f.h_q; e += 256) {
+      const int i = i0 + e / f.h_q, hh = e % f.h_q;
+      const int64_t R = static_cast<int64_t>(i) * G + hh % G;
+      if (R >= p.rows_cap) continue;
       float4 s0 = make_float4(FLT_MAX, 0.f, 0.f, 0.f), s2 = s0;   // a padding row has P = 0
-      if (R < n_rows) {
-        const int64_t qrow = static_cast<int64_t>(f.perm[R / G]) * f.h_q + g * G + R % G;
+      if (i < f.n) {
+        const int64_t qrow = static_cast<int64_t>(f.perm[i]) * f.h_q + hh;
         s0 = make_float4(p.lse[qrow] * kLog2e, p.delta[qrow], bf16_bits_to_f32(gates[qrow * 3]), 0.f);
         s2 = make_float4(p.lse[2 * nrow + qrow] * kLog2e, p.delta[2 * nrow + qrow],
                          bf16_bits_to_f32(gates[qrow * 3 + 2]), 0.f);
       }
-      p.st_rows[rbase + tid] = s0;
-      p.st_rows[static_cast<int64_t>(f.h_kv) * p.rows_cap + rbase + tid] = s2;
+      const int64_t r = static_cast<int64_t>(hh / G) * p.rows_cap + R;
+      p.st_rows[r] = s0;
+      p.st_rows[static_cast<int64_t>(f.h_kv) * p.rows_cap + r] = s2;
     }
   }
 }
@@ -940,8 +962,9 @@ hipError_t launch_bwd_kv_win_mfma(const BwdParams& p, ssa_dtype /*dtype*/, hipSt
 }
 
 hipError_t launch_bwd_rows_prep(const BwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(p.f.h_kv) * (p.rows_cap / kKeyTile);
-  const int grid = static_cast<int>(std::min<int64_t>(items, 8192));
+  const int64_t G = p.f.h_q / p.f.h_kv;
+  const int64_t tiles = ((p.rows_cap + G - 1) / G + kKeyTile - 1) / kKeyTile;
+  const int grid = static_cast<int>(std::min<int64_t>(tiles, 8192));
   if (p.f.d == 32) rows_prep_kernel<32><<<grid, 256, 0, stream>>>(p);
   else rows_prep_kernel<64><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
