@@ -8,7 +8,8 @@
 // G2 * o_win + G0 * o_cmp to the float32 accumulator; this kernel adds
 // G1 * o_sel, rounds once to bfloat16 and writes the output row.
 //
-// D / 16 lanes serve one (token, head) pair, each owning 16 dims; a wave
+// D / 16 lanes serve one (token, head) pair, each owning 16 dims (two runs
+// of 8, one in each half of the row); a wave
 // covers 64 / (D / 16) pairs of one head (pairs are ordered head-major, so the rows
 // gathered at any time belong to one or two heads and stay in the Infinity
 // Cache).  Keys and values come from the head-major sorted copies, where a
@@ -59,12 +60,13 @@ __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), c, false);
 }
 
-// 16 bf16 values of a row, packed
+// 16 bf16 values of a row, packed: 8 at p and 8 at p + hoff (the lane's
+// dims in the first and in the second half of the row)
 struct Row16 {
   u32x4 a, b;
-  __device__ __forceinline__ void load(const uint16_t* p) {
+  __device__ __forceinline__ void load(const uint16_t* p, int hoff) {
     a = *reinterpret_cast<const u32x4*>(p);
-    b = *reinterpret_cast<const u32x4*>(p + 8);
+    b = *reinterpret_cast<const u32x4*>(p + hoff);
   }
   // the row times 16 packed bf16 query values
   __device__ __forceinline__ float dot(const Row16& q) const {
@@ -136,6 +138,12 @@ sel_combine_kernel(FwdParams p) {
   constexpr int kD = D;
   constexpr int LP = D / kDL;             // lanes per pair
   constexpr int NP = 256 / LP;            // pairs per workgroup
+  // lane sub of a pair owns dims [8 sub, 8 sub + 8) and [D/2 + 8 sub, D/2 +
+  // 8 sub + 8): each 16-byte load instruction of a pair then covers one
+  // contiguous half row, so a row gather touches half as many 64-byte
+  // sectors per instruction as with 16 consecutive dims per lane
+  constexpr int kHalf = D / 2;
+  constexpr int kLaneOff = kDL / 2;
   __shared__ int32_t rows[NP * kList];    // per pair: row positions
   __shared__ int2 ranges[NP * KMAX];      // per pair: the selected blocks' row ranges
 
@@ -151,10 +159,10 @@ sel_combine_kernel(FwdParams p) {
   const int nb = p.counts[SSA_COUNT_NB];
   const float c2 = p.scale * kLog2e;
 
-  const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(g) * p.n * kD + kDL * sub;
-  const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(g) * p.n * kD + kDL * sub;
+  const uint16_t* KS = static_cast<const uint16_t*>(p.k_s) + static_cast<int64_t>(g) * p.n * kD + kLaneOff * sub;
+  const uint16_t* VS = static_cast<const uint16_t*>(p.v_s) + static_cast<int64_t>(g) * p.n * kD + kLaneOff * sub;
   Row16 q;
-  q.load(static_cast<const uint16_t*>(p.q) + (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub);
+  q.load(static_cast<const uint16_t*>(p.q) + (static_cast<int64_t>(t) * p.h_q + h) * kD + kLaneOff * sub, kHalf);
   const int32_t* sel = p.topk_idx + (static_cast<int64_t>(t) * p.h_kv + g) * p.topk;
 
   // ---------------- the selected blocks' row ranges, all loads in flight at once
@@ -193,8 +201,8 @@ sel_combine_kernel(FwdParams p) {
 #pragma unroll
     for (int u = 0; u < kStep; ++u) {
       const int64_t row = rows[pl * kList + min(i0 + u, listed - 1)];
-      kr[u].load(KS + row * kD);
-      vr[u].load(VS + row * kD);
+      kr[u].load(KS + row * kD, kHalf);
+      vr[u].load(VS + row * kD, kHalf);
     }
     float s2[kStep];
 #pragma unroll
@@ -212,8 +220,8 @@ sel_combine_kernel(FwdParams p) {
       for (int i = ab.x; i < ab.y; ++i, ++seen) {
         if (seen < kList) continue;
         Row16 kr, vr[1];
-        kr.load(KS + static_cast<int64_t>(i) * kD);
-        vr[0].load(VS + static_cast<int64_t>(i) * kD);
+        kr.load(KS + static_cast<int64_t>(i) * kD, kHalf);
+        vr[0].load(VS + static_cast<int64_t>(i) * kD, kHalf);
         float s2[1] = {pair_sum<LP>(kr.dot(q)) * c2};
         st.add<1>(s2, vr);
       }
@@ -221,7 +229,7 @@ sel_combine_kernel(FwdParams p) {
   }
 
   if (!active) return;
-  const int64_t orow = (static_cast<int64_t>(t) * p.h_q + h) * kD + kDL * sub;
+  const int64_t orow = (static_cast<int64_t>(t) * p.h_q + h) * kD + kLaneOff * sub;
   if (p.lse && sub == 0)
     p.lse[static_cast<int64_t>(p.n) * p.h_q + static_cast<int64_t>(t) * p.h_q + h] = (st.m + __log2f(st.l)) * kLn2;
   const uint16_t* gt = static_cast<const uint16_t*>(p.gates) + (static_cast<int64_t>(t) * p.h_q + h) * 3;
@@ -230,7 +238,7 @@ sel_combine_kernel(FwdParams p) {
   uint16_t res[kDL];
 #pragma unroll
   for (int c = 0; c < kDL / 4; ++c) {
-    const float4 a = *reinterpret_cast<const float4*>(acc + 4 * c);
+    const float4 a = *reinterpret_cast<const float4*>(acc + (c < 2 ? 4 * c : kHalf + 4 * (c - 2)));
     res[4 * c] = f32_to_bf16_bits(fmaf(st.o[4 * c], f, a.x));
     res[4 * c + 1] = f32_to_bf16_bits(fmaf(st.o[4 * c + 1], f, a.y));
     res[4 * c + 2] = f32_to_bf16_bits(fmaf(st.o[4 * c + 2], f, a.z));
@@ -244,7 +252,7 @@ sel_combine_kernel(FwdParams p) {
   }
   uint16_t* out = static_cast<uint16_t*>(p.out) + orow;
   *reinterpret_cast<u32x4*>(out) = w0;
-  *reinterpret_cast<u32x4*>(out + 8) = w1;
+  *reinterpret_cast<u32x4*>(out + kHalf) = w1;
 }
 
 // ---------------------------------------------------------------------------
