@@ -98,6 +98,24 @@ def stored_traffic(kernel: str, wid: int = WORKLOAD_ID):
     return rec.get("traffic_bytes")
 
 
+def mfma_path(kernel: str, wid: int = WORKLOAD_ID) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{WORKLOADS[wid]['tag']}_mfma.json")
+
+
+def stored_mfma(kernel: str, wid: int = WORKLOAD_ID):
+    """MFMA counter figures of `kernel` from the committed summary (busy share
+    of SIMD cycles, executed bf16 MFMA TFLOP per launch, implied clock), or
+    None when there is none or the kernel's source changed since."""
+    path = mfma_path(kernel, wid)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "executed_tflop", "executed_tflops", "clock_ghz", "launches")}
+
+
 def pool_bytes(wl, nb: int) -> float:
     """Algorithmic HBM bytes of the pooling kernel: every token's K and V row
     read once (gathered through perm, 4 B per token), pooled rows written."""
@@ -191,12 +209,13 @@ N_SIMD = 256 * 4            # MI355X: 256 compute units of 4 SIMDs
 N_XCC = 8
 
 
-def summarize_mfma(pmc_csv: str, wid: int):
+def summarize_mfma(pmc_csv: str, wid: int, command: str = ""):
     """Counter-based MFMA utilisation per attention kernel from one rocprofv3
     --pmc run of MFMA_COUNTERS: executed bf16 MFMA flops (512 per MOPS unit),
     the MFMA pipe's busy share of all SIMD cycles (cycles per XCC from
     GRBM_GUI_ACTIVE), and the clock those cycles imply; prints a markdown
-    table and the time-weighted utilisation."""
+    table and the time-weighted utilisation, and writes
+    profiles/<kernel>_<tokens>tok_mfma.json for the kernels it knows."""
     import csv
     import re
     from collections import defaultdict
@@ -228,6 +247,14 @@ def summarize_mfma(pmc_csv: str, wid: int):
         print(f"| {name} | {len(c['GRBM_GUI_ACTIVE'])} | {t * 1e6:.1f} | {flops / 1e12:.3f} | "
               f"{flops / t / 1e12:.0f} | {100 * flops / t / 1e12 / PEAK_BF16_TFLOPS:.1f} | {100 * busy:.1f} | "
               f"{cycles / t / 1e9:.2f} |")
+        if name in KERNEL_SOURCES:
+            rec = {"kernel": name, "workload": WORKLOADS[wid]["name"], "source_sha256": kernel_source_hash(name),
+                   "mfma_busy_frac": busy, "executed_tflop": flops / 1e12, "executed_tflops": flops / t / 1e12,
+                   "clock_ghz": cycles / t / 1e9, "launches": len(c["GRBM_GUI_ACTIVE"]),
+                   "counters": list(MFMA_COUNTERS), "command": command}
+            with open(mfma_path(name, wid), "w") as fh:
+                json.dump(rec, fh, indent=1)
+                fh.write("\n")
     if tw_t:
         print(f"\ntime-weighted MFMA busy share over these kernels: {100 * tw_busy / tw_t:.1f} %")
 
@@ -426,7 +453,10 @@ def main():
         summarize_mempath(args.summarize_mempath, args.mempath_grid)
         return
     if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma, wid)
+        extra = "" if wid == WORKLOAD_ID else f" --workload {wid}"
+        summarize_mfma(args.summarize_mfma, wid,
+                       f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d <dir> -o run -- "
+                       f"python bench.py --steps 1 --warmup 1 --no-cpu-baseline{extra}")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -584,7 +614,10 @@ def main():
                            "bytes": bp_bytes},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic(dom.split(":")[-1], wid)},
+                     "traffic": stored_traffic(dom.split(":")[-1], wid),
+                     # the same kernel's rocprofv3 MFMA counters (SQ_VALU_MFMA_BUSY_CYCLES, ...) from the
+                     # committed summary, while its source is unchanged
+                     "mfma_counters": stored_mfma(dom.split(":")[-1], wid)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, train=train)

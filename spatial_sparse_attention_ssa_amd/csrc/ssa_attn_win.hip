@@ -69,6 +69,9 @@ win_mfma_kernel(FwdParams p) {
     for (int qg0 = 0; qg0 < n_w; qg0 += 128) {
       const int qi = wa + qg0 + wv * 32 + (lane & 31);
       const bool q_valid = qi < wb;
+      // a wave whose 32 queries all lie past the window's end only helps to
+      // stage the chunks (uniform over the wave)
+      const bool wave_live = wa + qg0 + wv * 32 < wb;
       const int t = q_valid ? p.perm[qi] : 0;
       const uint16_t* q_row = Q + (static_cast<int64_t>(t) * p.h_q + h) * kD;
       bf16x8 qb[KSTEPS];
@@ -101,7 +104,7 @@ win_mfma_kernel(FwdParams p) {
           *reinterpret_cast<u32x4*>(v_lds + row * kKRow + 8 * c) = vr;
         }
         __syncthreads();
-        for (int kt = 0; kt < nk32; kt += kKeyTile) {
+        for (int kt = 0; wave_live && kt < nk32; kt += kKeyTile) {
           f32x16 s = {};
 #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
