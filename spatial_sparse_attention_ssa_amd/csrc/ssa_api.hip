@@ -116,13 +116,14 @@ int64_t nb_capacity(const ssa_blocks* b) {
   return (c + ssa::kKeyTile - 1) / ssa::kKeyTile * ssa::kKeyTile;
 }
 
-// the MFMA kernels cover bfloat16 with head_dim 64 and one query head per
-// key/value head, or head_dim 32 / 64 with 16 query heads per key/value head
+// the MFMA kernels cover bfloat16 with head_dim 32 or 64 and either one query
+// head per key/value head or 16 query heads per key/value head
 bool use_gqa_path(const ssa_attn* a) {
   return a->dtype == SSA_BF16 && (a->head_dim == 32 || a->head_dim == 64) && a->h_q == 16 * a->h_kv;
 }
 bool use_mfma_path(const ssa_attn* a) {
-  return (a->dtype == SSA_BF16 && a->head_dim == 64 && a->h_q == a->h_kv) || use_gqa_path(a);
+  return (a->dtype == SSA_BF16 && (a->head_dim == 32 || a->head_dim == 64) && a->h_q == a->h_kv) ||
+         use_gqa_path(a);
 }
 
 struct FwdLayout {

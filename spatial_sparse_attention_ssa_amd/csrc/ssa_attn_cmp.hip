@@ -1,5 +1,5 @@
-// Compressed-block attention with top-k block selection, on MFMA (bf16, D = 64,
-// one query head per key/value head).
+// Compressed-block attention with top-k block selection, on MFMA (bf16, D = 32
+// or 64, one query head per key/value head).
 //
 // Direct3D-S2 page, "Method": every query attends to the mean-pooled blocks of
 // its sequence, and the same query-to-block scores choose the top-k blocks
@@ -60,11 +60,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kD = 64;
-constexpr int kKRow = kD + 8;          // LDS row of a key tile (bf16), padded against bank conflicts
 constexpr int kVRow = kKeyTile + 8;    // LDS row of a transposed value tile (bf16)
-constexpr int kKTileElems = kKeyTile * kKRow;
-constexpr int kVTileElems = kD * kVRow;
+// tile shapes for head dim D (32 or 64)
+template <int D>
+struct CmpDims {
+  static constexpr int kKRow = D + 8;            // LDS row of a key tile (bf16), padded against bank conflicts
+  static constexpr int kKTileElems = kKeyTile * kKRow;
+  static constexpr int kVTileElems = D * kVRow;
+  static constexpr int KS = D / 16;              // MFMA k steps over the dims
+  static constexpr int VB = D / 32;              // 32-dim row blocks of O^T
+  static constexpr int kKStagers = kKeyTile * (D / 8);   // threads that stage a key tile (16 bytes each)
+  static constexpr int kVStagers = D * 4;                // threads that stage a value tile
+};
 constexpr int kBlockQ = 32;            // queries per MFMA column block
 // bf16 P by truncation: the mean relative loss of truncating a float32 with
 // a log-uniform mantissa to 8 significant bits is 2^-8 * (1/ln 2) * (1/2);
@@ -225,9 +232,10 @@ probe_select_kernel(FwdParams p) {
   }
   __syncthreads();
   const int tbin = sh_bin, need = sh_need;
-  const uint16_t* src = static_cast<const uint16_t*>(p.kbar) + (static_cast<int64_t>(g) * p.nb_cap + j0) * 64;
+  const int dh = p.d;   // 32 or 64
+  const uint16_t* src = static_cast<const uint16_t*>(p.kbar) + (static_cast<int64_t>(g) * p.nb_cap + j0) * dh;
   const int64_t set = static_cast<int64_t>(g) * p.max_probe_slots + s;
-  uint16_t* dst = p.probe ? static_cast<uint16_t*>(p.probe) + set * kProbeBlocks * 64 : nullptr;
+  uint16_t* dst = p.probe ? static_cast<uint16_t*>(p.probe) + set * kProbeBlocks * dh : nullptr;
   int32_t* ids = p.probe_ids ? p.probe_ids + set * kProbeBlocks : nullptr;
   const uint64_t below = (uint64_t(1) << lane) - 1;
   int base_gt = 0, base_eq = 0;   // chosen blocks above / in the threshold bin before this chunk
@@ -257,16 +265,15 @@ probe_select_kernel(FwdParams p) {
       const int pos = pgt + min(peq, need);
       if (ids) ids[pos] = j0 + j;
       if (dst) {
-        const u32x4* from = reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(j) * 64);
-        u32x4* to = reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(pos) * 64);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) to[c] = from[c];
+        const u32x4* from = reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(j) * dh);
+        u32x4* to = reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(pos) * dh);
+        for (int c = 0; c < dh / 8; ++c) to[c] = from[c];
       }
     }
   }
 }
 
-template <int KMAX>
+template <int KMAX, int D>
 struct CmpShape {
   // candidate slots per query, shared by its two lanes (with the bound above
   // a query rarely has more than KMAX + 6; overflow goes to the fallback)
@@ -274,7 +281,7 @@ struct CmpShape {
   // hit-tile words per lane and block (a lane typically has about KMAX / 2
   // candidates)
   static constexpr int kEnt = KMAX <= 16 ? 20 : 36;
-  static constexpr int kRingBytes = 2 * (kKTileElems + kVTileElems) * 2;
+  static constexpr int kRingBytes = 2 * (CmpDims<D>::kKTileElems + CmpDims<D>::kVTileElems) * 2;
   // candidate lists of one query block of every wave (the blocks take turns):
   // per query kSlots 64-bit keys (kSlots even, so a query's keys start on a
   // 16-byte boundary)
@@ -286,9 +293,9 @@ struct CmpShape {
 };
 
 // Per-lane state of one 32-query block.
-template <int KMAX>
+template <int KMAX, int D>
 struct QBlock {
-  bf16x8 qb[4];       // Q^T B operand: query (l % 32), d = 16 ks + 8 half + 0..7
+  bf16x8 qb[D / 16];  // Q^T B operand: query (l % 32), d = 16 ks + 8 half + 0..7
   const uint16_t* q_row;
   int qi;             // sorted position
   int t;              // token (input order)
@@ -296,7 +303,7 @@ struct QBlock {
   float L[KMAX];      // pass 1: descending list of group maxima
   float g;            // pass 1: running maximum of the open group
   f32x16 s;           // logits of the tile in flight
-  f32x16 o0, o1;      // O^T, dims 0..31 and 32..63
+  f32x16 o[D / 32];    // O^T, dims 32 vb .. 32 vb + 31
   float l0, l1;       // row-sum partials
   float k0;           // exponent offset: x = s * c2 + k0
   uint32_t f_or, f_and;
@@ -304,10 +311,17 @@ struct QBlock {
   int ecnt;           // hit-tile words written
 };
 
-template <int KMAX>
+template <int KMAX, int D>
 __global__ void __launch_bounds__(256, 2)
 cmp_mfma_kernel(FwdParams p) {
-  using Shape = CmpShape<KMAX>;
+  using Shape = CmpShape<KMAX, D>;
+  using Dims = CmpDims<D>;
+  constexpr int kD = D;
+  constexpr int kKRow = Dims::kKRow;
+  constexpr int kKTileElems = Dims::kKTileElems;
+  constexpr int kVTileElems = Dims::kVTileElems;
+  constexpr int KS = Dims::KS;
+  constexpr int VB = Dims::VB;
   constexpr int kCap = Shape::kCap;
   constexpr int kEnt = Shape::kEnt;
   // the key/value ring while the passes run; afterwards the same bytes hold
@@ -349,16 +363,16 @@ cmp_mfma_kernel(FwdParams p) {
   const int nbs = j1 - j0;
 
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  QBlock<KMAX> blk[2];
+  QBlock<KMAX, D> blk[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    QBlock<KMAX>& B = blk[x];
+    QBlock<KMAX, D>& B = blk[x];
     B.qi = q_begin + wv * 64 + x * kBlockQ + (lane & 31);
     B.valid = B.qi < q_end;
     B.t = B.valid ? p.perm[B.qi] : 0;
     B.q_row = Q + (static_cast<int64_t>(B.t) * p.h_q + h) * kD;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4 u = {0u, 0u, 0u, 0u};
       if (B.valid) u = *reinterpret_cast<const u32x4*>(B.q_row + 16 * ks + 8 * half);
       B.qb[ks] = __builtin_bit_cast(bf16x8, u);
@@ -371,36 +385,53 @@ cmp_mfma_kernel(FwdParams p) {
   const int n_kt = kt1 - kt0;
 
   // cooperative tile staging: thread -> 16 bytes of the key tile / value tile
-  const int k_row = tid >> 3, k_chunk = tid & 7;      // key tile: 32 rows x 8 chunks
-  const int v_row = tid >> 2, v_chunk = tid & 3;      // value tile: 64 rows x 4 chunks
+  // (D = 32: the first 128 threads stage each tile)
+  const int k_row = tid / (kD / 8), k_chunk = tid % (kD / 8);   // key tile: 32 rows x D / 8 chunks
+  const int v_row = tid >> 2, v_chunk = tid & 3;                // value tile: D rows x 4 chunks
+  // (compile-time true when every thread stages)
+  const bool k_stager = Dims::kKStagers >= 256 || tid < Dims::kKStagers;
+  const bool v_stager = Dims::kVStagers >= 256 || tid < Dims::kVStagers;
   const uint16_t* kg = KB + (static_cast<int64_t>(kt0) * kKeyTile + k_row) * kD + 8 * k_chunk;
   const uint16_t* vg = VT + (static_cast<int64_t>(kt0) * kD + v_row) * kKeyTile + 8 * v_chunk;
-  auto load_k = [&](int rel) { return *reinterpret_cast<const u32x4*>(kg + static_cast<int64_t>(rel) * kKeyTile * kD); };
-  auto load_v = [&](int rel) { return *reinterpret_cast<const u32x4*>(vg + static_cast<int64_t>(rel) * kKeyTile * kD); };
+  auto load_k = [&](int rel) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (k_stager) u = *reinterpret_cast<const u32x4*>(kg + static_cast<int64_t>(rel) * kKeyTile * kD);
+    return u;
+  };
+  auto load_v = [&](int rel) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (v_stager) u = *reinterpret_cast<const u32x4*>(vg + static_cast<int64_t>(rel) * kKeyTile * kD);
+    return u;
+  };
   const int ks_dst = k_row * kKRow + 8 * k_chunk;
   const int vs_dst = v_row * kVRow + 8 * v_chunk;
   const int ka = (lane & 31) * kKRow + 8 * half;
   const int va = (lane & 31) * kVRow + 8 * half;
+  auto store_k = [&](int slot, const u32x4& u) {
+    if (k_stager) *reinterpret_cast<u32x4*>(k_lds + slot * kKTileElems + ks_dst) = u;
+  };
+  auto store_v = [&](int slot, const u32x4& u) {
+    if (v_stager) *reinterpret_cast<u32x4*>(v_lds + slot * kVTileElems + vs_dst) = u;
+  };
 
   // MFMA A operands of key tile rel (slot rel & 1): rows = blocks, k = dims
-  auto read_k = [&](int rel, bf16x8 (&a)[4]) {
+  auto read_k = [&](int rel, bf16x8 (&a)[KS]) {
     const uint16_t* kl = k_lds + (rel & 1) * kKTileElems + ka;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = lds_b128(kl + 16 * ks);
+    for (int ks = 0; ks < KS; ++ks) a[ks] = lds_b128(kl + 16 * ks);
   };
   // MFMA A operands of value tile rel: rows = dims (0..31, 32..63), k = blocks
-  auto read_v = [&](int rel, bf16x8 (&a)[4]) {
+  auto read_v = [&](int rel, bf16x8 (&a)[2 * VB]) {
     const uint16_t* vl = v_lds + (rel & 1) * kVTileElems + va;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      a[2 * ks] = lds_b128(vl + 16 * ks);
-      a[2 * ks + 1] = lds_b128(vl + 32 * kVRow + 16 * ks);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) a[ks * VB + vb] = lds_b128(vl + vb * 32 * kVRow + 16 * ks);
   };
-  auto qk = [&](const bf16x8 (&a)[4], const bf16x8 (&qb)[4]) {
+  auto qk = [&](const bf16x8 (&a)[KS], const bf16x8 (&qb)[KS]) {
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qb[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qb[ks], s, 0, 0, 0);
     return s;
   };
   // keys of tile rel outside [j0, j1) get -FLT_MAX; returns the in-range mask
@@ -450,7 +481,7 @@ cmp_mfma_kernel(FwdParams p) {
     for (int x = 0; x < 2; ++x) {
       float qn2 = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float qv = static_cast<float>(blk[x].qb[ks][e]);
@@ -473,14 +504,14 @@ cmp_mfma_kernel(FwdParams p) {
   //   glog 32: two tiles (16 logits each), glog 16: one tile,
   //   glog 8: half a tile, glog 4: a quarter tile.
   const int glog = n1 >= 96 ? 32 : n1 >= 48 ? 16 : n1 >= 24 ? 8 : 4;
-  auto list_insert = [&](QBlock<KMAX>& B, float m) {
+  auto list_insert = [&](QBlock<KMAX, D>& B, float m) {
 #pragma unroll
     for (int i = KMAX - 1; i >= 1; --i) B.L[i] = __builtin_amdgcn_fmed3f(B.L[i - 1], m, B.L[i]);
     B.L[0] = fmaxf(B.L[0], m);
   };
   // the logits of tile rel of block B into its list (glog 32: into the open
   // two-tile group, inserted after the odd tile)
-  auto group_update = [&](QBlock<KMAX>& B, int rel, auto masked) {
+  auto group_update = [&](QBlock<KMAX, D>& B, int rel, auto masked) {
     if (decltype(masked)::value) mask(rel, B.s);
     const f32x16& s = B.s;
     if (glog >= 16) {
@@ -513,18 +544,20 @@ cmp_mfma_kernel(FwdParams p) {
       kg1 = static_cast<const uint16_t*>(p.probe) +
             (static_cast<int64_t>(h * p.max_probe_slots + pslot) * kProbeBlocks + k_row) * kD + 8 * k_chunk;
     auto load_k1 = [&](int rel) {
-      return *reinterpret_cast<const u32x4*>(kg1 + static_cast<int64_t>(rel) * kKeyTile * kD);
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (k_stager) u = *reinterpret_cast<const u32x4*>(kg1 + static_cast<int64_t>(rel) * kKeyTile * kD);
+      return u;
     };
     u32x4 kr = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(k_lds + ks_dst) = load_k1(0);
+    store_k(0, load_k1(0));
     if (n1 > 1) kr = load_k1(1);
     // step rel: S of block A for tile rel next to block B's update for tile
     // rel - 1, then S of block B next to block A's update
     auto step = [&](int rel, auto mask_a, auto has_b, auto mask_b) {
       __syncthreads();  // key tile rel stored; everyone is done with tile rel - 1
-      if (rel + 1 < n1) *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTileElems + ks_dst) = kr;
+      if (rel + 1 < n1) store_k((rel + 1) & 1, kr);
       if (rel + 2 < n1) kr = load_k1(rel + 2);
-      bf16x8 a[4];
+      bf16x8 a[KS];
       read_k(rel, a);
       const f32x16 sa = qk(a, blk[0].qb);
       if (decltype(has_b)::value) group_update(blk[1], rel - 1, mask_b);
@@ -550,7 +583,7 @@ cmp_mfma_kernel(FwdParams p) {
   // ---------------- per-query constants for pass 2
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    QBlock<KMAX>& B = blk[x];
+    QBlock<KMAX, D>& B = blk[x];
     // row maximum, and the best lower bound on the KMAX-th largest logit
     // (hence on the k-th, k <= KMAX): for any split a + b = KMAX the two
     // lanes hold a and b distinct elements >= min(L_this[a-1], L_other[b-1])
@@ -587,8 +620,8 @@ cmp_mfma_kernel(FwdParams p) {
       }
     }
     B.k0 += kTruncLog2;  // after the sign decisions: the shift is a factor of p only
-    B.o0 = f32x16{};
-    B.o1 = f32x16{};
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) B.o[vb] = f32x16{};
     B.l0 = 0.f;
     B.l1 = 0.f;
     B.ecnt = 0;
@@ -598,7 +631,7 @@ cmp_mfma_kernel(FwdParams p) {
   // probabilities, row sums and the candidate word of block x's tile rel;
   // returns P^T as two bf16 B operands (truncated: v_perm_b32 takes the high
   // halves of two float32 values)
-  auto softmax_tile = [&](QBlock<KMAX>& B, int x, int rel, bf16x8 (&pb)[2], auto masked) {
+  auto softmax_tile = [&](QBlock<KMAX, D>& B, int x, int rel, bf16x8 (&pb)[2], auto masked) {
     uint32_t valid = 0xFFFFu;
     if (decltype(masked)::value) valid = mask(rel, B.s);
     float pr[16];
@@ -629,23 +662,27 @@ cmp_mfma_kernel(FwdParams p) {
       pb[ks] = __builtin_bit_cast(bf16x8, u);
     }
   };
-  auto pv = [&](QBlock<KMAX>& B, const bf16x8 (&a)[4], const bf16x8 (&pb)[2]) {
+  auto pv = [&](QBlock<KMAX, D>& B, const bf16x8 (&a)[2 * VB], const bf16x8 (&pb)[2]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      B.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * ks], pb[ks], B.o0, 0, 0, 0);
-      B.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * ks + 1], pb[ks], B.o1, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+        B.o[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks * VB + vb], pb[ks], B.o[vb], 0, 0, 0);
   };
   {
     u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
     __syncthreads();  // every wave is done with pass 1's ring
-    *reinterpret_cast<u32x4*>(k_lds + ks_dst) = load_k(0);
-    *reinterpret_cast<u32x4*>(v_lds + vs_dst) = load_v(0);
+    store_k(0, load_k(0));
+    store_v(0, load_v(0));
     if (n_kt > 1) {
       kr = load_k(1);
       vr = load_v(1);
     }
-    bf16x8 va_prev[4];   // value tile rel - 1 (MFMA A operands)
+    bf16x8 va_prev[2 * VB];   // value tile rel - 1 (MFMA A operands)
+    // MFMAs of a step (two blocks' S and P V), and the VALU instructions
+    // placed after each (about 160 per step for the two softmaxes)
+    constexpr int kStepMfma = 2 * (KS + 2 * VB);
+    constexpr int kStepValu = 160 / kStepMfma;
     bf16x8 pa[2];        // P^T of block A for tile rel - 1
     // step rel: block A's P V for tile rel - 1 and its S for tile rel issue
     // next to block B's softmax for tile rel - 1; block B's P V for tile
@@ -655,14 +692,14 @@ cmp_mfma_kernel(FwdParams p) {
     auto step = [&](int rel, auto mask_a, auto has_b, auto mask_b) {
       __syncthreads();  // tiles rel stored; everyone is done with the tiles of rel - 1
       if (rel + 1 < n_kt) {
-        *reinterpret_cast<u32x4*>(k_lds + ((rel + 1) & 1) * kKTileElems + ks_dst) = kr;
-        *reinterpret_cast<u32x4*>(v_lds + ((rel + 1) & 1) * kVTileElems + vs_dst) = vr;
+        store_k((rel + 1) & 1, kr);
+        store_v((rel + 1) & 1, vr);
       }
       if (rel + 2 < n_kt) {
         kr = load_k(rel + 2);
         vr = load_v(rel + 2);
       }
-      bf16x8 a[4];
+      bf16x8 a[KS];
       read_k(rel, a);
       if (decltype(has_b)::value) pv(blk[0], va_prev, pa);
       const f32x16 sa = qk(a, blk[0].qb);
@@ -675,7 +712,7 @@ cmp_mfma_kernel(FwdParams p) {
       blk[0].s = sa;
       read_v(rel, va_prev);
       softmax_tile(blk[0], 0, rel, pa, mask_a);
-      if (decltype(has_b)::value) interleave_mfma_valu<16, 10>();
+      if (decltype(has_b)::value) interleave_mfma_valu<kStepMfma, kStepValu>();
     };
     run_tiles(step);
     pv(blk[0], va_prev, pa);
@@ -688,7 +725,7 @@ cmp_mfma_kernel(FwdParams p) {
   // window kernel, which runs first, wrote it)
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    QBlock<KMAX>& B = blk[x];
+    QBlock<KMAX, D>& B = blk[x];
     const float lsum = B.l0 + B.l1;
     const float lsum_q = lsum + __shfl_xor(lsum, 32);
     const float l_q = lsum_q * kTruncInv;
@@ -700,12 +737,16 @@ cmp_mfma_kernel(FwdParams p) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int d = 8 * rb + 4 * half;
-        float4 a = *reinterpret_cast<float4*>(dst + d);
-        float4 b = *reinterpret_cast<float4*>(dst + 32 + d);
-        a.x += B.o0[4 * rb] * f; a.y += B.o0[4 * rb + 1] * f; a.z += B.o0[4 * rb + 2] * f; a.w += B.o0[4 * rb + 3] * f;
-        b.x += B.o1[4 * rb] * f; b.y += B.o1[4 * rb + 1] * f; b.z += B.o1[4 * rb + 2] * f; b.w += B.o1[4 * rb + 3] * f;
-        *reinterpret_cast<float4*>(dst + d) = a;
-        *reinterpret_cast<float4*>(dst + 32 + d) = b;
+        float4 a[VB];
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) a[vb] = *reinterpret_cast<float4*>(dst + 32 * vb + d);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const f32x16& o = B.o[vb];
+          a[vb].x += o[4 * rb] * f; a[vb].y += o[4 * rb + 1] * f; a[vb].z += o[4 * rb + 2] * f; a[vb].w += o[4 * rb + 3] * f;
+        }
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) *reinterpret_cast<float4*>(dst + 32 * vb + d) = a[vb];
       }
       if (p.lse && half == 0) {
         // p_j = 2^(s_j scale log2e + k0), so the denominator of the logits is
@@ -721,7 +762,7 @@ cmp_mfma_kernel(FwdParams p) {
   const int qbase = (wv * kBlockQ + (lane & 31)) * kSlots;
   const int k_eff = min(p.topk, nbs);
   const uint16_t* kb0 = KB + static_cast<int64_t>(kt0) * kKeyTile * kD;
-  auto finish = [&](QBlock<KMAX>& B, int x) {
+  auto finish = [&](QBlock<KMAX, D>& B, int x) {
     // clear the query's slots (each lane half clears one half of them)
     {
       const u32x4 z = {0u, 0u, 0u, 0u};
@@ -824,9 +865,10 @@ cmp_mfma_kernel(FwdParams p) {
 // of the sequence in float32 and keeps a sorted list of its best KMAX (value
 // descending, block ascending); each wave then pops its KMAX best with wave
 // reductions, and wave 0 ranks the 4 x KMAX survivors.
-template <int KMAX>
+template <int KMAX, int D>
 __global__ void __launch_bounds__(256)
 topk_fixup_kernel(FwdParams p) {
+  constexpr int kD = D;
   __shared__ float wv_val[4 * KMAX];
   __shared__ int wv_idx[4 * KMAX];
   const int tid = threadIdx.x;
@@ -942,14 +984,24 @@ hipError_t launch_cmp_probe(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t
 
 hipError_t launch_cmp_mfma(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
   const dim3 grid(p.max_tiles, p.h_q);
-  if (p.topk <= 16) cmp_mfma_kernel<16><<<grid, 256, 0, stream>>>(p);
-  else cmp_mfma_kernel<32><<<grid, 256, 0, stream>>>(p);
+  if (p.d == 32) {
+    if (p.topk <= 16) cmp_mfma_kernel<16, 32><<<grid, 256, 0, stream>>>(p);
+    else cmp_mfma_kernel<32, 32><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (p.topk <= 16) cmp_mfma_kernel<16, 64><<<grid, 256, 0, stream>>>(p);
+    else cmp_mfma_kernel<32, 64><<<grid, 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_topk_fixup(const FwdParams& p, ssa_dtype /*dtype*/, hipStream_t stream) {
-  if (p.topk <= 16) topk_fixup_kernel<16><<<2048, 256, 0, stream>>>(p);
-  else topk_fixup_kernel<32><<<2048, 256, 0, stream>>>(p);
+  if (p.d == 32) {
+    if (p.topk <= 16) topk_fixup_kernel<16, 32><<<2048, 256, 0, stream>>>(p);
+    else topk_fixup_kernel<32, 32><<<2048, 256, 0, stream>>>(p);
+  } else {
+    if (p.topk <= 16) topk_fixup_kernel<16, 64><<<2048, 256, 0, stream>>>(p);
+    else topk_fixup_kernel<32, 64><<<2048, 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

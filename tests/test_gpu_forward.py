@@ -75,8 +75,11 @@ def _check_pooled(got, ref, dtype):
     # kernel's 32-entry list variant)
     dict(seqs=[2000, 0, 1100], h_q=4, h_kv=4, head_dim=64, topk=32, dtype="bf16"),
     dict(seqs=[1600], h_q=2, h_kv=2, head_dim=64, topk=20, dtype="bf16"),
-    # one query head per key/value head at head_dim 32 (the generic kernel), k above 16
+    # one query head per key/value head at head_dim 32 (the compressed MFMA
+    # kernel's D = 32 variant), k at most 16 and above 16
+    dict(seqs=[1500, 0, 900], h_q=4, h_kv=4, head_dim=32, topk=16, dtype="bf16"),
     dict(seqs=[800, 450], h_q=4, h_kv=4, head_dim=32, topk=20, dtype="bf16"),
+    dict(seqs=[333, 64, 1], h_q=2, h_kv=2, head_dim=32, topk=4, dtype="bf16"),
     # grouped heads, 16 query heads per key/value head (the MFMA group path)
     dict(seqs=[900, 0, 701], h_q=16, h_kv=1, head_dim=32, topk=8, dtype="bf16"),
     dict(seqs=[1203], h_q=32, h_kv=2, head_dim=64, topk=16, dtype="bf16"),
@@ -201,7 +204,7 @@ def test_varlen_workload5_sampled():
 
 
 @pytest.mark.parametrize("h_q,h_kv,head_dim,topk", [(4, 2, 64, 16), (16, 1, 32, 16), (32, 2, 64, 16),
-                                                   (4, 4, 64, 16), (4, 4, 64, 32)])
+                                                   (4, 4, 64, 16), (4, 4, 64, 32), (4, 4, 32, 16)])
 def test_zero_queries_pick_first_blocks(h_q, h_kv, head_dim, topk):
     # every score ties, so the lowest block ids of the sequence are chosen
     # (on the one-head-per-group kernel every query overflows its candidate
@@ -250,18 +253,18 @@ def test_gqa_top_blocks_in_one_lane(head_dim):
     assert np.isin(sel[:, 0, :], fav).mean() > 0.99
 
 
-@pytest.mark.parametrize("q_scale", [1.0, 4.0])
-def test_probe_bound_paths_full(q_scale):
+@pytest.mark.parametrize("head_dim,q_scale", [(64, 1.0), (64, 4.0), (32, 1.0), (32, 6.0)])
+def test_probe_bound_paths_full(head_dim, q_scale):
     # a sequence with more than 512 blocks takes the compressed kernel's
-    # first pass over its 512 largest-norm pooled keys; queries scaled by 4
-    # break the magnitude guard (|q| max |Kbar| scale log2 e <= 60), so the
-    # same sequence takes the pass over all of its key tiles
-    wl = make_custom([14000, 700], grid_res=128, n_prims=4, topk=16, h_q=4, h_kv=4, head_dim=64, dtype="bf16",
-                     seed=51)
+    # first pass over its 512 largest-norm pooled keys; scaled queries break
+    # the magnitude guard (|q| max |Kbar| scale log2 e <= 60), so the same
+    # sequence takes the pass over all of its key tiles
+    wl = make_custom([14000, 700], grid_res=128, n_prims=4, topk=16, h_q=4, h_kv=4, head_dim=head_dim,
+                     dtype="bf16", seed=51)
     assert np.diff(P.oracle_blocks(wl).seq_blk_off).max() > 512
     if q_scale != 1.0:
         wl.q = bf16_bits_to_f32(bf16_bits_from_f32(wl.q * np.float32(q_scale)))
-    _full_compare(wl, tag=f"probe paths, q x {q_scale:g}")
+    _full_compare(wl, tag=f"probe paths D={head_dim}, q x {q_scale:g}")
 
 
 @pytest.mark.parametrize("h_q,h_kv,head_dim,topk", [(32, 2, 64, 16), (16, 1, 32, 8)])
@@ -367,7 +370,7 @@ def test_many_sequences_full():
 
 
 @pytest.mark.parametrize("h_q,h_kv,head_dim,dtype", [(2, 2, 32, "f32"), (4, 4, 64, "bf16"), (16, 1, 32, "bf16"),
-                                                   (32, 2, 64, "bf16")])
+                                                   (32, 2, 64, "bf16"), (2, 2, 32, "bf16")])
 def test_dense_reduction(h_q, h_kv, head_dim, dtype):
     # one window over the grid, voxel blocks, top-k covering every block:
     # every branch is dense attention and out = (G0 + G1 + G2) * dense (the
