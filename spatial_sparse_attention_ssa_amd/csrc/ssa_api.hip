@@ -116,10 +116,11 @@ int64_t nb_capacity(const ssa_blocks* b) {
   return (c + ssa::kKeyTile - 1) / ssa::kKeyTile * ssa::kKeyTile;
 }
 
-// the MFMA kernels cover bfloat16 with head_dim 32 or 64 and either one query
-// head per key/value head or 16 query heads per key/value head
+// the MFMA kernels cover bfloat16 with head_dim 32 or 64 and 1 to 16 query
+// heads per key/value head (groups of 2 to 16 take the grouped kernels)
 bool use_gqa_path(const ssa_attn* a) {
-  return a->dtype == SSA_BF16 && (a->head_dim == 32 || a->head_dim == 64) && a->h_q == 16 * a->h_kv;
+  const int group = a->h_q / a->h_kv;
+  return a->dtype == SSA_BF16 && (a->head_dim == 32 || a->head_dim == 64) && group >= 2 && group <= 16;
 }
 bool use_mfma_path(const ssa_attn* a) {
   return (a->dtype == SSA_BF16 && (a->head_dim == 32 || a->head_dim == 64) && a->h_q == a->h_kv) ||

@@ -1,5 +1,5 @@
 // Compressed-block attention and top-k block selection for grouped query
-// heads on MFMA (bf16, D = 32 or 64, 16 query heads per key/value head).
+// heads on MFMA (bf16, D = 32 or 64, 2 to 16 query heads per key/value head).
 //
 // Direct3D-S2 page, "Method": every query attends to the mean-pooled blocks of
 // its sequence, and the attention scores choose the top-k blocks; LSRM
@@ -28,7 +28,10 @@
 //    exactly only when the bound 16 * max_h p_h reaches the admission score,
 //    which most pairs do not, so most pairs cost an FMA and a max per head
 //    instead of an exponential.  Exact: the top k of the blocks seen so far
-//    are always among the admitted candidates (see the kernel).
+//    are always among the admitted candidates (see the kernel).  A group of
+//    G < 16 heads fills heads 0 .. G - 1 of the 16 and leaves the rest empty
+//    (zero query, probability 0), so the group score and its order are those
+//    of the G heads; the bound uses 2^ceil(log2 G) instead of 16.
 #include <float.h>
 #include <math.h>
 #include <limits.h>
@@ -45,7 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kGroup = 16;            // query heads per key/value head on this path
+constexpr int kGroup = 16;            // heads per group in the top-k kernel's tiles (G <= 16 of them real)
 constexpr int kTopkTile = 16;         // sorted tokens per workgroup of the top-k kernel
 constexpr float kRescale = 8.0f;      // log2 headroom before the running shift moves
 // bf16 P by truncation (the fixed-shift loop): the mean relative loss of
@@ -417,6 +420,9 @@ gqa_topk_kernel(FwdParams p) {
   const int k_eff = min(p.topk, nbs);
   const float c2 = p.scale * kLog2e;
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+  const int G = p.h_q / p.h_kv;   // real heads of the 16 (2 .. 16)
+  // log2 of the bound's factor (a power of two >= G) plus a rounding margin
+  const float lg_bound = G > 8 ? 4.001f : G > 4 ? 3.001f : G > 2 ? 2.001f : 1.001f;
 
   // row blocks x = 0, 1 of this wave: tokens 4 wv + 2 x + {0, 1} (the wave's
   // tokens 2 x + 0 and 2 x + 1); A operand row (lane % 32) = (token
@@ -432,9 +438,9 @@ gqa_topk_kernel(FwdParams p) {
     tk[x][0] = t_begin + 4 * wv + 2 * x;
     tk[x][1] = tk[x][0] + 1;
     const int mine = tk[x][l32 >> 4];
-    const bool ok = mine < t_end;
+    const bool ok = mine < t_end && (lane & 15) < G;
     const int tt = ok ? p.perm[mine] : 0;
-    const int hq = g * kGroup + (lane & 15);
+    const int hq = g * G + (lane & 15);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 u = {0u, 0u, 0u, 0u};
@@ -446,9 +452,9 @@ gqa_topk_kernel(FwdParams p) {
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * half + (r & 3);
       const int pos = tk[x][row >> 4];
-      cz[x][r] = -INFINITY;  // no probability for a missing token
-      if (pos < t_end)
-        cz[x][r] = -p.norm[static_cast<int64_t>(p.perm[pos]) * p.h_q + g * kGroup + (row & 15)] / c2;
+      cz[x][r] = -INFINITY;  // no probability for a missing token or an empty head
+      if (pos < t_end && (row & 15) < G)
+        cz[x][r] = -p.norm[static_cast<int64_t>(p.perm[pos]) * p.h_q + g * G + (row & 15)] / c2;
     }
   }
 
@@ -586,7 +592,7 @@ gqa_topk_kernel(FwdParams p) {
       } else if (tau0 >= 0.f) {
         // scores are >= 0, so their float bits order like their values
         min_key[t] = static_cast<uint64_t>(__float_as_uint(tau0)) << 32;
-        theta[t] = tau0 > 0.f ? (__log2f(tau0) - 4.001f) / c2 : -INFINITY;
+        theta[t] = tau0 > 0.f ? (__log2f(tau0) - lg_bound) / c2 : -INFINITY;
       } else {
         min_key[t] = 0ull;       // fewer than k scored blocks: admit all
         theta[t] = -INFINITY;
@@ -596,9 +602,9 @@ gqa_topk_kernel(FwdParams p) {
 
   // ---------------- main pass over the sequence's tiles
   // A pair (token, block) whose largest z over the heads, m, satisfies
-  // 16 * 2^(m c2) < (the admission score) cannot be admitted, since its score
-  // is a sum of 16 terms 2^(z_h c2); theta holds log2 of that score minus 4
-  // (and a margin for rounding), divided by c2.  Pairs that pass are queued
+  // 2^lg * 2^(m c2) < (the admission score) cannot be admitted, since its
+  // score is a sum of G <= 2^lg terms 2^(z_h c2); theta holds log2 of that
+  // score minus lg (and a margin for rounding), divided by c2.  Pairs that pass are queued
   // with their 16 values z; a batch computes their scores exactly (in the
   // warm-up's arithmetic), and a pair whose key
   // (score, then lower block first) reaches min_key joins its token's list.
@@ -632,7 +638,7 @@ gqa_topk_kernel(FwdParams p) {
     cnt[t] = k_eff;   // n > kCompact >= k_eff
     min_key[t] = L[k_eff - 1] + 1;
     const float smin = __uint_as_float(static_cast<uint32_t>(min_key[t] >> 32));
-    theta[t] = smin > 0.f ? (__log2f(smin) - 4.001f) / c2 : -INFINITY;
+    theta[t] = smin > 0.f ? (__log2f(smin) - lg_bound) / c2 : -INFINITY;
   };
   auto process = [&]() {
     const int nbat = min(qn, 64);

@@ -90,7 +90,7 @@ int main() {
       {attn(16, 16, 64, 16, SSA_BF16, 1.f / 0.f), SSA_ERR_INVALID_ARGUMENT},
       {attn(16, 16, 64, 16, SSA_BF16, 0.f, 5), SSA_ERR_INVALID_ARGUMENT},
       {attn(16, 16, 64, 16, SSA_F32, 0.f, 1), SSA_ERR_UNSUPPORTED},
-      {attn(8, 2, 64, 16, SSA_BF16, 0.f, 1), SSA_ERR_UNSUPPORTED},
+      {attn(32, 1, 64, 16, SSA_BF16, 0.f, 1), SSA_ERR_UNSUPPORTED},   // geometric routing off the MFMA layouts
       {attn(16, 16, 64, 16, SSA_BF16, 0.f, 1), SSA_ERR_INVALID_ARGUMENT},   // no coordinates in the blocks
   };
   ssa_blocks fb = fake_blocks(1000, 1, -1);

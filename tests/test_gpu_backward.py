@@ -91,6 +91,7 @@ def _full_compare(wl, seed, one_hot=False):
     dict(seqs=[900, 0, 300], h_q=4, h_kv=4, head_dim=64, topk=24, dtype="bf16"),
     dict(seqs=[800, 450], h_q=4, h_kv=4, head_dim=32, topk=20, dtype="bf16"),
     dict(seqs=[700, 0, 433], h_q=4, h_kv=4, head_dim=32, topk=8, dtype="bf16"),
+    dict(seqs=[600, 257], h_q=8, h_kv=1, head_dim=64, topk=8, dtype="bf16"),
 ])
 def test_small_backward_full(case):
     wl = make_custom(case["seqs"], grid_res=64, n_prims=3, topk=case["topk"], h_q=case["h_q"],

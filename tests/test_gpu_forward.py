@@ -70,7 +70,11 @@ def _check_pooled(got, ref, dtype):
     dict(seqs=[1500, 0, 900], h_q=4, h_kv=4, head_dim=64, topk=16, dtype="bf16"),
     dict(seqs=[2100], h_q=8, h_kv=2, head_dim=32, topk=8, dtype="bf16"),
     dict(seqs=[700, 1300], h_q=2, h_kv=2, head_dim=32, topk=4, dtype="f32"),
+    # groups of 2, 4 and 8 query heads (the grouped MFMA kernels with the
+    # rest of the top-k kernel's 16 heads empty)
     dict(seqs=[333, 64, 1], h_q=2, h_kv=1, head_dim=64, topk=32, dtype="bf16"),
+    dict(seqs=[1700, 0, 600], h_q=16, h_kv=2, head_dim=64, topk=16, dtype="bf16"),
+    dict(seqs=[900, 1200], h_q=12, h_kv=4, head_dim=32, topk=8, dtype="bf16"),
     # one query head per key/value head with k above 16 (the compressed
     # kernel's 32-entry list variant)
     dict(seqs=[2000, 0, 1100], h_q=4, h_kv=4, head_dim=64, topk=32, dtype="bf16"),
@@ -333,15 +337,16 @@ def test_gqa_constant_keys_pick_first_blocks(head_dim):
         assert (sel[toks][:, :, :len(expect)] == expect).all()
 
 
-def test_gqa_probe_warmup_full():
+@pytest.mark.parametrize("h_q,h_kv", [(16, 1), (8, 2)])
+def test_gqa_probe_warmup_full(h_q, h_kv):
     # grouped heads on a sequence of more than 512 blocks (its lower bound on
     # each token's k-th score comes from the probe set) beside a short one
     # (bounded from its own blocks); compared in full with the oracle
-    wl = make_custom([14000, 700], grid_res=128, n_prims=4, topk=16, h_q=16, h_kv=1, head_dim=32, dtype="bf16",
+    wl = make_custom([14000, 700], grid_res=128, n_prims=4, topk=16, h_q=h_q, h_kv=h_kv, head_dim=32, dtype="bf16",
                      seed=54)
     nbs = np.diff(P.oracle_blocks(wl).seq_blk_off)
     assert nbs[0] > 512 >= nbs[1]
-    _full_compare(wl, tag="grouped probe warm-up")
+    _full_compare(wl, tag=f"grouped probe warm-up {h_q}/{h_kv}")
 
 
 def dense_cube(n, side, seed):
@@ -370,7 +375,7 @@ def test_many_sequences_full():
 
 
 @pytest.mark.parametrize("h_q,h_kv,head_dim,dtype", [(2, 2, 32, "f32"), (4, 4, 64, "bf16"), (16, 1, 32, "bf16"),
-                                                   (32, 2, 64, "bf16"), (2, 2, 32, "bf16")])
+                                                   (32, 2, 64, "bf16"), (2, 2, 32, "bf16"), (8, 2, 32, "bf16")])
 def test_dense_reduction(h_q, h_kv, head_dim, dtype):
     # one window over the grid, voxel blocks, top-k covering every block:
     # every branch is dense attention and out = (G0 + G1 + G2) * dense (the
