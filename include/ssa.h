@@ -106,8 +106,7 @@ typedef enum {
    * routing"): the smallest squared distance between the query's voxel
    * centre and the centres of the block's voxels, ties to the lower block id;
    * the same for every key/value group.  bfloat16 layouts of the MFMA path
-   * only (D = 32 or 64 with one query head per key/value head, or 16 query
-   * heads per key/value head) */
+   * only (D = 32 or 64 with 1 to 16 query heads per key/value head) */
   SSA_ROUTE_GEOMETRIC = 1
 } ssa_routing;
 
