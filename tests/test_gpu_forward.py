@@ -14,6 +14,7 @@ import torch
 import oracle
 from oracle import parallel as oracle_pool
 from tests import _parity as P
+import spatial_sparse_attention_ssa_amd as ssa
 from workloads import make_custom, make_workload
 from workloads.tensors import bf16_bits_from_f32, bf16_bits_to_f32
 
@@ -407,3 +408,21 @@ def test_run_to_run_bit_identical():
     a = P.gpu_forward(wl, gb, return_topk=True)
     b = P.gpu_forward(wl, gb, return_topk=True)
     assert torch.equal(a["out"], b["out"]) and torch.equal(a["topk"], b["topk"])
+
+
+@pytest.mark.parametrize("h_q,h_kv,head_dim", [(4, 4, 64), (16, 1, 32), (2, 2, 32)])
+def test_empty_token_set_forward_and_backward(h_q, h_kv, head_dim):
+    # no tokens in any of the batch's sequences: every call succeeds and
+    # returns empty tensors (the forward and backward launch nothing)
+    wl = make_custom(None, coords=np.zeros((0, 3), np.int64), cu_seqlens=[0, 0, 0], grid_res=64, topk=8, h_q=h_q,
+                     h_kv=h_kv, head_dim=head_dim, dtype="bf16", seed=1)
+    assert wl.n_tokens == 0
+    gb = P.gpu_build(wl)
+    res = P.gpu_forward(wl, gb, return_topk=True)
+    assert tuple(res["out"].shape) == (0, h_q, head_dim) and res["topk"].shape[0] == 0
+    dt = torch.bfloat16
+    q, k, v, g = (P.to_dev(a, dt) for a in (wl.q, wl.k, wl.v, wl.gates))
+    saved = ssa.forward_train(gb, q, k, v, g, wl.topk)
+    grads = ssa.backward(gb, q, k, v, g, saved, torch.zeros_like(q))
+    torch.cuda.synchronize()
+    assert tuple(grads["dq"].shape) == (0, h_q, head_dim) and tuple(grads["dk"].shape) == (0, h_kv, head_dim)
