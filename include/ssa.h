@@ -41,7 +41,7 @@ extern "C" {
 typedef enum {
   SSA_OK = 0,
   SSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad geometry, out-of-range coords (when synced) */
-  SSA_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (head_dim, top-k, key width) */
+  SSA_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement (head_dim, top-k, key width) */
   SSA_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than the *_workspace() query */
   SSA_ERR_DEVICE = 4            /* a HIP runtime call or kernel launch failed */
 } ssa_status;
