@@ -99,6 +99,8 @@ def test_small_full(case):
 @pytest.mark.parametrize("case", [
     dict(seqs=[1500, 0, 700], h_q=4, h_kv=4, head_dim=64, topk=16),
     dict(seqs=[900, 400], h_q=16, h_kv=1, head_dim=32, topk=8),
+    dict(seqs=[1000, 500], h_q=4, h_kv=4, head_dim=32, topk=16),
+    dict(seqs=[1200], h_q=8, h_kv=2, head_dim=64, topk=8),
 ])
 def test_shifted_windows_full(case):
     # window origin at -m_win / 2 on every axis (shifted windows)
@@ -117,6 +119,8 @@ def test_shifted_windows_headline_sampled():
     dict(seqs=[1500, 0, 700], h_q=4, h_kv=4, head_dim=64, topk=16),
     dict(seqs=[900, 400], h_q=16, h_kv=1, head_dim=32, topk=8),
     dict(seqs=[600], h_q=32, h_kv=2, head_dim=64, topk=32),
+    dict(seqs=[1100, 300], h_q=4, h_kv=4, head_dim=32, topk=16),
+    dict(seqs=[800], h_q=8, h_kv=2, head_dim=32, topk=8),
 ])
 def test_geometric_routing_full(case):
     # the k blocks nearest to each query voxel (exact integer distances): the

@@ -30,15 +30,16 @@ def _noalloc_forward(blocks, q, k, v, gates, topk):
 
 
 @pytest.mark.parametrize("order", ["large_then_small"])
-def test_noalloc_forward_matches_forward(order):
+@pytest.mark.parametrize("h_q,h_kv,head_dim", [(4, 4, 64), (8, 2, 32)])
+def test_noalloc_forward_matches_forward(order, h_q, h_kv, head_dim):
     # the first input has a sequence of more than 512 blocks (the compressed
-    # kernel's probe path); the second is smaller
+    # kernels' probe paths); the second is smaller
     cases = [dict(seqs=[14000, 700], grid_res=128, n_prims=4, seed=71),
              dict(seqs=[1500, 0, 900], grid_res=64, n_prims=3, seed=72)]
     for c in cases:
-        wl = make_custom(c["seqs"], grid_res=c["grid_res"], n_prims=c["n_prims"], topk=16, h_q=4, h_kv=4,
-                         head_dim=64, dtype="bf16", seed=c["seed"])
-        print(f"noalloc case: {c['seqs']} tokens, 4/4 heads, D = 64", flush=True)
+        wl = make_custom(c["seqs"], grid_res=c["grid_res"], n_prims=c["n_prims"], topk=16, h_q=h_q, h_kv=h_kv,
+                         head_dim=head_dim, dtype="bf16", seed=c["seed"])
+        print(f"noalloc case: {c['seqs']} tokens, {h_q}/{h_kv} heads, D = {head_dim}", flush=True)
         gb = P.gpu_build(wl)
         dt = torch.bfloat16
         q, k, v, g = (P.to_dev(x, dt) for x in (wl.q, wl.k, wl.v, wl.gates))
