@@ -800,16 +800,24 @@ cmp_mfma_kernel(FwdParams p) {
     // must fit 16 bits
     const bool overflow = over || cnt + cnt_other > kCap - 1 || n_kt * kKeyTile > 65536;
 
-    // exact float32 logits of this lane's candidates into the high key words
-    const int mine0 = qbase + (half ? kCap + 1 - cnt : 1);
-    if (B.valid && !overflow && cnt > 0) {
+    // the query's candidates as one list of tot entries: half 0's at slots
+    // 1 .. cnt0, then half 1's at kCap + 1 - cnt1 .. kCap; the two lanes of
+    // the query take alternate entries for the exact logits and the ranks,
+    // so both run the same number of steps whichever lane found them
+    const int tot = cnt + cnt_other;
+    const int cnt0 = half ? cnt_other : cnt;
+    const int tail0 = qbase + kCap + 1 - tot;   // slot of entry i >= cnt0 is tail0 + i
+    auto slot_of = [&](int i) { return i < cnt0 ? qbase + 1 + i : tail0 + i; };
+    wave_lds_sync();   // each lane now reads block ids the other lane of its query wrote
+    // exact float32 logits of the candidates into the high key words
+    if (B.valid && !overflow && tot > 0) {
       // products of bf16 pairs are exact in float32 (v_dot2_f32_bf16); four
       // partial sums keep the dependent chains short
       u32x4 qw[kD / 8];
 #pragma unroll
       for (int c = 0; c < kD / 8; ++c) qw[c] = *reinterpret_cast<const u32x4*>(B.q_row + 8 * c);
-      for (int i = 0; i < cnt; ++i) {
-        uint32_t* const slot = reinterpret_cast<uint32_t*>(cand_key + mine0 + i);
+      for (int i = half; i < tot; i += 2) {
+        uint32_t* const slot = reinterpret_cast<uint32_t*>(cand_key + slot_of(i));
         const uint16_t* kr = kb0 + static_cast<int64_t>(~slot[0]) * kD;
         float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -844,8 +852,8 @@ cmp_mfma_kernel(FwdParams p) {
         keys[e + 1] = (static_cast<uint64_t>(u[3]) << 32) | u[2];
       }
       const int jbase = kt0 * kKeyTile;
-      for (int i = 0; i < cnt; ++i) {
-        const uint64_t ck = cand_key[mine0 + i];
+      for (int i = half; i < tot; i += 2) {
+        const uint64_t ck = cand_key[slot_of(i)];
         int rank = 0;
 #pragma unroll
         for (int e = 0; e < kSlots; ++e) rank += keys[e] > ck ? 1 : 0;
